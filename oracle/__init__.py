@@ -55,7 +55,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 OK, WARN_RAW = 0, 1
 ERR_ARG, ERR_SHAPE, ERR_NONFINITE, ERR_TARGET, ERR_FORMAT, ERR_NOMEM = -1, -2, -3, -4, -5, -7
 BF16, FP16, FP8, INT8 = 0, 1, 2, 3
-PROB_BITS = 11
+PROB_BITS = 10
 N_STATES = 64
 TILE_VECS = 1024
 STATE_L = 1 << 14
