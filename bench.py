@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Decode-throughput benchmark for the fused lattice-rANS tile decoder.
+
+A step is one fused decode (every tile of one compressed matrix, decoded and
+reconstructed into its container) with the stream already resident in HBM.
+Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Timing:
+  * steps: K decodes captured in one HIP graph and replayed; the decodes
+    rotate over enough stream/output copies (> 2x the 256 MB MALL) that each
+    decode reads and writes HBM, not the Infinity Cache;
+  * kernel duration (roofline): HIP events on the launch stream around the
+    K replayed decodes, divided by K;
+  * cpu_baseline: the CPU oracle's decoder on the same stream, single thread.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decoded Gparams/s + achieved HBM GB/s vs peak, 4096x4096 BF16 @ 4.0 bpp"
+PEAK_HBM_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ep_decode_bf16_4096x4096_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "decode_tile_interleaved_amd", "csrc", "ep_decode.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_algorithmic: float):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(blob, numel: int):
+    import oracle
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.decompress_raw(blob)
+        runs.append(time.perf_counter() - t0)
+    t = statistics.median(runs)
+    return {"value": round(numel / t / 1e9, 5), "unit": "Gparams/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole stream ({numel} params), median of 3 single-thread decodes incl. reconstruction"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="rowscale4096_bf16_4.0")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager-only", action="store_true", help="skip the graph replay (profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (steps times), to calibrate HBM byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this decoder is benchmarked on one GPU; --gpus {args.gpus} is not supported "
+              "(tiles decode independently, so more GPUs would each decode their own matrices)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from decode_tile_interleaved_amd import ep
+    from decode_tile_interleaved_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(7)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "steps": args.steps}), flush=True)
+        return 0
+    x, target = W.make(args.workload)
+    rows, cols = x.shape
+    numel = rows * cols
+    t0 = time.perf_counter()
+    p = ep.compress(x, target)
+    encode_s = time.perf_counter() - t0
+    out_bytes = numel * x.element_size()
+    alg_bytes = p.nbytes + out_bytes  # stream read once + reconstruction written once
+
+    # resident copies, rotated so that each decode misses the MALL
+    copies = max(2, math.ceil(2 * MALL_BYTES / alg_bytes))
+    blobs = [torch.from_numpy(p.blob).to(dev) for _ in range(copies)]
+    outs = [torch.empty(rows, cols, dtype=x.dtype, device=dev) for _ in range(copies)]
+    packs = [ep.Packed(blob=p.blob, status=p.status, shape=p.shape, dtype=p.dtype, dev=b) for b in blobs]
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        ep.decompress(packs[i % copies], out=outs[i % copies], stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    stream.synchronize()
+
+    # per-launch event pairs around eager launches (context: these include
+    # each launch's event overhead, which back-to-back replay does not)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][1].record(stream)
+    stream.synchronize()
+    eager_ms = statistics.mean(a.elapsed_time(b) for a, b in ev)
+
+    # timed region: K decodes replayed from one graph, bracketed by HIP events
+    # on the launch stream and by device synchronization
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.eager_only:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            t_start.record(stream)
+            for i in range(args.steps):
+                step(i)
+            t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                step(i)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            t_start.record(stream)
+            g.replay()
+            t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    kernel_ms = t_start.elapsed_time(t_end) / args.steps  # average launch duration over the timed region
+    ms_per_step = wall * 1e3 / args.steps
+
+    # the last decode of each copy must equal a fresh eager decode
+    ref = ep.decompress(packs[0], stream=stream)
+    stream.synchronize()
+    for o in outs[: min(copies, args.steps)]:
+        assert torch.equal(o.view(torch.int16 if o.element_size() == 2 else torch.int8),
+                           ref.view(torch.int16 if ref.element_size() == 2 else torch.int8))
+    rel_l2 = ((ref.double() - x.double().to(dev)).norm() / x.double().to(dev).norm()).item()
+
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic(alg_bytes)
+    line = {
+        "metric": METRIC,
+        "value": round(numel / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gparams/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32+f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": rows, "cols": cols, "container": str(x.dtype).split(".")[-1],
+                   "target_bpp": target, "actual_bpp": round(p.actual_bpp, 5), "stream_bytes": p.nbytes,
+                   "tile": "1024 E8 vectors (8x1024 coords), 64 rANS states", "mall_rotation_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
+        "kernel_us": round(kernel_ms * 1e3, 3),
+        "kernel_us_eager_events": round(eager_ms * 1e3, 3),
+        "hbm_gbps_per_step": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "rel_l2": round(rel_l2, 5),
+        "encode_s": round(encode_s, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(p.blob, numel)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

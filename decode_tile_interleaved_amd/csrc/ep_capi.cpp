@@ -1,0 +1,121 @@
+// ep_capi.cpp -- host half of the C ABI: compression, stream facts, errors.
+// The GPU entry points (ep_decompress, ep_decode_symbols) live in ep_decode.hip.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ep.h"
+#include "ep_encode.hpp"
+#include "ep_stream.hpp"
+
+namespace ep {
+static thread_local std::string g_error;
+void set_error(const std::string &msg) { g_error = msg; }
+}  // namespace ep
+
+extern "C" {
+
+int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
+                   const struct ep_options *opt, uint8_t **blob_out, size_t *nbytes_out) {
+  ep::set_error("");
+  if (!blob_out || !nbytes_out) {
+    ep::set_error("null output pointer");
+    return EP_ERR_ARG;
+  }
+  double fixed_a = 0.0;
+  int threads = 0;
+  if (opt) {
+    for (int r : opt->reserved)
+      if (r != 0) {
+        ep::set_error("ep_options.reserved must be zero");
+        return EP_ERR_ARG;
+      }
+    fixed_a = opt->fixed_scale;
+    threads = opt->n_threads;
+    if (!(fixed_a >= 0.0) || std::isinf(fixed_a)) {
+      ep::set_error("fixed_scale must be finite and >= 0");
+      return EP_ERR_ARG;
+    }
+  }
+  std::vector<uint8_t> blob;
+  std::string err;
+  int rc;
+  try {
+    rc = ep::compress(host_src, dtype, rows, cols, target_bpp, fixed_a, threads, blob, err);
+  } catch (const std::bad_alloc &) {
+    ep::set_error("host allocation failed");
+    return EP_ERR_NOMEM;
+  }
+  if (rc < 0) {
+    ep::set_error(err);
+    return rc;
+  }
+  uint8_t *out = (uint8_t *)std::malloc(blob.size());
+  if (!out) {
+    ep::set_error("host allocation failed");
+    return EP_ERR_NOMEM;
+  }
+  std::memcpy(out, blob.data(), blob.size());
+  *blob_out = out;
+  *nbytes_out = blob.size();
+  if (rc > 0) ep::set_error(err);
+  return rc;
+}
+
+int ep_compress(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp, uint8_t **blob_out,
+                size_t *nbytes_out) {
+  return ep_compress_ex(host_src, dtype, rows, cols, target_bpp, nullptr, blob_out, nbytes_out);
+}
+
+void ep_free(uint8_t *blob) { std::free(blob); }
+
+int ep_blob_info(const uint8_t *blob, size_t nbytes, struct ep_info *info) {
+  ep::set_error("");
+  ep::StreamView s;
+  std::string e = ep::parse_stream(blob, nbytes, s);
+  if (!e.empty()) {
+    ep::set_error(e);
+    return EP_ERR_FORMAT;
+  }
+  if (!info) {
+    ep::set_error("null info pointer");
+    return EP_ERR_ARG;
+  }
+  info->rows = s.rows;
+  info->cols = s.cols;
+  info->dtype = s.dtype;
+  info->method = s.method;
+  info->n_states = s.states;
+  info->prob_bits = s.prob_bits;
+  info->n_tiles = s.tiles;
+  info->n_words = (int64_t)s.n_words;
+  info->scale_a = s.scale_a;
+  info->target_bpp = s.target;
+  return EP_OK;
+}
+
+double ep_actual_bpp(const uint8_t *blob, size_t nbytes) {
+  ep::StreamView s;
+  std::string e = ep::parse_stream(blob, nbytes, s);
+  if (!e.empty()) {
+    ep::set_error(e);
+    return NAN;
+  }
+  return 8.0 * (double)nbytes / ((double)s.rows * (double)s.cols);
+}
+
+int64_t ep_storage_nbytes(const uint8_t *blob, size_t nbytes, int include_header) {
+  ep::StreamView s;
+  std::string e = ep::parse_stream(blob, nbytes, s);
+  if (!e.empty()) {
+    ep::set_error(e);
+    return -1;
+  }
+  return include_header ? (int64_t)nbytes : (int64_t)nbytes - (int64_t)ep::kHeaderBytes;
+}
+
+const char *ep_last_error(void) { return ep::g_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,594 @@
+// ep_decode.hip -- fused lattice-rANS tile decode and weight reconstruction
+// for gfx950 (MI355X).
+//
+// The EntroPack abstract (mlsanity index page) states that the coordinates
+// are entropy-coded in independently decodable tiles so that symbol decoding
+// and numerical reconstruction fuse on the GPU.  This file is that pass.
+//
+// Work mapping: one wavefront per tile of 1024 E8 vectors; lane q owns rANS
+// state q and decodes local vectors q, q+64, ..., so every step's 64 vectors
+// are contiguous and each lane writes one 8-coordinate vector per step
+// (16 bytes for BF16/FP16, 8 bytes for FP8/INT8).
+//
+// Per workgroup (up to 8 waves, one workgroup per CU):
+//   1. every wave starts its global loads: its tile's state and row scales,
+//      one context's frequencies, and its tile's words straight into LDS
+//      (global_load_lds_dwordx4);
+//   2. one wave per context prefix-sums the frequencies (DPP scan), lists the
+//      used symbols, sets a bitmap of the slots where a symbol starts, and
+//      expands the context's table one 64-slot row at a time: a slot's symbol
+//      is the number of starts up to it, which v_mbcnt counts from the row's
+//      bitmap;
+//   3. each wave decodes its tile.
+//
+// Decode step for state x in [2^14, 2^30), kept as X = 4x so that the table
+// address is one AND-OR:  4*slot = X & 0xffc;  e = table[ctx][slot];
+//   x' = f * (x >> 10) + (slot - cum);  if x' < 2^14: x = x' << 16 | w
+// where w is the word the state holds in reserve.  After a refill the state
+// takes a new reserve word: refilling lanes take consecutive words in lane
+// order (ballot + mbcnt), so the word fetch never sits on the chain from one
+// table lookup to the next.
+//
+// Table entries (one dword per slot and context, 2^10 slots per context):
+//   narrow (every used value in [-128, 127]): two arrays 28 KB apart,
+//     d0 = 4f | (v + 128) << 24 and d1 = 4 (slot - cum), so that
+//     X' = mad_u32_u24(d0, X >> 12, d1) needs no unpacking and the value
+//     converts with one v_cvt_f32_ubyte3;
+//   wide (values in [-2048, 2047]): e = f | (slot - cum) << 10 | v << 20.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ep.h"
+#include "ep_encode.hpp"
+#include "ep_stream.hpp"
+
+namespace ep {
+namespace {
+
+constexpr int kMaxWaves = 8;
+constexpr uint32_t kTableDwords = kContexts * kProbTotal;  // 7168
+constexpr uint32_t kTableBytes = kTableDwords * 4;         // 28672
+constexpr uint32_t kRows = kProbTotal / 64;                // 16 rows of 64 slots per context
+constexpr uint32_t kMarkWords = kProbTotal / 32;           // 32 bitmap words per context
+constexpr uint32_t kLdsLimit = 160 * 1024;
+constexpr uint32_t kLdsPad = 256;  // slack after the last word buffer for reads of lanes that do not refill
+constexpr int kOutSym = 4;         // int16 lattice coordinates; 0..3 are the container dtypes
+constexpr uint32_t kWordLoads = 8;  // fixed 16-byte-per-lane loads per tile: 8 KB of words
+
+static_assert(kProbBits == 10, "table addressing below assumes 2^10 slots per context");
+
+struct Args {
+  const uint8_t *blob;
+  void *out;
+  uint64_t off_freq, off_scales, off_states, off_tile_offsets, off_words;
+  uint64_t cols;                  // columns of the output (padded layouts only)
+  uint32_t rows, vpr;             // rows; vectors per row
+  uint32_t row_magic, row_shift;  // vec / vpr = umulhi(vec, row_magic) >> row_shift  (vpr > 1)
+  uint32_t n_vec, n_tiles;
+  uint32_t rec_off, mark_off, words_off, wave_buf_bytes;  // LDS byte offsets
+  int32_t smin[kContexts];
+  uint32_t nsym[kContexts];
+  uint32_t fidx[kContexts];
+  uint32_t nzbase[kContexts];
+};
+
+typedef __attribute__((address_space(1))) void *gptr_t;
+typedef __attribute__((address_space(3))) void *lptr_t;
+typedef __attribute__((address_space(3))) const uint32_t *lds_u32_ptr;
+typedef __attribute__((address_space(3))) const uint16_t *lds_u16_ptr;
+
+// LDS loads by byte address; the decode kernel declares no static LDS, so its
+// dynamic LDS starts at address 0
+__device__ __forceinline__ uint32_t lds_u32(uint32_t byte) { return *(lds_u32_ptr)(uintptr_t)byte; }
+__device__ __forceinline__ uint32_t lds_u16(uint32_t byte) { return *(lds_u16_ptr)(uintptr_t)byte; }
+
+// hides a value from constant folding so that address arithmetic stays one v_and_or_b32
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// inclusive prefix sum over the 16 lanes of each DPP row
+__device__ __forceinline__ uint32_t row16_inclusive_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return v;
+}
+
+// inclusive prefix sum over the wavefront
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  v = row16_inclusive_sum(v);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+__device__ __forceinline__ int32_t symbol_value(uint32_t c, int32_t s) {
+  if (c == 0) return s;
+  if (c <= 2) return 2 * s + (int32_t)(c - 1);
+  const int32_t bp = (int32_t)c - 3;  // 2b + p
+  return 4 * s + 2 * (bp & 1) + (bp >> 1);
+}
+
+// one rANS decode step of every active lane; returns the table entry.
+// res holds each state's reserve word; wp (wave-uniform) is the LDS byte
+// address of the next unread word.
+template <bool WIDE>
+__device__ __forceinline__ uint32_t rans_step(uint32_t &X, uint32_t &res, uint32_t &wp, uint32_t ctx_base,
+                                              bool active) {
+  const uint32_t res4 = res << 2;  // off the chain: the reserve word arrived a step ago
+  const uint32_t a = (X & 0xffcu) | ctx_base;
+  const uint32_t q = X >> 12;
+  const uint32_t d0 = lds_u32(a);
+  uint32_t x;
+  if constexpr (WIDE) {
+    x = (__umul24(d0 & 0x3ffu, q) + ((d0 >> 10) & 0x3ffu)) << 2;
+  } else {
+    x = __umul24(d0, q) + lds_u32(a + kTableBytes);
+  }
+  const bool need = active && x < 0x10000u;
+  const uint32_t xr = (x << 16) | res4;
+  X = active ? (need ? xr : x) : X;
+  const uint64_t m = __ballot(need);
+  const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  // every lane reads (no branch); lanes that did not refill keep their word
+  const uint32_t w = lds_u16(wp + 2u * rank);
+  res = need ? w : res;
+  wp += 2u * (uint32_t)__popcll(m);
+  return d0;
+}
+
+template <bool WIDE>
+__device__ __forceinline__ int32_t entry_value(uint32_t e) {
+  if constexpr (WIDE) return (int32_t)e >> 20;
+  return (int32_t)(e >> 24) - 128;
+}
+
+template <bool WIDE>
+__device__ __forceinline__ float entry_weight(uint32_t e, float g, float ng) {
+  if constexpr (WIDE) return (float)((int32_t)e >> 20) * g;
+  return __builtin_fmaf((float)(e >> 24), g, ng);  // (v + 128) g - 128 g, one rounding
+}
+
+__device__ __forceinline__ uint32_t int8_byte(float y) {
+  const float c = __builtin_fminf(__builtin_fmaxf(y, -127.0f), 127.0f);
+  return __float_as_uint(c + 12582912.0f);  // 1.5 * 2^23: rounds to an integer, ties to even
+}
+
+__device__ __forceinline__ float fp8_clamp(float y) { return __builtin_fminf(__builtin_fmaxf(y, -448.0f), 448.0f); }
+
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+template <int OUT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  f2v v = {a, b};
+  if constexpr (OUT == EP_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2v));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
+}
+
+// writes one decoded vector
+template <int OUT, bool WIDE, bool PADDED>
+__device__ __forceinline__ void emit_vector(const Args &A, uint32_t vec, const uint32_t (&e)[8], float g) {
+  if constexpr (OUT == kOutSym) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = ((uint32_t)entry_value<WIDE>(e[2 * k]) & 0xffffu) | ((uint32_t)entry_value<WIDE>(e[2 * k + 1]) << 16);
+    const u32x4 pk = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(pk, reinterpret_cast<u32x4 *>(A.out) + vec);
+    return;
+  } else {
+    const float ng = -128.0f * g;
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = entry_weight<WIDE>(e[j], g, ng);
+    if constexpr (!PADDED) {
+      if constexpr (OUT == EP_BF16 || OUT == EP_FP16) {
+        const u32x4 pk = {pack2<OUT>(y[0], y[1]), pack2<OUT>(y[2], y[3]), pack2<OUT>(y[4], y[5]), pack2<OUT>(y[6], y[7])};
+        __builtin_nontemporal_store(pk, reinterpret_cast<u32x4 *>(A.out) + vec);
+      } else if constexpr (OUT == EP_FP8_E4M3FN) {
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[0]), fp8_clamp(y[1]), 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[2]), fp8_clamp(y[3]), lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[4]), fp8_clamp(y[5]), 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[6]), fp8_clamp(y[7]), hi, true);
+        const u32x2 pk = {(uint32_t)lo, (uint32_t)hi};
+        __builtin_nontemporal_store(pk, reinterpret_cast<u32x2 *>(A.out) + vec);
+      } else {
+        uint32_t b[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = int8_byte(y[j]);
+        const uint32_t lo =
+            __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u) << 16);
+        const uint32_t hi =
+            __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u) << 16);
+        const u32x2 pk = {lo, hi};
+        __builtin_nontemporal_store(pk, reinterpret_cast<u32x2 *>(A.out) + vec);
+      }
+    } else {
+      const uint32_t r = vec / A.vpr, k = vec - r * A.vpr;
+      const uint64_t base = (uint64_t)r * A.cols + 8ull * k;
+      const uint32_t left = (uint32_t)(A.cols - 8ull * k);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if ((uint32_t)j >= left) break;
+        if constexpr (OUT == EP_BF16 || OUT == EP_FP16) {
+          reinterpret_cast<uint16_t *>(A.out)[base + j] = (uint16_t)(pack2<OUT>(y[j], 0.0f) & 0xffffu);
+        } else if constexpr (OUT == EP_FP8_E4M3FN) {
+          reinterpret_cast<uint8_t *>(A.out)[base + j] =
+              (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[j]), 0.0f, 0, false) & 0xff);
+        } else {
+          reinterpret_cast<uint8_t *>(A.out)[base + j] = (uint8_t)(int8_byte(y[j]) & 0xffu);
+        }
+      }
+    }
+  }
+}
+
+// decodes one tile; PARTIAL handles the last tile of a stream (n < 1024).
+// wp is the LDS byte address of the tile's first word.
+template <int OUT, bool WIDE, bool PADDED, bool PARTIAL>
+__device__ __forceinline__ void decode_tile(const Args &A, uint32_t wp, uint32_t X, uint32_t tile, uint32_t n,
+                                            const float (&gs)[16], uint32_t lane) {
+  const uint32_t n_act = PARTIAL ? (n < 64u ? n : 64u) : 64u;
+  uint32_t res = lane < n_act ? lds_u16(wp + 2u * lane) : 0u;
+  wp += 2u * n_act;
+#pragma unroll 1
+  for (uint32_t s = 0; s < 16; ++s) {
+    const bool act = PARTIAL ? (s * 64 + lane < n) : true;
+    if (PARTIAL && s * 64 >= n) break;
+    uint32_t e[8];
+    e[0] = rans_step<WIDE>(X, res, wp, 0u, act);
+    // the coset bit b = v0 & 1 selects C_b; entries keep v's low bits at bit 24 (narrow) or 20 (wide)
+    const uint32_t cb = opaque(WIDE ? (0x1000u + ((e[0] >> 8) & 0x1000u)) : (0x1000u + ((e[0] >> 12) & 0x1000u)));
+    e[1] = rans_step<WIDE>(X, res, wp, cb, act);
+    e[2] = rans_step<WIDE>(X, res, wp, cb, act);
+    uint32_t acc = e[0] ^ e[1] ^ e[2];
+    e[3] = rans_step<WIDE>(X, res, wp, cb, act);
+    e[4] = rans_step<WIDE>(X, res, wp, cb, act);
+    acc ^= e[3] ^ e[4];
+    e[5] = rans_step<WIDE>(X, res, wp, cb, act);
+    e[6] = rans_step<WIDE>(X, res, wp, cb, act);
+    acc ^= e[5] ^ e[6];
+    // E_{b,p}: p = parity of z0..z6 = bit 1 of v0 ^ .. ^ v6
+    const uint32_t eb = opaque(WIDE ? (0x3000u + ((e[0] >> 7) & 0x2000u) + ((acc >> 9) & 0x1000u))
+                                    : (0x3000u + ((e[0] >> 11) & 0x2000u) + ((acc >> 13) & 0x1000u)));
+    e[7] = rans_step<WIDE>(X, res, wp, eb, act);
+    if (act) emit_vector<OUT, WIDE, PADDED>(A, tile * 1024u + s * 64u + lane, e, gs[s]);
+  }
+}
+
+template <int OUT, bool WIDE, bool PADDED>
+__global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t nwaves = blockDim.x >> 6;
+  const uint32_t tile = blockIdx.x * nwaves + wave;
+  const bool has_tile = tile < A.n_tiles;
+  const uint32_t tc = has_tile ? tile : A.n_tiles - 1u;  // waves without a tile load a valid one and drop it
+
+  // ---- 1. global loads, all unconditional so that each wait is exact ----
+  const uint32_t *toff = reinterpret_cast<const uint32_t *>(A.blob + A.off_tile_offsets);
+  const uint32_t w_begin = toff[tc], w_end = toff[tc + 1];
+  const uint32_t x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tc * 64u + lane];
+  float gs[16];
+  {
+    const float *scales = reinterpret_cast<const float *>(A.blob + A.off_scales);
+    const uint32_t last = A.rows - 1u, one = A.vpr == 1u ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const uint32_t vec = tc * 1024u + 64u * s + lane;
+      const uint32_t r = ((__umulhi(vec, A.row_magic) >> A.row_shift) & ~one) | (vec & one);
+      gs[s] = scales[r < last ? r : last];  // lanes past the end read the last row; their values are unused
+    }
+  }
+  // the first 256 frequencies of this wave's first context
+  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
+  const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
+  uint32_t fpre[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t s = 64u * i + lane;
+    const uint32_t v = freq[A.fidx[c0] + (s < A.nsym[c0] ? s : 0u)];
+    fpre[i] = s < A.nsym[c0] ? v : 0u;
+  }
+  // the tile's words go straight from global memory into this wave's LDS
+  // buffer (global_load_lds_dwordx4: lane i of load j fills bytes
+  // 1024 j + 16 i ..+15); lanes past the tile re-read its last chunk
+  const uint64_t byte0 = A.off_words + 2ull * w_begin;
+  const uint64_t abyte0 = byte0 & ~15ull;
+  const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * w_end + 15ull) & ~15ull) - abyte0) >> 4);
+  const uint32_t wb = A.words_off + wave * A.wave_buf_bytes;  // LDS byte address of this wave's words
+  {
+    const uint8_t *src = A.blob + abyte0;
+#pragma unroll
+    for (uint32_t i = 0; i < kWordLoads; ++i) {
+      const uint32_t ch = lane + 64u * i;
+      __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (ch < nchunks ? ch : nchunks - 1u)),
+                                       (lptr_t)(lds + wb + 1024u * i), 16, 0, 0);
+    }
+    for (uint32_t i = kWordLoads; 64u * i < nchunks; ++i)  // tiles longer than the fixed loads cover
+      if (lane + 64u * i < nchunks)
+        __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (lane + 64u * i)), (lptr_t)(lds + wb + 1024u * i), 16, 0,
+                                         0);
+  }
+
+  // ---- 2. one wave per context: prefix sums, used-symbol records, start
+  //         bitmap, then the context's 16 table rows of 64 slots ----------
+  uint2 *rec = reinterpret_cast<uint2 *>(lds + A.rec_off);          // (d0, cum term) per used symbol
+  uint32_t *mark = reinterpret_cast<uint32_t *>(lds + A.mark_off);  // [ctx][32] start bits
+  uint32_t *tab = reinterpret_cast<uint32_t *>(lds);
+  for (uint32_t c = wave; c < (uint32_t)kContexts; c += nwaves) {
+    const uint32_t n = A.nsym[c];
+    if (n == 0u) continue;  // context without symbols: its table is never read
+    if (lane < kMarkWords) mark[c * kMarkWords + lane] = 0u;
+    uint32_t carry = 0, nzb = A.nzbase[c];
+    for (uint32_t base = 0, it = 0; base < n; base += 64, ++it) {
+      const uint32_t s = base + lane;
+      uint32_t f;
+      if (c == wave && it < 4) f = it == 0 ? fpre[0] : it == 1 ? fpre[1] : it == 2 ? fpre[2] : fpre[3];
+      else f = s < n ? freq[A.fidx[c] + s] : 0u;
+      const uint32_t incl = wave_inclusive_sum(f);
+      const uint32_t cum = carry + incl - f;
+      const bool used = f != 0;
+      const uint64_t m = __ballot(used);
+      const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nzb));
+      if (used && cum < kProbTotal) {
+        const int32_t v = symbol_value(c, A.smin[c] + (int32_t)s);
+        rec[r] = WIDE ? make_uint2(f | ((uint32_t)v & 0xfffu) << 20, cum)
+                      : make_uint2((f << 2) | ((uint32_t)(v + 128) & 0xffu) << 24, cum << 2);
+        atomicOr(&mark[c * kMarkWords + (cum >> 5)], 1u << (cum & 31u));
+      }
+      carry += __builtin_amdgcn_readlane(incl, 63);
+      nzb += (uint32_t)__popcll(m);
+    }
+    // lane t < 16 holds row t: its start bits and the record index before it
+    uint32_t lo = 0, hi = 0;
+    if (lane < kRows) {
+      lo = mark[c * kMarkWords + 2 * lane];
+      hi = mark[c * kMarkWords + 2 * lane + 1];
+    }
+    const uint32_t cnt = (uint32_t)(__popc(lo) + __popc(hi));
+    const uint32_t first = A.nzbase[c] + row16_inclusive_sum(cnt) - cnt;
+    // slot record = first + (starts at or below the slot) - 1
+    //             = first + bit0 - 1 + popcount of (bits >> 1) below the lane
+#pragma unroll
+    for (uint32_t row = 0; row < kRows; ++row) {
+      const uint32_t rlo = __builtin_amdgcn_readlane(lo, row), rhi = __builtin_amdgcn_readlane(hi, row);
+      const uint32_t rfirst = __builtin_amdgcn_readlane(first, row);
+      const uint64_t sh = (((uint64_t)rhi << 32) | rlo) >> 1;
+      const uint32_t k = __builtin_amdgcn_mbcnt_hi((uint32_t)(sh >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)sh, rfirst + (rlo & 1u) - 1u));
+      const uint2 rc = rec[k];
+      const uint32_t slot = row * 64u + lane, idx = c * kProbTotal + slot;
+      if (WIDE) {
+        tab[idx] = rc.x | ((slot - rc.y) << 10);
+      } else {
+        tab[idx] = rc.x;
+        tab[kTableDwords + idx] = (slot << 2) - rc.y;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's words have landed in LDS
+  __syncthreads();
+
+  // ---- 3. decode ---------------------------------------------------------
+  if (!has_tile) return;
+  const uint32_t wp = wb + (uint32_t)(byte0 - abyte0);
+  const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
+  const uint32_t X = x0 << 2;
+  if (n == 1024u)
+    decode_tile<OUT, WIDE, PADDED, false>(A, wp, X, tile, n, gs, lane);
+  else
+    decode_tile<OUT, WIDE, PADDED, true>(A, wp, X, tile, n, gs, lane);
+}
+
+typedef void (*KernelFn)(Args);
+
+template <int OUT>
+KernelFn pick(bool wide, bool padded) {
+  if (wide) return padded ? decode_kernel<OUT, true, true> : decode_kernel<OUT, true, false>;
+  return padded ? decode_kernel<OUT, false, true> : decode_kernel<OUT, false, false>;
+}
+
+KernelFn pick_kernel(int out, bool wide, bool padded) {
+  switch (out) {
+    case EP_BF16: return pick<EP_BF16>(wide, padded);
+    case EP_FP16: return pick<EP_FP16>(wide, padded);
+    case EP_FP8_E4M3FN: return pick<EP_FP8_E4M3FN>(wide, padded);
+    case EP_INT8: return pick<EP_INT8>(wide, padded);
+    default: return pick<kOutSym>(wide, false);
+  }
+}
+
+int32_t host_symbol_value(int c, int32_t s) {
+  if (c == 0) return s;
+  if (c <= 2) return 2 * s + (c - 1);
+  const int bp = c - 3;
+  return 4 * s + 2 * (bp & 1) + (bp >> 1);
+}
+
+// magic number for n / d with n < 2^31: umulhi(n, m) >> (s - 1), s = ceil(log2 d), d >= 2
+void row_divider(uint32_t d, uint32_t &m, uint32_t &shift) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  m = (uint32_t)(((uint64_t(1) << (31 + s)) + d - 1) / d);
+  shift = s - 1;
+}
+
+// host-side checks and launch geometry; returns 0 or an ep_status
+int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *dev_out, int out, hipStream_t stream) {
+  if (!dev_blob || !dev_out) {
+    set_error("null device pointer");
+    return EP_ERR_ARG;
+  }
+  if (((uintptr_t)dev_blob & 15) || ((uintptr_t)dev_out & 15)) {
+    set_error("device buffers must be 16-byte aligned");
+    return EP_ERR_ARG;
+  }
+  if (s.n_vec >= (int64_t(1) << 31) || s.rows >= (int64_t(1) << 31)) {
+    set_error("stream too large");
+    return EP_ERR_FORMAT;
+  }
+  // tile offsets: monotone, inside the word section, enough reserve words
+  const uint8_t *toff = hb + s.off_tile_offsets;
+  uint64_t max_span = 0;
+  for (int64_t t = 0; t < s.tiles; ++t) {
+    const uint32_t b = rd<uint32_t>(toff + 4 * t), e = rd<uint32_t>(toff + 4 * t + 4);
+    const int64_t n = std::min<int64_t>(kTileVecs, s.n_vec - t * kTileVecs);
+    if (e < b || e > s.n_words || (int64_t)(e - b) < std::min<int64_t>(n, 64)) {
+      set_error("corrupt tile offsets");
+      return EP_ERR_FORMAT;
+    }
+    const uint64_t a0 = (s.off_words + 2ull * b) & ~15ull, a1 = (s.off_words + 2ull * e + 15ull) & ~15ull;
+    max_span = std::max<uint64_t>(max_span, a1 - a0);
+  }
+  if (rd<uint32_t>(toff + 4 * s.tiles) != s.n_words) {
+    set_error("corrupt tile offsets");
+    return EP_ERR_FORMAT;
+  }
+  // tables: frequencies sum to 2^10, used values inside the entry field
+  Args A{};
+  bool wide = false;
+  uint32_t nz_total = 0;
+  for (int c = 0; c < kContexts; ++c) {
+    A.smin[c] = s.smin[c];
+    A.nsym[c] = s.nsym[c];
+    A.fidx[c] = (uint32_t)s.freq_index[c];
+    A.nzbase[c] = nz_total;
+    uint32_t sum = 0;
+    for (uint32_t i = 0; i < s.nsym[c]; ++i) {
+      const uint16_t f = rd<uint16_t>(hb + s.off_freq + 2 * (s.freq_index[c] + i));
+      if (!f) continue;
+      sum += f;
+      ++nz_total;
+      const int32_t v = host_symbol_value(c, s.smin[c] + (int32_t)i);
+      if (v < kValueMin || v > kValueMax || f >= kProbTotal) {
+        set_error("table entry outside the decoder's range");
+        return EP_ERR_FORMAT;
+      }
+      if (v < -128 || v > 127) wide = true;
+    }
+    if (s.nsym[c] && sum != kProbTotal) {
+      set_error("frequencies do not sum to 2^10");
+      return EP_ERR_FORMAT;
+    }
+  }
+  // LDS layout: tables | records | bitmap | word buffers | pad
+  uint32_t off = wide ? kTableBytes : 2 * kTableBytes;
+  A.rec_off = off;
+  off += 8 * nz_total;
+  A.mark_off = off;
+  off = (uint32_t)align16(off + 4 * kContexts * kMarkWords);
+  A.words_off = off;
+  // the fixed word loads write kWordLoads KB per wave whatever the tile's length
+  A.wave_buf_bytes = (uint32_t)std::max<uint64_t>(max_span, 1024ull * kWordLoads);
+  if (off + A.wave_buf_bytes + kLdsPad > kLdsLimit) {
+    set_error("tile too large for the decoder's LDS budget");
+    return EP_ERR_FORMAT;
+  }
+  const uint32_t waves = (uint32_t)std::min<uint64_t>(kMaxWaves, (kLdsLimit - off - kLdsPad) / A.wave_buf_bytes);
+  const uint32_t lds_bytes = off + waves * A.wave_buf_bytes + kLdsPad;
+  A.blob = reinterpret_cast<const uint8_t *>(dev_blob);
+  A.out = dev_out;
+  A.off_freq = s.off_freq;
+  A.off_scales = s.off_scales;
+  A.off_states = s.off_states;
+  A.off_tile_offsets = s.off_tile_offsets;
+  A.off_words = s.off_words;
+  A.cols = (uint64_t)s.cols;
+  A.rows = (uint32_t)s.rows;
+  A.vpr = (uint32_t)(s.cols8 / 8);
+  if (A.vpr > 1) row_divider(A.vpr, A.row_magic, A.row_shift);
+  A.n_vec = (uint32_t)s.n_vec;
+  A.n_tiles = (uint32_t)s.tiles;
+  const bool padded = out != kOutSym && (s.cols % 8) != 0;
+  KernelFn fn = pick_kernel(out, wide, padded);
+  static std::mutex mu;
+  static std::vector<KernelFn> configured;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    bool done = false;
+    for (KernelFn k : configured) done |= k == fn;
+    if (!done) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kLdsLimit) != hipSuccess) {
+        set_error("hipFuncSetAttribute failed");
+        return EP_ERR_DEVICE;
+      }
+      configured.push_back(fn);
+    }
+  }
+  const uint32_t grid = (uint32_t)((s.tiles + waves - 1) / waves);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * waves), lds_bytes, stream, A);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    set_error(std::string("kernel launch failed: ") + hipGetErrorString(err));
+    return EP_ERR_DEVICE;
+  }
+  return EP_OK;
+}
+
+}  // namespace
+}  // namespace ep
+
+extern "C" {
+
+int ep_decompress(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, void *dev_out, int out_dtype,
+                  void *hip_stream) {
+  ep::set_error("");
+  ep::StreamView s;
+  std::string e = ep::parse_stream(host_blob, nbytes, s);
+  if (!e.empty()) {
+    ep::set_error(e);
+    return EP_ERR_FORMAT;
+  }
+  if (out_dtype != -1 && out_dtype != s.dtype) {
+    ep::set_error("out_dtype must be -1 or the container dtype");
+    return EP_ERR_ARG;
+  }
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  if (s.method == ep::kRaw) {
+    if (!dev_blob || !dev_out) {
+      ep::set_error("null device pointer");
+      return EP_ERR_ARG;
+    }
+    const size_t payload = (size_t)s.rows * (size_t)s.cols * ep::elem_bytes(s.dtype);
+    if (hipMemcpyAsync(dev_out, reinterpret_cast<const uint8_t *>(dev_blob) + ep::kHeaderBytes, payload,
+                       hipMemcpyDeviceToDevice, stream) != hipSuccess) {
+      ep::set_error("hipMemcpyAsync failed");
+      return EP_ERR_DEVICE;
+    }
+    return EP_OK;
+  }
+  return ep::launch(host_blob, s, dev_blob, dev_out, s.dtype, stream);
+}
+
+int ep_decode_symbols(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, int16_t *dev_sym,
+                      void *hip_stream) {
+  ep::set_error("");
+  ep::StreamView s;
+  std::string e = ep::parse_stream(host_blob, nbytes, s);
+  if (!e.empty()) {
+    ep::set_error(e);
+    return EP_ERR_FORMAT;
+  }
+  if (s.method != ep::kLattice) {
+    ep::set_error("raw streams hold no lattice symbols");
+    return EP_ERR_ARG;
+  }
+  return ep::launch(host_blob, s, dev_blob, dev_sym, ep::kOutSym, reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+"""Thin ctypes binding to libep.so (include/ep.h).
+
+Argument marshalling only: every step of compression runs in the library's
+host encoder and every step of decompression runs in its gfx950 kernels.
+PyTorch supplies host/device buffers and the current HIP stream.  There is
+no fallback: if libep.so is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libep.so")
+
+BF16, FP16, FP8_E4M3FN, INT8 = 0, 1, 2, 3
+OK, WARN_RAW = 0, 1
+ERR_ARG, ERR_SHAPE, ERR_NONFINITE, ERR_TARGET, ERR_FORMAT, ERR_DEVICE, ERR_NOMEM = -1, -2, -3, -4, -5, -6, -7
+
+_DTYPE_CODE = {torch.bfloat16: BF16, torch.float16: FP16, torch.float8_e4m3fn: FP8_E4M3FN, torch.int8: INT8}
+_CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
+
+EXPORTS = ["ep_compress", "ep_compress_ex", "ep_free", "ep_decompress", "ep_decode_symbols", "ep_actual_bpp",
+           "ep_storage_nbytes", "ep_blob_info", "ep_last_error"]
+
+
+class EPError(RuntimeError):
+    def __init__(self, code: int, what: str, msg: str):
+        super().__init__(f"{what} failed ({code}): {msg}")
+        self.code = code
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("fixed_scale", ctypes.c_double), ("n_threads", ctypes.c_int), ("reserved", ctypes.c_int * 6)]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("dtype", ctypes.c_int), ("method", ctypes.c_int),
+                ("n_states", ctypes.c_int), ("prob_bits", ctypes.c_int), ("n_tiles", ctypes.c_int64),
+                ("n_words", ctypes.c_int64), ("scale_a", ctypes.c_double), ("target_bpp", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libep.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with decode_tile_interleaved_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        L.ep_compress.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                  ctypes.POINTER(u8p), ctypes.POINTER(ctypes.c_size_t)]
+        L.ep_compress_ex.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                     ctypes.POINTER(_Options), ctypes.POINTER(u8p), ctypes.POINTER(ctypes.c_size_t)]
+        L.ep_free.argtypes = [u8p]
+        L.ep_free.restype = None
+        L.ep_decompress.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+        L.ep_decode_symbols.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+        L.ep_actual_bpp.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+        L.ep_actual_bpp.restype = ctypes.c_double
+        L.ep_storage_nbytes.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        L.ep_storage_nbytes.restype = ctypes.c_int64
+        L.ep_blob_info.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(_Info)]
+        L.ep_last_error.argtypes = []
+        L.ep_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().ep_last_error().decode()
+
+
+def _check(code: int, what: str) -> int:
+    if code < 0:
+        raise EPError(code, what, last_error())
+    return code
+
+
+@dataclass
+class Packed:
+    """A compressed matrix: the stream on the host, optionally on a device."""
+    blob: np.ndarray                  # uint8 stream (host)
+    status: int                       # OK or WARN_RAW
+    shape: tuple
+    dtype: torch.dtype
+    dev: torch.Tensor | None = None   # the same bytes on a GPU
+
+    @property
+    def nbytes(self) -> int:
+        return int(self.blob.size)
+
+    @property
+    def actual_bpp(self) -> float:
+        return actual_bpp(self.blob)
+
+    def info(self) -> dict:
+        return blob_info(self.blob)
+
+    def to(self, device) -> "Packed":
+        """Copies the stream to `device` (a torch uint8 tensor)."""
+        self.dev = torch.from_numpy(self.blob).to(device)
+        return self
+
+
+def _host_ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def compress(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, n_threads: int = 0) -> Packed:
+    """ep_compress_ex on a 2-D CPU tensor (BF16, FP16, FP8-E4M3FN or INT8)."""
+    if t.dtype not in _DTYPE_CODE:
+        raise EPError(ERR_ARG, "compress", f"unsupported dtype {t.dtype}")
+    if t.dim() != 2:
+        raise EPError(ERR_SHAPE, "compress", "input must be 2-D")
+    t = t.detach().to("cpu").contiguous()
+    opt = _Options(float(fixed_scale), int(n_threads), (ctypes.c_int * 6)())
+    out = ctypes.POINTER(ctypes.c_uint8)()
+    nb = ctypes.c_size_t(0)
+    src = t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16)
+    rc = lib().ep_compress_ex(ctypes.c_void_p(src.data_ptr() if t.numel() else 0), _DTYPE_CODE[t.dtype],
+                              t.shape[0], t.shape[1], float(target_bpp), ctypes.byref(opt), ctypes.byref(out),
+                              ctypes.byref(nb))
+    _check(rc, "ep_compress")
+    blob = np.ctypeslib.as_array(out, shape=(nb.value,)).copy()
+    lib().ep_free(out)
+    return Packed(blob=blob, status=rc, shape=tuple(t.shape), dtype=t.dtype)
+
+
+def actual_bpp(blob: np.ndarray) -> float:
+    v = lib().ep_actual_bpp(_host_ptr(blob), blob.size)
+    if math.isnan(v):
+        raise EPError(ERR_FORMAT, "ep_actual_bpp", last_error())
+    return v
+
+
+def storage_nbytes(blob: np.ndarray, include_header: bool = True) -> int:
+    return _check(lib().ep_storage_nbytes(_host_ptr(blob), blob.size, int(include_header)), "ep_storage_nbytes")
+
+
+def blob_info(blob: np.ndarray) -> dict:
+    info = _Info()
+    _check(lib().ep_blob_info(_host_ptr(blob), blob.size, ctypes.byref(info)), "ep_blob_info")
+    return {name: getattr(info, name) for name, _ in _Info._fields_}
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def decompress(p: Packed, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """ep_decompress: enqueues the fused decode on `stream` (default: the
+    current stream) into `out` (allocated if None) and returns it."""
+    if p.dev is None:
+        raise EPError(ERR_ARG, "decompress", "stream is not on a device; call Packed.to('cuda') first")
+    rows, cols = p.shape
+    if out is None:
+        out = torch.empty(rows, cols, dtype=p.dtype, device=p.dev.device)
+    if out.dtype != p.dtype or tuple(out.shape) != (rows, cols) or not out.is_contiguous():
+        raise EPError(ERR_ARG, "decompress", "out must be a contiguous tensor of the stored shape and dtype")
+    rc = lib().ep_decompress(_host_ptr(p.blob), p.blob.size, ctypes.c_void_p(p.dev.data_ptr()),
+                             ctypes.c_void_p(out.data_ptr()), -1, ctypes.c_void_p(_stream_handle(stream)))
+    _check(rc, "ep_decompress")
+    return out
+
+
+def decode_symbols(p: Packed, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """ep_decode_symbols: the lattice coordinates v (int16, rows x cols8)."""
+    if p.dev is None:
+        raise EPError(ERR_ARG, "decode_symbols", "stream is not on a device; call Packed.to('cuda') first")
+    rows, cols = p.shape
+    cols8 = (cols + 7) // 8 * 8
+    if out is None:
+        out = torch.empty(rows, cols8, dtype=torch.int16, device=p.dev.device)
+    rc = lib().ep_decode_symbols(_host_ptr(p.blob), p.blob.size, ctypes.c_void_p(p.dev.data_ptr()),
+                                 ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(_stream_handle(stream)))
+    _check(rc, "ep_decode_symbols")
+    return out
+
+
+def from_blob(blob: np.ndarray) -> Packed:
+    """Wraps an existing stream (for example one written elsewhere)."""
+    d = blob_info(blob)
+    return Packed(blob=np.ascontiguousarray(blob, dtype=np.uint8), status=OK if d["method"] == 0 else WARN_RAW,
+                  shape=(d["rows"], d["cols"]), dtype=_CODE_DTYPE[d["dtype"]])

@@ -1,0 +1,132 @@
+"""C ABI checks that need no GPU: the library loads and exports every entry
+point declared in include/ep.h; the host encoder writes the oracle's stream
+byte for byte; stream facts and error codes follow the pages' rules."""
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_tile_interleaved_amd import ep
+from decode_tile_interleaved_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ep.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(ep.EXPORTS)
+    L = ep.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("name", ["gauss256_bf16_3.5", "rowscale4096_bf16_4.0"])
+def test_stream_identical_to_oracle_at_target(name):
+    x, target = W.make(name)
+    p = ep.compress(x, target)
+    blob, rc, a = oracle.compress(x, target)
+    assert p.status == rc == 0
+    assert np.array_equal(p.blob, blob)
+    assert ep.blob_info(p.blob)["scale_a"] == a
+
+
+@pytest.mark.parametrize("shape,dtype,a", [((1, 8), torch.bfloat16, 0.3), ((3, 5), torch.bfloat16, 0.3),
+                                           ((7, 13), torch.float16, 0.2), ((3, 2736), torch.bfloat16, 0.5),
+                                           ((129, 64), torch.bfloat16, 0.05), ((64, 1032), torch.float16, 1.0)])
+def test_stream_identical_to_oracle_fixed_scale(shape, dtype, a):
+    x = W.gaussian(*shape, 0.02, seed=sum(shape), dtype=dtype)
+    p = ep.compress(x, 4.0, fixed_scale=a)
+    blob, rc, _ = oracle.compress(x, 4.0, fixed_a=a)
+    assert np.array_equal(p.blob, blob)
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_stream_identical_code_containers(kind):
+    x = W.absmax_codes(128, 512, seed=3, kind=kind)
+    p = ep.compress(x, 3.0)
+    blob, rc, _ = oracle.compress(x, 3.0)
+    assert np.array_equal(p.blob, blob)
+
+
+def test_stream_identical_heavy_tails():
+    x = W.t4_outliers(192, 1536, seed=4)
+    p = ep.compress(x, 2.75)
+    blob, rc, _ = oracle.compress(x, 2.75)
+    assert np.array_equal(p.blob, blob)
+
+
+def test_thread_count_does_not_change_stream():
+    x = W.rowscale_gaussian(300, 776, seed=6)
+    a = ep.compress(x, 3.3, n_threads=1)
+    b = ep.compress(x, 3.3, n_threads=7)
+    assert np.array_equal(a.blob, b.blob)
+
+
+def test_bpp_and_storage_definitions():
+    x, target = W.make("gauss256_bf16_3.5")
+    p = ep.compress(x, target)
+    assert ep.actual_bpp(p.blob) == 8 * p.nbytes / x.numel()
+    assert ep.storage_nbytes(p.blob, True) == p.nbytes
+    assert ep.storage_nbytes(p.blob, False) == p.nbytes - 128
+    assert abs(p.actual_bpp - target) / target <= 0.02
+
+
+def test_error_codes():
+    good = W.gaussian(64, 512, 0.02, seed=1)
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(torch.zeros(0, 16, dtype=torch.bfloat16), 4.0)
+    assert e.value.code == ep.ERR_SHAPE
+    bad = good.clone()
+    bad[1, 2] = float("nan")
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(bad, 4.0)
+    assert e.value.code == ep.ERR_NONFINITE
+    bad[1, 2] = float("inf")
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(bad, 4.0)
+    assert e.value.code == ep.ERR_NONFINITE
+    for t in (0.0005, 11.5, float("nan"), float("inf")):
+        with pytest.raises(ep.EPError) as e:
+            ep.compress(good, t)
+        assert e.value.code == ep.ERR_TARGET
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(W.absmax_codes(64, 512, seed=2, kind="int8"), 8.0)
+    assert e.value.code == ep.ERR_TARGET
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(good[:16, :16], 4.0)   # below the per-tile overhead
+    assert e.value.code == ep.ERR_TARGET
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(good.float(), 4.0)
+    assert e.value.code == ep.ERR_ARG
+
+
+def test_corrupt_stream_rejected():
+    x, target = W.make("gauss256_bf16_3.5")
+    p = ep.compress(x, target)
+    bad = p.blob.copy()
+    bad[0] ^= 1
+    with pytest.raises(ep.EPError) as e:
+        ep.blob_info(bad)
+    assert e.value.code == ep.ERR_FORMAT
+    with pytest.raises(ep.EPError):
+        ep.actual_bpp(p.blob[:-16].copy())
+
+
+def test_raw_fallback_matches_oracle():
+    t = torch.zeros(4, 4096, dtype=torch.bfloat16)
+    t[:, 0] = 1.0
+    t[:, 1:] = 1e-3
+    p = ep.compress(t, 10.0)
+    blob, rc, _ = oracle.compress(t, 10.0)
+    assert p.status == ep.WARN_RAW == rc
+    assert np.array_equal(p.blob, blob)
+    assert ep.blob_info(p.blob)["method"] == 1
