@@ -11,14 +11,14 @@
 // (16 bytes for BF16/FP16, 8 bytes for FP8/INT8).
 //
 // Per workgroup (up to 8 waves, one workgroup per CU):
-//   1. every wave starts its global loads: its tile's state and row scales,
-//      one context's frequencies, and its tile's words straight into LDS
-//      (global_load_lds_dwordx4);
+//   1. every wave starts its global loads: one context's frequencies first
+//      (they need only the kernel arguments), then its tile's word offsets,
+//      start states and row scales, then its tile's words into registers;
 //   2. one wave per context prefix-sums the frequencies (DPP scan), lists the
 //      used symbols, sets a bitmap of the slots where a symbol starts, and
-//      expands the context's table one 64-slot row at a time: a slot's symbol
-//      is the number of starts up to it, which v_mbcnt counts from the row's
-//      bitmap;
+//      expands the context's table 64 slots at a time: a slot's symbol is the
+//      number of starts up to it, which v_mbcnt counts from the row's bitmap;
+//      then each wave writes its words to LDS;
 //   3. each wave decodes its tile.
 //
 // Decode step for state x in [2^14, 2^30), kept as X = 4x so that the table
@@ -26,15 +26,31 @@
 //   x' = f * (x >> 10) + (slot - cum);  if x' < 2^14: x = x' << 16 | w
 // where w is the word the state holds in reserve.  After a refill the state
 // takes a new reserve word: refilling lanes take consecutive words in lane
-// order (ballot + mbcnt), so the word fetch never sits on the chain from one
-// table lookup to the next.
+// order (ballot + mbcnt).
 //
-// Table entries (one dword per slot and context, 2^10 slots per context):
-//   narrow (every used value in [-128, 127]): two arrays 28 KB apart,
-//     d0 = 4f | (v + 128) << 24 and d1 = 4 (slot - cum), so that
-//     X' = mad_u32_u24(d0, X >> 12, d1) needs no unpacking and the value
-//     converts with one v_cvt_f32_ubyte3;
+// The step is software-pipelined around its one serial dependence, table
+// lookup -> multiply-add -> compare -> select -> next lookup (on gfx950 a
+// dependent VALU op costs about fourteen cycles, a two-dword LDS lookup about
+// sixty).  The address without a refill (from x') and the address after one
+// (from the reserve word) are formed in parallel with the compare; the next
+// lookup leaves right after the select.  Only then do the refilling lanes,
+// under the exec mask, take the reserve into the state and read their next
+// reserve word straight into its register; that read is first needed one step
+// later, and its lane rank is computed from the ballot outside the masked
+// block so that it leaves early.
+//
+// Table entries (2^10 slots per context):
+//   narrow (every used value in [-128, 127]): two dwords 28 KB apart, read
+//     with one ds_read2st64: d0 = 4f | (v + 128) << 24, d1 = 4 (slot - cum),
+//     so that X' = mad_u32_u24(d0, X >> 12, d1) and the value converts with
+//     one v_cvt_f32_ubyte3;
 //   wide (values in [-2048, 2047]): e = f | (slot - cum) << 10 | v << 20.
+// Either way bits 0 and 1 of v sit at a fixed place in d0 (24/25 or 20/21):
+// bit 0 is the coset bit b, and the XOR of bit 1 over coordinates 0..6 is the
+// parity p that selects the last coordinate's context.
+//
+// LDS context order: F, C_0, C_1, then E_{b,p} at index 3 + b + 2p, so that
+// both context bases come from one bit-field extract.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -56,25 +72,27 @@ constexpr uint32_t kTableBytes = kTableDwords * 4;         // 28672
 constexpr uint32_t kRows = kProbTotal / 64;                // 16 rows of 64 slots per context
 constexpr uint32_t kMarkWords = kProbTotal / 32;           // 32 bitmap words per context
 constexpr uint32_t kLdsLimit = 160 * 1024;
-constexpr uint32_t kLdsPad = 256;  // slack after the last word buffer for reads of lanes that do not refill
+constexpr uint32_t kLdsPad = 256;  // slack after the last word buffer
 constexpr int kOutSym = 4;         // int16 lattice coordinates; 0..3 are the container dtypes
 constexpr uint32_t kWordLoads = 8;  // fixed 16-byte-per-lane loads per tile: 8 KB of words
 
 static_assert(kProbBits == 10, "table addressing below assumes 2^10 slots per context");
 
+// Kernel arguments.  The fields the first global loads need come first, so
+// that they arrive with the first batch of scalar loads.
 struct Args {
   const uint8_t *blob;
-  void *out;
-  uint64_t off_freq, off_scales, off_states, off_tile_offsets, off_words;
-  uint64_t cols;                  // columns of the output (padded layouts only)
-  uint32_t rows, vpr;             // rows; vectors per row
-  uint32_t row_magic, row_shift;  // vec / vpr = umulhi(vec, row_magic) >> row_shift  (vpr > 1)
-  uint32_t n_vec, n_tiles;
-  uint32_t rec_off, mark_off, words_off, wave_buf_bytes;  // LDS byte offsets
-  int32_t smin[kContexts];
+  uint64_t off_freq, off_tile_offsets, off_states, off_scales, off_words;
   uint32_t nsym[kContexts];
   uint32_t fidx[kContexts];
   uint32_t nzbase[kContexts];
+  int32_t smin[kContexts];
+  void *out;
+  uint64_t cols;                  // columns of the output (padded layouts only)
+  uint32_t rows, vpr;             // rows; vectors per row
+  uint32_t row_magic, row_shift;  // vec / vpr = umulhi(vec, row_magic) >> row_shift  (vpr > 1)
+  uint32_t n_vec, n_tiles, waves;
+  uint32_t rec_off, mark_off, rowrec_off, words_off, wave_buf_bytes;  // LDS byte offsets
 };
 
 typedef __attribute__((address_space(1))) void *gptr_t;
@@ -91,6 +109,39 @@ __device__ __forceinline__ uint32_t lds_u16(uint32_t byte) { return *(lds_u16_pt
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   asm volatile("" : "+v"(v));
   return v;
+}
+
+// the same for a wave-uniform value, which stays in one SGPR (or pair);
+// readfirstlane states the uniformity and costs nothing on a scalar value
+__device__ __forceinline__ uint32_t opaque_s(uint32_t v) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  asm volatile("" : "+s"(v));
+  return v;
+}
+typedef __attribute__((address_space(1))) uint8_t *gbyte_t;
+__device__ __forceinline__ gbyte_t opaque_s(gbyte_t p) {
+  uint64_t u = (uint64_t)p;
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  return (gbyte_t)(((uint64_t)hi << 32) | lo);
+}
+
+// a[i] for a wave-uniform i without indexing the kernel arguments by a
+// register (which costs a dependent scalar load)
+template <class T>
+__device__ __forceinline__ T pick(const T (&a)[kContexts], uint32_t i) {
+  uint32_t r = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < (uint32_t)kContexts; ++k) r |= (uint32_t)a[k] & (0u - (uint32_t)(i == k));
+  return (T)r;
+}
+
+// per-lane select by an SGPR lane mask: mask bit set -> if1.  Written as one
+// instruction so that the compiler keeps the order of dependent selects.
+__device__ __forceinline__ uint32_t select_mask(uint64_t mask, uint32_t if0, uint32_t if1) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if0), "v"(if1), "s"(mask));
+  return r;
 }
 
 // inclusive prefix sum over the 16 lanes of each DPP row
@@ -117,32 +168,54 @@ __device__ __forceinline__ int32_t symbol_value(uint32_t c, int32_t s) {
   return 4 * s + 2 * (bp & 1) + (bp >> 1);
 }
 
-// one rANS decode step of every active lane; returns the table entry.
-// res holds each state's reserve word; wp (wave-uniform) is the LDS byte
-// address of the next unread word.
+// Per-lane pipeline state of a tile's decode.
+struct Lane {
+  uint32_t d0, d1;  // this step's table entry (the lookup is in flight when a step starts)
+  uint32_t q;       // X >> 12 of this step's state
+  uint32_t r;       // reserve word (its read may be in flight when a step starts)
+  uint32_t wp;      // wave-uniform LDS byte address of the next word to hand out
+};
+
 template <bool WIDE>
-__device__ __forceinline__ uint32_t rans_step(uint32_t &X, uint32_t &res, uint32_t &wp, uint32_t ctx_base,
-                                              bool active) {
-  const uint32_t res4 = res << 2;  // off the chain: the reserve word arrived a step ago
-  const uint32_t a = (X & 0xffcu) | ctx_base;
-  const uint32_t q = X >> 12;
-  const uint32_t d0 = lds_u32(a);
+__device__ __forceinline__ void table_read(uint32_t a, uint32_t &d0, uint32_t &d1) {
+  d0 = lds_u32(a);
+  if constexpr (!WIDE) d1 = lds_u32(a + kTableBytes);
+}
+
+// one rANS decode step of every active lane: decodes this step's symbol,
+// issues the lookup for the next step (whose context base is nb) and the
+// reserve-word read; returns this step's entry.
+template <bool WIDE>
+__device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active) {
+  // the reserve word read last step returns right after this step's entry;
+  // reading it here keeps its use out of the refill block
+  uint32_t r4;
+  asm volatile("v_lshlrev_b32 %0, 2, %1" : "=v"(r4) : "v"(L.r));
+  const uint32_t ar = (r4 & 0xffcu) | nb;  // next address after a refill: the reserve word's low bits
+  const uint32_t e = L.d0;
   uint32_t x;
   if constexpr (WIDE) {
-    x = (__umul24(d0 & 0x3ffu, q) + ((d0 >> 10) & 0x3ffu)) << 2;
+    x = (__umul24(e & 0x3ffu, L.q) + ((e >> 10) & 0x3ffu)) << 2;
   } else {
-    x = __umul24(d0, q) + lds_u32(a + kTableBytes);
+    x = __umul24(e, L.q) + L.d1;
   }
   const bool need = active && x < 0x10000u;
-  const uint32_t xr = (x << 16) | res4;
-  X = active ? (need ? xr : x) : X;
   const uint64_t m = __ballot(need);
+  const uint32_t ax = (x & 0xffcu) | nb;  // next address without a refill
+  table_read<WIDE>(select_mask(m, ax, ar), L.d0, L.d1);
+  __builtin_amdgcn_sched_barrier(0);  // the next lookup goes out before the refill
+  // the word a refilling lane takes: ranks come from the ballot, outside the
+  // masked block, so the read leaves as early as the mask allows
   const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-  // every lane reads (no branch); lanes that did not refill keep their word
-  const uint32_t w = lds_u16(wp + 2u * rank);
-  res = need ? w : res;
-  wp += 2u * (uint32_t)__popcll(m);
-  return d0;
+  const uint32_t wa = opaque(L.wp + 2u * rank);
+  uint32_t X = x;
+  if (need) {  // refilling lanes only: take the reserve, read the next word into it
+    L.r = lds_u16(wa);
+    X = (x << 16) | r4;
+  }
+  L.q = X >> 12;
+  L.wp = opaque_s(L.wp + 2u * (uint32_t)__popcll(m));
+  return e;
 }
 
 template <bool WIDE>
@@ -177,16 +250,20 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
 }
 
-// writes one decoded vector
+// writes one decoded vector.  row is the wave-uniform address of this step's
+// 64 vectors (unpadded layouts); local is the vector's index in the tile.
 template <int OUT, bool WIDE, bool PADDED>
-__device__ __forceinline__ void emit_vector(const Args &A, uint32_t vec, const uint32_t (&e)[8], float g) {
+__device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t tile, uint32_t local,
+                                            uint32_t lane, const uint32_t (&e)[8], float g) {
+  constexpr uint32_t kVecBytes = (OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u;
+  const uint32_t lane_off = kVecBytes * lane;
   if constexpr (OUT == kOutSym) {
     uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       w[k] = ((uint32_t)entry_value<WIDE>(e[2 * k]) & 0xffffu) | ((uint32_t)entry_value<WIDE>(e[2 * k + 1]) << 16);
     const u32x4 pk = {w[0], w[1], w[2], w[3]};
-    __builtin_nontemporal_store(pk, reinterpret_cast<u32x4 *>(A.out) + vec);
+    __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x4 *)(row + lane_off));
     return;
   } else {
     const float ng = -128.0f * g;
@@ -196,14 +273,14 @@ __device__ __forceinline__ void emit_vector(const Args &A, uint32_t vec, const u
     if constexpr (!PADDED) {
       if constexpr (OUT == EP_BF16 || OUT == EP_FP16) {
         const u32x4 pk = {pack2<OUT>(y[0], y[1]), pack2<OUT>(y[2], y[3]), pack2<OUT>(y[4], y[5]), pack2<OUT>(y[6], y[7])};
-        __builtin_nontemporal_store(pk, reinterpret_cast<u32x4 *>(A.out) + vec);
+        __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x4 *)(row + lane_off));
       } else if constexpr (OUT == EP_FP8_E4M3FN) {
         int lo = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[0]), fp8_clamp(y[1]), 0, false);
         lo = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[2]), fp8_clamp(y[3]), lo, true);
         int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[4]), fp8_clamp(y[5]), 0, false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[6]), fp8_clamp(y[7]), hi, true);
         const u32x2 pk = {(uint32_t)lo, (uint32_t)hi};
-        __builtin_nontemporal_store(pk, reinterpret_cast<u32x2 *>(A.out) + vec);
+        __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x2 *)(row + lane_off));
       } else {
         uint32_t b[8];
 #pragma unroll
@@ -213,9 +290,10 @@ __device__ __forceinline__ void emit_vector(const Args &A, uint32_t vec, const u
         const uint32_t hi =
             __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u) | (__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u) << 16);
         const u32x2 pk = {lo, hi};
-        __builtin_nontemporal_store(pk, reinterpret_cast<u32x2 *>(A.out) + vec);
+        __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x2 *)(row + lane_off));
       }
     } else {
+      const uint32_t vec = tile * 1024u + local;
       const uint32_t r = vec / A.vpr, k = vec - r * A.vpr;
       const uint64_t base = (uint64_t)r * A.cols + 8ull * k;
       const uint32_t left = (uint32_t)(A.cols - 8ull * k);
@@ -236,35 +314,38 @@ __device__ __forceinline__ void emit_vector(const Args &A, uint32_t vec, const u
 }
 
 // decodes one tile; PARTIAL handles the last tile of a stream (n < 1024).
-// wp is the LDS byte address of the tile's first word.
+// wb is the LDS byte address of the tile's first word; X is 4 * the start state.
 template <int OUT, bool WIDE, bool PADDED, bool PARTIAL>
-__device__ __forceinline__ void decode_tile(const Args &A, uint32_t wp, uint32_t X, uint32_t tile, uint32_t n,
+__device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t X, uint32_t tile, uint32_t n,
                                             const float (&gs)[16], uint32_t lane) {
   const uint32_t n_act = PARTIAL ? (n < 64u ? n : 64u) : 64u;
-  uint32_t res = lane < n_act ? lds_u16(wp + 2u * lane) : 0u;
-  wp += 2u * n_act;
-#pragma unroll 1
+  Lane L;
+  table_read<WIDE>(X & 0xffcu, L.d0, L.d1);  // context F
+  L.q = X >> 12;
+  L.r = lane < n_act ? lds_u16(wb + 2u * lane) : 0u;
+  L.wp = opaque_s(wb + 2u * n_act);
+  constexpr uint32_t kBitB = WIDE ? 20u : 24u;  // where bit 0 of v sits in d0
+  const uint32_t kC = opaque_s(0x1000u), kE = opaque_s(0x3000u);  // LDS bases of C_0 and E_{0,0}
+  constexpr uint32_t kStepBytes = 64u * ((OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u);
+  const gbyte_t tile_out = (gbyte_t)A.out + (uint64_t)tile * (16u * kStepBytes);
+#pragma unroll
   for (uint32_t s = 0; s < 16; ++s) {
     const bool act = PARTIAL ? (s * 64 + lane < n) : true;
     if (PARTIAL && s * 64 >= n) break;
     uint32_t e[8];
-    e[0] = rans_step<WIDE>(X, res, wp, 0u, act);
-    // the coset bit b = v0 & 1 selects C_b; entries keep v's low bits at bit 24 (narrow) or 20 (wide)
-    const uint32_t cb = opaque(WIDE ? (0x1000u + ((e[0] >> 8) & 0x1000u)) : (0x1000u + ((e[0] >> 12) & 0x1000u)));
-    e[1] = rans_step<WIDE>(X, res, wp, cb, act);
-    e[2] = rans_step<WIDE>(X, res, wp, cb, act);
-    uint32_t acc = e[0] ^ e[1] ^ e[2];
-    e[3] = rans_step<WIDE>(X, res, wp, cb, act);
-    e[4] = rans_step<WIDE>(X, res, wp, cb, act);
-    acc ^= e[3] ^ e[4];
-    e[5] = rans_step<WIDE>(X, res, wp, cb, act);
-    e[6] = rans_step<WIDE>(X, res, wp, cb, act);
-    acc ^= e[5] ^ e[6];
-    // E_{b,p}: p = parity of z0..z6 = bit 1 of v0 ^ .. ^ v6
-    const uint32_t eb = opaque(WIDE ? (0x3000u + ((e[0] >> 7) & 0x2000u) + ((acc >> 9) & 0x1000u))
-                                    : (0x3000u + ((e[0] >> 11) & 0x2000u) + ((acc >> 13) & 0x1000u)));
-    e[7] = rans_step<WIDE>(X, res, wp, eb, act);
-    if (act) emit_vector<OUT, WIDE, PADDED>(A, tile * 1024u + s * 64u + lane, e, gs[s]);
+    // C_b at LDS context 1 + b; the coset bit is in the entry of coordinate 0
+    const uint32_t cb = opaque(opaque(__builtin_amdgcn_ubfe(L.d0, kBitB, 1u)) * 4096u + kC);
+    e[0] = rans_step<WIDE>(L, cb, act);
+#pragma unroll
+    for (int j = 1; j < 6; ++j) e[j] = rans_step<WIDE>(L, cb, act);
+    // bit kBitB of the XOR is b (all eight coordinates share it), bit kBitB + 1 is p
+    uint32_t acc = __builtin_amdgcn_bitop3_b32(e[0], e[1], e[2], 0x96);
+    acc = __builtin_amdgcn_bitop3_b32(acc, e[3], e[4], 0x96);
+    acc = __builtin_amdgcn_bitop3_b32(acc, e[5], L.d0, 0x96);
+    const uint32_t eb = opaque(opaque(__builtin_amdgcn_ubfe(acc, kBitB, 2u)) * 4096u + kE);
+    e[6] = rans_step<WIDE>(L, eb, act);
+    e[7] = rans_step<WIDE>(L, 0u, act);
+    if (act) emit_vector<OUT, WIDE, PADDED>(A, opaque_s(tile_out + s * kStepBytes), tile, s * 64u + lane, lane, e, gs[s]);
   }
 }
 
@@ -273,12 +354,26 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t nwaves = blockDim.x >> 6;
+  const uint32_t nwaves = A.waves;
+
+  // ---- 1. global loads, all unconditional so that each wait is exact ----
+  // the first 256 frequencies of this wave's first context (first: they need
+  // nothing but the kernel arguments)
+  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
+  const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
+  uint32_t fpre[4];
+  {
+    const uint32_t n0 = pick(A.nsym, c0), f0 = pick(A.fidx, c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t s = 64u * i + lane;
+      const uint32_t v = freq[f0 + (s < n0 ? s : 0u)];
+      fpre[i] = s < n0 ? v : 0u;
+    }
+  }
   const uint32_t tile = blockIdx.x * nwaves + wave;
   const bool has_tile = tile < A.n_tiles;
   const uint32_t tc = has_tile ? tile : A.n_tiles - 1u;  // waves without a tile load a valid one and drop it
-
-  // ---- 1. global loads, all unconditional so that each wait is exact ----
   const uint32_t *toff = reinterpret_cast<const uint32_t *>(A.blob + A.off_tile_offsets);
   const uint32_t w_begin = toff[tc], w_end = toff[tc + 1];
   const uint32_t x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tc * 64u + lane];
@@ -293,59 +388,51 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
       gs[s] = scales[r < last ? r : last];  // lanes past the end read the last row; their values are unused
     }
   }
-  // the first 256 frequencies of this wave's first context
-  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
-  const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
-  uint32_t fpre[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t s = 64u * i + lane;
-    const uint32_t v = freq[A.fidx[c0] + (s < A.nsym[c0] ? s : 0u)];
-    fpre[i] = s < A.nsym[c0] ? v : 0u;
-  }
-  // the tile's words go straight from global memory into this wave's LDS
-  // buffer (global_load_lds_dwordx4: lane i of load j fills bytes
-  // 1024 j + 16 i ..+15); lanes past the tile re-read its last chunk
+  __builtin_amdgcn_sched_barrier(0);  // the loads above go out before the word loads
+  // the tile's words: the first kWordLoads KB into registers now (lane i of
+  // load j holds bytes 1024 j + 16 i ..+15; lanes past the tile re-read its
+  // last chunk), written to this wave's LDS buffer after the tables are built.
+  // Register loads leave the waits of the table build exact: the compiler must
+  // assume that LDS writes from global_load_lds alias every LDS access.
   const uint64_t byte0 = A.off_words + 2ull * w_begin;
   const uint64_t abyte0 = byte0 & ~15ull;
   const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * w_end + 15ull) & ~15ull) - abyte0) >> 4);
   const uint32_t wb = A.words_off + wave * A.wave_buf_bytes;  // LDS byte address of this wave's words
+  u32x4 wv[kWordLoads];
   {
-    const uint8_t *src = A.blob + abyte0;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(A.blob + abyte0);
 #pragma unroll
     for (uint32_t i = 0; i < kWordLoads; ++i) {
       const uint32_t ch = lane + 64u * i;
-      __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (ch < nchunks ? ch : nchunks - 1u)),
-                                       (lptr_t)(lds + wb + 1024u * i), 16, 0, 0);
+      wv[i] = src[ch < nchunks ? ch : nchunks - 1u];
     }
-    for (uint32_t i = kWordLoads; 64u * i < nchunks; ++i)  // tiles longer than the fixed loads cover
-      if (lane + 64u * i < nchunks)
-        __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (lane + 64u * i)), (lptr_t)(lds + wb + 1024u * i), 16, 0,
-                                         0);
   }
 
   // ---- 2. one wave per context: prefix sums, used-symbol records, start
   //         bitmap, then the context's 16 table rows of 64 slots ----------
   uint2 *rec = reinterpret_cast<uint2 *>(lds + A.rec_off);          // (d0, cum term) per used symbol
   uint32_t *mark = reinterpret_cast<uint32_t *>(lds + A.mark_off);  // [ctx][32] start bits
+  uint4 *rowrec = reinterpret_cast<uint4 *>(lds + A.rowrec_off);     // [ctx][16] per-row fill records
   uint32_t *tab = reinterpret_cast<uint32_t *>(lds);
   for (uint32_t c = wave; c < (uint32_t)kContexts; c += nwaves) {
-    const uint32_t n = A.nsym[c];
+    const uint32_t n = pick(A.nsym, c), fidx = pick(A.fidx, c), nzbase = pick(A.nzbase, c);
+    const int32_t smin = pick(A.smin, c);
     if (n == 0u) continue;  // context without symbols: its table is never read
+    const uint32_t lc = c < 3u ? c : 3u + ((c - 3u) >> 1) + 2u * ((c - 3u) & 1u);  // LDS context of E_{b,p}
     if (lane < kMarkWords) mark[c * kMarkWords + lane] = 0u;
-    uint32_t carry = 0, nzb = A.nzbase[c];
+    uint32_t carry = 0, nzb = nzbase;
     for (uint32_t base = 0, it = 0; base < n; base += 64, ++it) {
       const uint32_t s = base + lane;
       uint32_t f;
       if (c == wave && it < 4) f = it == 0 ? fpre[0] : it == 1 ? fpre[1] : it == 2 ? fpre[2] : fpre[3];
-      else f = s < n ? freq[A.fidx[c] + s] : 0u;
+      else f = s < n ? freq[fidx + s] : 0u;
       const uint32_t incl = wave_inclusive_sum(f);
       const uint32_t cum = carry + incl - f;
       const bool used = f != 0;
       const uint64_t m = __ballot(used);
       const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nzb));
       if (used && cum < kProbTotal) {
-        const int32_t v = symbol_value(c, A.smin[c] + (int32_t)s);
+        const int32_t v = symbol_value(c, smin + (int32_t)s);
         rec[r] = WIDE ? make_uint2(f | ((uint32_t)v & 0xfffu) << 20, cum)
                       : make_uint2((f << 2) | ((uint32_t)(v + 128) & 0xffu) << 24, cum << 2);
         atomicOr(&mark[c * kMarkWords + (cum >> 5)], 1u << (cum & 31u));
@@ -353,45 +440,69 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
       carry += __builtin_amdgcn_readlane(incl, 63);
       nzb += (uint32_t)__popcll(m);
     }
-    // lane t < 16 holds row t: its start bits and the record index before it
-    uint32_t lo = 0, hi = 0;
-    if (lane < kRows) {
-      lo = mark[c * kMarkWords + 2 * lane];
-      hi = mark[c * kMarkWords + 2 * lane + 1];
+    // row t (lanes 0..15): its start bits shifted down by one and the record
+    // index before it, stored for the whole wave to read back by broadcast
+    {
+      uint32_t lo = 0, hi = 0;
+      if (lane < kRows) {
+        lo = mark[c * kMarkWords + 2 * lane];
+        hi = mark[c * kMarkWords + 2 * lane + 1];
+      }
+      const uint32_t cnt = (uint32_t)(__popc(lo) + __popc(hi));
+      const uint32_t first = nzbase + row16_inclusive_sum(cnt) - cnt;
+      if (lane < kRows)
+        rowrec[c * kRows + lane] = make_uint4(__builtin_amdgcn_alignbit(hi, lo, 1u), hi >> 1, first + (lo & 1u) - 1u, 0u);
     }
-    const uint32_t cnt = (uint32_t)(__popc(lo) + __popc(hi));
-    const uint32_t first = A.nzbase[c] + row16_inclusive_sum(cnt) - cnt;
     // slot record = first + (starts at or below the slot) - 1
-    //             = first + bit0 - 1 + popcount of (bits >> 1) below the lane
+    //             = first + bit0 - 1 + popcount of (bits >> 1) below the lane.
+    // All sixteen records are read before any table write: the compiler cannot
+    // tell the record list and the table apart, so interleaving would put an
+    // LDS round trip on every row.
+    // Three batches, each one LDS round trip: the row records (broadcast
+    // reads), then the slot records, then the table writes.
+    uint4 rr[kRows];
+#pragma unroll
+    for (uint32_t row = 0; row < kRows; ++row) rr[row] = rowrec[c * kRows + row];
+    __builtin_amdgcn_sched_barrier(0);
+    uint2 rc[kRows];
+#pragma unroll
+    for (uint32_t row = 0; row < kRows; ++row)
+      rc[row] = rec[__builtin_amdgcn_mbcnt_hi(rr[row].y, __builtin_amdgcn_mbcnt_lo(rr[row].x, rr[row].z))];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (uint32_t row = 0; row < kRows; ++row) {
-      const uint32_t rlo = __builtin_amdgcn_readlane(lo, row), rhi = __builtin_amdgcn_readlane(hi, row);
-      const uint32_t rfirst = __builtin_amdgcn_readlane(first, row);
-      const uint64_t sh = (((uint64_t)rhi << 32) | rlo) >> 1;
-      const uint32_t k = __builtin_amdgcn_mbcnt_hi((uint32_t)(sh >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)sh, rfirst + (rlo & 1u) - 1u));
-      const uint2 rc = rec[k];
-      const uint32_t slot = row * 64u + lane, idx = c * kProbTotal + slot;
+      const uint32_t slot = row * 64u + lane, idx = lc * kProbTotal + slot;
       if (WIDE) {
-        tab[idx] = rc.x | ((slot - rc.y) << 10);
+        tab[idx] = rc[row].x | ((slot - rc[row].y) << 10);
       } else {
-        tab[idx] = rc.x;
-        tab[kTableDwords + idx] = (slot << 2) - rc.y;
+        tab[idx] = rc[row].x;
+        tab[kTableDwords + idx] = (slot << 2) - rc[row].y;
       }
     }
+  }
+#pragma unroll
+  for (uint32_t i = 0; i < kWordLoads; ++i)
+    if (lane + 64u * i < nchunks) *reinterpret_cast<u32x4 *>(lds + wb + 1024u * i + 16u * lane) = wv[i];
+  // tiles longer than the fixed loads cover: the rest of their words
+  {
+    const uint8_t *src = A.blob + abyte0;
+    for (uint32_t i = kWordLoads; 64u * i < nchunks; ++i)
+      if (lane + 64u * i < nchunks)
+        __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (lane + 64u * i)), (lptr_t)(lds + wb + 1024u * i), 16, 0,
+                                         0);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's words have landed in LDS
   __syncthreads();
 
   // ---- 3. decode ---------------------------------------------------------
   if (!has_tile) return;
-  const uint32_t wp = wb + (uint32_t)(byte0 - abyte0);
+  const uint32_t wt = wb + (uint32_t)(byte0 - abyte0);
   const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
   const uint32_t X = x0 << 2;
   if (n == 1024u)
-    decode_tile<OUT, WIDE, PADDED, false>(A, wp, X, tile, n, gs, lane);
+    decode_tile<OUT, WIDE, PADDED, false>(A, wt, X, tile, n, gs, lane);
   else
-    decode_tile<OUT, WIDE, PADDED, true>(A, wp, X, tile, n, gs, lane);
+    decode_tile<OUT, WIDE, PADDED, true>(A, wt, X, tile, n, gs, lane);
 }
 
 typedef void (*KernelFn)(Args);
@@ -491,6 +602,8 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   off += 8 * nz_total;
   A.mark_off = off;
   off = (uint32_t)align16(off + 4 * kContexts * kMarkWords);
+  A.rowrec_off = off;
+  off += 16 * kContexts * kRows;
   A.words_off = off;
   // the fixed word loads write kWordLoads KB per wave whatever the tile's length
   A.wave_buf_bytes = (uint32_t)std::max<uint64_t>(max_span, 1024ull * kWordLoads);
@@ -530,6 +643,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
       configured.push_back(fn);
     }
   }
+  A.waves = waves;
   const uint32_t grid = (uint32_t)((s.tiles + waves - 1) / waves);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * waves), lds_bytes, stream, A);
   hipError_t err = hipGetLastError();
