@@ -11,14 +11,15 @@
 // (16 bytes for BF16/FP16, 8 bytes for FP8/INT8).
 //
 // Per workgroup (up to 8 waves, one workgroup per CU):
-//   1. every wave starts its global loads: one context's frequencies first
-//      (they need only the kernel arguments), then its tile's word offsets,
-//      start states and row scales, then its tile's words into registers;
+//   1. every wave starts its global loads: one context's frequencies, its
+//      tile's start states and row scales (vector loads, which need only the
+//      kernel arguments), then its tile's word offset (scalar loads); the last
+//      wave copies the words of all the workgroup's tiles (one range of the
+//      stream) into LDS with global_load_lds;
 //   2. one wave per context prefix-sums the frequencies (DPP scan), lists the
 //      used symbols, sets a bitmap of the slots where a symbol starts, and
 //      expands the context's table 64 slots at a time: a slot's symbol is the
 //      number of starts up to it, which v_mbcnt counts from the row's bitmap;
-//      then each wave writes its words to LDS;
 //   3. each wave decodes its tile.
 //
 // Decode step for state x in [2^14, 2^30), kept as X = 4x so that the table
@@ -74,7 +75,6 @@ constexpr uint32_t kMarkWords = kProbTotal / 32;           // 32 bitmap words pe
 constexpr uint32_t kLdsLimit = 160 * 1024;
 constexpr uint32_t kLdsPad = 256;  // slack after the last word buffer
 constexpr int kOutSym = 4;         // int16 lattice coordinates; 0..3 are the container dtypes
-constexpr uint32_t kWordLoads = 8;  // fixed 16-byte-per-lane loads per tile: 8 KB of words
 
 static_assert(kProbBits == 10, "table addressing below assumes 2^10 slots per context");
 
@@ -92,7 +92,7 @@ struct Args {
   uint32_t rows, vpr;             // rows; vectors per row
   uint32_t row_magic, row_shift;  // vec / vpr = umulhi(vec, row_magic) >> row_shift  (vpr > 1)
   uint32_t n_vec, n_tiles, waves;
-  uint32_t rec_off, mark_off, rowrec_off, words_off, wave_buf_bytes;  // LDS byte offsets
+  uint32_t rec_off, mark_off, rowrec_off, words_off;  // LDS byte offsets
 };
 
 typedef __attribute__((address_space(1))) void *gptr_t;
@@ -374,8 +374,6 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   const uint32_t tile = blockIdx.x * nwaves + wave;
   const bool has_tile = tile < A.n_tiles;
   const uint32_t tc = has_tile ? tile : A.n_tiles - 1u;  // waves without a tile load a valid one and drop it
-  const uint32_t *toff = reinterpret_cast<const uint32_t *>(A.blob + A.off_tile_offsets);
-  const uint32_t w_begin = toff[tc], w_end = toff[tc + 1];
   const uint32_t x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tc * 64u + lane];
   float gs[16];
   {
@@ -388,23 +386,28 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
       gs[s] = scales[r < last ? r : last];  // lanes past the end read the last row; their values are unused
     }
   }
-  __builtin_amdgcn_sched_barrier(0);  // the loads above go out before the word loads
-  // the tile's words: the first kWordLoads KB into registers now (lane i of
-  // load j holds bytes 1024 j + 16 i ..+15; lanes past the tile re-read its
-  // last chunk), written to this wave's LDS buffer after the tables are built.
-  // Register loads leave the waits of the table build exact: the compiler must
-  // assume that LDS writes from global_load_lds alias every LDS access.
-  const uint64_t byte0 = A.off_words + 2ull * w_begin;
-  const uint64_t abyte0 = byte0 & ~15ull;
-  const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * w_end + 15ull) & ~15ull) - abyte0) >> 4);
-  const uint32_t wb = A.words_off + wave * A.wave_buf_bytes;  // LDS byte address of this wave's words
-  u32x4 wv[kWordLoads];
-  {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(A.blob + abyte0);
-#pragma unroll
-    for (uint32_t i = 0; i < kWordLoads; ++i) {
+  __builtin_amdgcn_sched_barrier(0);  // the loads above go out before anything waits
+  // the tile's word range, read through the constant address space so that
+  // the loads are scalar and their wait leaves the vector loads above alone
+  typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
+  const cptr_u32 toff = (cptr_u32)(A.blob + A.off_tile_offsets);
+  const uint32_t w_begin = toff[tc];
+  // The workgroup's tiles are consecutive, so their words are one range of the
+  // stream: the last wave copies it into LDS with global_load_lds (1 KB per
+  // instruction, lanes past the end re-read the last 16 bytes).  Its waits
+  // are conservative about LDS written this way; the other waves never touch
+  // these loads, so the table build keeps exact waits.
+  const uint32_t g0 = blockIdx.x * nwaves;
+  const uint64_t gbyte0 = (A.off_words + 2ull * toff[g0]) & ~15ull;  // 16-byte aligned start of the range
+  const uint32_t wt = A.words_off + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);  // LDS address of this tile's first word
+  if (wave == nwaves - 1u) {
+    const uint32_t gend = g0 + nwaves < A.n_tiles ? g0 + nwaves : A.n_tiles;
+    const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * toff[gend] + 15ull) & ~15ull) - gbyte0) >> 4);
+    const uint8_t *src = A.blob + gbyte0;
+    for (uint32_t i = 0; 64u * i < nchunks; ++i) {
       const uint32_t ch = lane + 64u * i;
-      wv[i] = src[ch < nchunks ? ch : nchunks - 1u];
+      __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (ch < nchunks ? ch : nchunks - 1u)),
+                                       (lptr_t)(lds + A.words_off + 1024u * i), 16, 0, 0);
     }
   }
 
@@ -480,23 +483,11 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
       }
     }
   }
-#pragma unroll
-  for (uint32_t i = 0; i < kWordLoads; ++i)
-    if (lane + 64u * i < nchunks) *reinterpret_cast<u32x4 *>(lds + wb + 1024u * i + 16u * lane) = wv[i];
-  // tiles longer than the fixed loads cover: the rest of their words
-  {
-    const uint8_t *src = A.blob + abyte0;
-    for (uint32_t i = kWordLoads; 64u * i < nchunks; ++i)
-      if (lane + 64u * i < nchunks)
-        __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (lane + 64u * i)), (lptr_t)(lds + wb + 1024u * i), 16, 0,
-                                         0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's words have landed in LDS
+  __builtin_amdgcn_s_waitcnt(0);  // the loader's words have landed in LDS
   __syncthreads();
 
   // ---- 3. decode ---------------------------------------------------------
   if (!has_tile) return;
-  const uint32_t wt = wb + (uint32_t)(byte0 - abyte0);
   const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
   const uint32_t X = x0 << 2;
   if (n == 1024u)
@@ -554,7 +545,6 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   }
   // tile offsets: monotone, inside the word section, enough reserve words
   const uint8_t *toff = hb + s.off_tile_offsets;
-  uint64_t max_span = 0;
   for (int64_t t = 0; t < s.tiles; ++t) {
     const uint32_t b = rd<uint32_t>(toff + 4 * t), e = rd<uint32_t>(toff + 4 * t + 4);
     const int64_t n = std::min<int64_t>(kTileVecs, s.n_vec - t * kTileVecs);
@@ -562,8 +552,6 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
       set_error("corrupt tile offsets");
       return EP_ERR_FORMAT;
     }
-    const uint64_t a0 = (s.off_words + 2ull * b) & ~15ull, a1 = (s.off_words + 2ull * e + 15ull) & ~15ull;
-    max_span = std::max<uint64_t>(max_span, a1 - a0);
   }
   if (rd<uint32_t>(toff + 4 * s.tiles) != s.n_words) {
     set_error("corrupt tile offsets");
@@ -596,7 +584,9 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
       return EP_ERR_FORMAT;
     }
   }
-  // LDS layout: tables | records | bitmap | word buffers | pad
+  // LDS layout: tables | records | bitmap | row records | words | pad.  The
+  // words of a workgroup's consecutive tiles are one range; with k waves per
+  // workgroup the buffer holds the longest such range, in whole 1 KB copies.
   uint32_t off = wide ? kTableBytes : 2 * kTableBytes;
   A.rec_off = off;
   off += 8 * nz_total;
@@ -605,14 +595,30 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   A.rowrec_off = off;
   off += 16 * kContexts * kRows;
   A.words_off = off;
-  // the fixed word loads write kWordLoads KB per wave whatever the tile's length
-  A.wave_buf_bytes = (uint32_t)std::max<uint64_t>(max_span, 1024ull * kWordLoads);
-  if (off + A.wave_buf_bytes + kLdsPad > kLdsLimit) {
+  auto span_for = [&](uint32_t k) {
+    uint64_t span = 0;
+    for (int64_t t = 0; t < s.tiles; t += k) {
+      const int64_t e = std::min<int64_t>(t + k, s.tiles);
+      const uint64_t a0 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t)) & ~15ull;
+      const uint64_t a1 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * e) + 15ull) & ~15ull;
+      span = std::max<uint64_t>(span, a1 - a0);
+    }
+    return (span + 1023ull) & ~1023ull;
+  };
+  uint32_t waves = 0;
+  uint64_t span = 0;
+  for (uint32_t k = kMaxWaves; k >= 1; --k) {
+    span = span_for(k);
+    if (off + span + kLdsPad <= kLdsLimit) {
+      waves = k;
+      break;
+    }
+  }
+  if (!waves) {
     set_error("tile too large for the decoder's LDS budget");
     return EP_ERR_FORMAT;
   }
-  const uint32_t waves = (uint32_t)std::min<uint64_t>(kMaxWaves, (kLdsLimit - off - kLdsPad) / A.wave_buf_bytes);
-  const uint32_t lds_bytes = off + waves * A.wave_buf_bytes + kLdsPad;
+  const uint32_t lds_bytes = off + (uint32_t)span + kLdsPad;
   A.blob = reinterpret_cast<const uint8_t *>(dev_blob);
   A.out = dev_out;
   A.off_freq = s.off_freq;
