@@ -25,20 +25,18 @@
 // Decode step for state x in [2^14, 2^30), kept as X = 4x so that the table
 // address is one AND-OR:  4*slot = X & 0xffc;  e = table[ctx][slot];
 //   x' = f * (x >> 10) + (slot - cum);  if x' < 2^14: x = x' << 16 | w
-// where w is the word the state holds in reserve.  After a refill the state
-// takes a new reserve word: refilling lanes take consecutive words in lane
-// order (ballot + mbcnt).
+// where w is the state's next word.  A tile stores each state's words
+// together (behind one count byte per state), so a lane walks its own word
+// list with a private pointer and always holds its next word in a register.
 //
 // The step is software-pipelined around its one serial dependence, table
 // lookup -> multiply-add -> compare -> select -> next lookup (on gfx950 a
 // dependent VALU op costs about fourteen cycles, a two-dword LDS lookup about
 // sixty).  The address without a refill (from x') and the address after one
-// (from the reserve word) are formed in parallel with the compare; the next
+// (from the held word) are formed in parallel with the compare; the next
 // lookup leaves right after the select.  Only then do the refilling lanes,
-// under the exec mask, take the reserve into the state and read their next
-// reserve word straight into its register; that read is first needed one step
-// later, and its lane rank is computed from the ballot outside the masked
-// block so that it leaves early.
+// under the exec mask, shift the held word into the state and read their
+// following word, which is first needed one step later.
 //
 // Table entries (2^10 slots per context):
 //   narrow (every used value in [-128, 127]): two dwords 28 KB apart, read
@@ -50,8 +48,10 @@
 // bit 0 is the coset bit b, and the XOR of bit 1 over coordinates 0..6 is the
 // parity p that selects the last coordinate's context.
 //
-// LDS context order: F, C_0, C_1, then E_{b,p} at index 3 + b + 2p, so that
-// both context bases come from one bit-field extract.
+// LDS context order: F, C_0, C_1, then E_{b,p} at index 3 + b + 2p.  The
+// fixed part of a context's base (C_0 or E_{0,0}) rides in the lookup's
+// instruction offset; the lane's part (b or b + 2p, times 4 KB) comes from one
+// bit-field extract of the entry (narrow entries have zeros in bits 12..23).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -73,7 +73,9 @@ constexpr uint32_t kTableBytes = kTableDwords * 4;         // 28672
 constexpr uint32_t kRows = kProbTotal / 64;                // 16 rows of 64 slots per context
 constexpr uint32_t kMarkWords = kProbTotal / 32;           // 32 bitmap words per context
 constexpr uint32_t kLdsLimit = 160 * 1024;
-constexpr uint32_t kLdsPad = 256;  // slack after the last word buffer
+// slack after the last word buffer: a lane of a corrupt tile reads at most
+// 128 words past its clamped start, i.e. 258 bytes past the tile's end
+constexpr uint32_t kLdsPad = 512;
 constexpr int kOutSym = 4;         // int16 lattice coordinates; 0..3 are the container dtypes
 
 static_assert(kProbBits == 10, "table addressing below assumes 2^10 slots per context");
@@ -104,6 +106,9 @@ typedef __attribute__((address_space(3))) const uint16_t *lds_u16_ptr;
 // dynamic LDS starts at address 0
 __device__ __forceinline__ uint32_t lds_u32(uint32_t byte) { return *(lds_u32_ptr)(uintptr_t)byte; }
 __device__ __forceinline__ uint32_t lds_u16(uint32_t byte) { return *(lds_u16_ptr)(uintptr_t)byte; }
+__device__ __forceinline__ uint32_t lds_u8(uint32_t byte) {
+  return *(__attribute__((address_space(3))) const uint8_t *)(uintptr_t)byte;
+}
 
 // hides a value from constant folding so that address arithmetic stays one v_and_or_b32
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
@@ -172,26 +177,28 @@ __device__ __forceinline__ int32_t symbol_value(uint32_t c, int32_t s) {
 struct Lane {
   uint32_t d0, d1;  // this step's table entry (the lookup is in flight when a step starts)
   uint32_t q;       // X >> 12 of this step's state
-  uint32_t r;       // reserve word (its read may be in flight when a step starts)
-  uint32_t wp;      // wave-uniform LDS byte address of the next word to hand out
+  uint32_t r;       // the state's next word (its read may be in flight when a step starts)
+  uint32_t p;       // LDS byte address of that word
 };
 
-template <bool WIDE>
+// BASE: the fixed part of the context's LDS address, folded into the
+// instruction's offset
+template <bool WIDE, uint32_t BASE>
 __device__ __forceinline__ void table_read(uint32_t a, uint32_t &d0, uint32_t &d1) {
-  d0 = lds_u32(a);
-  if constexpr (!WIDE) d1 = lds_u32(a + kTableBytes);
+  d0 = lds_u32(a + BASE);
+  if constexpr (!WIDE) d1 = lds_u32(a + BASE + kTableBytes);
 }
 
 // one rANS decode step of every active lane: decodes this step's symbol,
-// issues the lookup for the next step (whose context base is nb) and the
-// reserve-word read; returns this step's entry.
-template <bool WIDE>
+// issues the lookup for the next step (context base BASE + nb) and, in
+// refilling lanes, the read of the following word; returns this step's entry.
+template <bool WIDE, uint32_t BASE>
 __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active) {
-  // the reserve word read last step returns right after this step's entry;
-  // reading it here keeps its use out of the refill block
+  // the word read last step returns right after this step's entry; reading
+  // it here keeps its use out of the refill block
   uint32_t r4;
   asm volatile("v_lshlrev_b32 %0, 2, %1" : "=v"(r4) : "v"(L.r));
-  const uint32_t ar = (r4 & 0xffcu) | nb;  // next address after a refill: the reserve word's low bits
+  const uint32_t ar = (r4 & 0xffcu) | nb;  // next address after a refill: the held word's low bits
   const uint32_t e = L.d0;
   uint32_t x;
   if constexpr (WIDE) {
@@ -202,19 +209,15 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   const bool need = active && x < 0x10000u;
   const uint64_t m = __ballot(need);
   const uint32_t ax = (x & 0xffcu) | nb;  // next address without a refill
-  table_read<WIDE>(select_mask(m, ax, ar), L.d0, L.d1);
+  table_read<WIDE, BASE>(select_mask(m, ax, ar), L.d0, L.d1);
   __builtin_amdgcn_sched_barrier(0);  // the next lookup goes out before the refill
-  // the word a refilling lane takes: ranks come from the ballot, outside the
-  // masked block, so the read leaves as early as the mask allows
-  const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-  const uint32_t wa = opaque(L.wp + 2u * rank);
   uint32_t X = x;
-  if (need) {  // refilling lanes only: take the reserve, read the next word into it
-    L.r = lds_u16(wa);
+  if (need) {  // refilling lanes only: take the held word, read the following one
+    L.r = lds_u16(L.p + 2u);
+    L.p += 2u;
     X = (x << 16) | r4;
   }
   L.q = X >> 12;
-  L.wp = opaque_s(L.wp + 2u * (uint32_t)__popcll(m));
   return e;
 }
 
@@ -314,18 +317,21 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
 }
 
 // decodes one tile; PARTIAL handles the last tile of a stream (n < 1024).
-// wb is the LDS byte address of the tile's first word; X is 4 * the start state.
+// wb and we are the LDS byte addresses of the tile's first word and of its
+// end; X is 4 * the start state.
 template <int OUT, bool WIDE, bool PADDED, bool PARTIAL>
-__device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t X, uint32_t tile, uint32_t n,
-                                            const float (&gs)[16], uint32_t lane) {
-  const uint32_t n_act = PARTIAL ? (n < 64u ? n : 64u) : 64u;
+__device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t we, uint32_t X, uint32_t tile,
+                                            uint32_t n, const float (&gs)[16], uint32_t lane) {
   Lane L;
-  table_read<WIDE>(X & 0xffcu, L.d0, L.d1);  // context F
+  table_read<WIDE, 0u>(X & 0xffcu, L.d0, L.d1);  // context F
   L.q = X >> 12;
-  L.r = lane < n_act ? lds_u16(wb + 2u * lane) : 0u;
-  L.wp = opaque_s(wb + 2u * n_act);
-  constexpr uint32_t kBitB = WIDE ? 20u : 24u;  // where bit 0 of v sits in d0
-  const uint32_t kC = opaque_s(0x1000u), kE = opaque_s(0x3000u);  // LDS bases of C_0 and E_{0,0}
+  // this state's words follow the count bytes of the states before it; the
+  // clamp keeps every read of a corrupt tile inside the LDS allocation
+  const uint32_t cnt = lds_u8(wb + lane);
+  const uint32_t p = wb + 2u * kCountWords + 2u * (wave_inclusive_sum(cnt) - cnt);
+  L.p = p < we ? p : we;
+  L.r = lds_u16(L.p);
+  constexpr uint32_t kC = 0x1000u, kE = 0x3000u;  // LDS bases of C_0 and E_{0,0}
   constexpr uint32_t kStepBytes = 64u * ((OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u);
   const gbyte_t tile_out = (gbyte_t)A.out + (uint64_t)tile * (16u * kStepBytes);
 #pragma unroll
@@ -333,18 +339,20 @@ __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t
     const bool act = PARTIAL ? (s * 64 + lane < n) : true;
     if (PARTIAL && s * 64 >= n) break;
     uint32_t e[8];
-    // C_b at LDS context 1 + b; the coset bit is in the entry of coordinate 0
-    const uint32_t cb = opaque(opaque(__builtin_amdgcn_ubfe(L.d0, kBitB, 1u)) * 4096u + kC);
-    e[0] = rans_step<WIDE>(L, cb, act);
+    // C_b at LDS context 1 + b; the coset bit is in the entry of coordinate 0.
+    // A narrow entry's bits 12..23 are zero, so one extract moves bit 24 to 12.
+    const uint32_t cb = WIDE ? __builtin_amdgcn_ubfe(L.d0, 20u, 1u) << 12 : __builtin_amdgcn_ubfe(L.d0, 12u, 13u);
+    e[0] = rans_step<WIDE, kC>(L, cb, act);
 #pragma unroll
-    for (int j = 1; j < 6; ++j) e[j] = rans_step<WIDE>(L, cb, act);
-    // bit kBitB of the XOR is b (all eight coordinates share it), bit kBitB + 1 is p
+    for (int j = 1; j < 6; ++j) e[j] = rans_step<WIDE, kC>(L, cb, act);
+    // the XOR's copy of v's bit 0 is b (all eight coordinates share it), its
+    // copy of bit 1 is p
     uint32_t acc = __builtin_amdgcn_bitop3_b32(e[0], e[1], e[2], 0x96);
     acc = __builtin_amdgcn_bitop3_b32(acc, e[3], e[4], 0x96);
     acc = __builtin_amdgcn_bitop3_b32(acc, e[5], L.d0, 0x96);
-    const uint32_t eb = opaque(opaque(__builtin_amdgcn_ubfe(acc, kBitB, 2u)) * 4096u + kE);
-    e[6] = rans_step<WIDE>(L, eb, act);
-    e[7] = rans_step<WIDE>(L, 0u, act);
+    const uint32_t eb = WIDE ? __builtin_amdgcn_ubfe(acc, 20u, 2u) << 12 : __builtin_amdgcn_ubfe(acc, 12u, 14u);
+    e[6] = rans_step<WIDE, kE>(L, eb, act);
+    e[7] = rans_step<WIDE, 0u>(L, 0u, act);
     if (act) emit_vector<OUT, WIDE, PADDED>(A, opaque_s(tile_out + s * kStepBytes), tile, s * 64u + lane, lane, e, gs[s]);
   }
 }
@@ -391,7 +399,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   // the loads are scalar and their wait leaves the vector loads above alone
   typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
   const cptr_u32 toff = (cptr_u32)(A.blob + A.off_tile_offsets);
-  const uint32_t w_begin = toff[tc];
+  const uint32_t w_begin = toff[tc], w_end = toff[tc + 1u];
   // The workgroup's tiles are consecutive, so their words are one range of the
   // stream: the last wave copies it into LDS with global_load_lds (1 KB per
   // instruction, lanes past the end re-read the last 16 bytes).  Its waits
@@ -403,8 +411,14 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   if (wave == nwaves - 1u) {
     const uint32_t gend = g0 + nwaves < A.n_tiles ? g0 + nwaves : A.n_tiles;
     const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * toff[gend] + 15ull) & ~15ull) - gbyte0) >> 4);
-    const uint8_t *src = A.blob + gbyte0;
-    for (uint32_t i = 0; 64u * i < nchunks; ++i) {
+    const gbyte_t src = (gbyte_t)(A.blob + gbyte0);
+    // whole kilobytes first: no per-lane clamp, so each load issues right
+    // after the last one
+    uint32_t i = 0;
+    for (; 64u * i + 64u <= nchunks; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + A.words_off + 1024u * i),
+                                       16, 0, 0);
+    if (64u * i < nchunks) {
       const uint32_t ch = lane + 64u * i;
       __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (ch < nchunks ? ch : nchunks - 1u)),
                                        (lptr_t)(lds + A.words_off + 1024u * i), 16, 0, 0);
@@ -490,10 +504,11 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   if (!has_tile) return;
   const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
   const uint32_t X = x0 << 2;
+  const uint32_t we = wt + 2u * (w_end - w_begin);
   if (n == 1024u)
-    decode_tile<OUT, WIDE, PADDED, false>(A, wt, X, tile, n, gs, lane);
+    decode_tile<OUT, WIDE, PADDED, false>(A, wt, we, X, tile, n, gs, lane);
   else
-    decode_tile<OUT, WIDE, PADDED, true>(A, wt, X, tile, n, gs, lane);
+    decode_tile<OUT, WIDE, PADDED, true>(A, wt, we, X, tile, n, gs, lane);
 }
 
 typedef void (*KernelFn)(Args);
@@ -543,12 +558,11 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     set_error("stream too large");
     return EP_ERR_FORMAT;
   }
-  // tile offsets: monotone, inside the word section, enough reserve words
+  // tile offsets: monotone, inside the word section, room for the count bytes
   const uint8_t *toff = hb + s.off_tile_offsets;
   for (int64_t t = 0; t < s.tiles; ++t) {
     const uint32_t b = rd<uint32_t>(toff + 4 * t), e = rd<uint32_t>(toff + 4 * t + 4);
-    const int64_t n = std::min<int64_t>(kTileVecs, s.n_vec - t * kTileVecs);
-    if (e < b || e > s.n_words || (int64_t)(e - b) < std::min<int64_t>(n, 64)) {
+    if (e < b || e > s.n_words || e - b < (uint32_t)kCountWords) {
       set_error("corrupt tile offsets");
       return EP_ERR_FORMAT;
     }

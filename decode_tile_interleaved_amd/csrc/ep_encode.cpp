@@ -5,8 +5,9 @@
 // Arbitrary Bitrates" (arXiv abstract, mlsanity index page).  The pages give
 // the steps, not their internals; the choices made here (RMS row scale, a
 // 7-context model built on E8's coset bit and even-sum parity, 10-bit
-// frequencies, 64 interleaved states per 1024-vector tile, one reserve word
-// per state) define the stream that ep_decode.hip reads.
+// frequencies, 64 interleaved states per 1024-vector tile, each state's words
+// stored together behind a count byte) define the stream that ep_decode.hip
+// reads.
 #include <algorithm>
 #include <atomic>
 #include <cmath>
@@ -312,9 +313,7 @@ static double estimate_bpp(const Problem &P, double a) {
       uint64_t n = part[0].get(c, tb.smin[c] + i);
       if (n) info += (double)n * ((double)kProbBits - std::log2((double)tb.freq[c][i]));
     }
-  // 40 bits per state: the final state L (14 bits), the unused high bits of
-  // the stored start state (10 on average) and the never-consumed reserve word
-  double bits = info * ((double)P.n_vec / (double)S) + 40.0 * (double)(kStatesPerTile * P.tiles) +
+  double bits = info * ((double)P.n_vec / (double)S) + kStateBits * (double)(kStatesPerTile * P.tiles) +
                 8.0 * (double)metadata_bytes(P, tb.total_symbols());
   return bits / ((double)P.R * (double)P.C);
 }
@@ -358,7 +357,7 @@ static double estimate_bpp_full(const Problem &P, double a) {
       uint64_t n = part[0].get(c, tb.smin[c] + i);
       if (n) info += (double)n * ((double)kProbBits - std::log2((double)tb.freq[c][i]));
     }
-  double bits = info + 40.0 * (double)(kStatesPerTile * P.tiles) + 8.0 * (double)metadata_bytes(P, tb.total_symbols());
+  double bits = info + kStateBits * (double)(kStatesPerTile * P.tiles) + 8.0 * (double)metadata_bytes(P, tb.total_symbols());
   return bits / ((double)P.R * (double)P.C);
 }
 
@@ -392,7 +391,8 @@ static double choose_scale(const Problem &P, double target, double *closest) {
 }
 
 // ---------------------------------------------------------------------------
-// one tile: interleaved rANS, reverse order, then the lookahead word order
+// one tile: interleaved rANS in reverse order, then the count bytes and each
+// state's words in the order the decoder consumes them
 // ---------------------------------------------------------------------------
 struct TileOut {
   uint32_t states[kStatesPerTile];
@@ -402,7 +402,6 @@ struct TileOut {
 static void encode_tile(const Problem &P, const Tables &tb, const std::vector<int32_t> &V, int64_t tile, TileOut &out) {
   const int64_t first = tile * kTileVecs;
   const int n = (int)std::min<int64_t>(kTileVecs, P.n_vec - first);
-  const int active = std::min(n, kStatesPerTile);
   // (frequency, cumulative) of every coordinate, vector-major
   std::vector<uint32_t> fc((size_t)n * 8 * 2);
   for (int i = 0; i < n; ++i) {
@@ -441,14 +440,10 @@ static void encode_tile(const Problem &P, const Tables &tb, const std::vector<in
   std::vector<std::vector<uint16_t>> lane(kStatesPerTile);
   for (size_t k = emitted.size(); k-- > 0;) lane[who[k]].push_back(emitted[k]);
   out.words.clear();
-  out.words.reserve(emitted.size() + active);
-  for (int q = 0; q < active; ++q) out.words.push_back(lane[q].empty() ? 0 : lane[q][0]);
-  size_t used[kStatesPerTile] = {};
-  for (size_t k = emitted.size(); k-- > 0;) {
-    int q = who[k];
-    ++used[q];
-    out.words.push_back(used[q] < lane[q].size() ? lane[q][used[q]] : 0);
-  }
+  out.words.reserve(emitted.size() + kCountWords);
+  for (int q = 0; q < kStatesPerTile; q += 2)  // at most 8 words per vector: every count fits a byte
+    out.words.push_back((uint16_t)(lane[q].size() | lane[q + 1].size() << 8));
+  for (int q = 0; q < kStatesPerTile; ++q) out.words.insert(out.words.end(), lane[q].begin(), lane[q].end());
 }
 
 // ---------------------------------------------------------------------------
@@ -626,7 +621,7 @@ int compress(const void *src, int dtype, int64_t rows, int64_t cols, double targ
   double a = fixed_a;
   if (!(fixed_a > 0.0)) {
     const double floor_bpp =
-        (40.0 * (double)(kStatesPerTile * P.tiles) + 8.0 * (double)metadata_bytes(P, kContexts)) /
+        (kStateBits * (double)(kStatesPerTile * P.tiles) + 8.0 * (double)metadata_bytes(P, kContexts)) /
         ((double)P.R * (double)P.C);
     if (target < 1.02 * floor_bpp) {
       err = "target_bpp below this stream's fixed per-tile overhead (" + std::to_string(floor_bpp) + " bpp)";

@@ -10,7 +10,9 @@
 //   scales           float32 g_r per row
 //   states           uint32 initial decoder state per (tile, state)
 //   tile offsets     uint32 word index of each tile's first word, plus the end
-//   words            uint16 entropy-coded words
+//   words            uint16 words, tile after tile: 32 words of count bytes
+//                    (byte q = number of words state q consumes), then each
+//                    state's words in consumption order, states ascending
 // A raw stream (method 1) is the header followed by the container bytes.
 #pragma once
 
@@ -28,8 +30,13 @@ constexpr int kContexts = 7;
 constexpr int kProbBits = 10;
 constexpr uint32_t kProbTotal = 1u << kProbBits;
 constexpr uint32_t kStateLow = 1u << 14;   // rANS states live in [2^14, 2^30)
+constexpr int kCountWords = 32;            // words of per-state count bytes at the start of a tile
+// stream bits per state beyond its symbols' information, as the rate
+// estimate counts them: the fixed final state L (14), the unused high bits of
+// the stored start state (10 on average) and the count byte (8)
+constexpr double kStateBits = 32.0;
 constexpr int kTileVecs = 1024;            // E8 vectors (8 coordinates) per tile
-constexpr int kStatesPerTile = 64;         // interleaved rANS states per tile
+constexpr int kStatesPerTile = 64;         // interleaved rANS states per tile (2 count bytes per word)
 constexpr int kValueMin = -2048, kValueMax = 2047;  // lattice coordinates the stream can hold (12-bit field)
 
 enum Method : uint8_t { kLattice = 0, kRaw = 1 };

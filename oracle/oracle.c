@@ -45,6 +45,7 @@
 #define OR_HDR 128
 #define OR_MAGIC 0x314B5045u /* "EPK1" little-endian */
 #define OR_VERSION 1
+#define OR_STATE_BITS 32.0  /* estimated stream bits per rANS state beyond its symbols' information */
 #define OR_STATE_L 16384u    /* rANS lower state bound L = 2^14; states lie in [L, 2^30); words are 16 bits */
 
 static int esize_of(int dt) { return (dt == OR_BF16 || dt == OR_FP16) ? 2 : 1; }
@@ -351,14 +352,13 @@ static int quantize_all(const double *x, const or_geom *g, const float *gs, int3
 /* Decode order: step s, coordinate j, state q (ascending), for local vector */
 /* i = s*S + q when i < n.  The first min(n, S) states are active.           */
 /* Decode: slot = x mod M; x = f*(x >> prob_bits) + slot - c;                */
-/*         if x < L: x = (x << 16) | w_q, where w_q is the word state q      */
-/*         holds in reserve.                                                 */
+/*         if x < L: x = (x << 16) | w, w = state q's next word.             */
 /* Encode: if x >= f * 2^(30 - prob_bits): emit x & 0xffff, x >>= 16;       */
 /*         x = (x / f) * M + (x mod f) + c.                                  */
-/* Lookahead word order: every active state first takes one reserve word    */
-/* (states ascending); after each (s, j), every state that refilled takes a  */
-/* new reserve word (states ascending).  The reserve a state takes after its */
-/* last refill is never used and is stored as 0.                             */
+/* Tile word layout: one count byte per state (the number of words it        */
+/* consumes; states ascending, two to a 16-bit word, the last word padded    */
+/* with 0), then every state's words in the order it consumes them, states   */
+/* ascending.                                                                */
 /* ------------------------------------------------------------------------ */
 typedef struct {
   uint16_t *w;
@@ -383,7 +383,6 @@ static int encode_tile(const or_geom *g, const or_tables *t, const int32_t *v, i
   int64_t first = tile * g->tile_vecs;
   int64_t n = g->n_vec - first;
   if (n > g->tile_vecs) n = g->tile_vecs;
-  int64_t n_act = n < g->S ? n : g->S;
   int64_t steps = (g->tile_vecs + g->S - 1) / g->S;
   uint32_t M = 1u << g->prob_bits;
   int rc = OR_OK;
@@ -433,16 +432,14 @@ static int encode_tile(const or_geom *g, const or_tables *t, const int32_t *v, i
     int32_t q = owner[k - 1];
     lane_words[start[q] + cur[q]++] = rev.w[k - 1];
   }
-  /* lookahead order: initial reserves, then one reserve per consumed word */
-  for (int64_t q = 0; q < n_act; q++)
-    if ((rc = words_push(out, cnt[q] > 0 ? lane_words[start[q]] : 0))) goto done;
-  for (int64_t q = 0; q < g->S; q++) cur[q] = 0;
-  for (uint64_t k = rev.n; k > 0; k--) {
-    int32_t q = owner[k - 1];
-    cur[q]++;
-    uint16_t w = cur[q] < cnt[q] ? lane_words[start[q] + cur[q]] : 0;
-    if ((rc = words_push(out, w))) goto done;
+  /* count bytes, then the per-state lists back to back */
+  for (int64_t q = 0; q < g->S; q += 2) {
+    int64_t hi = q + 1 < g->S ? cnt[q + 1] : 0;
+    if (cnt[q] > 255 || hi > 255) { rc = OR_ERR_SHAPE; goto done; }
+    if ((rc = words_push(out, (uint16_t)(cnt[q] | (hi << 8))))) goto done;
   }
+  for (uint64_t k = 0; k < rev.n; k++)
+    if ((rc = words_push(out, lane_words[k]))) goto done;
 done:
   free(rev.w);
   free(owner);
@@ -585,12 +582,11 @@ done:
 /* Sampled storage estimate (the pages' resolution selection without         */
 /* repeated full-stream encoding).  S = min(n_vec, 65536) vectors at indices */
 /* floor(k * n_vec / S); tables are built from the sample alone;             */
-/* bits = (n_vec/S) * sum c_s (prob_bits - log2 f_s) + 40 * states           */
+/* bits = (n_vec/S) * sum c_s (prob_bits - log2 f_s) + 32 * states           */
 /*        + 8 * (header, tables, scales, tile offsets).                      */
-/* 40 bits per state: 14 for the fixed final state L, on average 10 unused   */
+/* 32 bits per state: 14 for the fixed final state L, on average 10 unused   */
 /* high bits of the stored 32-bit start state (log-uniform in [2^14, 2^30)), */
-/* and the one 16-bit reserve word that is never consumed.  Out-of-range     */
-/* lattice values give +inf.                                                 */
+/* and the state's 8-bit word count.  Out-of-range lattice values give +inf. */
 /* ------------------------------------------------------------------------ */
 #define OR_SAMPLE_VECS 65536
 
@@ -619,7 +615,7 @@ double or_estimate_bpp_rows(const double *x, const double *rms, const or_geom *g
       uint64_t cnt = (t.smin[c] + s + OR_SYM_OFF < OR_SYM_SPAN) ? h->cnt[c][t.smin[c] + s + OR_SYM_OFF] : 0;
       if (cnt) info += (double)cnt * ((double)g->prob_bits - log2((double)t.freq[c][s]));
     }
-  double bits = info * ((double)g->n_vec / (double)S) + 40.0 * (double)(g->S * g->T) +
+  double bits = info * ((double)g->n_vec / (double)S) + OR_STATE_BITS * (double)(g->S * g->T) +
                 8.0 * (double)meta_bytes(g, tables_total_nsym(&t));
   tables_free(&t);
   free(h);
@@ -653,7 +649,7 @@ static double estimate_bpp_full(const double *x, const or_geom *g, double a) {
         uint64_t cnt = (t.smin[c] + s + OR_SYM_OFF < OR_SYM_SPAN) ? h->cnt[c][t.smin[c] + s + OR_SYM_OFF] : 0;
         if (cnt) info += (double)cnt * ((double)g->prob_bits - log2((double)t.freq[c][s]));
       }
-    double bits = info + 40.0 * (double)(g->S * g->T) + 8.0 * (double)meta_bytes(g, tables_total_nsym(&t));
+    double bits = info + OR_STATE_BITS * (double)(g->S * g->T) + 8.0 * (double)meta_bytes(g, tables_total_nsym(&t));
     result = bits / ((double)g->R * (double)g->C);
   }
 done:
@@ -767,7 +763,7 @@ int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, in
     for (int64_t r = 0; r < R; r++) rms[r] = row_rms(x + r * C, C);
     or_sel_ctx sc = {x, rms, &g, dtype, target};
     /* targets below the fixed per-tile overhead cannot be met */
-    double floor_bpp = (40.0 * (double)(g.S * g.T) + 8.0 * (double)meta_bytes(&g, OR_NCTX)) /
+    double floor_bpp = (OR_STATE_BITS * (double)(g.S * g.T) + 8.0 * (double)meta_bytes(&g, OR_NCTX)) /
                        ((double)R * (double)C);
     if (target < 1.02 * floor_bpp) { free(rms); return OR_ERR_TARGET; }
     double best_est = INFINITY;
@@ -921,11 +917,11 @@ static int decode_lattice(const uint8_t *b, const or_header *h, int32_t *v) {
   uint32_t M = 1u << g->prob_bits;
   int64_t steps = (g->tile_vecs + g->S - 1) / g->S;
   uint32_t *x = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)g->S);
-  uint32_t *res = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)g->S); /* reserve word per state */
+  uint64_t *pos = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)g->S); /* next word of each state */
+  uint64_t *end = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)g->S); /* end of each state's words */
   int32_t *vb = (int32_t *)malloc(sizeof(int32_t) * (size_t)g->S);     /* coset bit per state */
   int32_t *zp = (int32_t *)malloc(sizeof(int32_t) * (size_t)g->S);     /* running z sum per state */
-  uint8_t *refilled = (uint8_t *)malloc((size_t)g->S);
-  if (!x || !res || !vb || !zp || !refilled) { rc = OR_ERR_NOMEM; goto done; }
+  if (!x || !pos || !end || !vb || !zp) { rc = OR_ERR_NOMEM; goto done; }
   for (int64_t tile = 0; tile < g->T; tile++) {
     int64_t first = tile * g->tile_vecs;
     int64_t n = g->n_vec - first;
@@ -933,13 +929,21 @@ static int decode_lattice(const uint8_t *b, const or_header *h, int32_t *v) {
     int64_t n_act = n < g->S ? n : g->S;
     uint64_t wp = get_u32(b + h->o_to + 4 * tile);
     uint64_t wend = get_u32(b + h->o_to + 4 * (tile + 1));
-    if (wend < wp || wend > h->n_words || wend - wp < (uint64_t)n_act) { rc = OR_ERR_FORMAT; goto done; }
+    uint64_t ncw = (uint64_t)(g->S + 1) / 2; /* words holding the count bytes */
+    if (wend < wp || wend > h->n_words || wend - wp < ncw) { rc = OR_ERR_FORMAT; goto done; }
     for (int64_t q = 0; q < g->S; q++) x[q] = get_u32(b + h->o_st + 4 * (tile * g->S + q));
-    for (int64_t q = 0; q < n_act; q++) res[q] = get_u16(b + h->o_w + 2 * (wp++));
+    uint64_t next = wp + ncw;
+    for (int64_t q = 0; q < g->S; q++) {
+      uint64_t c = b[h->o_w + 2 * wp + (uint64_t)q];
+      if (q >= n_act && c != 0) { rc = OR_ERR_FORMAT; goto done; }
+      pos[q] = next;
+      next += c;
+      end[q] = next;
+    }
+    if (next != wend) { rc = OR_ERR_FORMAT; goto done; }
     for (int64_t s = 0; s < steps; s++)
       for (int j = 0; j < 8; j++) {
         for (int64_t q = 0; q < g->S; q++) {
-          refilled[q] = 0;
           int64_t i = s * g->S + q;
           if (i >= n) continue;
           int ctx;
@@ -952,8 +956,8 @@ static int decode_lattice(const uint8_t *b, const or_header *h, int32_t *v) {
           while (!(t.cum[ctx][si] <= slot && slot < t.cum[ctx][si + 1])) si++;
           x[q] = t.freq[ctx][si] * (x[q] >> g->prob_bits) + slot - t.cum[ctx][si];
           if (x[q] < OR_STATE_L) {
-            x[q] = (x[q] << 16) | res[q];
-            refilled[q] = 1;
+            if (pos[q] >= end[q]) { rc = OR_ERR_FORMAT; goto done; }
+            x[q] = (x[q] << 16) | get_u16(b + h->o_w + 2 * (pos[q]++));
           }
           int32_t sym = t.smin[ctx] + si;
           int64_t vid = first + i;
@@ -967,22 +971,16 @@ static int decode_lattice(const uint8_t *b, const or_header *h, int32_t *v) {
             if (j < 7) zp[q] += sym;
           }
         }
-        for (int64_t q = 0; q < g->S; q++)
-          if (refilled[q]) {
-            if (wp >= wend) { rc = OR_ERR_FORMAT; goto done; }
-            res[q] = get_u16(b + h->o_w + 2 * (wp++));
-          }
       }
-    if (wp != wend) { rc = OR_ERR_FORMAT; goto done; }
     for (int64_t q = 0; q < n_act; q++)
-      if (x[q] != OR_STATE_L) { rc = OR_ERR_FORMAT; goto done; }
+      if (x[q] != OR_STATE_L || pos[q] != end[q]) { rc = OR_ERR_FORMAT; goto done; }
   }
 done:
   free(x);
-  free(res);
+  free(pos);
+  free(end);
   free(vb);
   free(zp);
-  free(refilled);
   tables_free(&t);
   return rc;
 }

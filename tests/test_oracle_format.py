@@ -109,8 +109,8 @@ def test_rate_within_two_percent_rowscale4096():
     d = oracle.info(blob)
     y = oracle.decompress(blob)
     e = rel_l2(y, t)
-    # payload rate: everything but the per-state overhead (40 bits each) and metadata
-    meta_bits = 8 * (128 + 4 * t.shape[0] + 4 * (d["n_tiles"] + 1) + 28) + 40 * 64 * d["n_tiles"]
+    # payload rate: everything but the per-state overhead (32 bits each) and metadata
+    meta_bits = 8 * (128 + 4 * t.shape[0] + 4 * (d["n_tiles"] + 1) + 28) + 32 * 64 * d["n_tiles"]
     r_pay = (8 * blob.size - meta_bits) / t.numel()
     G = E8C["normalized_second_moment_num"] / E8C["normalized_second_moment_den"]
     theory = math.sqrt(2 * math.pi * math.e * G) * 2 ** (-r_pay)
@@ -209,3 +209,47 @@ def test_corrupt_streams_rejected():
         assert not np.array_equal(v, oracle.decode_symbols(blob))
     except oracle.OracleError:
         pass
+
+
+def tile_words(blob):
+    """(count bytes, word lists) of every tile, read straight from the layout:
+    tile offsets u32[T+1] at header byte 88, words at header byte 96."""
+    hdr = blob[:128].view(np.uint64)
+    o_to, o_w, n_words = int(hdr[11]), int(hdr[12]), int(hdr[13])
+    d = oracle.info(blob)
+    toff = blob[o_to:o_to + 4 * (d["n_tiles"] + 1)].view(np.uint32)
+    words = blob[o_w:o_w + 2 * n_words].view(np.uint16)
+    assert toff[0] == 0 and toff[-1] == n_words
+    return [(words[b:e][:32].view(np.uint8).astype(np.int64), words[b:e][32:]) for b, e in zip(toff[:-1], toff[1:])]
+
+
+@pytest.mark.parametrize("shape", [(8, 8), (129, 64), (96, 1024)])
+def test_tile_word_layout(shape):
+    """Each tile: 64 count bytes (a state consumes at most one word per symbol,
+    so at most 16 * 8 = 128), then the states' word lists back to back; states
+    without vectors in a partial tile consume nothing."""
+    t = W.gaussian(*shape, 0.02, seed=3 + shape[0])
+    blob, rc, _ = oracle.compress(t, 4.0, fixed_a=0.3)
+    assert rc == 0
+    n_vec = shape[0] * ((shape[1] + 7) // 8)
+    for k, (cnt, rest) in enumerate(tile_words(blob)):
+        n = min(1024, n_vec - 1024 * k)
+        assert cnt.sum() == rest.size
+        assert cnt.max() <= 8 * math.ceil(n / 64)
+        assert np.all(cnt[min(n, 64):] == 0)
+        assert np.all(cnt[: min(n, 64)] > 0)  # at 4 bpp every state refills
+
+
+def test_count_bytes_decide_word_ownership():
+    """Moving one word from state 0's list to state 1's (count bytes only) is
+    caught: state 0 runs out of words or a state ends off its list."""
+    t = W.gaussian(64, 1024, 0.02, seed=77)
+    blob, rc, _ = oracle.compress(t, 4.0, fixed_a=0.3)
+    assert rc == 0
+    o_w = int(blob[:128].view(np.uint64)[12])
+    bad = blob.copy()
+    assert bad[o_w] > 0
+    bad[o_w] -= 1
+    bad[o_w + 1] += 1
+    with pytest.raises(oracle.OracleError):
+        oracle.decode_symbols(bad)
