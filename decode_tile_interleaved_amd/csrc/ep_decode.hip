@@ -94,7 +94,7 @@ struct Args {
   uint32_t rows, vpr;             // rows; vectors per row
   uint32_t row_magic, row_shift;  // vec / vpr = umulhi(vec, row_magic) >> row_shift  (vpr > 1)
   uint32_t n_vec, n_tiles, waves;
-  uint32_t rec_off, mark_off, rowrec_off, words_off;  // LDS byte offsets
+  uint32_t rec_off, mark_off, words_off;  // LDS byte offsets
 };
 
 typedef __attribute__((address_space(1))) void *gptr_t;
@@ -194,11 +194,6 @@ __device__ __forceinline__ void table_read(uint32_t a, uint32_t &d0, uint32_t &d
 // refilling lanes, the read of the following word; returns this step's entry.
 template <bool WIDE, uint32_t BASE>
 __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active) {
-  // the word read last step returns right after this step's entry; reading
-  // it here keeps its use out of the refill block
-  uint32_t r4;
-  asm volatile("v_lshlrev_b32 %0, 2, %1" : "=v"(r4) : "v"(L.r));
-  const uint32_t ar = (r4 & 0xffcu) | nb;  // next address after a refill: the held word's low bits
   const uint32_t e = L.d0;
   uint32_t x;
   if constexpr (WIDE) {
@@ -206,6 +201,12 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   } else {
     x = __umul24(e, L.q) + L.d1;
   }
+  // the word read last step returns right after this step's entry; using it
+  // here (after the multiply-add, which starts the chain) keeps its use out
+  // of the refill block
+  uint32_t r4;
+  asm volatile("v_lshlrev_b32 %0, 2, %1" : "=v"(r4) : "v"(L.r), "v"(x));
+  const uint32_t ar = (r4 & 0xffcu) | nb;  // next address after a refill: the held word's low bits
   const bool need = active && x < 0x10000u;
   const uint64_t m = __ballot(need);
   const uint32_t ax = (x & 0xffcu) | nb;  // next address without a refill
@@ -429,7 +430,6 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   //         bitmap, then the context's 16 table rows of 64 slots ----------
   uint2 *rec = reinterpret_cast<uint2 *>(lds + A.rec_off);          // (d0, cum term) per used symbol
   uint32_t *mark = reinterpret_cast<uint32_t *>(lds + A.mark_off);  // [ctx][32] start bits
-  uint4 *rowrec = reinterpret_cast<uint4 *>(lds + A.rowrec_off);     // [ctx][16] per-row fill records
   uint32_t *tab = reinterpret_cast<uint32_t *>(lds);
   for (uint32_t c = wave; c < (uint32_t)kContexts; c += nwaves) {
     const uint32_t n = pick(A.nsym, c), fidx = pick(A.fidx, c), nzbase = pick(A.nzbase, c);
@@ -457,8 +457,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
       carry += __builtin_amdgcn_readlane(incl, 63);
       nzb += (uint32_t)__popcll(m);
     }
-    // row t (lanes 0..15): its start bits shifted down by one and the record
-    // index before it, stored for the whole wave to read back by broadcast
+    // row t (lane t < 16): its start bits shifted down by one and the record
+    // index before it
+    uint32_t rlo = 0, rhi = 0, rbase = 0;
     {
       uint32_t lo = 0, hi = 0;
       if (lane < kRows) {
@@ -467,24 +468,23 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
       }
       const uint32_t cnt = (uint32_t)(__popc(lo) + __popc(hi));
       const uint32_t first = nzbase + row16_inclusive_sum(cnt) - cnt;
-      if (lane < kRows)
-        rowrec[c * kRows + lane] = make_uint4(__builtin_amdgcn_alignbit(hi, lo, 1u), hi >> 1, first + (lo & 1u) - 1u, 0u);
+      rlo = __builtin_amdgcn_alignbit(hi, lo, 1u);
+      rhi = hi >> 1;
+      rbase = first + (lo & 1u) - 1u;
     }
     // slot record = first + (starts at or below the slot) - 1
     //             = first + bit0 - 1 + popcount of (bits >> 1) below the lane.
-    // All sixteen records are read before any table write: the compiler cannot
+    // The row values reach every lane through readlane (no LDS traffic), and
+    // all sixteen records are read before any table write: the compiler cannot
     // tell the record list and the table apart, so interleaving would put an
     // LDS round trip on every row.
-    // Three batches, each one LDS round trip: the row records (broadcast
-    // reads), then the slot records, then the table writes.
-    uint4 rr[kRows];
-#pragma unroll
-    for (uint32_t row = 0; row < kRows; ++row) rr[row] = rowrec[c * kRows + row];
-    __builtin_amdgcn_sched_barrier(0);
     uint2 rc[kRows];
 #pragma unroll
-    for (uint32_t row = 0; row < kRows; ++row)
-      rc[row] = rec[__builtin_amdgcn_mbcnt_hi(rr[row].y, __builtin_amdgcn_mbcnt_lo(rr[row].x, rr[row].z))];
+    for (uint32_t row = 0; row < kRows; ++row) {
+      const uint32_t mlo = __builtin_amdgcn_readlane(rlo, row), mhi = __builtin_amdgcn_readlane(rhi, row);
+      const uint32_t b = __builtin_amdgcn_readlane(rbase, row);
+      rc[row] = rec[__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, b))];
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (uint32_t row = 0; row < kRows; ++row) {
@@ -598,7 +598,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
       return EP_ERR_FORMAT;
     }
   }
-  // LDS layout: tables | records | bitmap | row records | words | pad.  The
+  // LDS layout: tables | records | bitmap | words | pad.  The
   // words of a workgroup's consecutive tiles are one range; with k waves per
   // workgroup the buffer holds the longest such range, in whole 1 KB copies.
   uint32_t off = wide ? kTableBytes : 2 * kTableBytes;
@@ -606,8 +606,6 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   off += 8 * nz_total;
   A.mark_off = off;
   off = (uint32_t)align16(off + 4 * kContexts * kMarkWords);
-  A.rowrec_off = off;
-  off += 16 * kContexts * kRows;
   A.words_off = off;
   auto span_for = [&](uint32_t k) {
     uint64_t span = 0;
