@@ -22,36 +22,36 @@
 //      number of starts up to it, which v_mbcnt counts from the row's bitmap;
 //   3. each wave decodes its tile.
 //
-// Decode step for state x in [2^14, 2^30), kept as X = 4x so that the table
-// address is one AND-OR:  4*slot = X & 0xffc;  e = table[ctx][slot];
-//   x' = f * (x >> 10) + (slot - cum);  if x' < 2^14: x = x' << 16 | w
+// Decode step for state x in [2^13, 2^29), kept as X = 8x so that the table
+// address is one AND-OR:  8*slot = X & 0x1ff8;  e = table[ctx][slot];
+//   x' = f * (x >> 10) + (slot - cum);  if x' < 2^13: x = x' << 16 | w
 // where w is the state's next word.  A tile stores each state's words
 // together (behind one count byte per state), so a lane walks its own word
 // list with a private pointer and always holds its next word in a register.
 //
 // The step is software-pipelined around its one serial dependence, table
 // lookup -> multiply-add -> compare -> select -> next lookup (on gfx950 a
-// dependent VALU op costs about fourteen cycles, a two-dword LDS lookup about
-// sixty).  The address without a refill (from x') and the address after one
+// dependent VALU op costs about fourteen cycles, an eight-byte LDS lookup
+// about sixty).  The address without a refill (from x') and the address after one
 // (from the held word) are formed in parallel with the compare; the next
 // lookup leaves right after the select.  Only then do the refilling lanes,
 // under the exec mask, shift the held word into the state and read their
 // following word, which is first needed one step later.
 //
-// Table entries (2^10 slots per context):
-//   narrow (every used value in [-128, 127]): two dwords 28 KB apart, read
-//     with one ds_read2st64: d0 = 4f | (v + 128) << 24, d1 = 4 (slot - cum),
-//     so that X' = mad_u32_u24(d0, X >> 12, d1) and the value converts with
-//     one v_cvt_f32_ubyte3;
-//   wide (values in [-2048, 2047]): e = f | (slot - cum) << 10 | v << 20.
+// Table entries (2^10 slots of 8 bytes per context; one ds_read_b64 meets
+// fewer LDS bank conflicts than two dword reads):
+//   narrow (every used value in [-128, 127]): d0 = 8f | (v + 128) << 24,
+//     d1 = 8 (slot - cum), so that X' = mad_u32_u24(d0, X >> 13, d1) and the
+//     value converts with one v_cvt_f32_ubyte3;
+//   wide (values in [-2048, 2047]): d0 = f | (slot - cum) << 10 | v << 20.
 // Either way bits 0 and 1 of v sit at a fixed place in d0 (24/25 or 20/21):
 // bit 0 is the coset bit b, and the XOR of bit 1 over coordinates 0..6 is the
 // parity p that selects the last coordinate's context.
 //
-// LDS context order: F, C_0, C_1, then E_{b,p} at index 3 + b + 2p.  The
-// fixed part of a context's base (C_0 or E_{0,0}) rides in the lookup's
-// instruction offset; the lane's part (b or b + 2p, times 4 KB) comes from one
-// bit-field extract of the entry (narrow entries have zeros in bits 12..23).
+// LDS context order: F, C_0, C_1, then E_{b,p} at index 3 + b + 2p, 8 KB
+// apart.  The fixed part of a context's base (C_0 or E_{0,0}) rides in the
+// lookup's instruction offset; the lane's part (b or b + 2p, times 8 KB)
+// comes from the entry.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -68,8 +68,8 @@ namespace ep {
 namespace {
 
 constexpr int kMaxWaves = 8;
-constexpr uint32_t kTableDwords = kContexts * kProbTotal;  // 7168
-constexpr uint32_t kTableBytes = kTableDwords * 4;         // 28672
+constexpr uint32_t kCtxBytes = kProbTotal * 8;             // 8 KB per context
+constexpr uint32_t kTableBytes = kContexts * kCtxBytes;     // 57344
 constexpr uint32_t kRows = kProbTotal / 64;                // 16 rows of 64 slots per context
 constexpr uint32_t kMarkWords = kProbTotal / 32;           // 32 bitmap words per context
 constexpr uint32_t kLdsLimit = 160 * 1024;
@@ -176,17 +176,25 @@ __device__ __forceinline__ int32_t symbol_value(uint32_t c, int32_t s) {
 // Per-lane pipeline state of a tile's decode.
 struct Lane {
   uint32_t d0, d1;  // this step's table entry (the lookup is in flight when a step starts)
-  uint32_t q;       // X >> 12 of this step's state
+  uint32_t q;       // X >> 13 of this step's state
   uint32_t r;       // the state's next word (its read may be in flight when a step starts)
   uint32_t p;       // LDS byte address of that word
 };
 
 // BASE: the fixed part of the context's LDS address, folded into the
 // instruction's offset
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2 *lds_u64_ptr;
+
 template <bool WIDE, uint32_t BASE>
 __device__ __forceinline__ void table_read(uint32_t a, uint32_t &d0, uint32_t &d1) {
-  d0 = lds_u32(a + BASE);
-  if constexpr (!WIDE) d1 = lds_u32(a + BASE + kTableBytes);
+  if constexpr (WIDE) {
+    d0 = lds_u32(a + BASE);
+  } else {
+    const u32x2 v = *(lds_u64_ptr)(uintptr_t)(a + BASE);
+    d0 = v.x;
+    d1 = v.y;
+  }
 }
 
 // one rANS decode step of every active lane: decodes this step's symbol,
@@ -197,28 +205,28 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   const uint32_t e = L.d0;
   uint32_t x;
   if constexpr (WIDE) {
-    x = (__umul24(e & 0x3ffu, L.q) + ((e >> 10) & 0x3ffu)) << 2;
+    x = (__umul24(e & 0x3ffu, L.q) + ((e >> 10) & 0x3ffu)) << 3;
   } else {
     x = __umul24(e, L.q) + L.d1;
   }
   // the word read last step returns right after this step's entry; using it
   // here (after the multiply-add, which starts the chain) keeps its use out
   // of the refill block
-  uint32_t r4;
-  asm volatile("v_lshlrev_b32 %0, 2, %1" : "=v"(r4) : "v"(L.r), "v"(x));
-  const uint32_t ar = (r4 & 0xffcu) | nb;  // next address after a refill: the held word's low bits
+  uint32_t r8;
+  asm volatile("v_lshlrev_b32 %0, 3, %1" : "=v"(r8) : "v"(L.r), "v"(x));
+  const uint32_t ar = (r8 & 0x1ff8u) | nb;  // next address after a refill: the held word's low bits
   const bool need = active && x < 0x10000u;
   const uint64_t m = __ballot(need);
-  const uint32_t ax = (x & 0xffcu) | nb;  // next address without a refill
+  const uint32_t ax = (x & 0x1ff8u) | nb;  // next address without a refill
   table_read<WIDE, BASE>(select_mask(m, ax, ar), L.d0, L.d1);
   __builtin_amdgcn_sched_barrier(0);  // the next lookup goes out before the refill
   uint32_t X = x;
   if (need) {  // refilling lanes only: take the held word, read the following one
     L.r = lds_u16(L.p + 2u);
     L.p += 2u;
-    X = (x << 16) | r4;
+    X = (x << 16) | r8;
   }
-  L.q = X >> 12;
+  L.q = X >> 13;
   return e;
 }
 
@@ -319,20 +327,21 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
 
 // decodes one tile; PARTIAL handles the last tile of a stream (n < 1024).
 // wb and we are the LDS byte addresses of the tile's first word and of its
-// end; X is 4 * the start state.
+// end; X is 8 * the start state.
 template <int OUT, bool WIDE, bool PADDED, bool PARTIAL>
 __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t we, uint32_t X, uint32_t tile,
                                             uint32_t n, const float (&gs)[16], uint32_t lane) {
   Lane L;
-  table_read<WIDE, 0u>(X & 0xffcu, L.d0, L.d1);  // context F
-  L.q = X >> 12;
+  table_read<WIDE, 0u>(X & 0x1ff8u, L.d0, L.d1);  // context F
+  L.q = X >> 13;
   // this state's words follow the count bytes of the states before it; the
   // clamp keeps every read of a corrupt tile inside the LDS allocation
   const uint32_t cnt = lds_u8(wb + lane);
   const uint32_t p = wb + 2u * kCountWords + 2u * (wave_inclusive_sum(cnt) - cnt);
   L.p = p < we ? p : we;
   L.r = lds_u16(L.p);
-  constexpr uint32_t kC = 0x1000u, kE = 0x3000u;  // LDS bases of C_0 and E_{0,0}
+  constexpr uint32_t kC = kCtxBytes, kE = 3u * kCtxBytes;  // LDS bases of C_0 and E_{0,0}
+  constexpr uint32_t kBitB = WIDE ? 20u : 24u;  // where bit 0 of v sits in d0
   constexpr uint32_t kStepBytes = 64u * ((OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u);
   const gbyte_t tile_out = (gbyte_t)A.out + (uint64_t)tile * (16u * kStepBytes);
 #pragma unroll
@@ -340,9 +349,8 @@ __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t
     const bool act = PARTIAL ? (s * 64 + lane < n) : true;
     if (PARTIAL && s * 64 >= n) break;
     uint32_t e[8];
-    // C_b at LDS context 1 + b; the coset bit is in the entry of coordinate 0.
-    // A narrow entry's bits 12..23 are zero, so one extract moves bit 24 to 12.
-    const uint32_t cb = WIDE ? __builtin_amdgcn_ubfe(L.d0, 20u, 1u) << 12 : __builtin_amdgcn_ubfe(L.d0, 12u, 13u);
+    // C_b at LDS context 1 + b; the coset bit is in the entry of coordinate 0
+    const uint32_t cb = __builtin_amdgcn_ubfe(L.d0, kBitB, 1u) << 13;
     e[0] = rans_step<WIDE, kC>(L, cb, act);
 #pragma unroll
     for (int j = 1; j < 6; ++j) e[j] = rans_step<WIDE, kC>(L, cb, act);
@@ -351,7 +359,7 @@ __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t
     uint32_t acc = __builtin_amdgcn_bitop3_b32(e[0], e[1], e[2], 0x96);
     acc = __builtin_amdgcn_bitop3_b32(acc, e[3], e[4], 0x96);
     acc = __builtin_amdgcn_bitop3_b32(acc, e[5], L.d0, 0x96);
-    const uint32_t eb = WIDE ? __builtin_amdgcn_ubfe(acc, 20u, 2u) << 12 : __builtin_amdgcn_ubfe(acc, 12u, 14u);
+    const uint32_t eb = __builtin_amdgcn_ubfe(acc, kBitB, 2u) << 13;
     e[6] = rans_step<WIDE, kE>(L, eb, act);
     e[7] = rans_step<WIDE, 0u>(L, 0u, act);
     if (act) emit_vector<OUT, WIDE, PADDED>(A, opaque_s(tile_out + s * kStepBytes), tile, s * 64u + lane, lane, e, gs[s]);
@@ -451,7 +459,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
       if (used && cum < kProbTotal) {
         const int32_t v = symbol_value(c, smin + (int32_t)s);
         rec[r] = WIDE ? make_uint2(f | ((uint32_t)v & 0xfffu) << 20, cum)
-                      : make_uint2((f << 2) | ((uint32_t)(v + 128) & 0xffu) << 24, cum << 2);
+                      : make_uint2((f << 3) | ((uint32_t)(v + 128) & 0xffu) << 24, cum << 3);
         atomicOr(&mark[c * kMarkWords + (cum >> 5)], 1u << (cum & 31u));
       }
       carry += __builtin_amdgcn_readlane(incl, 63);
@@ -488,12 +496,12 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (uint32_t row = 0; row < kRows; ++row) {
-      const uint32_t slot = row * 64u + lane, idx = lc * kProbTotal + slot;
+      const uint32_t slot = row * 64u + lane, idx = 2u * (lc * kProbTotal + slot);
       if (WIDE) {
         tab[idx] = rc[row].x | ((slot - rc[row].y) << 10);
       } else {
         tab[idx] = rc[row].x;
-        tab[kTableDwords + idx] = (slot << 2) - rc[row].y;
+        tab[idx + 1u] = (slot << 3) - rc[row].y;
       }
     }
   }
@@ -503,7 +511,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   // ---- 3. decode ---------------------------------------------------------
   if (!has_tile) return;
   const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
-  const uint32_t X = x0 << 2;
+  const uint32_t X = x0 << 3;
   const uint32_t we = wt + 2u * (w_end - w_begin);
   if (n == 1024u)
     decode_tile<OUT, WIDE, PADDED, false>(A, wt, we, X, tile, n, gs, lane);
@@ -601,7 +609,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   // LDS layout: tables | records | bitmap | words | pad.  The
   // words of a workgroup's consecutive tiles are one range; with k waves per
   // workgroup the buffer holds the longest such range, in whole 1 KB copies.
-  uint32_t off = wide ? kTableBytes : 2 * kTableBytes;
+  uint32_t off = kTableBytes;
   A.rec_off = off;
   off += 8 * nz_total;
   A.mark_off = off;

@@ -428,7 +428,7 @@ static void encode_tile(const Problem &P, const Tables &tb, const std::vector<in
         if (i >= n) continue;
         uint32_t f = fc[(size_t)(i * 8 + j) * 2], c = fc[(size_t)(i * 8 + j) * 2 + 1];
         uint32_t st = x[q];
-        if ((uint64_t)st >= ((uint64_t)f << (30 - kProbBits))) {
+        if ((uint64_t)st >= ((uint64_t)f << (29 - kProbBits))) {
           emitted.push_back((uint16_t)st);
           who.push_back((uint8_t)q);
           st >>= 16;

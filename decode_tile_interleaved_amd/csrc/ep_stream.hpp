@@ -29,11 +29,11 @@ constexpr uint32_t kHeaderBytes = 128;
 constexpr int kContexts = 7;
 constexpr int kProbBits = 10;
 constexpr uint32_t kProbTotal = 1u << kProbBits;
-constexpr uint32_t kStateLow = 1u << 14;   // rANS states live in [2^14, 2^30)
+constexpr uint32_t kStateLow = 1u << 13;   // rANS states live in [2^13, 2^29)
 constexpr int kCountWords = 32;            // words of per-state count bytes at the start of a tile
 // stream bits per state beyond its symbols' information, as the rate
-// estimate counts them: the fixed final state L (14), the unused high bits of
-// the stored start state (10 on average) and the count byte (8)
+// estimate counts them: the fixed final state L (13), the unused high bits of
+// the stored start state (11 on average) and the count byte (8)
 constexpr double kStateBits = 32.0;
 constexpr int kTileVecs = 1024;            // E8 vectors (8 coordinates) per tile
 constexpr int kStatesPerTile = 64;         // interleaved rANS states per tile (2 count bytes per word)

@@ -58,7 +58,7 @@ BF16, FP16, FP8, INT8 = 0, 1, 2, 3
 PROB_BITS = 10
 N_STATES = 64
 TILE_VECS = 1024
-STATE_L = 1 << 14
+STATE_L = 1 << 13
 
 
 def build(force: bool = False) -> str:

@@ -46,7 +46,7 @@
 #define OR_MAGIC 0x314B5045u /* "EPK1" little-endian */
 #define OR_VERSION 1
 #define OR_STATE_BITS 32.0  /* estimated stream bits per rANS state beyond its symbols' information */
-#define OR_STATE_L 16384u    /* rANS lower state bound L = 2^14; states lie in [L, 2^30); words are 16 bits */
+#define OR_STATE_L 8192u     /* rANS lower state bound L = 2^13; states lie in [L, 2^29); words are 16 bits */
 
 static int esize_of(int dt) { return (dt == OR_BF16 || dt == OR_FP16) ? 2 : 1; }
 
@@ -353,7 +353,7 @@ static int quantize_all(const double *x, const or_geom *g, const float *gs, int3
 /* i = s*S + q when i < n.  The first min(n, S) states are active.           */
 /* Decode: slot = x mod M; x = f*(x >> prob_bits) + slot - c;                */
 /*         if x < L: x = (x << 16) | w, w = state q's next word.             */
-/* Encode: if x >= f * 2^(30 - prob_bits): emit x & 0xffff, x >>= 16;       */
+/* Encode: if x >= f * 2^(29 - prob_bits): emit x & 0xffff, x >>= 16;       */
 /*         x = (x / f) * M + (x mod f) + c.                                  */
 /* Tile word layout: one count byte per state (the number of words it        */
 /* consumes; states ascending, two to a 16-bit word, the last word padded    */
@@ -408,7 +408,7 @@ static int encode_tile(const or_geom *g, const or_tables *t, const int32_t *v, i
         int si = sym[j] - t->smin[ctx[j]];
         uint32_t f = t->freq[ctx[j]][si], c = t->cum[ctx[j]][si];
         uint32_t x = states[q];
-        if ((uint64_t)x >= ((uint64_t)f << (30 - g->prob_bits))) {
+        if ((uint64_t)x >= ((uint64_t)f << (29 - g->prob_bits))) {
           if ((rc = words_push(&rev, (uint16_t)(x & 0xffffu)))) goto done;
           if (rev.n > owner_cap) {
             owner_cap = rev.cap;
@@ -584,8 +584,8 @@ done:
 /* floor(k * n_vec / S); tables are built from the sample alone;             */
 /* bits = (n_vec/S) * sum c_s (prob_bits - log2 f_s) + 32 * states           */
 /*        + 8 * (header, tables, scales, tile offsets).                      */
-/* 32 bits per state: 14 for the fixed final state L, on average 10 unused   */
-/* high bits of the stored 32-bit start state (log-uniform in [2^14, 2^30)), */
+/* 32 bits per state: 13 for the fixed final state L, on average 11 unused   */
+/* high bits of the stored 32-bit start state (log-uniform in [2^13, 2^29)), */
 /* and the state's 8-bit word count.  Out-of-range lattice values give +inf. */
 /* ------------------------------------------------------------------------ */
 #define OR_SAMPLE_VECS 65536
@@ -1161,7 +1161,7 @@ int or_rans_encode(const uint32_t *freq, int nsym, int prob_bits, const int32_t 
     int s = syms[k];
     if (s < 0 || s >= nsym || freq[s] == 0) { free(cum); free(rev.w); return OR_ERR_ARG; }
     uint32_t f = freq[s], x = states_out[q];
-    if ((uint64_t)x >= ((uint64_t)f << (30 - prob_bits))) {
+    if ((uint64_t)x >= ((uint64_t)f << (29 - prob_bits))) {
       if (words_push(&rev, (uint16_t)(x & 0xffffu))) { free(cum); free(rev.w); return OR_ERR_NOMEM; }
       x >>= 16;
     }

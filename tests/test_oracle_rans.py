@@ -39,7 +39,7 @@ def test_round_trip_and_end_state(nsym, nstates, n):
     f = random_table(rng, nsym, with_ones=nsym > 3)
     syms = draw(rng, f, n)
     states, words = oracle.rans_encode(f, syms, nstates)
-    assert all(L <= s < (1 << 30) for s in states)
+    assert all(L <= s < (1 << 29) for s in states)
     dec, final = oracle.rans_decode(f, states, words, n)
     assert np.array_equal(dec, syms)
     assert np.all(final == L)
