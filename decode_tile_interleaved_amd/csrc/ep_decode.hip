@@ -95,6 +95,9 @@ struct Args {
   uint32_t row_magic, row_shift;  // vec / vpr = umulhi(vec, row_magic) >> row_shift  (vpr > 1)
   uint32_t n_vec, n_tiles, waves;
   uint32_t rec_off, mark_off, words_off;  // LDS byte offsets
+  uint32_t rounds;                           // rounds of k tiles per workgroup (round kernel)
+  uint32_t buf0, buf1;                       // LDS byte offsets of its two round buffers
+  uint32_t toff_rel, scales_rel, words_rel;  // sections of a round buffer
 };
 
 typedef __attribute__((address_space(1))) void *gptr_t;
@@ -366,6 +369,236 @@ __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t
   }
 }
 
+// The table build: waves 0..k-1 take contexts wave, wave + k, ...: prefix
+// sums of the frequencies, the used symbols' records, a bitmap of the slots
+// where a symbol starts, then the context's 16 table rows of 64 slots.  fpre
+// holds the first 256 frequencies of context `wave`, loaded early.
+template <bool WIDE>
+__device__ __forceinline__ void build_tables(const Args &A, uint8_t *lds, uint32_t wave, uint32_t lane, uint32_t k,
+                                             const uint32_t (&fpre)[4]) {
+  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
+  uint2 *rec = reinterpret_cast<uint2 *>(lds + A.rec_off);          // (d0, cum term) per used symbol
+  uint32_t *mark = reinterpret_cast<uint32_t *>(lds + A.mark_off);  // [ctx][32] start bits
+  uint32_t *tab = reinterpret_cast<uint32_t *>(lds);
+  for (uint32_t c = wave; c < (uint32_t)kContexts; c += k) {
+    const uint32_t n = pick(A.nsym, c), fidx = pick(A.fidx, c), nzbase = pick(A.nzbase, c);
+    const int32_t smin = pick(A.smin, c);
+    if (n == 0u) continue;  // context without symbols: its table is never read
+    const uint32_t lc = c < 3u ? c : 3u + ((c - 3u) >> 1) + 2u * ((c - 3u) & 1u);  // LDS context of E_{b,p}
+    if (lane < kMarkWords) mark[c * kMarkWords + lane] = 0u;
+    uint32_t carry = 0, nzb = nzbase;
+    for (uint32_t base = 0, it = 0; base < n; base += 64, ++it) {
+      const uint32_t s = base + lane;
+      uint32_t f;
+      if (c == wave && it < 4) f = it == 0 ? fpre[0] : it == 1 ? fpre[1] : it == 2 ? fpre[2] : fpre[3];
+      else f = s < n ? freq[fidx + s] : 0u;
+      const uint32_t incl = wave_inclusive_sum(f);
+      const uint32_t cum = carry + incl - f;
+      const bool used = f != 0;
+      const uint64_t m = __ballot(used);
+      const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nzb));
+      if (used && cum < kProbTotal) {
+        const int32_t v = symbol_value(c, smin + (int32_t)s);
+        rec[r] = WIDE ? make_uint2(f | ((uint32_t)v & 0xfffu) << 20, cum)
+                      : make_uint2((f << 3) | ((uint32_t)(v + 128) & 0xffu) << 24, cum << 3);
+        atomicOr(&mark[c * kMarkWords + (cum >> 5)], 1u << (cum & 31u));
+      }
+      carry += __builtin_amdgcn_readlane(incl, 63);
+      nzb += (uint32_t)__popcll(m);
+    }
+    // row t (lane t < 16): its start bits shifted down by one and the record
+    // index before it
+    uint32_t rlo = 0, rhi = 0, rbase = 0;
+    {
+      uint32_t lo = 0, hi = 0;
+      if (lane < kRows) {
+        lo = mark[c * kMarkWords + 2 * lane];
+        hi = mark[c * kMarkWords + 2 * lane + 1];
+      }
+      const uint32_t cnt = (uint32_t)(__popc(lo) + __popc(hi));
+      const uint32_t first = nzbase + row16_inclusive_sum(cnt) - cnt;
+      rlo = __builtin_amdgcn_alignbit(hi, lo, 1u);
+      rhi = hi >> 1;
+      rbase = first + (lo & 1u) - 1u;
+    }
+    // slot record = first + (starts at or below the slot) - 1
+    //             = first + bit0 - 1 + popcount of (bits >> 1) below the lane.
+    // The row values reach every lane through readlane (no LDS traffic), and
+    // all sixteen records are read before any table write: the compiler cannot
+    // tell the record list and the table apart, so interleaving would put an
+    // LDS round trip on every row.
+    uint2 rc[kRows];
+#pragma unroll
+    for (uint32_t row = 0; row < kRows; ++row) {
+      const uint32_t mlo = __builtin_amdgcn_readlane(rlo, row), mhi = __builtin_amdgcn_readlane(rhi, row);
+      const uint32_t b = __builtin_amdgcn_readlane(rbase, row);
+      rc[row] = rec[__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, b))];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (uint32_t row = 0; row < kRows; ++row) {
+      const uint32_t slot = row * 64u + lane, idx = 2u * (lc * kProbTotal + slot);
+      if (WIDE) {
+        tab[idx] = rc[row].x | ((slot - rc[row].y) << 10);
+      } else {
+        tab[idx] = rc[row].x;
+        tab[idx + 1u] = (slot << 3) - rc[row].y;
+      }
+    }
+  }
+}
+
+// LDS copy of one round: the round's tiles are consecutive, so their start
+// states, tile offsets, row scales and words are each one range of the stream.
+// Each range is copied from a 16-byte aligned start; the decoding waves find
+// their pieces relative to that start.
+struct RoundBuf {
+  uint32_t states, toff, scales, words;  // LDS byte offsets
+};
+
+__device__ __forceinline__ RoundBuf round_buf(const Args &A, uint32_t r) {
+  const uint32_t b = (r & 1u) ? A.buf1 : A.buf0;
+  return RoundBuf{b, b + A.toff_rel, b + A.scales_rel, b + A.words_rel};
+}
+
+// the row of vector vec
+__device__ __forceinline__ uint32_t row_of(const Args &A, uint32_t vec) {
+  return A.vpr == 1u ? vec : __umulhi(vec, A.row_magic) >> A.row_shift;
+}
+
+// Copies n 16-byte pieces from src into LDS at dst with global_load_lds
+// (1 KB per instruction); lanes past the end stay idle.
+__device__ __forceinline__ void copy_to_lds(uint8_t *lds, gbyte_t src, uint32_t n, uint32_t dst, uint32_t lane) {
+  for (uint32_t i = 0; 64u * i < n; ++i) {
+    if (64u * i + lane < n)
+      __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + dst + 1024u * i), 16,
+                                       0, 0);
+  }
+}
+
+// The copying wave's work for round r: tiles [t0, t1) of this workgroup.
+__device__ __forceinline__ void stage_round(const Args &A, uint8_t *lds, uint32_t r, uint32_t lane) {
+  const uint32_t k = A.waves;
+  const uint32_t t0 = (r * gridDim.x + blockIdx.x) * k;
+  if (t0 >= A.n_tiles) return;
+  const uint32_t t1 = t0 + k < A.n_tiles ? t0 + k : A.n_tiles;
+  const RoundBuf B = round_buf(A, r);
+  // word range: its ends from two scalar loads, issued first
+  typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
+  const cptr_u32 toff = (cptr_u32)(A.blob + A.off_tile_offsets);
+  const uint32_t w0 = toff[t0], w1 = toff[t1];
+  // start states: 256 bytes per tile, contiguous and aligned
+  copy_to_lds(lds, (gbyte_t)(A.blob + A.off_states + 256ull * t0), 16u * (t1 - t0), B.states, lane);
+  // tile offsets t0..t1
+  {
+    const uint64_t a0 = (A.off_tile_offsets + 4ull * t0) & ~15ull, a1 = A.off_tile_offsets + 4ull * t1 + 4ull;
+    copy_to_lds(lds, (gbyte_t)(A.blob + a0), (uint32_t)((a1 - a0 + 15ull) >> 4), B.toff, lane);
+  }
+  // row scales of the rows the tiles touch
+  {
+    const uint32_t last_vec = (t1 * 1024u < A.n_vec ? t1 * 1024u : A.n_vec) - 1u;
+    const uint64_t a0 = (A.off_scales + 4ull * row_of(A, t0 * 1024u)) & ~15ull;
+    const uint64_t a1 = A.off_scales + 4ull * row_of(A, last_vec) + 4ull;
+    copy_to_lds(lds, (gbyte_t)(A.blob + a0), (uint32_t)((a1 - a0 + 15ull) >> 4), B.scales, lane);
+  }
+  // words, whole kilobytes first: no per-lane test, so each copy issues right
+  // after the last one
+  {
+    const uint64_t a0 = (A.off_words + 2ull * w0) & ~15ull;
+    const uint32_t n = (uint32_t)((((A.off_words + 2ull * w1 + 15ull) & ~15ull) - a0) >> 4);
+    const gbyte_t src = (gbyte_t)(A.blob + a0);
+    uint32_t i = 0;
+    for (; 64u * i + 64u <= n; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + B.words + 1024u * i), 16,
+                                       0, 0);
+    if (64u * i + lane < n)
+      __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + B.words + 1024u * i), 16,
+                                       0, 0);
+  }
+}
+
+// workgroup barrier that orders LDS accesses: every LDS access before it has
+// completed, none after it has started
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Streams with more tiles than one round of workgroups covers: one workgroup
+// per CU, whose waves 0..k-1 build the tables once and then decode one tile
+// each per round; wave k copies each round's stream ranges into LDS, the next
+// round's while the current one is decoded (two round buffers).
+template <int OUT, bool WIDE, bool PADDED>
+__global__ void __launch_bounds__(64 * (kMaxWaves + 1)) decode_rounds_kernel(Args A) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t k = A.waves;  // decoding waves; wave k copies
+
+  if (wave == k) {
+    // ---- copying wave ----------------------------------------------------
+    stage_round(A, lds, 0, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // round 0 has landed
+    lds_barrier();                  // tables built, round 0 in LDS
+    for (uint32_t r = 0; r < A.rounds; ++r) {
+      if (r + 1u < A.rounds) stage_round(A, lds, r + 1u, lane);
+      __builtin_amdgcn_s_waitcnt(0);  // round r + 1 has landed
+      lds_barrier();                  // round r decoded: its buffer is free
+    }
+    return;
+  }
+
+  // ---- decoding waves: 1. the first context's frequencies ------------------
+  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
+  const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
+  uint32_t fpre[4];
+  {
+    const uint32_t n0 = pick(A.nsym, c0), f0 = pick(A.fidx, c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t s = 64u * i + lane;
+      const uint32_t v = freq[f0 + (s < n0 ? s : 0u)];
+      fpre[i] = s < n0 ? v : 0u;
+    }
+  }
+
+  // ---- 2. the tables -------------------------------------------------------
+  build_tables<WIDE>(A, lds, wave, lane, k, fpre);
+  lds_barrier();  // tables built, round 0 in LDS
+
+  // ---- 3. rounds: one tile per wave -----------------------------------------
+  for (uint32_t r = 0; r < A.rounds; ++r) {
+    const uint32_t t0 = (r * gridDim.x + blockIdx.x) * k;
+    const uint32_t tile = t0 + wave;
+    if (tile < A.n_tiles) {
+      const RoundBuf B = round_buf(A, r);
+      // this tile's word range and the round's aligned start, from the copy of
+      // the tile offsets
+      const uint32_t tpos = B.toff + (uint32_t)((A.off_tile_offsets + 4ull * t0) & 15ull);
+      const uint32_t r_begin = lds_u32(tpos), w_begin = lds_u32(tpos + 4u * wave), w_end = lds_u32(tpos + 4u * wave + 4u);
+      const uint64_t gbyte0 = (A.off_words + 2ull * r_begin) & ~15ull;
+      const uint32_t wt = B.words + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);  // this tile's first word
+      const uint32_t we = wt + 2u * (w_end - w_begin);
+      const uint32_t X = lds_u32(B.states + 256u * wave + 4u * lane) << 3;
+      // row scales, from the copy that starts at row0's aligned address
+      const uint32_t row0 = row_of(A, t0 * 1024u);
+      const uint32_t sbase = B.scales + (uint32_t)((A.off_scales + 4ull * row0) & 15ull) - 4u * row0;
+      float gs[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint32_t vec = tile * 1024u + 64u * s + lane;
+        const uint32_t last = A.n_vec - 1u;  // lanes past the end read the last vector's scale, unused
+        gs[s] = __uint_as_float(lds_u32(sbase + 4u * row_of(A, vec < last ? vec : last)));
+      }
+      const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
+      if (n == 1024u)
+        decode_tile<OUT, WIDE, PADDED, false>(A, wt, we, X, tile, n, gs, lane);
+      else
+        decode_tile<OUT, WIDE, PADDED, true>(A, wt, we, X, tile, n, gs, lane);
+    }
+    lds_barrier();  // round r decoded; round r + 1 in LDS
+  }
+}
+
+// Streams that one round of workgroups covers: workgroups of up to 8 waves,
+// one tile each.
 template <int OUT, bool WIDE, bool PADDED>
 __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -434,77 +667,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
     }
   }
 
-  // ---- 2. one wave per context: prefix sums, used-symbol records, start
-  //         bitmap, then the context's 16 table rows of 64 slots ----------
-  uint2 *rec = reinterpret_cast<uint2 *>(lds + A.rec_off);          // (d0, cum term) per used symbol
-  uint32_t *mark = reinterpret_cast<uint32_t *>(lds + A.mark_off);  // [ctx][32] start bits
-  uint32_t *tab = reinterpret_cast<uint32_t *>(lds);
-  for (uint32_t c = wave; c < (uint32_t)kContexts; c += nwaves) {
-    const uint32_t n = pick(A.nsym, c), fidx = pick(A.fidx, c), nzbase = pick(A.nzbase, c);
-    const int32_t smin = pick(A.smin, c);
-    if (n == 0u) continue;  // context without symbols: its table is never read
-    const uint32_t lc = c < 3u ? c : 3u + ((c - 3u) >> 1) + 2u * ((c - 3u) & 1u);  // LDS context of E_{b,p}
-    if (lane < kMarkWords) mark[c * kMarkWords + lane] = 0u;
-    uint32_t carry = 0, nzb = nzbase;
-    for (uint32_t base = 0, it = 0; base < n; base += 64, ++it) {
-      const uint32_t s = base + lane;
-      uint32_t f;
-      if (c == wave && it < 4) f = it == 0 ? fpre[0] : it == 1 ? fpre[1] : it == 2 ? fpre[2] : fpre[3];
-      else f = s < n ? freq[fidx + s] : 0u;
-      const uint32_t incl = wave_inclusive_sum(f);
-      const uint32_t cum = carry + incl - f;
-      const bool used = f != 0;
-      const uint64_t m = __ballot(used);
-      const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nzb));
-      if (used && cum < kProbTotal) {
-        const int32_t v = symbol_value(c, smin + (int32_t)s);
-        rec[r] = WIDE ? make_uint2(f | ((uint32_t)v & 0xfffu) << 20, cum)
-                      : make_uint2((f << 3) | ((uint32_t)(v + 128) & 0xffu) << 24, cum << 3);
-        atomicOr(&mark[c * kMarkWords + (cum >> 5)], 1u << (cum & 31u));
-      }
-      carry += __builtin_amdgcn_readlane(incl, 63);
-      nzb += (uint32_t)__popcll(m);
-    }
-    // row t (lane t < 16): its start bits shifted down by one and the record
-    // index before it
-    uint32_t rlo = 0, rhi = 0, rbase = 0;
-    {
-      uint32_t lo = 0, hi = 0;
-      if (lane < kRows) {
-        lo = mark[c * kMarkWords + 2 * lane];
-        hi = mark[c * kMarkWords + 2 * lane + 1];
-      }
-      const uint32_t cnt = (uint32_t)(__popc(lo) + __popc(hi));
-      const uint32_t first = nzbase + row16_inclusive_sum(cnt) - cnt;
-      rlo = __builtin_amdgcn_alignbit(hi, lo, 1u);
-      rhi = hi >> 1;
-      rbase = first + (lo & 1u) - 1u;
-    }
-    // slot record = first + (starts at or below the slot) - 1
-    //             = first + bit0 - 1 + popcount of (bits >> 1) below the lane.
-    // The row values reach every lane through readlane (no LDS traffic), and
-    // all sixteen records are read before any table write: the compiler cannot
-    // tell the record list and the table apart, so interleaving would put an
-    // LDS round trip on every row.
-    uint2 rc[kRows];
-#pragma unroll
-    for (uint32_t row = 0; row < kRows; ++row) {
-      const uint32_t mlo = __builtin_amdgcn_readlane(rlo, row), mhi = __builtin_amdgcn_readlane(rhi, row);
-      const uint32_t b = __builtin_amdgcn_readlane(rbase, row);
-      rc[row] = rec[__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, b))];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (uint32_t row = 0; row < kRows; ++row) {
-      const uint32_t slot = row * 64u + lane, idx = 2u * (lc * kProbTotal + slot);
-      if (WIDE) {
-        tab[idx] = rc[row].x | ((slot - rc[row].y) << 10);
-      } else {
-        tab[idx] = rc[row].x;
-        tab[idx + 1u] = (slot << 3) - rc[row].y;
-      }
-    }
-  }
+  // ---- 2. one wave per context: the tables --------------------------------
+  build_tables<WIDE>(A, lds, wave, lane, nwaves, fpre);
   __builtin_amdgcn_s_waitcnt(0);  // the loader's words have landed in LDS
   __syncthreads();
 
@@ -521,20 +685,42 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
 
 typedef void (*KernelFn)(Args);
 
-template <int OUT>
-KernelFn pick(bool wide, bool padded) {
-  if (wide) return padded ? decode_kernel<OUT, true, true> : decode_kernel<OUT, true, false>;
-  return padded ? decode_kernel<OUT, false, true> : decode_kernel<OUT, false, false>;
+template <int OUT, bool WIDE, bool PADDED>
+KernelFn pick3(bool rounds) {
+  return rounds ? decode_rounds_kernel<OUT, WIDE, PADDED> : decode_kernel<OUT, WIDE, PADDED>;
 }
 
-KernelFn pick_kernel(int out, bool wide, bool padded) {
+template <int OUT>
+KernelFn pick(bool wide, bool padded, bool rounds) {
+  if (wide) return padded ? pick3<OUT, true, true>(rounds) : pick3<OUT, true, false>(rounds);
+  return padded ? pick3<OUT, false, true>(rounds) : pick3<OUT, false, false>(rounds);
+}
+
+KernelFn pick_kernel(int out, bool wide, bool padded, bool rounds) {
   switch (out) {
-    case EP_BF16: return pick<EP_BF16>(wide, padded);
-    case EP_FP16: return pick<EP_FP16>(wide, padded);
-    case EP_FP8_E4M3FN: return pick<EP_FP8_E4M3FN>(wide, padded);
-    case EP_INT8: return pick<EP_INT8>(wide, padded);
-    default: return pick<kOutSym>(wide, false);
+    case EP_BF16: return pick<EP_BF16>(wide, padded, rounds);
+    case EP_FP16: return pick<EP_FP16>(wide, padded, rounds);
+    case EP_FP8_E4M3FN: return pick<EP_FP8_E4M3FN>(wide, padded, rounds);
+    case EP_INT8: return pick<EP_INT8>(wide, padded, rounds);
+    default: return pick<kOutSym>(wide, false, rounds);
   }
+}
+
+// compute units of the current device (one workgroup each at most in the
+// round kernel)
+int64_t num_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 int32_t host_symbol_value(int c, int32_t s) {
@@ -638,7 +824,54 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     set_error("tile too large for the decoder's LDS budget");
     return EP_ERR_FORMAT;
   }
-  const uint32_t lds_bytes = off + (uint32_t)span + kLdsPad;
+  uint32_t lds_bytes = off + (uint32_t)span + kLdsPad;
+  uint32_t grid = (uint32_t)((s.tiles + waves - 1) / waves);
+  // More workgroups than compute units: the round kernel instead, with one
+  // workgroup per CU that builds the tables once.  A round buffer holds k
+  // tiles' start states, tile offsets, row scales and words; two buffers (the
+  // next round is copied while the current one is decoded).
+  const bool rounds = (int64_t)grid > num_cus();
+  if (rounds) {
+    const uint32_t fixed = A.words_off;
+    auto row_of_vec = [&](int64_t vec) { return vec / (s.cols8 / 8); };
+    bool ok = false;
+    for (uint32_t k = kMaxWaves; k >= 1 && !ok; --k) {
+      const int64_t groups = (s.tiles + k - 1) / k;
+      const uint32_t g = (uint32_t)std::min<int64_t>(groups, num_cus());
+      uint64_t wspan = 0, sspan = 0;  // the largest ranges over all groups of k consecutive tiles
+      for (int64_t t = 0; t < s.tiles; t += k) {
+        const int64_t e = std::min<int64_t>(t + k, s.tiles);
+        const uint64_t a0 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t)) & ~15ull;
+        const uint64_t a1 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * e) + 15ull) & ~15ull;
+        wspan = std::max<uint64_t>(wspan, a1 - a0);
+        const int64_t last_vec = std::min<int64_t>(e * kTileVecs, s.n_vec) - 1;
+        const uint64_t b0 = (s.off_scales + 4ull * row_of_vec(t * kTileVecs)) & ~15ull;
+        const uint64_t b1 = s.off_scales + 4ull * row_of_vec(last_vec) + 4ull;
+        sspan = std::max<uint64_t>(sspan, (b1 - b0 + 15ull) & ~15ull);
+      }
+      const uint32_t toff_rel = 256u * k;
+      const uint32_t scales_rel = toff_rel + (uint32_t)align16(4u * (k + 1u) + 15u);
+      if (sspan > kLdsLimit) continue;
+      const uint32_t words_rel = scales_rel + (uint32_t)sspan;
+      const uint64_t buf = align16(words_rel + ((wspan + 1023ull) & ~1023ull));  // words copied in whole kilobytes
+      const uint64_t total = fixed + 2 * buf + kLdsPad;
+      if (total > kLdsLimit) continue;
+      ok = true;
+      waves = k;
+      grid = g;
+      A.rounds = (uint32_t)((groups + g - 1) / g);
+      A.buf0 = fixed;
+      A.buf1 = fixed + (uint32_t)buf;
+      A.toff_rel = toff_rel;
+      A.scales_rel = scales_rel;
+      A.words_rel = words_rel;
+      lds_bytes = (uint32_t)total;
+    }
+    if (!ok) {
+      set_error("tile too large for the decoder's LDS budget");
+      return EP_ERR_FORMAT;
+    }
+  }
   A.blob = reinterpret_cast<const uint8_t *>(dev_blob);
   A.out = dev_out;
   A.off_freq = s.off_freq;
@@ -653,7 +886,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   A.n_vec = (uint32_t)s.n_vec;
   A.n_tiles = (uint32_t)s.tiles;
   const bool padded = out != kOutSym && (s.cols % 8) != 0;
-  KernelFn fn = pick_kernel(out, wide, padded);
+  KernelFn fn = pick_kernel(out, wide, padded, rounds);
   static std::mutex mu;
   static std::vector<KernelFn> configured;
   {
@@ -670,8 +903,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     }
   }
   A.waves = waves;
-  const uint32_t grid = (uint32_t)((s.tiles + waves - 1) / waves);
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * waves), lds_bytes, stream, A);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * (waves + (rounds ? 1u : 0u))), lds_bytes, stream, A);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) {
     set_error(std::string("kernel launch failed: ") + hipGetErrorString(err));

@@ -95,6 +95,8 @@ def lib():
                                          i32p]
         L.or_decode_symbols.argtypes = [u8p, ctypes.c_size_t, i16p]
         L.or_decompress.argtypes = [u8p, ctypes.c_size_t, ctypes.c_void_p]
+        L.or_decompress_tiles.argtypes = [u8p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int64, i32p,
+                                          ctypes.c_void_p]
         L.or_reconstruct.argtypes = [i32p, f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
         L.or_blob_info.argtypes = [u8p, ctypes.c_size_t, i64p, f64p]
         L.or_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -239,6 +241,33 @@ def decompress_raw(blob: np.ndarray) -> np.ndarray:
     rc = lib().or_decompress(_ptr(blob, ctypes.c_uint8), blob.size, out.ctypes.data_as(ctypes.c_void_p))
     if rc:
         raise OracleError(rc, "decompress")
+    return out
+
+
+def decompress_raw_threads(blob: np.ndarray, threads: int) -> np.ndarray:
+    """decompress_raw with the tiles split into ``threads`` contiguous ranges,
+    each decoded by ``or_decompress_tiles`` on its own thread (ctypes releases
+    the GIL during the call).  Same arithmetic, same result."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    d = info(blob)
+    if d["method"] != 0:
+        return decompress_raw(blob)
+    out = np.zeros((d["rows"], d["cols"]), _NP_CONTAINER[d["dtype"]])
+    work = np.zeros((d["rows"], (d["cols"] + 7) // 8 * 8), np.int32)
+    T = d["n_tiles"]
+    bounds = [T * k // threads for k in range(threads + 1)]
+
+    def run(k):
+        return lib().or_decompress_tiles(_ptr(blob, ctypes.c_uint8), blob.size, bounds[k], bounds[k + 1],
+                                         _ptr(work, ctypes.c_int32), out.ctypes.data)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        rcs = list(ex.map(run, range(threads)))
+    for rc in rcs:
+        if rc:
+            raise OracleError(rc, "decompress_tiles")
     return out
 
 

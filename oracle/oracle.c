@@ -908,8 +908,8 @@ static int read_tables(const uint8_t *b, const or_header *h, or_tables *t) {
   return OR_OK;
 }
 
-/* Decode every tile into v (R x Cp lattice coordinates, int32). */
-static int decode_lattice(const uint8_t *b, const or_header *h, int32_t *v) {
+/* Decode tiles [t0, t1) into v (R x Cp lattice coordinates, int32). */
+static int decode_lattice_tiles(const uint8_t *b, const or_header *h, int32_t *v, int64_t t0, int64_t t1) {
   or_tables t;
   int rc = read_tables(b, h, &t);
   if (rc) { tables_free(&t); return rc; }
@@ -922,7 +922,7 @@ static int decode_lattice(const uint8_t *b, const or_header *h, int32_t *v) {
   int32_t *vb = (int32_t *)malloc(sizeof(int32_t) * (size_t)g->S);     /* coset bit per state */
   int32_t *zp = (int32_t *)malloc(sizeof(int32_t) * (size_t)g->S);     /* running z sum per state */
   if (!x || !pos || !end || !vb || !zp) { rc = OR_ERR_NOMEM; goto done; }
-  for (int64_t tile = 0; tile < g->T; tile++) {
+  for (int64_t tile = t0; tile < t1; tile++) {
     int64_t first = tile * g->tile_vecs;
     int64_t n = g->n_vec - first;
     if (n > g->tile_vecs) n = g->tile_vecs;
@@ -983,6 +983,11 @@ done:
   free(zp);
   tables_free(&t);
   return rc;
+}
+
+/* Decode every tile into v (R x Cp lattice coordinates, int32). */
+static int decode_lattice(const uint8_t *b, const or_header *h, int32_t *v) {
+  return decode_lattice_tiles(b, h, v, 0, h->g.T);
 }
 
 /* lattice coordinates v (int16, R x Cp) of a lattice stream */
@@ -1113,6 +1118,26 @@ int or_decompress(const uint8_t *b, size_t nb, void *out) {
     }
   free(v);
   return rc;
+}
+
+/* The decompression of tiles [t0, t1) only: their lattice coordinates go to
+ * v_work (R x Cp int32, caller-owned) and their reconstruction to out (the
+ * whole R x C container).  Calls on disjoint tile ranges touch disjoint
+ * memory, so a harness may run them on several threads. */
+int or_decompress_tiles(const uint8_t *b, size_t nb, int64_t t0, int64_t t1, int32_t *v_work, void *out) {
+  or_header h;
+  int rc = parse_header(b, nb, &h);
+  if (rc) return rc;
+  if (!out || !v_work || h.method != 0 || t0 < 0 || t1 > h.g.T || t0 > t1) return OR_ERR_ARG;
+  rc = decode_lattice_tiles(b, &h, v_work, t0, t1);
+  if (rc) return rc;
+  int64_t vend = t1 * h.g.tile_vecs < h.g.n_vec ? t1 * h.g.tile_vecs : h.g.n_vec;
+  for (int64_t vid = t0 * h.g.tile_vecs; vid < vend; vid++) {
+    int64_t r = vid / h.g.vpr, c0 = 8 * (vid % h.g.vpr);
+    float g = get_f32(b + h.o_sc + 4 * r);
+    for (int64_t c = c0; c < c0 + 8 && c < h.g.C; c++) store_value(out, h.dtype, r * h.g.C + c, v_work[r * h.g.Cp + c], g);
+  }
+  return OR_OK;
 }
 
 /* closed form: convert(f32(v * g)) for given coordinates and scales */

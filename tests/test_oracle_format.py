@@ -253,3 +253,15 @@ def test_count_bytes_decide_word_ownership():
     bad[o_w + 1] += 1
     with pytest.raises(oracle.OracleError):
         oracle.decode_symbols(bad)
+
+
+@pytest.mark.parametrize("shape", [(129, 64), (7, 13), (64, 1032)])
+def test_tile_range_decode_matches_whole(shape):
+    """The threaded harness (tile ranges on several threads) gives the same
+    bytes as the one-call decoder: tiles are independently decodable."""
+    t = W.gaussian(*shape, 0.02, seed=11 + shape[0])
+    blob, rc, _ = oracle.compress(t, 4.0, fixed_a=0.3)
+    assert rc == 0
+    whole = oracle.decompress_raw(blob)
+    for threads in (1, 2, 3):
+        assert np.array_equal(oracle.decompress_raw_threads(blob, threads), whole)
