@@ -67,7 +67,8 @@
 namespace ep {
 namespace {
 
-constexpr int kMaxWaves = 8;
+constexpr int kMaxWaves = 8;        // decoding waves per workgroup, single-round kernel
+constexpr int kMaxRoundWaves = 12;  // round kernel: three per SIMD, which the VALU can feed
 constexpr uint32_t kCtxBytes = kProbTotal * 8;             // 8 KB per context
 constexpr uint32_t kTableBytes = kContexts * kCtxBytes;     // 57344
 constexpr uint32_t kRows = kProbTotal / 64;                // 16 rows of 64 slots per context
@@ -526,7 +527,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // each per round; wave k copies each round's stream ranges into LDS, the next
 // round's while the current one is decoded (two round buffers).
 template <int OUT, bool WIDE, bool PADDED>
-__global__ void __launch_bounds__(64 * (kMaxWaves + 1)) decode_rounds_kernel(Args A) {
+__global__ void __launch_bounds__(64 * (kMaxRoundWaves + 1)) decode_rounds_kernel(Args A) {
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -835,7 +836,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     const uint32_t fixed = A.words_off;
     auto row_of_vec = [&](int64_t vec) { return vec / (s.cols8 / 8); };
     bool ok = false;
-    for (uint32_t k = kMaxWaves; k >= 1 && !ok; --k) {
+    for (uint32_t k = kMaxRoundWaves; k >= 1 && !ok; --k) {
       const int64_t groups = (s.tiles + k - 1) / k;
       const uint32_t g = (uint32_t)std::min<int64_t>(groups, num_cus());
       uint64_t wspan = 0, sspan = 0;  // the largest ranges over all groups of k consecutive tiles
