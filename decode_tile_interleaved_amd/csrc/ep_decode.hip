@@ -97,6 +97,7 @@ struct Args {
   uint32_t n_vec, n_tiles, waves;
   uint32_t rec_off, mark_off, words_off;  // LDS byte offsets
   uint32_t rounds;                           // rounds of k tiles per workgroup (round kernel)
+  uint32_t wg_q, wg_rem;                     // round kernel: workgroup b decodes wg_q tiles, one more if b < wg_rem
   uint32_t buf0, buf1;                       // LDS byte offsets of its two round buffers
   uint32_t toff_rel, scales_rel, words_rel;  // sections of a round buffer
 };
@@ -467,6 +468,13 @@ __device__ __forceinline__ uint32_t row_of(const Args &A, uint32_t vec) {
   return A.vpr == 1u ? vec : __umulhi(vec, A.row_magic) >> A.row_shift;
 }
 
+// Round kernel: workgroup b decodes the consecutive tiles [wg_first(b),
+// wg_first(b + 1)), k per round; the counts differ by at most one tile, so
+// that every workgroup's last round is about as full as the others'.
+__device__ __forceinline__ uint32_t wg_first(const Args &A, uint32_t b) {
+  return b * A.wg_q + (b < A.wg_rem ? b : A.wg_rem);
+}
+
 // Copies n 16-byte pieces from src into LDS at dst with global_load_lds
 // (1 KB per instruction); lanes past the end stay idle.
 __device__ __forceinline__ void copy_to_lds(uint8_t *lds, gbyte_t src, uint32_t n, uint32_t dst, uint32_t lane) {
@@ -479,10 +487,10 @@ __device__ __forceinline__ void copy_to_lds(uint8_t *lds, gbyte_t src, uint32_t 
 
 // The copying wave's work for round r: tiles [t0, t1) of this workgroup.
 __device__ __forceinline__ void stage_round(const Args &A, uint8_t *lds, uint32_t r, uint32_t lane) {
-  const uint32_t k = A.waves;
-  const uint32_t t0 = (r * gridDim.x + blockIdx.x) * k;
-  if (t0 >= A.n_tiles) return;
-  const uint32_t t1 = t0 + k < A.n_tiles ? t0 + k : A.n_tiles;
+  const uint32_t k = A.waves, end = wg_first(A, blockIdx.x + 1u);
+  const uint32_t t0 = wg_first(A, blockIdx.x) + r * k;
+  if (t0 >= end) return;
+  const uint32_t t1 = t0 + k < end ? t0 + k : end;
   const RoundBuf B = round_buf(A, r);
   // word range: its ends from two scalar loads, issued first
   typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
@@ -565,10 +573,11 @@ __global__ void __launch_bounds__(64 * (kMaxRoundWaves + 1)) decode_rounds_kerne
   lds_barrier();  // tables built, round 0 in LDS
 
   // ---- 3. rounds: one tile per wave -----------------------------------------
+  const uint32_t first = wg_first(A, blockIdx.x), end = wg_first(A, blockIdx.x + 1u);
   for (uint32_t r = 0; r < A.rounds; ++r) {
-    const uint32_t t0 = (r * gridDim.x + blockIdx.x) * k;
+    const uint32_t t0 = first + r * k;
     const uint32_t tile = t0 + wave;
-    if (tile < A.n_tiles) {
+    if (tile < end) {
       const RoundBuf B = round_buf(A, r);
       // this tile's word range and the round's aligned start, from the copy of
       // the tile offsets
@@ -833,22 +842,32 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   // next round is copied while the current one is decoded).
   const bool rounds = (int64_t)grid > num_cus();
   if (rounds) {
+    // One workgroup per CU, each with a run of consecutive tiles (counts that
+    // differ by at most one), decoded k at a time: the fewest rounds that k
+    // decoding waves allow, then the smallest k that keeps that many rounds,
+    // so that every round is about equally full.
     const uint32_t fixed = A.words_off;
     auto row_of_vec = [&](int64_t vec) { return vec / (s.cols8 / 8); };
+    const int64_t g = std::min<int64_t>(s.tiles, num_cus());
+    const int64_t q = s.tiles / g, rem = s.tiles % g, qmax = q + (rem ? 1 : 0);
+    auto first_of = [&](int64_t b) { return b * q + std::min<int64_t>(b, rem); };
     bool ok = false;
-    for (uint32_t k = kMaxRoundWaves; k >= 1 && !ok; --k) {
-      const int64_t groups = (s.tiles + k - 1) / k;
-      const uint32_t g = (uint32_t)std::min<int64_t>(groups, num_cus());
-      uint64_t wspan = 0, sspan = 0;  // the largest ranges over all groups of k consecutive tiles
-      for (int64_t t = 0; t < s.tiles; t += k) {
-        const int64_t e = std::min<int64_t>(t + k, s.tiles);
-        const uint64_t a0 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t)) & ~15ull;
-        const uint64_t a1 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * e) + 15ull) & ~15ull;
-        wspan = std::max<uint64_t>(wspan, a1 - a0);
-        const int64_t last_vec = std::min<int64_t>(e * kTileVecs, s.n_vec) - 1;
-        const uint64_t b0 = (s.off_scales + 4ull * row_of_vec(t * kTileVecs)) & ~15ull;
-        const uint64_t b1 = s.off_scales + 4ull * row_of_vec(last_vec) + 4ull;
-        sspan = std::max<uint64_t>(sspan, (b1 - b0 + 15ull) & ~15ull);
+    for (int64_t kk = kMaxRoundWaves; kk >= 1 && !ok; --kk) {
+      const int64_t R = (qmax + kk - 1) / kk;
+      const uint32_t k = (uint32_t)((qmax + R - 1) / R);
+      uint64_t wspan = 0, sspan = 0;  // the largest ranges over every round of every workgroup
+      for (int64_t b = 0; b < g; ++b) {
+        const int64_t end = first_of(b + 1);
+        for (int64_t t = first_of(b); t < end; t += k) {
+          const int64_t e = std::min<int64_t>(t + k, end);
+          const uint64_t a0 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t)) & ~15ull;
+          const uint64_t a1 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * e) + 15ull) & ~15ull;
+          wspan = std::max<uint64_t>(wspan, a1 - a0);
+          const int64_t last_vec = std::min<int64_t>(e * kTileVecs, s.n_vec) - 1;
+          const uint64_t b0 = (s.off_scales + 4ull * row_of_vec(t * kTileVecs)) & ~15ull;
+          const uint64_t b1 = s.off_scales + 4ull * row_of_vec(last_vec) + 4ull;
+          sspan = std::max<uint64_t>(sspan, (b1 - b0 + 15ull) & ~15ull);
+        }
       }
       const uint32_t toff_rel = 256u * k;
       const uint32_t scales_rel = toff_rel + (uint32_t)align16(4u * (k + 1u) + 15u);
@@ -859,8 +878,10 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
       if (total > kLdsLimit) continue;
       ok = true;
       waves = k;
-      grid = g;
-      A.rounds = (uint32_t)((groups + g - 1) / g);
+      grid = (uint32_t)g;
+      A.rounds = (uint32_t)R;
+      A.wg_q = (uint32_t)q;
+      A.wg_rem = (uint32_t)rem;
       A.buf0 = fixed;
       A.buf1 = fixed + (uint32_t)buf;
       A.toff_rel = toff_rel;
