@@ -30,13 +30,17 @@
 // list with a private pointer and always holds its next word in a register.
 //
 // The step is software-pipelined around its one serial dependence, table
-// lookup -> multiply-add -> compare -> select -> next lookup (on gfx950 a
-// dependent VALU op costs about fourteen cycles, an eight-byte LDS lookup
-// about sixty).  The address without a refill (from x') and the address after one
-// (from the held word) are formed in parallel with the compare; the next
-// lookup leaves right after the select.  Only then do the refilling lanes,
-// under the exec mask, shift the held word into the state and read their
-// following word, which is first needed one step later.
+// lookup -> multiply-add -> compare -> select -> address -> next lookup (on
+// gfx950 a dependent VALU op costs about fourteen cycles, an eight-byte LDS
+// lookup about sixty).  The refilled state (x' with the held word shifted in)
+// is formed in parallel with the compare, one v_cndmask selects the next
+// state, one v_and_or makes its address, and the next lookup leaves.  Only
+// then do the refilling lanes, under the exec mask, read their following
+// word, which is first needed one step later.  Eight VALU instructions per
+// step: the chain is one instruction longer than with both candidate
+// addresses formed before the select, but the step is one instruction
+// shorter, which pays where the VALU is the bound (more than two waves per
+// SIMD).
 //
 // Table entries (2^10 slots of 8 bytes per context; one ds_read_b64 meets
 // fewer LDS bank conflicts than two dword reads):
@@ -219,17 +223,14 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   // of the refill block
   uint32_t r8;
   asm volatile("v_lshlrev_b32 %0, 3, %1" : "=v"(r8) : "v"(L.r), "v"(x));
-  const uint32_t ar = (r8 & 0x1ff8u) | nb;  // next address after a refill: the held word's low bits
   const bool need = active && x < 0x10000u;
   const uint64_t m = __ballot(need);
-  const uint32_t ax = (x & 0x1ff8u) | nb;  // next address without a refill
-  table_read<WIDE, BASE>(select_mask(m, ax, ar), L.d0, L.d1);
+  const uint32_t X = select_mask(m, x, (x << 16) | r8);  // next state: refilling lanes shift the held word in
+  table_read<WIDE, BASE>((X & 0x1ff8u) | nb, L.d0, L.d1);
   __builtin_amdgcn_sched_barrier(0);  // the next lookup goes out before the refill
-  uint32_t X = x;
-  if (need) {  // refilling lanes only: take the held word, read the following one
+  if (need) {  // refilling lanes only: read the following word
     L.r = lds_u16(L.p + 2u);
     L.p += 2u;
-    X = (x << 16) | r8;
   }
   L.q = X >> 13;
   return e;
