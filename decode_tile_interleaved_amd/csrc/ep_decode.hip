@@ -125,13 +125,8 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   return v;
 }
 
-// the same for a wave-uniform value, which stays in one SGPR (or pair);
+// the same for a wave-uniform address, which stays in one SGPR pair;
 // readfirstlane states the uniformity and costs nothing on a scalar value
-__device__ __forceinline__ uint32_t opaque_s(uint32_t v) {
-  v = __builtin_amdgcn_readfirstlane(v);
-  asm volatile("" : "+s"(v));
-  return v;
-}
 typedef __attribute__((address_space(1))) uint8_t *gbyte_t;
 __device__ __forceinline__ gbyte_t opaque_s(gbyte_t p) {
   uint64_t u = (uint64_t)p;
@@ -226,7 +221,8 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   const bool need = active && x < 0x10000u;
   const uint64_t m = __ballot(need);
   const uint32_t X = select_mask(m, x, (x << 16) | r8);  // next state: refilling lanes shift the held word in
-  table_read<WIDE, BASE>((X & 0x1ff8u) | nb, L.d0, L.d1);
+  // opaque: keeps BASE in the lookup's offset instead of an add into nb
+  table_read<WIDE, BASE>(opaque((X & 0x1ff8u) | nb), L.d0, L.d1);
   __builtin_amdgcn_sched_barrier(0);  // the next lookup goes out before the refill
   if (need) {  // refilling lanes only: read the following word
     L.r = lds_u16(L.p + 2u);
@@ -293,9 +289,13 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
         const u32x4 pk = {pack2<OUT>(y[0], y[1]), pack2<OUT>(y[2], y[3]), pack2<OUT>(y[4], y[5]), pack2<OUT>(y[6], y[7])};
         __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x4 *)(row + lane_off));
       } else if constexpr (OUT == EP_FP8_E4M3FN) {
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[0]), fp8_clamp(y[1]), 0, false);
+        // the first conversion of each word fills its low half; the high half
+        // it keeps (here the first input's bits) is overwritten by the second,
+        // so the word needs no zeroing first
+        const float c0 = fp8_clamp(y[0]), c4 = fp8_clamp(y[4]);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c0, fp8_clamp(y[1]), __float_as_int(c0), false);
         lo = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[2]), fp8_clamp(y[3]), lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[4]), fp8_clamp(y[5]), 0, false);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c4, fp8_clamp(y[5]), __float_as_int(c4), false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[6]), fp8_clamp(y[7]), hi, true);
         const u32x2 pk = {(uint32_t)lo, (uint32_t)hi};
         __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x2 *)(row + lane_off));
