@@ -21,6 +21,10 @@
 //      expands the context's table 64 slots at a time: a slot's symbol is the
 //      number of starts up to it, which v_mbcnt counts from the row's bitmap;
 //   3. each wave decodes its tile.
+// Streams with more tiles than one such round of workgroups covers take the
+// multi-tile kernel instead: one workgroup of up to 16 waves per CU builds
+// the tables once, and each wave then loads and decodes one tile after
+// another on its own.
 //
 // Decode step for state x in [2^13, 2^29), kept as X = 8x so that the table
 // address is one AND-OR:  8*slot = X & 0x1ff8;  e = table[ctx][slot];
@@ -72,7 +76,7 @@ namespace ep {
 namespace {
 
 constexpr int kMaxWaves = 8;        // decoding waves per workgroup, single-round kernel
-constexpr int kMaxRoundWaves = 12;  // round kernel: three per SIMD, which the VALU can feed
+constexpr int kMaxTileWaves = 16;  // multi-tile kernel: four per SIMD cover the decode chain
 constexpr uint32_t kCtxBytes = kProbTotal * 8;             // 8 KB per context
 constexpr uint32_t kTableBytes = kContexts * kCtxBytes;     // 57344
 constexpr uint32_t kRows = kProbTotal / 64;                // 16 rows of 64 slots per context
@@ -100,10 +104,8 @@ struct Args {
   uint32_t row_magic, row_shift;  // vec / vpr = umulhi(vec, row_magic) >> row_shift  (vpr > 1)
   uint32_t n_vec, n_tiles, waves;
   uint32_t rec_off, mark_off, words_off;  // LDS byte offsets
-  uint32_t rounds;                           // rounds of k tiles per workgroup (round kernel)
-  uint32_t wg_q, wg_rem;                     // round kernel: workgroup b decodes wg_q tiles, one more if b < wg_rem
-  uint32_t buf0, buf1;                       // LDS byte offsets of its two round buffers
-  uint32_t toff_rel, scales_rel, words_rel;  // sections of a round buffer
+  uint32_t wg_q, wg_rem;  // multi-tile kernel: workgroup b decodes wg_q tiles, one more if b < wg_rem
+  uint32_t wbuf;          // multi-tile kernel: bytes of each wave's word buffer
 };
 
 typedef __attribute__((address_space(1))) void *gptr_t;
@@ -451,111 +453,77 @@ __device__ __forceinline__ void build_tables(const Args &A, uint8_t *lds, uint32
   }
 }
 
-// LDS copy of one round: the round's tiles are consecutive, so their start
-// states, tile offsets, row scales and words are each one range of the stream.
-// Each range is copied from a 16-byte aligned start; the decoding waves find
-// their pieces relative to that start.
-struct RoundBuf {
-  uint32_t states, toff, scales, words;  // LDS byte offsets
-};
-
-__device__ __forceinline__ RoundBuf round_buf(const Args &A, uint32_t r) {
-  const uint32_t b = (r & 1u) ? A.buf1 : A.buf0;
-  return RoundBuf{b, b + A.toff_rel, b + A.scales_rel, b + A.words_rel};
-}
-
-// the row of vector vec
-__device__ __forceinline__ uint32_t row_of(const Args &A, uint32_t vec) {
-  return A.vpr == 1u ? vec : __umulhi(vec, A.row_magic) >> A.row_shift;
-}
-
-// Round kernel: workgroup b decodes the consecutive tiles [wg_first(b),
-// wg_first(b + 1)), k per round; the counts differ by at most one tile, so
-// that every workgroup's last round is about as full as the others'.
+// Multi-tile kernel: workgroup b decodes the consecutive tiles
+// [wg_first(b), wg_first(b + 1)); the counts differ by at most one tile.
 __device__ __forceinline__ uint32_t wg_first(const Args &A, uint32_t b) {
   return b * A.wg_q + (b < A.wg_rem ? b : A.wg_rem);
 }
 
-// Copies n 16-byte pieces from src into LDS at dst with global_load_lds
-// (1 KB per instruction); lanes past the end stay idle.
-__device__ __forceinline__ void copy_to_lds(uint8_t *lds, gbyte_t src, uint32_t n, uint32_t dst, uint32_t lane) {
-  for (uint32_t i = 0; 64u * i < n; ++i) {
-    if (64u * i + lane < n)
-      __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + dst + 1024u * i), 16,
-                                       0, 0);
-  }
-}
+// What a wave needs in registers to decode one tile: its start states, the
+// row scale of each of its lane's vectors, and where its words land in LDS.
+struct TileIn {
+  uint32_t x0;
+  float gs[16];
+  uint32_t wt, we;  // LDS byte addresses of the tile's first word and of its end
+};
 
-// The copying wave's work for round r: tiles [t0, t1) of this workgroup.
-__device__ __forceinline__ void stage_round(const Args &A, uint8_t *lds, uint32_t r, uint32_t lane) {
-  const uint32_t k = A.waves, end = wg_first(A, blockIdx.x + 1u);
-  const uint32_t t0 = wg_first(A, blockIdx.x) + r * k;
-  if (t0 >= end) return;
-  const uint32_t t1 = t0 + k < end ? t0 + k : end;
-  const RoundBuf B = round_buf(A, r);
-  // word range: its ends from two scalar loads, issued first
+// Issues a tile's loads: start states and row scales (vector loads), word
+// offsets (scalar loads), and the copy of its words into LDS at buf with
+// global_load_lds (1 KB per instruction; lanes past the end of the last,
+// partial kilobyte re-read its last 16 bytes).  Nothing here waits for them.
+__device__ __forceinline__ TileIn issue_tile(const Args &A, uint8_t *lds, uint32_t tile, uint32_t buf, uint32_t lane) {
+  TileIn T;
+  T.x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tile * 64u + lane];
+  {
+    const float *scales = reinterpret_cast<const float *>(A.blob + A.off_scales);
+    const uint32_t last = A.rows - 1u, one = A.vpr == 1u ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const uint32_t vec = tile * 1024u + 64u * s + lane;
+      const uint32_t r = ((__umulhi(vec, A.row_magic) >> A.row_shift) & ~one) | (vec & one);
+      T.gs[s] = scales[r < last ? r : last];  // lanes past the end read the last row; their values are unused
+    }
+  }
   typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
   const cptr_u32 toff = (cptr_u32)(A.blob + A.off_tile_offsets);
-  const uint32_t w0 = toff[t0], w1 = toff[t1];
-  // start states: 256 bytes per tile, contiguous and aligned
-  copy_to_lds(lds, (gbyte_t)(A.blob + A.off_states + 256ull * t0), 16u * (t1 - t0), B.states, lane);
-  // tile offsets t0..t1
-  {
-    const uint64_t a0 = (A.off_tile_offsets + 4ull * t0) & ~15ull, a1 = A.off_tile_offsets + 4ull * t1 + 4ull;
-    copy_to_lds(lds, (gbyte_t)(A.blob + a0), (uint32_t)((a1 - a0 + 15ull) >> 4), B.toff, lane);
+  const uint32_t w_begin = toff[tile], w_end = toff[tile + 1u];
+  const uint64_t gbyte0 = (A.off_words + 2ull * w_begin) & ~15ull;
+  const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * w_end + 15ull) & ~15ull) - gbyte0) >> 4);
+  const gbyte_t src = (gbyte_t)(A.blob + gbyte0);
+  uint32_t i = 0;
+  for (; 64u * i + 64u <= nchunks; ++i)
+    __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + buf + 1024u * i), 16, 0, 0);
+  if (64u * i < nchunks) {
+    const uint32_t ch = lane + 64u * i;
+    __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (ch < nchunks ? ch : nchunks - 1u)),
+                                     (lptr_t)(lds + buf + 1024u * i), 16, 0, 0);
   }
-  // row scales of the rows the tiles touch
-  {
-    const uint32_t last_vec = (t1 * 1024u < A.n_vec ? t1 * 1024u : A.n_vec) - 1u;
-    const uint64_t a0 = (A.off_scales + 4ull * row_of(A, t0 * 1024u)) & ~15ull;
-    const uint64_t a1 = A.off_scales + 4ull * row_of(A, last_vec) + 4ull;
-    copy_to_lds(lds, (gbyte_t)(A.blob + a0), (uint32_t)((a1 - a0 + 15ull) >> 4), B.scales, lane);
-  }
-  // words, whole kilobytes first: no per-lane test, so each copy issues right
-  // after the last one
-  {
-    const uint64_t a0 = (A.off_words + 2ull * w0) & ~15ull;
-    const uint32_t n = (uint32_t)((((A.off_words + 2ull * w1 + 15ull) & ~15ull) - a0) >> 4);
-    const gbyte_t src = (gbyte_t)(A.blob + a0);
-    uint32_t i = 0;
-    for (; 64u * i + 64u <= n; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + B.words + 1024u * i), 16,
-                                       0, 0);
-    if (64u * i + lane < n)
-      __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + B.words + 1024u * i), 16,
-                                       0, 0);
-  }
+  T.wt = buf + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);
+  T.we = T.wt + 2u * (w_end - w_begin);
+  return T;
 }
 
 // workgroup barrier that orders LDS accesses: every LDS access before it has
 // completed, none after it has started
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Streams with more tiles than one round of workgroups covers: one workgroup
-// per CU, whose waves 0..k-1 build the tables once and then decode one tile
-// each per round; wave k copies each round's stream ranges into LDS, the next
-// round's while the current one is decoded (two round buffers).
+// Streams with more tiles than one round of workgroups covers: one
+// workgroup per CU builds the tables once, then each of its k waves decodes
+// tiles first + wave, first + wave + k, ... of the workgroup's run on its
+// own, copying each tile's words into a buffer of its own.  After the tables
+// no wave waits for another: while one waits for its next tile's loads, the
+// other waves of its SIMD keep the VALU busy (four waves per SIMD cover the
+// decode chain's latency).
 template <int OUT, bool WIDE, bool PADDED>
-__global__ void __launch_bounds__(64 * (kMaxRoundWaves + 1)) decode_rounds_kernel(Args A) {
+__global__ void __launch_bounds__(64 * kMaxTileWaves) decode_waves_kernel(Args A) {
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t k = A.waves;  // decoding waves; wave k copies
+  const uint32_t k = A.waves;
+  const uint32_t end = wg_first(A, blockIdx.x + 1u);
+  const uint32_t buf = A.words_off + wave * A.wbuf;  // this wave's word buffer
 
-  if (wave == k) {
-    // ---- copying wave ----------------------------------------------------
-    stage_round(A, lds, 0, lane);
-    __builtin_amdgcn_s_waitcnt(0);  // round 0 has landed
-    lds_barrier();                  // tables built, round 0 in LDS
-    for (uint32_t r = 0; r < A.rounds; ++r) {
-      if (r + 1u < A.rounds) stage_round(A, lds, r + 1u, lane);
-      __builtin_amdgcn_s_waitcnt(0);  // round r + 1 has landed
-      lds_barrier();                  // round r decoded: its buffer is free
-    }
-    return;
-  }
-
-  // ---- decoding waves: 1. the first context's frequencies ------------------
+  // ---- 1. the first context's frequencies ----------------------------------
   const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
   const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
   uint32_t fpre[4];
@@ -568,43 +536,34 @@ __global__ void __launch_bounds__(64 * (kMaxRoundWaves + 1)) decode_rounds_kerne
       fpre[i] = s < n0 ? v : 0u;
     }
   }
+  uint32_t tile = wg_first(A, blockIdx.x) + wave;
+  const uint32_t tc = tile < end ? tile : end - 1u;  // waves without a tile load a valid one and drop it
+  // Waves that build no table issue their first tile's loads now and start
+  // decoding right after the barrier; the table builders issue theirs after
+  // their table, so that no wait for a tile's loads (the compiler waits for
+  // every copy into LDS before the next LDS access) delays a table.
+  const bool builder = wave < (uint32_t)kContexts;
+  TileIn T;
+  if (!builder) T = issue_tile(A, lds, tc, buf, lane);
 
   // ---- 2. the tables -------------------------------------------------------
   build_tables<WIDE>(A, lds, wave, lane, k, fpre);
-  lds_barrier();  // tables built, round 0 in LDS
+  if (builder) T = issue_tile(A, lds, tc, buf, lane);
+  lds_barrier();  // tables built (every wave's LDS writes done)
 
-  // ---- 3. rounds: one tile per wave -----------------------------------------
-  const uint32_t first = wg_first(A, blockIdx.x), end = wg_first(A, blockIdx.x + 1u);
-  for (uint32_t r = 0; r < A.rounds; ++r) {
-    const uint32_t t0 = first + r * k;
-    const uint32_t tile = t0 + wave;
+  // ---- 3. this wave's tiles --------------------------------------------------
+  while (tile < end) {
+    __builtin_amdgcn_s_waitcnt(0);  // the tile's states, scales and words have landed
+    const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
+    if (n == 1024u)
+      decode_tile<OUT, WIDE, PADDED, false>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
+    else
+      decode_tile<OUT, WIDE, PADDED, true>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
+    tile += k;
     if (tile < end) {
-      const RoundBuf B = round_buf(A, r);
-      // this tile's word range and the round's aligned start, from the copy of
-      // the tile offsets
-      const uint32_t tpos = B.toff + (uint32_t)((A.off_tile_offsets + 4ull * t0) & 15ull);
-      const uint32_t r_begin = lds_u32(tpos), w_begin = lds_u32(tpos + 4u * wave), w_end = lds_u32(tpos + 4u * wave + 4u);
-      const uint64_t gbyte0 = (A.off_words + 2ull * r_begin) & ~15ull;
-      const uint32_t wt = B.words + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);  // this tile's first word
-      const uint32_t we = wt + 2u * (w_end - w_begin);
-      const uint32_t X = lds_u32(B.states + 256u * wave + 4u * lane) << 3;
-      // row scales, from the copy that starts at row0's aligned address
-      const uint32_t row0 = row_of(A, t0 * 1024u);
-      const uint32_t sbase = B.scales + (uint32_t)((A.off_scales + 4ull * row0) & 15ull) - 4u * row0;
-      float gs[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const uint32_t vec = tile * 1024u + 64u * s + lane;
-        const uint32_t last = A.n_vec - 1u;  // lanes past the end read the last vector's scale, unused
-        gs[s] = __uint_as_float(lds_u32(sbase + 4u * row_of(A, vec < last ? vec : last)));
-      }
-      const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
-      if (n == 1024u)
-        decode_tile<OUT, WIDE, PADDED, false>(A, wt, we, X, tile, n, gs, lane);
-      else
-        decode_tile<OUT, WIDE, PADDED, true>(A, wt, we, X, tile, n, gs, lane);
+      __builtin_amdgcn_s_waitcnt(0);  // every read of the finished tile's words is done before they are overwritten
+      T = issue_tile(A, lds, tile, buf, lane);
     }
-    lds_barrier();  // round r decoded; round r + 1 in LDS
   }
 }
 
@@ -697,28 +656,28 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
 typedef void (*KernelFn)(Args);
 
 template <int OUT, bool WIDE, bool PADDED>
-KernelFn pick3(bool rounds) {
-  return rounds ? decode_rounds_kernel<OUT, WIDE, PADDED> : decode_kernel<OUT, WIDE, PADDED>;
+KernelFn pick3(bool multi) {
+  return multi ? decode_waves_kernel<OUT, WIDE, PADDED> : decode_kernel<OUT, WIDE, PADDED>;
 }
 
 template <int OUT>
-KernelFn pick(bool wide, bool padded, bool rounds) {
-  if (wide) return padded ? pick3<OUT, true, true>(rounds) : pick3<OUT, true, false>(rounds);
-  return padded ? pick3<OUT, false, true>(rounds) : pick3<OUT, false, false>(rounds);
+KernelFn pick(bool wide, bool padded, bool multi) {
+  if (wide) return padded ? pick3<OUT, true, true>(multi) : pick3<OUT, true, false>(multi);
+  return padded ? pick3<OUT, false, true>(multi) : pick3<OUT, false, false>(multi);
 }
 
-KernelFn pick_kernel(int out, bool wide, bool padded, bool rounds) {
+KernelFn pick_kernel(int out, bool wide, bool padded, bool multi) {
   switch (out) {
-    case EP_BF16: return pick<EP_BF16>(wide, padded, rounds);
-    case EP_FP16: return pick<EP_FP16>(wide, padded, rounds);
-    case EP_FP8_E4M3FN: return pick<EP_FP8_E4M3FN>(wide, padded, rounds);
-    case EP_INT8: return pick<EP_INT8>(wide, padded, rounds);
-    default: return pick<kOutSym>(wide, false, rounds);
+    case EP_BF16: return pick<EP_BF16>(wide, padded, multi);
+    case EP_FP16: return pick<EP_FP16>(wide, padded, multi);
+    case EP_FP8_E4M3FN: return pick<EP_FP8_E4M3FN>(wide, padded, multi);
+    case EP_INT8: return pick<EP_INT8>(wide, padded, multi);
+    default: return pick<kOutSym>(wide, false, multi);
   }
 }
 
-// compute units of the current device (one workgroup each at most in the
-// round kernel)
+// compute units of the current device (one workgroup each in the multi-tile
+// kernel)
 int64_t num_cus() {
   static std::mutex mu;
   static std::vector<int> cache;
@@ -837,63 +796,37 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   }
   uint32_t lds_bytes = off + (uint32_t)span + kLdsPad;
   uint32_t grid = (uint32_t)((s.tiles + waves - 1) / waves);
-  // More workgroups than compute units: the round kernel instead, with one
-  // workgroup per CU that builds the tables once.  A round buffer holds k
-  // tiles' start states, tile offsets, row scales and words; two buffers (the
-  // next round is copied while the current one is decoded).
-  const bool rounds = (int64_t)grid > num_cus();
-  if (rounds) {
+  // More workgroups than compute units: the multi-tile kernel instead, with
+  // one workgroup per CU that builds the tables once.
+  const bool multi = (int64_t)grid > num_cus();
+  if (multi) {
     // One workgroup per CU, each with a run of consecutive tiles (counts that
-    // differ by at most one), decoded k at a time: the fewest rounds that k
-    // decoding waves allow, then the smallest k that keeps that many rounds,
-    // so that every round is about equally full.
-    const uint32_t fixed = A.words_off;
-    auto row_of_vec = [&](int64_t vec) { return vec / (s.cols8 / 8); };
-    const int64_t g = std::min<int64_t>(s.tiles, num_cus());
-    const int64_t q = s.tiles / g, rem = s.tiles % g, qmax = q + (rem ? 1 : 0);
-    auto first_of = [&](int64_t b) { return b * q + std::min<int64_t>(b, rem); };
-    bool ok = false;
-    for (int64_t kk = kMaxRoundWaves; kk >= 1 && !ok; --kk) {
-      const int64_t R = (qmax + kk - 1) / kk;
-      const uint32_t k = (uint32_t)((qmax + R - 1) / R);
-      uint64_t wspan = 0, sspan = 0;  // the largest ranges over every round of every workgroup
-      for (int64_t b = 0; b < g; ++b) {
-        const int64_t end = first_of(b + 1);
-        for (int64_t t = first_of(b); t < end; t += k) {
-          const int64_t e = std::min<int64_t>(t + k, end);
-          const uint64_t a0 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t)) & ~15ull;
-          const uint64_t a1 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * e) + 15ull) & ~15ull;
-          wspan = std::max<uint64_t>(wspan, a1 - a0);
-          const int64_t last_vec = std::min<int64_t>(e * kTileVecs, s.n_vec) - 1;
-          const uint64_t b0 = (s.off_scales + 4ull * row_of_vec(t * kTileVecs)) & ~15ull;
-          const uint64_t b1 = s.off_scales + 4ull * row_of_vec(last_vec) + 4ull;
-          sspan = std::max<uint64_t>(sspan, (b1 - b0 + 15ull) & ~15ull);
-        }
-      }
-      const uint32_t toff_rel = 256u * k;
-      const uint32_t scales_rel = toff_rel + (uint32_t)align16(4u * (k + 1u) + 15u);
-      if (sspan > kLdsLimit) continue;
-      const uint32_t words_rel = scales_rel + (uint32_t)sspan;
-      const uint64_t buf = align16(words_rel + ((wspan + 1023ull) & ~1023ull));  // words copied in whole kilobytes
-      const uint64_t total = fixed + 2 * buf + kLdsPad;
-      if (total > kLdsLimit) continue;
-      ok = true;
-      waves = k;
-      grid = (uint32_t)g;
-      A.rounds = (uint32_t)R;
-      A.wg_q = (uint32_t)q;
-      A.wg_rem = (uint32_t)rem;
-      A.buf0 = fixed;
-      A.buf1 = fixed + (uint32_t)buf;
-      A.toff_rel = toff_rel;
-      A.scales_rel = scales_rel;
-      A.words_rel = words_rel;
-      lds_bytes = (uint32_t)total;
+    // differ by at most one); its k waves take the run's tiles in turn.  k is
+    // the smallest wave count that keeps the fewest passes over the run that
+    // the LDS allows, so that the waves' tile counts differ by at most one.
+    // Every wave has a buffer for one tile's words, copied in whole
+    // kilobytes from a 16-byte aligned start.
+    uint64_t wbuf = 0;
+    for (int64_t t = 0; t < s.tiles; ++t) {
+      const uint64_t a0 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t)) & ~15ull;
+      const uint64_t a1 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t + 4) + 15ull) & ~15ull;
+      wbuf = std::max<uint64_t>(wbuf, (a1 - a0 + 1023ull) & ~1023ull);
     }
-    if (!ok) {
+    const uint64_t room = kLdsLimit - std::min<uint64_t>(kLdsLimit, (uint64_t)A.words_off + kLdsPad);
+    const int64_t kmax = std::min<int64_t>(kMaxTileWaves, (int64_t)(room / wbuf));
+    if (kmax < 1) {
       set_error("tile too large for the decoder's LDS budget");
       return EP_ERR_FORMAT;
     }
+    const int64_t g = std::min<int64_t>(s.tiles, num_cus());
+    const int64_t q = s.tiles / g, rem = s.tiles % g, qmax = q + (rem ? 1 : 0);
+    const int64_t passes = (qmax + kmax - 1) / kmax;
+    waves = (uint32_t)((qmax + passes - 1) / passes);
+    grid = (uint32_t)g;
+    A.wg_q = (uint32_t)q;
+    A.wg_rem = (uint32_t)rem;
+    A.wbuf = (uint32_t)wbuf;
+    lds_bytes = A.words_off + waves * (uint32_t)wbuf + kLdsPad;
   }
   A.blob = reinterpret_cast<const uint8_t *>(dev_blob);
   A.out = dev_out;
@@ -909,7 +842,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   A.n_vec = (uint32_t)s.n_vec;
   A.n_tiles = (uint32_t)s.tiles;
   const bool padded = out != kOutSym && (s.cols % 8) != 0;
-  KernelFn fn = pick_kernel(out, wide, padded, rounds);
+  KernelFn fn = pick_kernel(out, wide, padded, multi);
   static std::mutex mu;
   static std::vector<KernelFn> configured;
   {
@@ -926,7 +859,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     }
   }
   A.waves = waves;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * (waves + (rounds ? 1u : 0u))), lds_bytes, stream, A);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * waves), lds_bytes, stream, A);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) {
     set_error(std::string("kernel launch failed: ") + hipGetErrorString(err));

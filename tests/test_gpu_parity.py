@@ -64,8 +64,9 @@ WORKLOADS = ["gauss256_bf16_3.5", "rowscale4096_bf16_4.0", "t4outlier3072x12288_
              "absmax8192_fp8_3.0"]
 RAGGED = ["ragged_1_8_bf16_0.3", "ragged_3_5_bf16_0.3", "ragged_7_13_fp16_0.2", "ragged_3_2736_bf16_0.5",
           "ragged_129_64_bf16_0.05", "ragged_64_1032_fp16_1.0", "ragged_5_4100_bf16_2.0", "ragged_1030_8_bf16_0.3",
-          # more tiles than one round of workgroups covers (the round kernel):
-          # wide tables with padded columns, and FP16
+          # more tiles than one round of workgroups covers (the multi-tile
+          # kernel, some waves without a tile in the last pass): wide tables
+          # with padded columns, and FP16
           "ragged_3200_8190_bf16_0.05", "ragged_3200_8192_fp16_0.3"]
 DIT = ["dit_0_0", "dit_0_4", "dit_0_5"]
 
