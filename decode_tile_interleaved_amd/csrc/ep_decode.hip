@@ -47,11 +47,12 @@
 // SIMD).
 //
 // Table entries (2^10 slots of 8 bytes per context; one ds_read_b64 meets
-// fewer LDS bank conflicts than two dword reads):
-//   narrow (every used value in [-128, 127]): d0 = 8f | (v + 128) << 24,
-//     d1 = 8 (slot - cum), so that X' = mad_u32_u24(d0, X >> 13, d1) and the
-//     value converts with one v_cvt_f32_ubyte3;
-//   wide (values in [-2048, 2047]): d0 = f | (slot - cum) << 10 | v << 20.
+// fewer LDS bank conflicts than two dword reads), d1 = 8 (slot - cum) and
+//   narrow (every used value in [-128, 127]): d0 = 8f | (v + 128) << 24, so
+//     that X' = mad_u32_u24(d0, X >> 13, d1) and the value converts with one
+//     v_cvt_f32_ubyte3;
+//   wide (values in [-2048, 2047]): d0 = 8f | v << 20, whose low 13 bits
+//     (one AND) are the multiplier.
 // Either way bits 0 and 1 of v sit at a fixed place in d0 (24/25 or 20/21):
 // bit 0 is the coset bit b, and the XOR of bit 1 over coordinates 0..6 is the
 // parity p that selects the last coordinate's context.
@@ -110,12 +111,10 @@ struct Args {
 
 typedef __attribute__((address_space(1))) void *gptr_t;
 typedef __attribute__((address_space(3))) void *lptr_t;
-typedef __attribute__((address_space(3))) const uint32_t *lds_u32_ptr;
 typedef __attribute__((address_space(3))) const uint16_t *lds_u16_ptr;
 
 // LDS loads by byte address; the decode kernel declares no static LDS, so its
 // dynamic LDS starts at address 0
-__device__ __forceinline__ uint32_t lds_u32(uint32_t byte) { return *(lds_u32_ptr)(uintptr_t)byte; }
 __device__ __forceinline__ uint32_t lds_u16(uint32_t byte) { return *(lds_u16_ptr)(uintptr_t)byte; }
 __device__ __forceinline__ uint32_t lds_u8(uint32_t byte) {
   return *(__attribute__((address_space(3))) const uint8_t *)(uintptr_t)byte;
@@ -192,15 +191,11 @@ struct Lane {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) const u32x2 *lds_u64_ptr;
 
-template <bool WIDE, uint32_t BASE>
+template <uint32_t BASE>
 __device__ __forceinline__ void table_read(uint32_t a, uint32_t &d0, uint32_t &d1) {
-  if constexpr (WIDE) {
-    d0 = lds_u32(a + BASE);
-  } else {
-    const u32x2 v = *(lds_u64_ptr)(uintptr_t)(a + BASE);
-    d0 = v.x;
-    d1 = v.y;
-  }
+  const u32x2 v = *(lds_u64_ptr)(uintptr_t)(a + BASE);
+  d0 = v.x;
+  d1 = v.y;
 }
 
 // one rANS decode step of every active lane: decodes this step's symbol,
@@ -211,7 +206,7 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   const uint32_t e = L.d0;
   uint32_t x;
   if constexpr (WIDE) {
-    x = (__umul24(e & 0x3ffu, L.q) + ((e >> 10) & 0x3ffu)) << 3;
+    x = __umul24(e & 0x1fffu, L.q) + L.d1;  // v sits in bits 20..31, inside the 24-bit operand
   } else {
     x = __umul24(e, L.q) + L.d1;
   }
@@ -224,7 +219,7 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   const uint64_t m = __ballot(need);
   const uint32_t X = select_mask(m, x, (x << 16) | r8);  // next state: refilling lanes shift the held word in
   // opaque: keeps BASE in the lookup's offset instead of an add into nb
-  table_read<WIDE, BASE>(opaque((X & 0x1ff8u) | nb), L.d0, L.d1);
+  table_read<BASE>(opaque((X & 0x1ff8u) | nb), L.d0, L.d1);
   __builtin_amdgcn_sched_barrier(0);  // the next lookup goes out before the refill
   if (need) {  // refilling lanes only: read the following word
     L.r = lds_u16(L.p + 2u);
@@ -340,7 +335,7 @@ template <int OUT, bool WIDE, bool PADDED, bool PARTIAL>
 __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t we, uint32_t X, uint32_t tile,
                                             uint32_t n, const float (&gs)[16], uint32_t lane) {
   Lane L;
-  table_read<WIDE, 0u>(X & 0x1ff8u, L.d0, L.d1);  // context F
+  table_read<0u>(X & 0x1ff8u, L.d0, L.d1);  // context F
   L.q = X >> 13;
   // this state's words follow the count bytes of the states before it; the
   // clamp keeps every read of a corrupt tile inside the LDS allocation
@@ -404,8 +399,8 @@ __device__ __forceinline__ void build_tables(const Args &A, uint8_t *lds, uint32
       const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nzb));
       if (used && cum < kProbTotal) {
         const int32_t v = symbol_value(c, smin + (int32_t)s);
-        rec[r] = WIDE ? make_uint2(f | ((uint32_t)v & 0xfffu) << 20, cum)
-                      : make_uint2((f << 3) | ((uint32_t)(v + 128) & 0xffu) << 24, cum << 3);
+        rec[r] = make_uint2((f << 3) | (WIDE ? ((uint32_t)v & 0xfffu) << 20 : ((uint32_t)(v + 128) & 0xffu) << 24),
+                            cum << 3);
         atomicOr(&mark[c * kMarkWords + (cum >> 5)], 1u << (cum & 31u));
       }
       carry += __builtin_amdgcn_readlane(incl, 63);
@@ -443,12 +438,8 @@ __device__ __forceinline__ void build_tables(const Args &A, uint8_t *lds, uint32
 #pragma unroll
     for (uint32_t row = 0; row < kRows; ++row) {
       const uint32_t slot = row * 64u + lane, idx = 2u * (lc * kProbTotal + slot);
-      if (WIDE) {
-        tab[idx] = rc[row].x | ((slot - rc[row].y) << 10);
-      } else {
-        tab[idx] = rc[row].x;
-        tab[idx + 1u] = (slot << 3) - rc[row].y;
-      }
+      tab[idx] = rc[row].x;
+      tab[idx + 1u] = (slot << 3) - rc[row].y;
     }
   }
 }
