@@ -48,12 +48,12 @@
 //
 // Table entries (2^10 slots of 8 bytes per context; one ds_read_b64 meets
 // fewer LDS bank conflicts than two dword reads), d1 = 8 (slot - cum) and
-//   narrow (every used value in [-128, 127]): d0 = 8f | (v + 128) << 24, so
-//     that X' = mad_u32_u24(d0, X >> 13, d1) and the value converts with one
-//     v_cvt_f32_ubyte3;
-//   wide (values in [-2048, 2047]): d0 = 8f | v << 20, whose low 13 bits
-//     (one AND) are the multiplier.
-// Either way bits 0 and 1 of v sit at a fixed place in d0 (24/25 or 20/21):
+//   narrow (every used value in [-128, 127]): d0 = 8f | v << 24 (v as a
+//     signed byte), so that X' = mad_u32_u24(d0, X >> 13, d1) and the value
+//     converts in place (SDWA, byte 3 sign-extended);
+//   wide (values in [-2048, 2047]): d0 = 8f | v << 16, whose low 13 bits
+//     (one AND) are the multiplier and whose high half converts in place.
+// Either way bits 0 and 1 of v sit at a fixed place in d0 (24/25 or 16/17):
 // bit 0 is the coset bit b, and the XOR of bit 1 over coordinates 0..6 is the
 // parity p that selects the last coordinate's context.
 //
@@ -206,7 +206,7 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   const uint32_t e = L.d0;
   uint32_t x;
   if constexpr (WIDE) {
-    x = __umul24(e & 0x1fffu, L.q) + L.d1;  // v sits in bits 20..31, inside the 24-bit operand
+    x = __umul24(e & 0x1fffu, L.q) + L.d1;  // v sits in bits 16..31, partly inside the 24-bit operand
   } else {
     x = __umul24(e, L.q) + L.d1;
   }
@@ -231,14 +231,15 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
 
 template <bool WIDE>
 __device__ __forceinline__ int32_t entry_value(uint32_t e) {
-  if constexpr (WIDE) return (int32_t)e >> 20;
-  return (int32_t)(e >> 24) - 128;
+  if constexpr (WIDE) return (int32_t)e >> 16;
+  return (int32_t)e >> 24;
 }
 
 template <bool WIDE>
-__device__ __forceinline__ float entry_weight(uint32_t e, float g, float ng) {
-  if constexpr (WIDE) return (float)((int32_t)e >> 20) * g;
-  return __builtin_fmaf((float)(e >> 24), g, ng);  // (v + 128) g - 128 g, one rounding
+__device__ __forceinline__ float entry_weight(uint32_t e, float g) {
+  // the value converts in place from its byte or half (SDWA); one rounding
+  if constexpr (WIDE) return (float)(int16_t)(e >> 16) * g;
+  return (float)(int8_t)(e >> 24) * g;
 }
 
 __device__ __forceinline__ uint32_t int8_byte(float y) {
@@ -277,10 +278,9 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
     __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x4 *)(row + lane_off));
     return;
   } else {
-    const float ng = -128.0f * g;
     float y[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = entry_weight<WIDE>(e[j], g, ng);
+    for (int j = 0; j < 8; ++j) y[j] = entry_weight<WIDE>(e[j], g);
     if constexpr (!PADDED) {
       if constexpr (OUT == EP_BF16 || OUT == EP_FP16) {
         const u32x4 pk = {pack2<OUT>(y[0], y[1]), pack2<OUT>(y[2], y[3]), pack2<OUT>(y[4], y[5]), pack2<OUT>(y[6], y[7])};
@@ -344,7 +344,7 @@ __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t
   L.p = p < we ? p : we;
   L.r = lds_u16(L.p);
   constexpr uint32_t kC = kCtxBytes, kE = 3u * kCtxBytes;  // LDS bases of C_0 and E_{0,0}
-  constexpr uint32_t kBitB = WIDE ? 20u : 24u;  // where bit 0 of v sits in d0
+  constexpr uint32_t kBitB = WIDE ? 16u : 24u;  // where bit 0 of v sits in d0
   constexpr uint32_t kStepBytes = 64u * ((OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u);
   const gbyte_t tile_out = (gbyte_t)A.out + (uint64_t)tile * (16u * kStepBytes);
 #pragma unroll
@@ -399,7 +399,7 @@ __device__ __forceinline__ void build_tables(const Args &A, uint8_t *lds, uint32
       const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nzb));
       if (used && cum < kProbTotal) {
         const int32_t v = symbol_value(c, smin + (int32_t)s);
-        rec[r] = make_uint2((f << 3) | (WIDE ? ((uint32_t)v & 0xfffu) << 20 : ((uint32_t)(v + 128) & 0xffu) << 24),
+        rec[r] = make_uint2((f << 3) | (WIDE ? ((uint32_t)v & 0xffffu) << 16 : ((uint32_t)v & 0xffu) << 24),
                             cum << 3);
         atomicOr(&mark[c * kMarkWords + (cum >> 5)], 1u << (cum & 31u));
       }
