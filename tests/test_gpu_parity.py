@@ -35,6 +35,10 @@ def oracle_case(name: str):
         _, blk, j = name.split("_")
         x, target = W.dit_matrix(int(blk), int(j)), 4.0
         blob, rc, _ = oracle.compress(x, target)
+    elif name.startswith("codes"):
+        _, r, c, kind, t = name.split("_")
+        x = W.absmax_codes(int(r), int(c), seed=int(r) * 7 + int(c), kind=kind)
+        blob, rc, _ = oracle.compress(x, float(t))
     elif name.startswith("ragged"):
         _, r, c, dt, a = name.split("_")
         dtype = {"bf16": torch.bfloat16, "fp16": torch.float16}[dt]
@@ -69,9 +73,13 @@ RAGGED = ["ragged_1_8_bf16_0.3", "ragged_3_5_bf16_0.3", "ragged_7_13_fp16_0.2", 
           # with padded columns, and FP16
           "ragged_3200_8190_bf16_0.05", "ragged_3200_8192_fp16_0.3"]
 DIT = ["dit_0_0", "dit_0_4", "dit_0_5"]
+# 8-bit code containers with padded columns (per-element stores), narrow and
+# wide tables, in one round of workgroups and in the multi-tile kernel
+CODES = ["codes_37_1030_int8_3.0", "codes_37_1030_fp8_3.0", "codes_300_1030_int8_7.0", "codes_2100_8190_int8_3.0",
+         "codes_2100_8190_fp8_7.0"]
 
 
-@pytest.mark.parametrize("name", WORKLOADS + RAGGED + DIT)
+@pytest.mark.parametrize("name", WORKLOADS + RAGGED + DIT + CODES)
 def test_symbols_bit_exact(name):
     x, blob, v_ref, _ = oracle_case(name)
     p = gpu_packed(blob)
@@ -83,7 +91,7 @@ def test_symbols_bit_exact(name):
     assert bad.size == 0, f"{bad.shape[0]} symbol mismatches, first at {bad[:4].tolist()}"
 
 
-@pytest.mark.parametrize("name", WORKLOADS + RAGGED + DIT)
+@pytest.mark.parametrize("name", WORKLOADS + RAGGED + DIT + CODES)
 def test_decompress_matches_oracle(name):
     x, blob, _, ref = oracle_case(name)
     p = gpu_packed(blob)
