@@ -231,6 +231,14 @@ def main() -> int:
         assert torch.equal(o.view(torch.int16 if o.element_size() == 2 else torch.int8),
                            ref.view(torch.int16 if ref.element_size() == 2 else torch.int8))
     rel_l2 = ((ref.double() - x.double().to(dev)).norm() / x.double().to(dev).norm()).item()
+    rel_l2_weights = None
+    if args.workload.startswith("absmax"):
+        # 8-bit codes: also against the N(0,1) weights the codes stand for
+        # (decoded code times the row's code scale)
+        w, scale = W.absmax_weights(rows, cols, W.WORKLOADS[args.workload][4],
+                                    "int8" if x.dtype == torch.int8 else "fp8")
+        wd = w.double().to(dev)
+        rel_l2_weights = ((ref.double() * scale.double().to(dev) - wd).norm() / wd.norm()).item()
 
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(alg_bytes)
@@ -258,6 +266,7 @@ def main() -> int:
         "clock_settle_s": round(settle_s, 3),
         "hbm_gbps_per_step": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "rel_l2": round(rel_l2, 5),
+        "rel_l2_vs_weights": round(rel_l2_weights, 5) if rel_l2_weights is not None else None,
         "encode_s": round(encode_s, 3),
     }
     if not args.no_cpu_baseline:

@@ -67,17 +67,24 @@ def t4_outliers(rows: int, cols: int, seed: int, std: float = 0.02, frac: float 
     return w.reshape(rows, cols).to(dtype)
 
 
-def absmax_codes(rows: int, cols: int, seed: int, kind: str) -> torch.Tensor:
-    """Symmetric per-row absmax codes of N(0,1) weights: INT8 in [-127, 127]
-    (round half to even) or FP8-E4M3FN in [-448, 448]."""
+def absmax_weights(rows: int, cols: int, seed: int, kind: str) -> tuple[torch.Tensor, torch.Tensor]:
+    """The N(0,1) float32 weights behind absmax_codes and their per-row code
+    scale (absmax/127 for INT8, absmax/448 for FP8): weight ~ code * scale."""
+    if kind not in ("int8", "fp8"):
+        raise ValueError(kind)
     g = _gen(seed)
     w = torch.randn(rows, cols, generator=g, dtype=torch.float32)
     amax = w.abs().amax(dim=1, keepdim=True).clamp_min(1e-30)
+    return w, amax / (127.0 if kind == "int8" else 448.0)
+
+
+def absmax_codes(rows: int, cols: int, seed: int, kind: str) -> torch.Tensor:
+    """Symmetric per-row absmax codes of N(0,1) weights: INT8 in [-127, 127]
+    (round half to even) or FP8-E4M3FN in [-448, 448]."""
+    w, scale = absmax_weights(rows, cols, seed, kind)
     if kind == "int8":
-        return torch.clamp(torch.round(w / (amax / 127.0)), -127, 127).to(torch.int8)
-    if kind == "fp8":
-        return torch.clamp(w / (amax / 448.0), -448.0, 448.0).to(torch.float8_e4m3fn)
-    raise ValueError(kind)
+        return torch.clamp(torch.round(w / scale), -127, 127).to(torch.int8)
+    return torch.clamp(w / scale, -448.0, 448.0).to(torch.float8_e4m3fn)
 
 
 def make(name: str) -> tuple[torch.Tensor, float]:
