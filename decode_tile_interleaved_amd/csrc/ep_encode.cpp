@@ -128,19 +128,11 @@ static void e8_quantize(const double *u, int32_t *v) {
 // ---------------------------------------------------------------------------
 // rows
 // ---------------------------------------------------------------------------
-struct Problem {
-  const void *src;
-  int dtype;
-  int64_t R, C, C8, vpr, n_vec, tiles;
-  int threads;
-  std::vector<double> rms;
-};
-
 static float row_scale(double rms, double a) { return (float)((rms * a) * 0.5); }
 
-// quantizes vector k of row r at stored scale g; false if a coordinate leaves
-// the stream's value range
-static bool quantize(const Problem &P, int64_t r, int64_t k, float g, int32_t *v) {
+// quantizes vector k of row r (container src, C columns) at stored scale g;
+// false if a coordinate leaves the stream's value range
+static bool quantize(const void *src, int dtype, int64_t C, int64_t r, int64_t k, float g, int32_t *v) {
   if (g == 0.0f) {
     for (int j = 0; j < 8; ++j) v[j] = 0;
     return true;
@@ -149,7 +141,7 @@ static bool quantize(const Problem &P, int64_t r, int64_t k, float g, int32_t *v
   const double two_g = 2.0 * (double)g;
   for (int j = 0; j < 8; ++j) {
     int64_t c = 8 * k + j;
-    double x = c < P.C ? widen(P.src, P.dtype, r * P.C + c) : 0.0;
+    double x = c < C ? widen(src, dtype, r * C + c) : 0.0;
     u[j] = x / two_g;
   }
   e8_quantize(u, v);
@@ -185,34 +177,8 @@ static Coded model(const int32_t *v) {
 }
 
 // ---------------------------------------------------------------------------
-// histograms and normalized frequency tables
+// normalized frequency tables
 // ---------------------------------------------------------------------------
-constexpr int kSymBias = 2048;  // symbols lie in [-2048, 2047]
-constexpr int kSymSpan = 4096;
-
-struct Histogram {
-  std::vector<uint64_t> n = std::vector<uint64_t>(kContexts * kSymSpan, 0);
-  uint64_t &at(int c, int sym) { return n[(size_t)c * kSymSpan + sym + kSymBias]; }
-  uint64_t get(int c, int sym) const {
-    int i = sym + kSymBias;
-    return (i >= 0 && i < kSymSpan) ? n[(size_t)c * kSymSpan + i] : 0;
-  }
-  void add(const Histogram &o) {
-    for (size_t i = 0; i < n.size(); ++i) n[i] += o.n[i];
-  }
-};
-
-struct Tables {
-  int16_t smin[kContexts] = {};
-  uint16_t nsym[kContexts] = {};
-  std::vector<uint32_t> freq[kContexts], cum[kContexts];
-  int total_symbols() const {
-    int t = 0;
-    for (int c = 0; c < kContexts; ++c) t += nsym[c];
-    return t;
-  }
-};
-
 // Frequencies summing to 2^10 from counts over one context's alphabet.
 static bool normalize(const uint64_t *cnt, int n, std::vector<uint32_t> &f) {
   const uint64_t M = kProbTotal;
@@ -248,11 +214,11 @@ static bool normalize(const uint64_t *cnt, int n, std::vector<uint32_t> &f) {
   return true;
 }
 
-static bool build_tables(const Histogram &h, Tables &t) {
+static bool build_tables(const std::vector<uint64_t> &h, Tables &t) {
   for (int c = 0; c < kContexts; ++c) {
     int lo = kSymSpan, hi = -1;
     for (int i = 0; i < kSymSpan; ++i)
-      if (h.n[(size_t)c * kSymSpan + i]) {
+      if (h[(size_t)c * kSymSpan + i]) {
         lo = std::min(lo, i);
         hi = i;
       }
@@ -263,7 +229,7 @@ static bool build_tables(const Histogram &h, Tables &t) {
       t.cum[c].assign(1, 0);
       continue;
     }
-    if (!normalize(&h.n[(size_t)c * kSymSpan + lo], hi - lo + 1, t.freq[c])) return false;
+    if (!normalize(&h[(size_t)c * kSymSpan + lo], hi - lo + 1, t.freq[c])) return false;
     t.smin[c] = (int16_t)(lo - kSymBias);
     t.nsym[c] = (uint16_t)t.freq[c].size();
     t.cum[c].assign(t.freq[c].size() + 1, 0);
@@ -272,141 +238,154 @@ static bool build_tables(const Histogram &h, Tables &t) {
   return true;
 }
 
-static uint64_t metadata_bytes(const Problem &P, int total_symbols) {
-  return kHeaderBytes + align16(4 * kContexts + 2 * (uint64_t)total_symbols) + align16(4 * (uint64_t)P.R) +
-         align16(4 * (uint64_t)(P.tiles + 1));
-}
-
 // ---------------------------------------------------------------------------
-// sampled storage estimate (bits per element) at lattice scale a
-// ---------------------------------------------------------------------------
-constexpr int64_t kSampleVecs = 65536;
-
-static double estimate_bpp(const Problem &P, double a) {
-  const int64_t S = std::min(P.n_vec, kSampleVecs);
-  const int nt = std::max(1, std::min(P.threads, 16));
-  std::vector<Histogram> part(nt);
-  std::atomic<bool> overflow{false};
-  std::vector<std::thread> pool;
-  for (int t = 0; t < nt; ++t)
-    pool.emplace_back([&, t]() {
-      int32_t v[8];
-      for (int64_t k = t * S / nt; k < (t + 1) * S / nt; ++k) {
-        int64_t vid = (int64_t)(((uint64_t)k * (uint64_t)P.n_vec) / (uint64_t)S);
-        int64_t r = vid / P.vpr;
-        if (!quantize(P, r, vid % P.vpr, row_scale(P.rms[r], a), v)) {
-          overflow = true;
-          return;
-        }
-        Coded cd = model(v);
-        for (int j = 0; j < 8; ++j) ++part[t].at(cd.ctx[j], cd.sym[j]);
-      }
-    });
-  for (auto &th : pool) th.join();
-  if (overflow) return INFINITY;
-  for (int t = 1; t < nt; ++t) part[0].add(part[t]);
-  Tables tb;
-  if (!build_tables(part[0], tb)) return INFINITY;
-  double info = 0.0;
-  for (int c = 0; c < kContexts; ++c)
-    for (int i = 0; i < tb.nsym[c]; ++i) {
-      uint64_t n = part[0].get(c, tb.smin[c] + i);
-      if (n) info += (double)n * ((double)kProbBits - std::log2((double)tb.freq[c][i]));
-    }
-  double bits = info * ((double)P.n_vec / (double)S) + kStateBits * (double)(kStatesPerTile * P.tiles) +
-                8.0 * (double)metadata_bytes(P, tb.total_symbols());
-  return bits / ((double)P.R * (double)P.C);
-}
-
-// the same estimate from the exact tables of the whole matrix (every vector
-// quantized and histogrammed; no entropy coding)
-static double estimate_bpp_full(const Problem &P, double a) {
-  const int nt = std::max(1, P.threads);
-  std::vector<Histogram> part(nt);
-  std::atomic<bool> overflow{false};
-  std::atomic<int64_t> next{0};
-  auto worker = [&](int t) {
-    int32_t v[8];
-    for (;;) {
-      int64_t r0 = next.fetch_add(16);
-      if (r0 >= P.R || overflow) break;
-      for (int64_t r = r0; r < std::min(P.R, r0 + 16); ++r) {
-        const float g = row_scale(P.rms[(size_t)r], a);
-        for (int64_t k = 0; k < P.vpr; ++k) {
-          if (!quantize(P, r, k, g, v)) {
-            overflow = true;
-            return;
-          }
-          Coded cd = model(v);
-          for (int j = 0; j < 8; ++j) ++part[t].at(cd.ctx[j], cd.sym[j]);
-        }
-      }
-    }
-  };
-  std::vector<std::thread> pool;
-  for (int t = 1; t < nt; ++t) pool.emplace_back(worker, t);
-  worker(0);
-  for (auto &th : pool) th.join();
-  if (overflow) return INFINITY;
-  for (int t = 1; t < nt; ++t) part[0].add(part[t]);
-  Tables tb;
-  if (!build_tables(part[0], tb)) return INFINITY;
-  double info = 0.0;
-  for (int c = 0; c < kContexts; ++c)
-    for (int i = 0; i < tb.nsym[c]; ++i) {
-      uint64_t n = part[0].get(c, tb.smin[c] + i);
-      if (n) info += (double)n * ((double)kProbBits - std::log2((double)tb.freq[c][i]));
-    }
-  double bits = info + kStateBits * (double)(kStatesPerTile * P.tiles) + 8.0 * (double)metadata_bytes(P, tb.total_symbols());
-  return bits / ((double)P.R * (double)P.C);
-}
-
-// bisection on log2(a); returns the probed a whose estimate is closest to the target
-static double choose_scale(const Problem &P, double target, double *closest) {
-  const double la0 = 0.5 * std::log2(17.079468445347132) - target;  // high-rate guess sqrt(2 pi e) 2^-target
-  double lo = la0 - 1.0, hi = la0 + 1.0;
-  double best_la = la0, best_gap = INFINITY, best_e = INFINITY;
-  auto probe = [&](double la) {
-    double e = estimate_bpp(P, std::exp2(la));
-    double gap = std::fabs(e - target);
-    if (gap < best_gap) {
-      best_gap = gap;
-      best_la = la;
-      best_e = e;
-    }
-    return e;
-  };
-  double e_lo = probe(lo);
-  for (int k = 0; k < 30 && e_lo < target; ++k) e_lo = probe(lo -= 2.0);
-  double e_hi = probe(hi);
-  for (int k = 0; k < 30 && e_hi > target; ++k) e_hi = probe(hi += 2.0);
-  for (int it = 0; it < 40; ++it) {
-    double mid = 0.5 * (lo + hi);
-    double e = probe(mid);
-    if (std::fabs(e - target) <= 5e-4 * target) break;
-    (e > target ? lo : hi) = mid;
-  }
-  *closest = best_e;
-  return std::exp2(best_la);
-}
-
-// ---------------------------------------------------------------------------
-// one tile: interleaved rANS in reverse order, then the count bytes and each
-// state's words in the order the decoder consumes them
+// the passes over the matrix on host threads
 // ---------------------------------------------------------------------------
 struct TileOut {
   uint32_t states[kStatesPerTile];
   std::vector<uint16_t> words;
 };
 
-static void encode_tile(const Problem &P, const Tables &tb, const std::vector<int32_t> &V, int64_t tile, TileOut &out) {
+class HostBackend final : public EncodeBackend {
+ public:
+  HostBackend(const void *src, const EncodeShape &S, int threads) : src_(src), S_(S), threads_(threads) {}
+
+  int row_rms(std::vector<double> &rms, std::string &err) override {
+    rms.assign((size_t)S_.R, 0.0);
+    std::atomic<bool> bad{false};
+    parallel_for(S_.R, threads_, [&](int64_t b, int64_t e) {
+      for (int64_t r = b; r < e; ++r) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < S_.C; ++c) {
+          double x = widen(src_, S_.dtype, r * S_.C + c);
+          if (!std::isfinite(x)) bad = true;
+          acc += x * x;
+        }
+        rms[(size_t)r] = std::sqrt(acc / (double)S_.C);
+      }
+    });
+    if (!bad) return 0;
+    err = "input holds NaN or Inf";
+    return EP_ERR_NONFINITE;
+  }
+
+  int histogram(const std::vector<float> &g, int64_t S, std::vector<uint64_t> &hist, std::string &) override {
+    if (S >= S_.n_vec) return full_pass(g, hist);
+    const int nt = std::max(1, std::min(threads_, 16));
+    std::vector<std::vector<uint64_t>> part(nt, std::vector<uint64_t>((size_t)kContexts * kSymSpan, 0));
+    std::atomic<bool> overflow{false};
+    std::vector<std::thread> pool;
+    for (int t = 0; t < nt; ++t)
+      pool.emplace_back([&, t]() {
+        int32_t v[8];
+        for (int64_t k = t * S / nt; k < (t + 1) * S / nt; ++k) {
+          int64_t vid = (int64_t)(((uint64_t)k * (uint64_t)S_.n_vec) / (uint64_t)S);
+          int64_t r = vid / S_.vpr;
+          if (!quantize(src_, S_.dtype, S_.C, r, vid % S_.vpr, g[(size_t)r], v)) {
+            overflow = true;
+            return;
+          }
+          Coded cd = model(v);
+          for (int j = 0; j < 8; ++j) ++part[t][(size_t)cd.ctx[j] * kSymSpan + cd.sym[j] + kSymBias];
+        }
+      });
+    for (auto &th : pool) th.join();
+    if (overflow) return 1;
+    hist = std::move(part[0]);
+    for (int t = 1; t < nt; ++t)
+      for (size_t i = 0; i < hist.size(); ++i) hist[i] += part[t][i];
+    return 0;
+  }
+
+  int encode_tiles(const std::vector<float> &g, const Tables &tb, std::vector<uint32_t> &states,
+                   std::vector<uint32_t> &tile_first, std::vector<uint16_t> &words, std::string &err) override {
+    if (V_.empty() || Vg_ != g) {  // the lattice vectors of the last full pass, if it was at these scales
+      std::vector<uint64_t> ignored;
+      if (full_pass(g, ignored) != 0) {
+        err = "a lattice coordinate left the stream's value range";
+        return EP_ERR_ARG;
+      }
+    }
+    std::vector<TileOut> tiles((size_t)S_.tiles);
+    parallel_for(S_.tiles, std::max(1, threads_), [&](int64_t b, int64_t e) {
+      for (int64_t t = b; t < e; ++t) encode_tile(tb, t, tiles[(size_t)t]);
+    });
+    uint64_t n_words = 0;
+    for (auto &t : tiles) n_words += t.words.size();
+    if (n_words > 0xffffffffull) {
+      err = "stream too large for 32-bit tile offsets";
+      return EP_ERR_SHAPE;
+    }
+    states.resize((size_t)S_.tiles * kStatesPerTile);
+    tile_first.resize((size_t)S_.tiles + 1);
+    words.resize((size_t)n_words);
+    uint64_t w = 0;
+    for (int64_t t = 0; t < S_.tiles; ++t) {
+      std::memcpy(&states[(size_t)t * kStatesPerTile], tiles[(size_t)t].states, 4 * kStatesPerTile);
+      tile_first[(size_t)t] = (uint32_t)w;
+      std::memcpy(&words[(size_t)w], tiles[(size_t)t].words.data(), 2 * tiles[(size_t)t].words.size());
+      w += tiles[(size_t)t].words.size();
+    }
+    tile_first[(size_t)S_.tiles] = (uint32_t)w;
+    return 0;
+  }
+
+  int copy_input(uint8_t *dst, std::string &) override {
+    std::memcpy(dst, src_, (size_t)S_.R * (size_t)S_.C * elem_bytes(S_.dtype));
+    return 0;
+  }
+
+ private:
+  // every vector quantized at row scales g (kept for encode_tiles) and
+  // counted; 1 if a coordinate leaves the value range
+  int full_pass(const std::vector<float> &g, std::vector<uint64_t> &hist) {
+    V_.assign((size_t)(S_.R * S_.C8), 0);
+    Vg_.clear();
+    const int nt = std::max(1, threads_);
+    std::vector<std::vector<uint64_t>> part(nt, std::vector<uint64_t>((size_t)kContexts * kSymSpan, 0));
+    std::atomic<bool> overflow{false};
+    std::atomic<int64_t> next{0};
+    auto worker = [&](int t) {
+      for (;;) {
+        int64_t r0 = next.fetch_add(16);
+        if (r0 >= S_.R || overflow) break;
+        for (int64_t r = r0; r < std::min(S_.R, r0 + 16); ++r)
+          for (int64_t k = 0; k < S_.vpr; ++k) {
+            int32_t *v = &V_[(size_t)(r * S_.C8 + 8 * k)];
+            if (!quantize(src_, S_.dtype, S_.C, r, k, g[(size_t)r], v)) {
+              overflow = true;
+              return;
+            }
+            Coded cd = model(v);
+            for (int j = 0; j < 8; ++j) ++part[t][(size_t)cd.ctx[j] * kSymSpan + cd.sym[j] + kSymBias];
+          }
+      }
+    };
+    std::vector<std::thread> pool;
+    for (int t = 1; t < nt; ++t) pool.emplace_back(worker, t);
+    worker(0);
+    for (auto &th : pool) th.join();
+    if (overflow) {
+      V_.clear();
+      return 1;
+    }
+    Vg_ = g;
+    hist = std::move(part[0]);
+    for (int t = 1; t < nt; ++t)
+      for (size_t i = 0; i < hist.size(); ++i) hist[i] += part[t][i];
+    return 0;
+  }
+
+  // one tile: interleaved rANS in reverse order, then the count bytes and
+  // each state's words in the order the decoder consumes them
+  void encode_tile(const Tables &tb, int64_t tile, TileOut &out) const {
   const int64_t first = tile * kTileVecs;
-  const int n = (int)std::min<int64_t>(kTileVecs, P.n_vec - first);
+  const int n = (int)std::min<int64_t>(kTileVecs, S_.n_vec - first);
   // (frequency, cumulative) of every coordinate, vector-major
   std::vector<uint32_t> fc((size_t)n * 8 * 2);
   for (int i = 0; i < n; ++i) {
     int64_t vid = first + i;
-    const int32_t *v = &V[(size_t)((vid / P.vpr) * P.C8 + 8 * (vid % P.vpr))];
+    const int32_t *v = &V_[(size_t)((vid / S_.vpr) * S_.C8 + 8 * (vid % S_.vpr))];
     Coded cd = model(v);
     for (int j = 0; j < 8; ++j) {
       int c = cd.ctx[j], s = cd.sym[j] - tb.smin[c];
@@ -446,63 +425,113 @@ static void encode_tile(const Problem &P, const Tables &tb, const std::vector<in
   for (int q = 0; q < kStatesPerTile; ++q) out.words.insert(out.words.end(), lane[q].begin(), lane[q].end());
 }
 
+
+  const void *src_;
+  EncodeShape S_;
+  int threads_;
+  std::vector<int32_t> V_;  // lattice vectors of the last full pass, rows of C8 coordinates
+  std::vector<float> Vg_;   // the row scales they were quantized at
+};
+
 // ---------------------------------------------------------------------------
-// full stream at a fixed resolution
+// the encoder's control flow, on any backend
 // ---------------------------------------------------------------------------
-static int encode_at(const Problem &P, double a, double target, std::vector<uint8_t> &blob, std::string &err) {
-  std::vector<float> g((size_t)P.R);
-  for (int64_t r = 0; r < P.R; ++r) g[(size_t)r] = row_scale(P.rms[(size_t)r], a);
-  std::vector<int32_t> V((size_t)(P.R * P.C8));
-  std::atomic<bool> overflow{false};
-  const int nt = std::max(1, P.threads);
-  std::vector<Histogram> part(nt);
-  // quantize rows and histogram the symbols
-  {
-    std::atomic<int64_t> next{0};
-    auto worker = [&](int t) {
-      for (;;) {
-        int64_t r0 = next.fetch_add(16);
-        if (r0 >= P.R || overflow) break;
-        for (int64_t r = r0; r < std::min(P.R, r0 + 16); ++r)
-          for (int64_t k = 0; k < P.vpr; ++k) {
-            int32_t *v = &V[(size_t)(r * P.C8 + 8 * k)];
-            if (!quantize(P, r, k, g[(size_t)r], v)) {
-              overflow = true;
-              return;
-            }
-            Coded cd = model(v);
-            for (int j = 0; j < 8; ++j) ++part[t].at(cd.ctx[j], cd.sym[j]);
-          }
-      }
-    };
-    std::vector<std::thread> pool;
-    for (int t = 1; t < nt; ++t) pool.emplace_back(worker, t);
-    worker(0);
-    for (auto &th : pool) th.join();
-  }
-  if (overflow) return EP_WARN_RAW;
-  for (int t = 1; t < nt; ++t) part[0].add(part[t]);
+namespace {
+
+struct Problem {
+  EncodeShape S;
+  EncodeBackend *be;
+  std::vector<double> rms;
+};
+
+uint64_t metadata_bytes(const EncodeShape &S, int total_symbols) {
+  return kHeaderBytes + align16(4 * kContexts + 2 * (uint64_t)total_symbols) + align16(4 * (uint64_t)S.R) +
+         align16(4 * (uint64_t)(S.tiles + 1));
+}
+
+std::vector<float> row_scales(const Problem &P, double a) {
+  std::vector<float> g((size_t)P.S.R);
+  for (int64_t r = 0; r < P.S.R; ++r) g[(size_t)r] = row_scale(P.rms[(size_t)r], a);
+  return g;
+}
+
+// storage estimate (bits per element) at lattice scale a from the tables of
+// S vectors (S >= n_vec: the whole matrix, no entropy coding); infinite if a
+// coordinate leaves the value range
+double estimate_bpp(const Problem &P, double a, int64_t S, std::string &err, int &status) {
+  std::vector<uint64_t> hist;
+  const int rc = P.be->histogram(row_scales(P, a), S, hist, err);
+  if (rc < 0) status = rc;
+  if (rc != 0) return INFINITY;
   Tables tb;
-  if (!build_tables(part[0], tb)) {
+  if (!build_tables(hist, tb)) return INFINITY;
+  double info = 0.0;
+  for (int c = 0; c < kContexts; ++c)
+    for (int i = 0; i < tb.nsym[c]; ++i) {
+      uint64_t n = hist[(size_t)c * kSymSpan + (tb.smin[c] + i) + kSymBias];
+      if (n) info += (double)n * ((double)kProbBits - std::log2((double)tb.freq[c][i]));
+    }
+  const double scale = S >= P.S.n_vec ? 1.0 : (double)P.S.n_vec / (double)S;
+  double bits = info * scale + kStateBits * (double)(kStatesPerTile * P.S.tiles) +
+                8.0 * (double)metadata_bytes(P.S, tb.total_symbols());
+  return bits / ((double)P.S.R * (double)P.S.C);
+}
+
+// bisection on log2(a) over sampled estimates; returns the probed a whose
+// estimate is closest to the target
+double choose_scale(const Problem &P, double target, double *closest, std::string &err, int &status) {
+  const int64_t S = std::min(P.S.n_vec, kSampleVecs);
+  const double la0 = 0.5 * std::log2(17.079468445347132) - target;  // high-rate guess sqrt(2 pi e) 2^-target
+  double lo = la0 - 1.0, hi = la0 + 1.0;
+  double best_la = la0, best_gap = INFINITY, best_e = INFINITY;
+  auto probe = [&](double la) {
+    double e = estimate_bpp(P, std::exp2(la), S, err, status);
+    double gap = std::fabs(e - target);
+    if (gap < best_gap) {
+      best_gap = gap;
+      best_la = la;
+      best_e = e;
+    }
+    return e;
+  };
+  double e_lo = probe(lo);
+  for (int k = 0; k < 30 && e_lo < target && status == 0; ++k) e_lo = probe(lo -= 2.0);
+  double e_hi = probe(hi);
+  for (int k = 0; k < 30 && e_hi > target && status == 0; ++k) e_hi = probe(hi += 2.0);
+  for (int it = 0; it < 40 && status == 0; ++it) {
+    double mid = 0.5 * (lo + hi);
+    double e = probe(mid);
+    if (std::fabs(e - target) <= 5e-4 * target) break;
+    (e > target ? lo : hi) = mid;
+  }
+  *closest = best_e;
+  return std::exp2(best_la);
+}
+
+// the full stream at resolution a
+int encode_at(const Problem &P, double a, double target, std::vector<uint8_t> &blob, std::string &err) {
+  const EncodeShape &S = P.S;
+  const std::vector<float> g = row_scales(P, a);
+  std::vector<uint64_t> hist;
+  int rc = P.be->histogram(g, S.n_vec, hist, err);
+  if (rc < 0) return rc;
+  if (rc == 1) return EP_WARN_RAW;
+  Tables tb;
+  if (!build_tables(hist, tb)) {
     err = "frequency normalization failed";
     return EP_ERR_TARGET;
   }
-  std::vector<TileOut> tiles((size_t)P.tiles);
-  parallel_for(P.tiles, nt, [&](int64_t b, int64_t e) {
-    for (int64_t t = b; t < e; ++t) encode_tile(P, tb, V, t, tiles[(size_t)t]);
-  });
-  uint64_t n_words = 0;
-  for (auto &t : tiles) n_words += t.words.size();
-  if (n_words > 0xffffffffull) {
-    err = "stream too large for 32-bit tile offsets";
-    return EP_ERR_SHAPE;
-  }
+  std::vector<uint32_t> states, tile_first;
+  std::vector<uint16_t> words;
+  rc = P.be->encode_tiles(g, tb, states, tile_first, words, err);
+  if (rc < 0) return rc;
+  const uint64_t n_words = words.size();
   const int nsum = tb.total_symbols();
   const uint64_t o_tab = kHeaderBytes;
   const uint64_t o_sc = o_tab + align16(4 * kContexts + 2 * (uint64_t)nsum);
-  const uint64_t o_st = o_sc + align16(4 * (uint64_t)P.R);
-  const uint64_t o_to = o_st + align16(4 * (uint64_t)P.tiles * kStatesPerTile);
-  const uint64_t o_w = o_to + align16(4 * (uint64_t)(P.tiles + 1));
+  const uint64_t o_st = o_sc + align16(4 * (uint64_t)S.R);
+  const uint64_t o_to = o_st + align16(4 * (uint64_t)S.tiles * kStatesPerTile);
+  const uint64_t o_w = o_to + align16(4 * (uint64_t)(S.tiles + 1));
   const uint64_t total = o_w + align16(2 * n_words);
   blob.assign(total, 0);
   uint8_t *b = blob.data();
@@ -510,15 +539,15 @@ static int encode_at(const Problem &P, double a, double target, std::vector<uint
   wr<uint16_t>(b + hdr::version, kVersion);
   wr<uint16_t>(b + hdr::header_bytes, (uint16_t)kHeaderBytes);
   b[hdr::method] = kLattice;
-  b[hdr::dtype] = (uint8_t)P.dtype;
+  b[hdr::dtype] = (uint8_t)S.dtype;
   b[hdr::prob_bits] = kProbBits;
   b[hdr::contexts] = kContexts;
   wr<uint32_t>(b + hdr::tile_vecs, kTileVecs);
   wr<uint32_t>(b + hdr::states, kStatesPerTile);
-  wr<uint32_t>(b + hdr::tiles, (uint32_t)P.tiles);
-  wr<uint64_t>(b + hdr::rows, (uint64_t)P.R);
-  wr<uint64_t>(b + hdr::cols, (uint64_t)P.C);
-  wr<uint64_t>(b + hdr::cols8, (uint64_t)P.C8);
+  wr<uint32_t>(b + hdr::tiles, (uint32_t)S.tiles);
+  wr<uint64_t>(b + hdr::rows, (uint64_t)S.R);
+  wr<uint64_t>(b + hdr::cols, (uint64_t)S.C);
+  wr<uint64_t>(b + hdr::cols8, (uint64_t)S.C8);
   wr<double>(b + hdr::scale_a, a);
   wr<double>(b + hdr::target, target);
   wr<uint64_t>(b + hdr::off_tables, o_tab);
@@ -537,83 +566,67 @@ static int encode_at(const Problem &P, double a, double target, std::vector<uint
       p += 2;
     }
   }
-  std::memcpy(b + o_sc, g.data(), 4 * (size_t)P.R);
-  uint64_t w = 0;
-  for (int64_t t = 0; t < P.tiles; ++t) {
-    std::memcpy(b + o_st + 4 * (uint64_t)t * kStatesPerTile, tiles[(size_t)t].states, 4 * kStatesPerTile);
-    wr<uint32_t>(b + o_to + 4 * (uint64_t)t, (uint32_t)w);
-    std::memcpy(b + o_w + 2 * w, tiles[(size_t)t].words.data(), 2 * tiles[(size_t)t].words.size());
-    w += tiles[(size_t)t].words.size();
-  }
-  wr<uint32_t>(b + o_to + 4 * (uint64_t)P.tiles, (uint32_t)w);
+  std::memcpy(b + o_sc, g.data(), 4 * (size_t)S.R);
+  std::memcpy(b + o_st, states.data(), 4 * states.size());
+  std::memcpy(b + o_to, tile_first.data(), 4 * tile_first.size());
+  std::memcpy(b + o_w, words.data(), 2 * n_words);
   return EP_OK;
 }
 
-static void raw_stream(const Problem &P, double target, std::vector<uint8_t> &blob) {
-  const uint64_t payload = (uint64_t)P.R * (uint64_t)P.C * elem_bytes(P.dtype);
+int raw_stream(const Problem &P, double target, std::vector<uint8_t> &blob, std::string &err) {
+  const EncodeShape &S = P.S;
+  const uint64_t payload = (uint64_t)S.R * (uint64_t)S.C * elem_bytes(S.dtype);
   blob.assign(kHeaderBytes + align16(payload), 0);
   uint8_t *b = blob.data();
   wr<uint32_t>(b + hdr::magic, kMagic);
   wr<uint16_t>(b + hdr::version, kVersion);
   wr<uint16_t>(b + hdr::header_bytes, (uint16_t)kHeaderBytes);
   b[hdr::method] = kRaw;
-  b[hdr::dtype] = (uint8_t)P.dtype;
-  wr<uint64_t>(b + hdr::rows, (uint64_t)P.R);
-  wr<uint64_t>(b + hdr::cols, (uint64_t)P.C);
-  wr<uint64_t>(b + hdr::cols8, (uint64_t)P.C);
+  b[hdr::dtype] = (uint8_t)S.dtype;
+  wr<uint64_t>(b + hdr::rows, (uint64_t)S.R);
+  wr<uint64_t>(b + hdr::cols, (uint64_t)S.C);
+  wr<uint64_t>(b + hdr::cols8, (uint64_t)S.C);
   wr<double>(b + hdr::target, target);
   wr<uint64_t>(b + hdr::off_words, kHeaderBytes);
   wr<uint64_t>(b + hdr::total, (uint64_t)blob.size());
-  std::memcpy(b + kHeaderBytes, P.src, payload);
+  return P.be->copy_input(b + kHeaderBytes, err);
 }
 
-int compress(const void *src, int dtype, int64_t rows, int64_t cols, double target, double fixed_a, int threads,
-             std::vector<uint8_t> &blob, std::string &err) {
+}  // namespace
+
+bool make_shape(int dtype, int64_t rows, int64_t cols, EncodeShape &S, int &status, std::string &err) {
   if (dtype < 0 || dtype > 3) {
     err = "unknown container dtype";
-    return EP_ERR_ARG;
+    status = EP_ERR_ARG;
+    return false;
   }
   if (rows <= 0 || cols <= 0) {
     err = "input must be a non-empty 2-D matrix";
-    return EP_ERR_SHAPE;
+    status = EP_ERR_SHAPE;
+    return false;
   }
-  if (!src) {
-    err = "null input";
-    return EP_ERR_ARG;
-  }
-  Problem P;
-  P.src = src;
-  P.dtype = dtype;
-  P.R = rows;
-  P.C = cols;
-  P.C8 = (cols + 7) / 8 * 8;
-  P.vpr = P.C8 / 8;
-  P.n_vec = rows * P.vpr;
-  if (P.n_vec >= (int64_t(1) << 31)) {
+  S.dtype = dtype;
+  S.R = rows;
+  S.C = cols;
+  S.C8 = (cols + 7) / 8 * 8;
+  S.vpr = S.C8 / 8;
+  S.n_vec = rows * S.vpr;
+  if (S.n_vec >= (int64_t(1) << 31)) {
     err = "matrix too large for one stream";
-    return EP_ERR_SHAPE;
+    status = EP_ERR_SHAPE;
+    return false;
   }
-  P.tiles = (P.n_vec + kTileVecs - 1) / kTileVecs;
-  P.threads = threads > 0 ? threads : std::max(1u, std::thread::hardware_concurrency());
+  S.tiles = (S.n_vec + kTileVecs - 1) / kTileVecs;
+  return true;
+}
+
+int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, double fixed_a,
+                  std::vector<uint8_t> &blob, std::string &err) {
+  Problem P{shape, &be, {}};
+  const EncodeShape &S = P.S;
   // finiteness and row RMS (sequential sum per row)
-  P.rms.assign((size_t)rows, 0.0);
-  std::atomic<bool> bad{false};
-  parallel_for(rows, P.threads, [&](int64_t b, int64_t e) {
-    for (int64_t r = b; r < e; ++r) {
-      double acc = 0.0;
-      for (int64_t c = 0; c < cols; ++c) {
-        double x = widen(src, dtype, r * cols + c);
-        if (!std::isfinite(x)) bad = true;
-        acc += x * x;
-      }
-      P.rms[(size_t)r] = std::sqrt(acc / (double)cols);
-    }
-  });
-  if (bad) {
-    err = "input holds NaN or Inf";
-    return EP_ERR_NONFINITE;
-  }
-  const bool eight_bit = elem_bytes(dtype) == 1;
+  if (const int rc = be.row_rms(P.rms, err); rc != 0) return rc;
+  const bool eight_bit = elem_bytes(S.dtype) == 1;
   if (!std::isfinite(target) || target < 0.001 || (!eight_bit && target > 11.0) || (eight_bit && target >= 8.0)) {
     err = "target_bpp outside the supported range for this container";
     return EP_ERR_TARGET;
@@ -621,16 +634,19 @@ int compress(const void *src, int dtype, int64_t rows, int64_t cols, double targ
   double a = fixed_a;
   if (!(fixed_a > 0.0)) {
     const double floor_bpp =
-        (kStateBits * (double)(kStatesPerTile * P.tiles) + 8.0 * (double)metadata_bytes(P, kContexts)) /
-        ((double)P.R * (double)P.C);
+        (kStateBits * (double)(kStatesPerTile * S.tiles) + 8.0 * (double)metadata_bytes(S, kContexts)) /
+        ((double)S.R * (double)S.C);
     if (target < 1.02 * floor_bpp) {
       err = "target_bpp below this stream's fixed per-tile overhead (" + std::to_string(floor_bpp) + " bpp)";
       return EP_ERR_TARGET;
     }
+    int status = 0;
     double closest;
-    a = choose_scale(P, target, &closest);
+    a = choose_scale(P, target, &closest, err, status);
+    if (status < 0) return status;
     if (!(std::fabs(closest - target) <= 0.02 * target)) {
-      raw_stream(P, target, blob);
+      const int rc = raw_stream(P, target, blob, err);
+      if (rc < 0) return rc;
       err = "no lattice resolution reaches the target; stored the raw container";
       return EP_WARN_RAW;
     }
@@ -638,20 +654,37 @@ int compress(const void *src, int dtype, int64_t rows, int64_t cols, double targ
     // frequency of at least 1.  One histogram of the whole matrix at the chosen
     // scale (no entropy coding) measures that bias; beyond 0.5% the sampled
     // bisection runs again toward the target minus the bias.
-    const double full = estimate_bpp_full(P, a);
+    const double full = estimate_bpp(P, a, S.n_vec, err, status);
+    if (status < 0) return status;
     if (std::isfinite(full) && !(std::fabs(full - target) <= 0.005 * target)) {
       double ignored;
-      a = choose_scale(P, target - (full - closest), &ignored);
+      a = choose_scale(P, target - (full - closest), &ignored, err, status);
+      if (status < 0) return status;
     }
   }
   int rc = encode_at(P, a, target, blob, err);
-  const uint64_t raw_total = kHeaderBytes + align16((uint64_t)P.R * (uint64_t)P.C * elem_bytes(dtype));
+  if (rc < 0) return rc;
+  const uint64_t raw_total = kHeaderBytes + align16((uint64_t)S.R * (uint64_t)S.C * elem_bytes(S.dtype));
   if (rc == EP_OK && !(fixed_a > 0.0) && blob.size() >= raw_total) rc = EP_WARN_RAW;
   if (rc == EP_WARN_RAW) {
-    raw_stream(P, target, blob);
+    const int rr = raw_stream(P, target, blob, err);
+    if (rr < 0) return rr;
     err = "lattice coding failed (values out of range or no gain); stored the raw container";
   }
   return rc;
+}
+
+int compress(const void *src, int dtype, int64_t rows, int64_t cols, double target, double fixed_a, int threads,
+             std::vector<uint8_t> &blob, std::string &err) {
+  EncodeShape S;
+  int status = 0;
+  if (!make_shape(dtype, rows, cols, S, status, err)) return status;
+  if (!src) {
+    err = "null input";
+    return EP_ERR_ARG;
+  }
+  HostBackend be(src, S, threads > 0 ? threads : (int)std::max(1u, std::thread::hardware_concurrency()));
+  return compress_with(be, S, target, fixed_a, blob, err);
 }
 
 }  // namespace ep
