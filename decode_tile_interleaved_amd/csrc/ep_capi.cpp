@@ -15,10 +15,11 @@ static thread_local std::string g_error;
 void set_error(const std::string &msg) { g_error = msg; }
 }  // namespace ep
 
-extern "C" {
+namespace {
 
-int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
-                   const struct ep_options *opt, uint8_t **blob_out, size_t *nbytes_out) {
+// option checks, the call, and the copy of the stream into malloc'ed memory
+template <class F>
+int compress_entry(const struct ep_options *opt, uint8_t **blob_out, size_t *nbytes_out, F &&run) {
   ep::set_error("");
   if (!blob_out || !nbytes_out) {
     ep::set_error("null output pointer");
@@ -43,7 +44,7 @@ int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, 
   std::string err;
   int rc;
   try {
-    rc = ep::compress(host_src, dtype, rows, cols, target_bpp, fixed_a, threads, blob, err);
+    rc = run(fixed_a, threads, blob, err);
   } catch (const std::bad_alloc &) {
     ep::set_error("host allocation failed");
     return EP_ERR_NOMEM;
@@ -62,6 +63,26 @@ int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, 
   *nbytes_out = blob.size();
   if (rc > 0) ep::set_error(err);
   return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
+                   const struct ep_options *opt, uint8_t **blob_out, size_t *nbytes_out) {
+  return compress_entry(opt, blob_out, nbytes_out, [&](double fixed_a, int threads, std::vector<uint8_t> &blob,
+                                                        std::string &err) {
+    return ep::compress(host_src, dtype, rows, cols, target_bpp, fixed_a, threads, blob, err);
+  });
+}
+
+int ep_compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
+                       const struct ep_options *opt, void *hip_stream, uint8_t **blob_out, size_t *nbytes_out) {
+  return compress_entry(opt, blob_out, nbytes_out, [&](double fixed_a, int, std::vector<uint8_t> &blob,
+                                                        std::string &err) {
+    return ep::compress_device(dev_src, dtype, rows, cols, target_bpp, fixed_a, hip_stream, blob, err);
+  });
 }
 
 int ep_compress(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp, uint8_t **blob_out,

@@ -1,0 +1,470 @@
+// ep_encode_gpu.hip -- the encoder's passes over the matrix on the GPU
+// (gfx950): row sums of squares, (context, symbol) histograms for the rate
+// estimates and the tables, and the interleaved rANS tiles.
+//
+// The EntroPack abstract (mlsanity index page) calls the encoder fast and
+// its rate selection sampled: resolution selection reads sampled storage
+// estimates instead of encoding the stream again and again.  The control
+// flow (selection, tables, stream assembly) stays on the host
+// (ep_encode.cpp); here only the passes that touch every element run, each
+// computing exactly what the host threads compute, in the same f64/f32 steps:
+//   * row sums of squares: one thread per row, columns in order;
+//   * E8 nearest point per 8-vector (the same D8 / D8 + 1/2 rounding, parity
+//     fix and tie rule), then the 7-context model; counts in LDS, added to a
+//     global histogram;
+//   * one wave per tile, lane q = rANS state q, walking its 16 vectors and 8
+//     coordinates backwards; each lane writes its words into a slot of its
+//     own, and a second kernel lays them out in the order the decoder
+//     consumes them, behind the count bytes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ep.h"
+#include "ep_encode.hpp"
+#include "ep_stream.hpp"
+
+namespace ep {
+namespace {
+
+// ---------------------------------------------------------------------------
+// device side
+// ---------------------------------------------------------------------------
+// element i of a container matrix, widened exactly to f64
+__device__ __forceinline__ double widen_d(const void *src, int dtype, int64_t i) {
+  switch (dtype) {
+    case EP_BF16:
+      return (double)__uint_as_float((uint32_t)((const uint16_t *)src)[i] << 16);
+    case EP_FP16: {
+      const uint32_t h = ((const uint16_t *)src)[i];
+      const int e = (int)((h >> 10) & 31u), m = (int)(h & 1023u);
+      const double mag = e == 0 ? ldexp((double)m, -24) : e == 31 ? (m ? NAN : INFINITY) : ldexp(1024.0 + m, e - 25);
+      return (h & 0x8000u) ? -mag : mag;
+    }
+    case EP_FP8_E4M3FN: {
+      const uint32_t c = ((const uint8_t *)src)[i];
+      const int e = (int)((c >> 3) & 15u), m = (int)(c & 7u);
+      const double mag = (e == 15 && m == 7) ? NAN : e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+      return (c & 0x80u) ? -mag : mag;
+    }
+    default:
+      return (double)((const int8_t *)src)[i];
+  }
+}
+
+struct Shape {
+  const void *src;
+  int dtype;
+  int64_t R, C, C8, vpr, n_vec, tiles;
+};
+
+// one thread per row: sum of squares in column order, and whether every
+// element is finite
+__global__ void row_sums_kernel(Shape S, double *sums, uint32_t *nonfinite) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= S.R) return;
+  double acc = 0.0;
+  bool bad = false;
+  for (int64_t c = 0; c < S.C; ++c) {
+    const double x = widen_d(S.src, S.dtype, r * S.C + c);
+    bad |= !isfinite(x);
+    acc += x * x;
+  }
+  sums[r] = acc;
+  if (bad) atomicOr(nonfinite, 1u);
+}
+
+// Conway & Sloane's nearest point of D8 (rint, then the coordinate with the
+// largest rounding error moves if the sum is odd)
+__device__ __forceinline__ void d8_round_d(const double *u, double *p) {
+  double total = 0.0;
+  for (int i = 0; i < 8; ++i) {
+    p[i] = rint(u[i]);
+    total += p[i];
+  }
+  if (fmod(total, 2.0) != 0.0) {
+    int worst = 0;
+    double err = -1.0;
+    for (int i = 0; i < 8; ++i) {
+      const double e = fabs(u[i] - p[i]);
+      if (e > err) {
+        err = e;
+        worst = i;
+      }
+    }
+    p[worst] += (u[worst] < p[worst]) ? -1.0 : 1.0;
+  }
+}
+
+// v = 2y, y the E8 point nearest u (D8 or D8 + 1/2; exact ties go to D8);
+// false if a coordinate leaves [-2048, 2047]
+__device__ __forceinline__ bool quantize_d(const Shape &S, int64_t vid, float g, int32_t *v) {
+  const int64_t r = vid / S.vpr, k = vid - r * S.vpr;
+  if (g == 0.0f) {
+    for (int j = 0; j < 8; ++j) v[j] = 0;
+    return true;
+  }
+  double u[8];
+  const double two_g = 2.0 * (double)g;
+  for (int j = 0; j < 8; ++j) {
+    const int64_t c = 8 * k + j;
+    const double x = c < S.C ? widen_d(S.src, S.dtype, r * S.C + c) : 0.0;
+    u[j] = x / two_g;
+  }
+  double a[8], b[8], sh[8];
+  d8_round_d(u, a);
+  for (int i = 0; i < 8; ++i) sh[i] = u[i] - 0.5;
+  d8_round_d(sh, b);
+  double da = 0.0, db = 0.0;
+  for (int i = 0; i < 8; ++i) {
+    b[i] += 0.5;
+    const double ea = u[i] - a[i], eb = u[i] - b[i];
+    da += ea * ea;
+    db += eb * eb;
+  }
+  const bool use_b = db < da;
+  bool ok = true;
+  for (int i = 0; i < 8; ++i) {
+    v[i] = (int32_t)(2.0 * (use_b ? b[i] : a[i]));
+    ok &= v[i] >= kValueMin && v[i] <= kValueMax;
+  }
+  return ok;
+}
+
+// the 7-context model: context and symbol of each coordinate
+__device__ __forceinline__ void model_d(const int32_t *v, int32_t *ctx, int32_t *sym) {
+  const int32_t coset = v[0] & 1;
+  int32_t zsum = (v[0] - coset) / 2;
+  ctx[0] = 0;
+  sym[0] = v[0];
+  for (int j = 1; j < 7; ++j) {
+    const int32_t z = (v[j] - coset) / 2;
+    ctx[j] = 1 + coset;
+    sym[j] = z;
+    zsum += z;
+  }
+  const int32_t par = zsum & 1;
+  ctx[7] = 3 + 2 * coset + par;
+  sym[7] = ((v[7] - coset) / 2 - par) / 2;
+}
+
+// LDS histogram bins: context F over [-2048, 2047], C_b over [-1024, 1023],
+// E_{b,p} over [-512, 511] (the ranges the value range allows)
+constexpr int kBinsF = 4096, kBinsC = 2048, kBinsE = 1024;
+constexpr int kLdsBins = kBinsF + 2 * kBinsC + 4 * kBinsE;  // 12288 (48 KB)
+__device__ __forceinline__ int lds_bin(int c, int sym) {
+  return c == 0 ? sym + 2048 : c <= 2 ? kBinsF + (c - 1) * kBinsC + sym + 1024 : kBinsF + 2 * kBinsC + (c - 3) * kBinsE + sym + 512;
+}
+__device__ __forceinline__ void bin_symbol(int b, int &c, int &sym) {
+  if (b < kBinsF) {
+    c = 0;
+    sym = b - 2048;
+  } else if (b < kBinsF + 2 * kBinsC) {
+    c = 1 + (b - kBinsF) / kBinsC;
+    sym = (b - kBinsF) % kBinsC - 1024;
+  } else {
+    c = 3 + (b - kBinsF - 2 * kBinsC) / kBinsE;
+    sym = (b - kBinsF - 2 * kBinsC) % kBinsE - 512;
+  }
+}
+
+// counts of (context, symbol) over vectors floor(k * n_vec / S), k < S
+// (S >= n_vec: every vector); hist is kContexts x kSymSpan u64
+__global__ void __launch_bounds__(256) histogram_kernel(Shape S, const float *g, int64_t nsamp, uint64_t *hist,
+                                                        uint32_t *overflow) {
+  __shared__ uint32_t bins[kLdsBins];
+  for (int b = threadIdx.x; b < kLdsBins; b += blockDim.x) bins[b] = 0u;
+  __syncthreads();
+  const bool all = nsamp >= S.n_vec;
+  const int64_t n = all ? S.n_vec : nsamp;
+  bool bad = false;
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t vid = all ? k : (int64_t)(((uint64_t)k * (uint64_t)S.n_vec) / (uint64_t)nsamp);
+    int32_t v[8], ctx[8], sym[8];
+    if (!quantize_d(S, vid, g[vid / S.vpr], v)) {
+      bad = true;
+      continue;
+    }
+    model_d(v, ctx, sym);
+    for (int j = 0; j < 8; ++j) atomicAdd(&bins[lds_bin(ctx[j], sym[j])], 1u);
+  }
+  if (bad) atomicOr(overflow, 1u);
+  __syncthreads();
+  for (int b = threadIdx.x; b < kLdsBins; b += blockDim.x) {
+    const uint32_t cnt = bins[b];
+    if (cnt) {
+      int c, sym;
+      bin_symbol(b, c, sym);
+      atomicAdd((unsigned long long *)&hist[(size_t)c * kSymSpan + sym + kSymBias], (unsigned long long)cnt);
+    }
+  }
+}
+
+// Tables on the device: per context the symbol range and, per symbol,
+// frequency | cumulative << 16.
+struct DevTables {
+  int32_t smin[kContexts];
+  int32_t nsym[kContexts];
+  uint32_t base[kContexts];  // index of each context's first entry in fc
+};
+
+constexpr int kWordsPerState = 128;  // at most one word per symbol: 16 vectors x 8 coordinates
+
+// One wave per tile, lane q = state q: its vectors q, q + 64, ... quantized
+// again at the same scales, their symbols encoded backwards (vector 15 down
+// to 0, coordinate 7 down to 0).  Words go to the lane's slot in emission
+// order; the count and the final state are kept.
+__global__ void __launch_bounds__(64) encode_tiles_kernel(Shape S, const float *g, DevTables T, const uint32_t *fc,
+                                                          uint16_t *slots, uint8_t *counts, uint32_t *states,
+                                                          uint32_t *fault) {
+  const int64_t tile = blockIdx.x;
+  const int q = threadIdx.x;
+  const int64_t first = tile * kTileVecs;
+  const int n = (int)min((int64_t)kTileVecs, S.n_vec - first);
+  uint16_t *slot = slots + ((size_t)tile * kStatesPerTile + q) * kWordsPerState;
+  uint32_t x = kStateLow;
+  int emitted = 0;
+  bool bad = false;
+  for (int s = kTileVecs / kStatesPerTile - 1; s >= 0; --s) {
+    const int i = s * kStatesPerTile + q;
+    if (i >= n) continue;
+    const int64_t vid = first + i;
+    int32_t v[8], ctx[8], sym[8];
+    bad |= !quantize_d(S, vid, g[vid / S.vpr], v);
+    model_d(v, ctx, sym);
+    for (int j = 7; j >= 0; --j) {
+      const int c = ctx[j];
+      const int idx = sym[j] - T.smin[c];
+      if (idx < 0 || idx >= T.nsym[c]) {  // a symbol the tables do not hold: the passes disagree
+        bad = true;
+        continue;
+      }
+      const uint32_t e = fc[T.base[c] + (uint32_t)idx];
+      const uint32_t f = e & 0xffffu, cum = e >> 16;
+      if (f == 0u) {
+        bad = true;
+        continue;
+      }
+      if ((uint64_t)x >= ((uint64_t)f << (29 - kProbBits))) {
+        if (emitted < kWordsPerState) slot[emitted] = (uint16_t)x;
+        ++emitted;
+        x >>= 16;
+      }
+      x = (x / f) * kProbTotal + x % f + cum;
+    }
+  }
+  if (emitted > kWordsPerState) bad = true;
+  counts[tile * kStatesPerTile + q] = (uint8_t)min(emitted, kWordsPerState);
+  states[tile * kStatesPerTile + q] = x;
+  if (bad) atomicOr(fault, 1u);
+}
+
+// inclusive prefix sum over a wave
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, int lane) {
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// One wave per tile: the count words (state 2w in the low byte, 2w + 1 in
+// the high), then each state's words in the order the decoder consumes them
+// (the reverse of emission), at the tile's first word.
+__global__ void __launch_bounds__(64) lay_out_kernel(const uint16_t *slots, const uint8_t *counts,
+                                                     const uint32_t *tile_first, uint16_t *words) {
+  const int64_t tile = blockIdx.x;
+  const int q = threadIdx.x;
+  const uint32_t cnt = counts[tile * kStatesPerTile + q];
+  const uint32_t before = wave_scan(cnt, q) - cnt;
+  uint16_t *w = words + tile_first[tile];
+  if (q < kCountWords) w[q] = (uint16_t)(counts[tile * kStatesPerTile + 2 * q] | counts[tile * kStatesPerTile + 2 * q + 1] << 8);
+  const uint16_t *slot = slots + ((size_t)tile * kStatesPerTile + q) * kWordsPerState;
+  uint16_t *mine = w + kCountWords + before;
+  for (uint32_t k = 0; k < cnt; ++k) mine[k] = slot[cnt - 1u - k];
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+template <class T>
+struct DevBuf {
+  T *p = nullptr;
+  size_t n = 0;
+  ~DevBuf() {
+    if (p) (void)hipFree(p);
+  }
+  bool reserve(size_t count) {
+    if (count <= n && p) return true;
+    if (p) (void)hipFree(p);
+    p = nullptr;
+    n = 0;
+    if (hipMalloc(&p, sizeof(T) * (count ? count : 1)) != hipSuccess) {
+      p = nullptr;
+      return false;
+    }
+    n = count;
+    return true;
+  }
+};
+
+class GpuBackend final : public EncodeBackend {
+ public:
+  GpuBackend(const void *dev_src, const EncodeShape &S, hipStream_t stream) : es_(S), stream_(stream) {
+    S_ = Shape{dev_src, S.dtype, S.R, S.C, S.C8, S.vpr, S.n_vec, S.tiles};
+  }
+
+  int row_rms(std::vector<double> &rms, std::string &err) override {
+    if (!sums_.reserve((size_t)es_.R) || !flag_.reserve(1)) return nomem(err);
+    if (hipMemsetAsync(flag_.p, 0, sizeof(uint32_t), stream_) != hipSuccess) return device(err, "hipMemsetAsync");
+    hipLaunchKernelGGL(row_sums_kernel, dim3((unsigned)((es_.R + 63) / 64)), dim3(64), 0, stream_, S_, sums_.p, flag_.p);
+    if (hipGetLastError() != hipSuccess) return device(err, "row sums launch");
+    std::vector<double> sums((size_t)es_.R);
+    uint32_t bad = 0;
+    if (hipMemcpyAsync(sums.data(), sums_.p, 8 * (size_t)es_.R, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipMemcpyAsync(&bad, flag_.p, 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipStreamSynchronize(stream_) != hipSuccess)
+      return device(err, "row sums");
+    if (bad) {
+      err = "input holds NaN or Inf";
+      return EP_ERR_NONFINITE;
+    }
+    rms.resize((size_t)es_.R);
+    for (int64_t r = 0; r < es_.R; ++r) rms[(size_t)r] = std::sqrt(sums[(size_t)r] / (double)es_.C);
+    return 0;
+  }
+
+  int histogram(const std::vector<float> &g, int64_t nsamp, std::vector<uint64_t> &hist, std::string &err) override {
+    if (const int rc = upload_scales(g, err); rc != 0) return rc;
+    if (!hist_.reserve((size_t)kContexts * kSymSpan) || !flag_.reserve(1)) return nomem(err);
+    if (hipMemsetAsync(hist_.p, 0, 8 * hist_.n, stream_) != hipSuccess ||
+        hipMemsetAsync(flag_.p, 0, sizeof(uint32_t), stream_) != hipSuccess)
+      return device(err, "hipMemsetAsync");
+    const int64_t n = nsamp >= es_.n_vec ? es_.n_vec : nsamp;
+    const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4096));
+    hipLaunchKernelGGL(histogram_kernel, dim3(blocks), dim3(256), 0, stream_, S_, g_.p, nsamp, hist_.p, flag_.p);
+    if (hipGetLastError() != hipSuccess) return device(err, "histogram launch");
+    hist.assign((size_t)kContexts * kSymSpan, 0);
+    uint32_t over = 0;
+    if (hipMemcpyAsync(hist.data(), hist_.p, 8 * hist.size(), hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipMemcpyAsync(&over, flag_.p, 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipStreamSynchronize(stream_) != hipSuccess)
+      return device(err, "histogram");
+    return over ? 1 : 0;
+  }
+
+  int encode_tiles(const std::vector<float> &g, const Tables &tb, std::vector<uint32_t> &states,
+                   std::vector<uint32_t> &tile_first, std::vector<uint16_t> &words, std::string &err) override {
+    if (const int rc = upload_scales(g, err); rc != 0) return rc;
+    // tables: frequency | cumulative << 16 per symbol, contexts one after another
+    DevTables T{};
+    std::vector<uint32_t> fc;
+    for (int c = 0; c < kContexts; ++c) {
+      T.smin[c] = tb.smin[c];
+      T.nsym[c] = tb.nsym[c];
+      T.base[c] = (uint32_t)fc.size();
+      for (int i = 0; i < tb.nsym[c]; ++i) fc.push_back(tb.freq[c][(size_t)i] | tb.cum[c][(size_t)i] << 16);
+    }
+    const size_t nt = (size_t)es_.tiles, ns = nt * kStatesPerTile;
+    if (!fc_.reserve(fc.size()) || !slots_.reserve(ns * kWordsPerState) || !counts_.reserve(ns) ||
+        !states_.reserve(ns) || !first_.reserve(nt + 1) || !flag_.reserve(1))
+      return nomem(err);
+    if (hipMemcpyAsync(fc_.p, fc.data(), 4 * fc.size(), hipMemcpyHostToDevice, stream_) != hipSuccess ||
+        hipMemsetAsync(flag_.p, 0, sizeof(uint32_t), stream_) != hipSuccess)
+      return device(err, "table upload");
+    hipLaunchKernelGGL(encode_tiles_kernel, dim3((unsigned)nt), dim3(kStatesPerTile), 0, stream_, S_, g_.p, T, fc_.p,
+                       slots_.p, counts_.p, states_.p, flag_.p);
+    if (hipGetLastError() != hipSuccess) return device(err, "tile encode launch");
+    std::vector<uint8_t> counts(ns);
+    uint32_t fault = 0;
+    states.resize(ns);
+    if (hipMemcpyAsync(counts.data(), counts_.p, ns, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipMemcpyAsync(states.data(), states_.p, 4 * ns, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipMemcpyAsync(&fault, flag_.p, 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipStreamSynchronize(stream_) != hipSuccess)
+      return device(err, "tile encode");
+    if (fault) {
+      err = "the tile encoder met a symbol outside the tables";
+      return EP_ERR_DEVICE;
+    }
+    // each tile's first word: the count words plus its states' words
+    tile_first.resize(nt + 1);
+    uint64_t w = 0;
+    for (size_t t = 0; t < nt; ++t) {
+      tile_first[t] = (uint32_t)w;
+      w += kCountWords;
+      for (int q = 0; q < kStatesPerTile; ++q) w += counts[t * kStatesPerTile + q];
+      if (w > 0xffffffffull) {
+        err = "stream too large for 32-bit tile offsets";
+        return EP_ERR_SHAPE;
+      }
+    }
+    tile_first[nt] = (uint32_t)w;
+    if (!words_.reserve((size_t)w)) return nomem(err);
+    if (hipMemcpyAsync(first_.p, tile_first.data(), 4 * (nt + 1), hipMemcpyHostToDevice, stream_) != hipSuccess)
+      return device(err, "tile offsets upload");
+    hipLaunchKernelGGL(lay_out_kernel, dim3((unsigned)nt), dim3(kStatesPerTile), 0, stream_, slots_.p, counts_.p, first_.p,
+                       words_.p);
+    if (hipGetLastError() != hipSuccess) return device(err, "layout launch");
+    words.resize((size_t)w);
+    if (hipMemcpyAsync(words.data(), words_.p, 2 * (size_t)w, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipStreamSynchronize(stream_) != hipSuccess)
+      return device(err, "word copy");
+    return 0;
+  }
+
+  int copy_input(uint8_t *dst, std::string &err) override {
+    if (hipMemcpyAsync(dst, S_.src, (size_t)es_.R * (size_t)es_.C * elem_bytes(es_.dtype), hipMemcpyDeviceToHost,
+                       stream_) != hipSuccess ||
+        hipStreamSynchronize(stream_) != hipSuccess)
+      return device(err, "input copy");
+    return 0;
+  }
+
+ private:
+  int upload_scales(const std::vector<float> &g, std::string &err) {
+    if (!g_.reserve(g.size())) return nomem(err);
+    if (hipMemcpyAsync(g_.p, g.data(), 4 * g.size(), hipMemcpyHostToDevice, stream_) != hipSuccess)
+      return device(err, "scale upload");
+    return 0;
+  }
+  static int nomem(std::string &err) {
+    err = "device allocation failed";
+    return EP_ERR_NOMEM;
+  }
+  static int device(std::string &err, const char *what) {
+    err = std::string(what) + " failed: " + hipGetErrorString(hipGetLastError());
+    return EP_ERR_DEVICE;
+  }
+
+  EncodeShape es_;
+  Shape S_;
+  hipStream_t stream_;
+  DevBuf<double> sums_;
+  DevBuf<float> g_;
+  DevBuf<uint64_t> hist_;
+  DevBuf<uint32_t> flag_, fc_, states_, first_;
+  DevBuf<uint16_t> slots_, words_;
+  DevBuf<uint8_t> counts_;
+};
+
+}  // namespace
+
+int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target, double fixed_a,
+                    void *stream, std::vector<uint8_t> &blob, std::string &err) {
+  EncodeShape S;
+  int status = 0;
+  if (!make_shape(dtype, rows, cols, S, status, err)) return status;
+  if (!dev_src) {
+    err = "null input";
+    return EP_ERR_ARG;
+  }
+  GpuBackend be(dev_src, S, reinterpret_cast<hipStream_t>(stream));
+  return compress_with(be, S, target, fixed_a, blob, err);
+}
+
+}  // namespace ep

@@ -1,7 +1,8 @@
 """Thin ctypes binding to libep.so (include/ep.h).
 
 Argument marshalling only: every step of compression runs in the library's
-host encoder and every step of decompression runs in its gfx950 kernels.
+host encoder (or, for a matrix on the GPU, its gfx950 encoder passes) and
+every step of decompression runs in its gfx950 kernels.
 PyTorch supplies host/device buffers and the current HIP stream.  There is
 no fallback: if libep.so is missing the calls raise.
 """
@@ -25,7 +26,7 @@ ERR_ARG, ERR_SHAPE, ERR_NONFINITE, ERR_TARGET, ERR_FORMAT, ERR_DEVICE, ERR_NOMEM
 _DTYPE_CODE = {torch.bfloat16: BF16, torch.float16: FP16, torch.float8_e4m3fn: FP8_E4M3FN, torch.int8: INT8}
 _CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
 
-EXPORTS = ["ep_compress", "ep_compress_ex", "ep_free", "ep_decompress", "ep_decode_symbols", "ep_actual_bpp",
+EXPORTS = ["ep_compress", "ep_compress_ex", "ep_compress_device", "ep_free", "ep_decompress", "ep_decode_symbols", "ep_actual_bpp",
            "ep_storage_nbytes", "ep_blob_info", "ep_last_error"]
 
 
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(u8p), ctypes.POINTER(ctypes.c_size_t)]
         L.ep_compress_ex.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                      ctypes.POINTER(_Options), ctypes.POINTER(u8p), ctypes.POINTER(ctypes.c_size_t)]
+        L.ep_compress_device.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_double, ctypes.POINTER(_Options), ctypes.c_void_p,
+                                         ctypes.POINTER(u8p), ctypes.POINTER(ctypes.c_size_t)]
         L.ep_free.argtypes = [u8p]
         L.ep_free.restype = None
         L.ep_decompress.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -132,6 +136,32 @@ def compress(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, n_thr
                               t.shape[0], t.shape[1], float(target_bpp), ctypes.byref(opt), ctypes.byref(out),
                               ctypes.byref(nb))
     _check(rc, "ep_compress")
+    blob = np.ctypeslib.as_array(out, shape=(nb.value,)).copy()
+    lib().ep_free(out)
+    return Packed(blob=blob, status=rc, shape=tuple(t.shape), dtype=t.dtype)
+
+
+def compress_device(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, stream=None) -> Packed:
+    """ep_compress_device on a 2-D tensor in GPU memory: the same stream as
+    compress() of the same values, with the passes over the matrix on the GPU
+    (on `stream`, default: the current stream, synchronized on return)."""
+    if t.dtype not in _DTYPE_CODE:
+        raise EPError(ERR_ARG, "compress_device", f"unsupported dtype {t.dtype}")
+    if t.dim() != 2:
+        raise EPError(ERR_SHAPE, "compress_device", "input must be 2-D")
+    if not t.is_cuda:
+        raise EPError(ERR_ARG, "compress_device", "input must be on a GPU")
+    t = t.detach().contiguous()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    opt = _Options(float(fixed_scale), 0, (ctypes.c_int * 6)())
+    out = ctypes.POINTER(ctypes.c_uint8)()
+    nb = ctypes.c_size_t(0)
+    with torch.cuda.device(t.device):
+        rc = lib().ep_compress_device(ctypes.c_void_p(t.data_ptr() if t.numel() else 0), _DTYPE_CODE[t.dtype],
+                                      t.shape[0], t.shape[1], float(target_bpp), ctypes.byref(opt),
+                                      ctypes.c_void_p(stream.cuda_stream), ctypes.byref(out), ctypes.byref(nb))
+    _check(rc, "ep_compress_device")
     blob = np.ctypeslib.as_array(out, shape=(nb.value,)).copy()
     lib().ep_free(out)
     return Packed(blob=blob, status=rc, shape=tuple(t.shape), dtype=t.dtype)

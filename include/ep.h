@@ -46,7 +46,7 @@ enum ep_status {
                              stream's fixed per-tile overhead for this shape */
   EP_ERR_FORMAT = -5,     /* stream header or section table is corrupt */
   EP_ERR_DEVICE = -6,     /* HIP launch or device query failed */
-  EP_ERR_NOMEM = -7       /* host allocation failed */
+  EP_ERR_NOMEM = -7       /* host (or, for ep_compress_device, device) allocation failed */
 };
 
 /* Optional knobs for ep_compress_ex.  Zero-initialize and set what you need;
@@ -77,7 +77,28 @@ int ep_compress(const void *host_src, int dtype, int64_t rows, int64_t cols, dou
 int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
                    const struct ep_options *opt, uint8_t **blob_out, size_t *nbytes_out);
 
-/* Release a stream returned by ep_compress / ep_compress_ex.  NULL is a no-op. */
+/*
+ * ep_compress_device -- the same compression for a matrix in device memory,
+ * with the passes over its elements on the GPU (the abstract calls the
+ * encoder fast and its rate selection sampled: storage estimates from a
+ * sample of the vectors pick the resolution).  The stream is the one
+ * ep_compress_ex returns for the same input and options, byte for byte.
+ *   dev_src    : rows*cols elements of `dtype`, row-major, device memory
+ *                (caller-owned, read only).
+ *   opt        : as for ep_compress_ex (n_threads is not used); may be NULL.
+ *   hip_stream : hipStream_t the work runs on (NULL = default stream); it is
+ *                synchronized before the call returns.
+ *   blob_out, nbytes_out : as for ep_compress (host memory; ep_free).
+ * Allocates device scratch with hipMalloc for the call (about 16 KB per tile
+ * of 1024 vectors, plus the word section) and frees it before returning.
+ * Returns as ep_compress; EP_ERR_DEVICE if a HIP call fails, EP_ERR_NOMEM if
+ * a device allocation does.
+ */
+int ep_compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
+                       const struct ep_options *opt, void *hip_stream, uint8_t **blob_out, size_t *nbytes_out);
+
+/* Release a stream returned by ep_compress / ep_compress_ex / ep_compress_device.
+ * NULL is a no-op. */
 void ep_free(uint8_t *blob);
 
 /*
