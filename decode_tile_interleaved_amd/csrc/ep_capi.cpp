@@ -40,7 +40,7 @@ int compress_entry(const struct ep_options *opt, uint8_t **blob_out, size_t *nby
       return EP_ERR_ARG;
     }
   }
-  std::vector<uint8_t> blob;
+  ep::Blob blob;
   std::string err;
   int rc;
   try {
@@ -53,14 +53,8 @@ int compress_entry(const struct ep_options *opt, uint8_t **blob_out, size_t *nby
     ep::set_error(err);
     return rc;
   }
-  uint8_t *out = (uint8_t *)std::malloc(blob.size());
-  if (!out) {
-    ep::set_error("host allocation failed");
-    return EP_ERR_NOMEM;
-  }
-  std::memcpy(out, blob.data(), blob.size());
-  *blob_out = out;
   *nbytes_out = blob.size();
+  *blob_out = blob.release();  // malloc'ed: ep_free releases it
   if (rc > 0) ep::set_error(err);
   return rc;
 }
@@ -71,7 +65,7 @@ extern "C" {
 
 int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
                    const struct ep_options *opt, uint8_t **blob_out, size_t *nbytes_out) {
-  return compress_entry(opt, blob_out, nbytes_out, [&](double fixed_a, int threads, std::vector<uint8_t> &blob,
+  return compress_entry(opt, blob_out, nbytes_out, [&](double fixed_a, int threads, ep::Blob &blob,
                                                         std::string &err) {
     return ep::compress(host_src, dtype, rows, cols, target_bpp, fixed_a, threads, blob, err);
   });
@@ -79,7 +73,7 @@ int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, 
 
 int ep_compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
                        const struct ep_options *opt, void *hip_stream, uint8_t **blob_out, size_t *nbytes_out) {
-  return compress_entry(opt, blob_out, nbytes_out, [&](double fixed_a, int, std::vector<uint8_t> &blob,
+  return compress_entry(opt, blob_out, nbytes_out, [&](double fixed_a, int, ep::Blob &blob,
                                                         std::string &err) {
     return ep::compress_device(dev_src, dtype, rows, cols, target_bpp, fixed_a, hip_stream, blob, err);
   });

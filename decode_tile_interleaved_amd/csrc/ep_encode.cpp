@@ -298,7 +298,7 @@ class HostBackend final : public EncodeBackend {
   }
 
   int encode_tiles(const std::vector<float> &g, const Tables &tb, std::vector<uint32_t> &states,
-                   std::vector<uint32_t> &tile_first, std::vector<uint16_t> &words, std::string &err) override {
+                   std::vector<uint32_t> &tile_first, std::string &err) override {
     if (V_.empty() || Vg_ != g) {  // the lattice vectors of the last full pass, if it was at these scales
       std::vector<uint64_t> ignored;
       if (full_pass(g, ignored) != 0) {
@@ -306,27 +306,31 @@ class HostBackend final : public EncodeBackend {
         return EP_ERR_ARG;
       }
     }
-    std::vector<TileOut> tiles((size_t)S_.tiles);
+    tiles_.assign((size_t)S_.tiles, TileOut{});
     parallel_for(S_.tiles, std::max(1, threads_), [&](int64_t b, int64_t e) {
-      for (int64_t t = b; t < e; ++t) encode_tile(tb, t, tiles[(size_t)t]);
+      for (int64_t t = b; t < e; ++t) encode_tile(tb, t, tiles_[(size_t)t]);
     });
-    uint64_t n_words = 0;
-    for (auto &t : tiles) n_words += t.words.size();
-    if (n_words > 0xffffffffull) {
-      err = "stream too large for 32-bit tile offsets";
-      return EP_ERR_SHAPE;
-    }
     states.resize((size_t)S_.tiles * kStatesPerTile);
     tile_first.resize((size_t)S_.tiles + 1);
-    words.resize((size_t)n_words);
     uint64_t w = 0;
     for (int64_t t = 0; t < S_.tiles; ++t) {
-      std::memcpy(&states[(size_t)t * kStatesPerTile], tiles[(size_t)t].states, 4 * kStatesPerTile);
+      std::memcpy(&states[(size_t)t * kStatesPerTile], tiles_[(size_t)t].states, 4 * kStatesPerTile);
       tile_first[(size_t)t] = (uint32_t)w;
-      std::memcpy(&words[(size_t)w], tiles[(size_t)t].words.data(), 2 * tiles[(size_t)t].words.size());
-      w += tiles[(size_t)t].words.size();
+      w += tiles_[(size_t)t].words.size();
+      if (w > 0xffffffffull) {
+        err = "stream too large for 32-bit tile offsets";
+        return EP_ERR_SHAPE;
+      }
     }
     tile_first[(size_t)S_.tiles] = (uint32_t)w;
+    return 0;
+  }
+
+  int copy_words(uint16_t *dst, std::string &) override {
+    for (const TileOut &t : tiles_) {
+      std::memcpy(dst, t.words.data(), 2 * t.words.size());
+      dst += t.words.size();
+    }
     return 0;
   }
 
@@ -430,6 +434,7 @@ class HostBackend final : public EncodeBackend {
   EncodeShape S_;
   int threads_;
   std::vector<int32_t> V_;  // lattice vectors of the last full pass, rows of C8 coordinates
+  std::vector<TileOut> tiles_;  // the last encode_tiles
   std::vector<float> Vg_;   // the row scales they were quantized at
 };
 
@@ -509,7 +514,7 @@ double choose_scale(const Problem &P, double target, double *closest, std::strin
 }
 
 // the full stream at resolution a
-int encode_at(const Problem &P, double a, double target, std::vector<uint8_t> &blob, std::string &err) {
+int encode_at(const Problem &P, double a, double target, Blob &blob, std::string &err) {
   const EncodeShape &S = P.S;
   const std::vector<float> g = row_scales(P, a);
   std::vector<uint64_t> hist;
@@ -522,10 +527,9 @@ int encode_at(const Problem &P, double a, double target, std::vector<uint8_t> &b
     return EP_ERR_TARGET;
   }
   std::vector<uint32_t> states, tile_first;
-  std::vector<uint16_t> words;
-  rc = P.be->encode_tiles(g, tb, states, tile_first, words, err);
+  rc = P.be->encode_tiles(g, tb, states, tile_first, err);
   if (rc < 0) return rc;
-  const uint64_t n_words = words.size();
+  const uint64_t n_words = tile_first.back();
   const int nsum = tb.total_symbols();
   const uint64_t o_tab = kHeaderBytes;
   const uint64_t o_sc = o_tab + align16(4 * kContexts + 2 * (uint64_t)nsum);
@@ -533,8 +537,13 @@ int encode_at(const Problem &P, double a, double target, std::vector<uint8_t> &b
   const uint64_t o_to = o_st + align16(4 * (uint64_t)S.tiles * kStatesPerTile);
   const uint64_t o_w = o_to + align16(4 * (uint64_t)(S.tiles + 1));
   const uint64_t total = o_w + align16(2 * n_words);
-  blob.assign(total, 0);
+  if (!blob.alloc(total)) {
+    err = "host allocation failed";
+    return EP_ERR_NOMEM;
+  }
   uint8_t *b = blob.data();
+  std::memset(b, 0, o_w);                                           // every section before the words, with its padding
+  std::memset(b + o_w + 2 * n_words, 0, total - o_w - 2 * n_words);  // the words' padding
   wr<uint32_t>(b + hdr::magic, kMagic);
   wr<uint16_t>(b + hdr::version, kVersion);
   wr<uint16_t>(b + hdr::header_bytes, (uint16_t)kHeaderBytes);
@@ -569,15 +578,19 @@ int encode_at(const Problem &P, double a, double target, std::vector<uint8_t> &b
   std::memcpy(b + o_sc, g.data(), 4 * (size_t)S.R);
   std::memcpy(b + o_st, states.data(), 4 * states.size());
   std::memcpy(b + o_to, tile_first.data(), 4 * tile_first.size());
-  std::memcpy(b + o_w, words.data(), 2 * n_words);
-  return EP_OK;
+  return P.be->copy_words(reinterpret_cast<uint16_t *>(b + o_w), err);
 }
 
-int raw_stream(const Problem &P, double target, std::vector<uint8_t> &blob, std::string &err) {
+int raw_stream(const Problem &P, double target, Blob &blob, std::string &err) {
   const EncodeShape &S = P.S;
   const uint64_t payload = (uint64_t)S.R * (uint64_t)S.C * elem_bytes(S.dtype);
-  blob.assign(kHeaderBytes + align16(payload), 0);
+  if (!blob.alloc(kHeaderBytes + align16(payload))) {
+    err = "host allocation failed";
+    return EP_ERR_NOMEM;
+  }
   uint8_t *b = blob.data();
+  std::memset(b, 0, kHeaderBytes);
+  std::memset(b + kHeaderBytes + payload, 0, blob.size() - kHeaderBytes - payload);
   wr<uint32_t>(b + hdr::magic, kMagic);
   wr<uint16_t>(b + hdr::version, kVersion);
   wr<uint16_t>(b + hdr::header_bytes, (uint16_t)kHeaderBytes);
@@ -621,7 +634,7 @@ bool make_shape(int dtype, int64_t rows, int64_t cols, EncodeShape &S, int &stat
 }
 
 int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, double fixed_a,
-                  std::vector<uint8_t> &blob, std::string &err) {
+                  Blob &blob, std::string &err) {
   Problem P{shape, &be, {}};
   const EncodeShape &S = P.S;
   // finiteness and row RMS (sequential sum per row)
@@ -675,7 +688,7 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, do
 }
 
 int compress(const void *src, int dtype, int64_t rows, int64_t cols, double target, double fixed_a, int threads,
-             std::vector<uint8_t> &blob, std::string &err) {
+             Blob &blob, std::string &err) {
   EncodeShape S;
   int status = 0;
   if (!make_shape(dtype, rows, cols, S, status, err)) return status;

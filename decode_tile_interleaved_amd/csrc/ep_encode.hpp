@@ -4,6 +4,7 @@
 #pragma once
 
 #include <cstdint>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -20,6 +21,35 @@ constexpr int kSymSpan = 4096;
 // Sampled rate estimates quantize min(n_vec, kSampleVecs) vectors, vector
 // floor(k * n_vec / S) for k < S.
 constexpr int64_t kSampleVecs = 65536;
+
+// A stream in memory from malloc, so that the C ABI hands it to the caller
+// as it is (ep_free releases it).
+class Blob {
+ public:
+  Blob() = default;
+  Blob(const Blob &) = delete;
+  Blob &operator=(const Blob &) = delete;
+  ~Blob() { std::free(p_); }
+  // n bytes, contents undefined; false if malloc fails
+  bool alloc(size_t n) {
+    std::free(p_);
+    p_ = (uint8_t *)std::malloc(n ? n : 1);
+    n_ = p_ ? n : 0;
+    return p_ != nullptr;
+  }
+  uint8_t *data() { return p_; }
+  size_t size() const { return n_; }
+  uint8_t *release() {
+    uint8_t *p = p_;
+    p_ = nullptr;
+    n_ = 0;
+    return p;
+  }
+
+ private:
+  uint8_t *p_ = nullptr;
+  size_t n_ = 0;
+};
 
 struct EncodeShape {
   int dtype = 0;
@@ -55,10 +85,13 @@ class EncodeBackend {
   // coordinate leaves [-2048, 2047], or a negative ep_status.
   virtual int histogram(const std::vector<float> &g, int64_t S, std::vector<uint64_t> &hist, std::string &err) = 0;
   // Every tile at row scales g with tables t: start states (kStatesPerTile
-  // per tile), the index of each tile's first word (tiles + 1 entries) and
-  // the word section.  Returns 0 or a negative ep_status.
+  // per tile) and the index of each tile's first word (tiles + 1 entries;
+  // the last is the word count).  The words stay with the backend until
+  // copy_words.  Returns 0 or a negative ep_status.
   virtual int encode_tiles(const std::vector<float> &g, const Tables &t, std::vector<uint32_t> &states,
-                           std::vector<uint32_t> &tile_first, std::vector<uint16_t> &words, std::string &err) = 0;
+                           std::vector<uint32_t> &tile_first, std::string &err) = 0;
+  // The word section of the last encode_tiles, to dst.
+  virtual int copy_words(uint16_t *dst, std::string &err) = 0;
   // The container elements, row-major (rows * cols * element bytes).
   virtual int copy_input(uint8_t *dst, std::string &err) = 0;
 };
@@ -68,7 +101,7 @@ class EncodeBackend {
 // fixed_a > 0 skips rate selection.  Returns an ep_status; on EP_OK or
 // EP_WARN_RAW `blob` holds the stream, otherwise `err` says why.
 int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, double fixed_a,
-                  std::vector<uint8_t> &blob, std::string &err);
+                  Blob &blob, std::string &err);
 
 // The shape of a rows x cols matrix of a container dtype; false (with err) if
 // it cannot be one stream.
@@ -77,12 +110,12 @@ bool make_shape(int dtype, int64_t rows, int64_t cols, EncodeShape &shape, int &
 // Lossy lattice-rANS compression of a rows x cols container matrix in host
 // memory, on host threads (threads <= 0: every hardware thread).
 int compress(const void *src, int dtype, int64_t rows, int64_t cols, double target, double fixed_a, int threads,
-             std::vector<uint8_t> &blob, std::string &err);
+             Blob &blob, std::string &err);
 
 // The same for a matrix in device memory, on the GPU (work enqueued on
 // `stream`, which is synchronized before the call returns).
 int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target, double fixed_a,
-                    void *stream, std::vector<uint8_t> &blob, std::string &err);
+                    void *stream, Blob &blob, std::string &err);
 
 // Per-thread error text shared by the C ABI functions.
 void set_error(const std::string &msg);

@@ -34,26 +34,29 @@ namespace {
 // ---------------------------------------------------------------------------
 // device side
 // ---------------------------------------------------------------------------
-// element i of a container matrix, widened exactly to f64
-__device__ __forceinline__ double widen_d(const void *src, int dtype, int64_t i) {
+// a container element given by its bits, widened exactly to f64
+__device__ __forceinline__ double widen_bits(uint32_t bits, int dtype) {
   switch (dtype) {
     case EP_BF16:
-      return (double)__uint_as_float((uint32_t)((const uint16_t *)src)[i] << 16);
+      return (double)__uint_as_float(bits << 16);
     case EP_FP16: {
-      const uint32_t h = ((const uint16_t *)src)[i];
-      const int e = (int)((h >> 10) & 31u), m = (int)(h & 1023u);
+      const int e = (int)((bits >> 10) & 31u), m = (int)(bits & 1023u);
       const double mag = e == 0 ? ldexp((double)m, -24) : e == 31 ? (m ? NAN : INFINITY) : ldexp(1024.0 + m, e - 25);
-      return (h & 0x8000u) ? -mag : mag;
+      return (bits & 0x8000u) ? -mag : mag;
     }
     case EP_FP8_E4M3FN: {
-      const uint32_t c = ((const uint8_t *)src)[i];
-      const int e = (int)((c >> 3) & 15u), m = (int)(c & 7u);
+      const int e = (int)((bits >> 3) & 15u), m = (int)(bits & 7u);
       const double mag = (e == 15 && m == 7) ? NAN : e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
-      return (c & 0x80u) ? -mag : mag;
+      return (bits & 0x80u) ? -mag : mag;
     }
     default:
-      return (double)((const int8_t *)src)[i];
+      return (double)(int8_t)(uint8_t)bits;
   }
+}
+
+// element i of a container matrix, widened exactly to f64
+__device__ __forceinline__ double widen_d(const void *src, int dtype, int64_t i) {
+  return widen_bits(dtype <= EP_FP16 ? (uint32_t)((const uint16_t *)src)[i] : (uint32_t)((const uint8_t *)src)[i], dtype);
 }
 
 struct Shape {
@@ -63,16 +66,34 @@ struct Shape {
 };
 
 // one thread per row: sum of squares in column order, and whether every
-// element is finite
+// element is finite.  VEC: rows start on 16-byte boundaries and hold whole
+// 16-byte pieces, read one piece per load (the sum still runs element by
+// element, in column order).
+template <bool VEC>
 __global__ void row_sums_kernel(Shape S, double *sums, uint32_t *nonfinite) {
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= S.R) return;
   double acc = 0.0;
   bool bad = false;
-  for (int64_t c = 0; c < S.C; ++c) {
-    const double x = widen_d(S.src, S.dtype, r * S.C + c);
-    bad |= !isfinite(x);
-    acc += x * x;
+  if (VEC) {
+    const uint32_t eb = S.dtype <= EP_FP16 ? 2u : 1u, per = 16u / eb;
+    const uint4 *row = (const uint4 *)((const uint8_t *)S.src + (uint64_t)r * (uint64_t)S.C * eb);
+    for (int64_t i = 0; i < S.C / per; ++i) {
+      const uint4 q = row[i];
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+      for (uint32_t k = 0; k < per; ++k) {
+        const uint32_t bits = eb == 2u ? (w[k >> 1] >> (16u * (k & 1u))) & 0xffffu : (w[k >> 2] >> (8u * (k & 3u))) & 0xffu;
+        const double x = widen_bits(bits, S.dtype);
+        bad |= !isfinite(x);
+        acc += x * x;
+      }
+    }
+  } else {
+    for (int64_t c = 0; c < S.C; ++c) {
+      const double x = widen_d(S.src, S.dtype, r * S.C + c);
+      bad |= !isfinite(x);
+      acc += x * x;
+    }
   }
   sums[r] = acc;
   if (bad) atomicOr(nonfinite, 1u);
@@ -321,7 +342,10 @@ class GpuBackend final : public EncodeBackend {
   int row_rms(std::vector<double> &rms, std::string &err) override {
     if (!sums_.reserve((size_t)es_.R) || !flag_.reserve(1)) return nomem(err);
     if (hipMemsetAsync(flag_.p, 0, sizeof(uint32_t), stream_) != hipSuccess) return device(err, "hipMemsetAsync");
-    hipLaunchKernelGGL(row_sums_kernel, dim3((unsigned)((es_.R + 63) / 64)), dim3(64), 0, stream_, S_, sums_.p, flag_.p);
+    const uint64_t row_bytes = (uint64_t)es_.C * elem_bytes(es_.dtype);
+    const bool vec = ((uintptr_t)S_.src & 15u) == 0 && row_bytes % 16 == 0;
+    hipLaunchKernelGGL(vec ? row_sums_kernel<true> : row_sums_kernel<false>, dim3((unsigned)((es_.R + 63) / 64)), dim3(64),
+                       0, stream_, S_, sums_.p, flag_.p);
     if (hipGetLastError() != hipSuccess) return device(err, "row sums launch");
     std::vector<double> sums((size_t)es_.R);
     uint32_t bad = 0;
@@ -358,7 +382,7 @@ class GpuBackend final : public EncodeBackend {
   }
 
   int encode_tiles(const std::vector<float> &g, const Tables &tb, std::vector<uint32_t> &states,
-                   std::vector<uint32_t> &tile_first, std::vector<uint16_t> &words, std::string &err) override {
+                   std::vector<uint32_t> &tile_first, std::string &err) override {
     if (const int rc = upload_scales(g, err); rc != 0) return rc;
     // tables: frequency | cumulative << 16 per symbol, contexts one after another
     DevTables T{};
@@ -410,8 +434,12 @@ class GpuBackend final : public EncodeBackend {
     hipLaunchKernelGGL(lay_out_kernel, dim3((unsigned)nt), dim3(kStatesPerTile), 0, stream_, slots_.p, counts_.p, first_.p,
                        words_.p);
     if (hipGetLastError() != hipSuccess) return device(err, "layout launch");
-    words.resize((size_t)w);
-    if (hipMemcpyAsync(words.data(), words_.p, 2 * (size_t)w, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+    n_words_ = (size_t)w;
+    return 0;
+  }
+
+  int copy_words(uint16_t *dst, std::string &err) override {
+    if (hipMemcpyAsync(dst, words_.p, 2 * n_words_, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
         hipStreamSynchronize(stream_) != hipSuccess)
       return device(err, "word copy");
     return 0;
@@ -450,12 +478,13 @@ class GpuBackend final : public EncodeBackend {
   DevBuf<uint32_t> flag_, fc_, states_, first_;
   DevBuf<uint16_t> slots_, words_;
   DevBuf<uint8_t> counts_;
+  size_t n_words_ = 0;
 };
 
 }  // namespace
 
 int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target, double fixed_a,
-                    void *stream, std::vector<uint8_t> &blob, std::string &err) {
+                    void *stream, Blob &blob, std::string &err) {
   EncodeShape S;
   int status = 0;
   if (!make_shape(dtype, rows, cols, S, status, err)) return status;

@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import weakref
 from dataclasses import dataclass
 
 import numpy as np
@@ -117,6 +118,14 @@ class Packed:
         return self
 
 
+def _take_blob(ptr, n: int) -> np.ndarray:
+    """The library's malloc'ed stream as a uint8 array, without a copy; the
+    memory goes back to ep_free once the array and every view of it are gone."""
+    arr = np.ctypeslib.as_array(ptr, shape=(n,))
+    weakref.finalize(arr.base, lib().ep_free, ptr)
+    return arr
+
+
 def _host_ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
@@ -136,9 +145,7 @@ def compress(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, n_thr
                               t.shape[0], t.shape[1], float(target_bpp), ctypes.byref(opt), ctypes.byref(out),
                               ctypes.byref(nb))
     _check(rc, "ep_compress")
-    blob = np.ctypeslib.as_array(out, shape=(nb.value,)).copy()
-    lib().ep_free(out)
-    return Packed(blob=blob, status=rc, shape=tuple(t.shape), dtype=t.dtype)
+    return Packed(blob=_take_blob(out, nb.value), status=rc, shape=tuple(t.shape), dtype=t.dtype)
 
 
 def compress_device(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, stream=None) -> Packed:
@@ -162,9 +169,7 @@ def compress_device(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0
                                       t.shape[0], t.shape[1], float(target_bpp), ctypes.byref(opt),
                                       ctypes.c_void_p(stream.cuda_stream), ctypes.byref(out), ctypes.byref(nb))
     _check(rc, "ep_compress_device")
-    blob = np.ctypeslib.as_array(out, shape=(nb.value,)).copy()
-    lib().ep_free(out)
-    return Packed(blob=blob, status=rc, shape=tuple(t.shape), dtype=t.dtype)
+    return Packed(blob=_take_blob(out, nb.value), status=rc, shape=tuple(t.shape), dtype=t.dtype)
 
 
 def actual_bpp(blob: np.ndarray) -> float:
