@@ -130,3 +130,28 @@ def test_raw_fallback_matches_oracle():
     assert p.status == ep.WARN_RAW == rc
     assert np.array_equal(p.blob, blob)
     assert ep.blob_info(p.blob)["method"] == 1
+
+
+def test_device_compress_argument_errors_before_any_device_work():
+    """ep_compress_device checks its arguments on the host before touching a
+    device, so these run without a GPU."""
+    import ctypes
+    L = ep.lib()
+    out = ctypes.POINTER(ctypes.c_uint8)()
+    nb = ctypes.c_size_t(0)
+    # null input
+    rc = L.ep_compress_device(None, ep.BF16, 64, 512, 4.0, None, None, ctypes.byref(out), ctypes.byref(nb))
+    assert rc == ep.ERR_ARG
+    # unknown container dtype, empty shape, too many vectors for one stream
+    for dtype, rows, cols, code in ((7, 64, 512, ep.ERR_ARG), (ep.BF16, 0, 512, ep.ERR_SHAPE),
+                                    (ep.BF16, 1 << 20, 1 << 15, ep.ERR_SHAPE)):
+        rc = L.ep_compress_device(ctypes.c_void_p(0x1000), dtype, rows, cols, 4.0, None, None, ctypes.byref(out),
+                                  ctypes.byref(nb))
+        assert rc == code, (dtype, rows, cols, rc)
+    # null outputs and non-zero reserved options
+    rc = L.ep_compress_device(ctypes.c_void_p(0x1000), ep.BF16, 64, 512, 4.0, None, None, None, ctypes.byref(nb))
+    assert rc == ep.ERR_ARG
+    opt = ep._Options(0.0, 0, (ctypes.c_int * 6)(0, 1, 0, 0, 0, 0))
+    rc = L.ep_compress_device(ctypes.c_void_p(0x1000), ep.BF16, 64, 512, 4.0, ctypes.byref(opt), None,
+                              ctypes.byref(out), ctypes.byref(nb))
+    assert rc == ep.ERR_ARG
