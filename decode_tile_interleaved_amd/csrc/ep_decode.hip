@@ -316,7 +316,11 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
       for (int j = 0; j < 8; ++j) {
         if ((uint32_t)j >= left) break;
         if constexpr (OUT == EP_BF16 || OUT == EP_FP16) {
-          reinterpret_cast<uint16_t *>(A.out)[base + j] = (uint16_t)(pack2<OUT>(y[j], 0.0f) & 0xffffu);
+          // y is hidden from the conversion: otherwise the compiler folds the
+          // multiply and the narrowing into one v_fma_mixlo_f16, a single
+          // rounding where the reconstruction rounds to f32 first
+          const float yj = __uint_as_float(opaque(__float_as_uint(y[j])));
+          reinterpret_cast<uint16_t *>(A.out)[base + j] = (uint16_t)(pack2<OUT>(yj, 0.0f) & 0xffffu);
         } else if constexpr (OUT == EP_FP8_E4M3FN) {
           reinterpret_cast<uint8_t *>(A.out)[base + j] =
               (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[j]), 0.0f, 0, false) & 0xff);

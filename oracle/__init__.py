@@ -271,6 +271,26 @@ def decompress_raw_threads(blob: np.ndarray, threads: int) -> np.ndarray:
     return out
 
 
+def decompress_tile_range(blob: np.ndarray, t0: int, t1: int, out: np.ndarray | None = None,
+                          work: np.ndarray | None = None) -> np.ndarray:
+    """Decodes tiles [t0, t1) only, into a full-size container array (other
+    elements untouched: zero in a fresh array).  out/work may be passed in to
+    reuse them across calls."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    d = info(blob)
+    if d["method"] != 0:
+        raise OracleError(ERR_ARG, "decompress_tile_range")
+    if out is None:
+        out = np.zeros((d["rows"], d["cols"]), _NP_CONTAINER[d["dtype"]])
+    if work is None:
+        work = np.zeros((d["rows"], (d["cols"] + 7) // 8 * 8), np.int32)
+    rc = lib().or_decompress_tiles(_ptr(blob, ctypes.c_uint8), blob.size, t0, t1, _ptr(work, ctypes.c_int32),
+                                   out.ctypes.data)
+    if rc:
+        raise OracleError(rc, "decompress_tiles")
+    return out
+
+
 def to_torch(raw: np.ndarray, dtype: int):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(raw))

@@ -265,3 +265,9 @@ def test_tile_range_decode_matches_whole(shape):
     whole = oracle.decompress_raw(blob)
     for threads in (1, 2, 3):
         assert np.array_equal(oracle.decompress_raw_threads(blob, threads), whole)
+    # one tile range at a time into a shared buffer gives the same bytes too
+    T = oracle.info(blob)["n_tiles"]
+    out = np.zeros_like(whole)
+    for t0 in range(0, T, 2):
+        oracle.decompress_tile_range(blob, t0, min(T, t0 + 2), out=out)
+    assert np.array_equal(out, whole)
