@@ -12,6 +12,8 @@ import oracle
 from decode_tile_interleaved_amd import ep
 from decode_tile_interleaved_amd import workloads as W
 
+from cases import extreme_cases
+
 pytestmark = pytest.mark.gpu
 
 CASES = {
@@ -67,3 +69,15 @@ def test_device_raw_fallback_and_errors():
     with pytest.raises(ep.EPError) as e:
         ep.compress_device(W.gaussian(16, 64, 0.02, seed=3).cuda(), 20.0)
     assert e.value.code == ep.ERR_TARGET
+
+
+@pytest.mark.parametrize("name", list(extreme_cases()))
+def test_device_stream_at_format_extremes(name):
+    """The GPU encoder at the ends of the formats (tiny and huge BF16, FP16
+    near its maximum and subnormal, a short row, zero rows, an all-zero
+    matrix, a spike): the oracle's stream, byte for byte."""
+    x, target, fixed = extreme_cases()[name]
+    ref, rc, _ = oracle.compress(x, target, fixed_a=fixed)
+    dev = ep.compress_device(x.cuda(), target, fixed_scale=fixed)
+    assert dev.status == rc
+    assert np.array_equal(dev.blob, ref)

@@ -9,6 +9,8 @@ import oracle
 from decode_tile_interleaved_amd import ep
 from decode_tile_interleaved_amd import workloads as W
 
+from cases import extreme_cases
+
 pytestmark = pytest.mark.gpu
 
 
@@ -104,32 +106,7 @@ def test_fp16_padded_rounds_through_f32():
     assert bad.size == 0, f"{len(bad)} elements differ, first {bad[:4].tolist()}"
 
 
-def _extreme_cases():
-    g = torch.Generator().manual_seed(77)
-
-    def gauss(r, c, std, dtype):
-        return (torch.randn(r, c, generator=g) * std).to(dtype)
-    zero_row = gauss(48, 1000, 0.02, torch.bfloat16)
-    zero_row[5] = 0
-    spike = gauss(40, 777, 0.02, torch.bfloat16)
-    spike[3, 100] = 3.0e4
-    near_max = gauss(64, 1000, 8000.0, torch.float16)
-    near_max[::7, ::13] = 65504.0
-    near_max[1::7, 5::13] = -65504.0
-    # name: (matrix, target, fixed resolution or 0)
-    return {
-        "bf16_tiny_1e-38": (gauss(64, 1000, 1e-38, torch.bfloat16), 4.0, 0.0),
-        "bf16_huge_1e30": (gauss(64, 1000, 1e30, torch.bfloat16), 4.0, 0.0),
-        "fp16_near_max_coarse": (near_max, 4.0, 1.5),
-        "fp16_subnormal_inputs": (gauss(64, 1000, 3e-6, torch.float16), 4.0, 0.0),
-        "one_row_of_seven": (gauss(1, 7, 0.02, torch.bfloat16), 4.0, 0.1),
-        "one_zero_row": (zero_row, 4.0, 0.0),
-        "all_zero": (torch.zeros(32, 512, dtype=torch.bfloat16), 4.0, 0.0),
-        "one_spike_row": (spike, 3.0, 0.0),
-    }
-
-
-@pytest.mark.parametrize("name", list(_extreme_cases()))
+@pytest.mark.parametrize("name", list(extreme_cases()))
 def test_extreme_inputs(name):
     """Magnitudes at the ends of each format (f32 subnormal products, FP16
     values at its maximum reconstructed past it, FP16 subnormal inputs), a
@@ -137,7 +114,7 @@ def test_extreme_inputs(name):
     container) and a 10^6-sigma spike: the oracle's stream, decoded on the
     GPU, equals the oracle's decode exactly, and the host encoder writes the
     oracle's stream."""
-    x, target, fixed = _extreme_cases()[name]
+    x, target, fixed = extreme_cases()[name]
     blob, rc, _ = oracle.compress(x, target, fixed_a=fixed)
     host = ep.compress(x, target, fixed_scale=fixed)
     assert host.status == rc and np.array_equal(host.blob, blob)
