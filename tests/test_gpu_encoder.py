@@ -81,3 +81,34 @@ def test_device_stream_at_format_extremes(name):
     dev = ep.compress_device(x.cuda(), target, fixed_scale=fixed)
     assert dev.status == rc
     assert np.array_equal(dev.blob, ref)
+
+
+def _random_targets(n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    kinds = ["bf16", "fp16", "int8", "fp8"]
+    for i in range(n):
+        kind = kinds[i % 4]
+        rows, cols = int(rng.integers(16, 600)), int(rng.integers(16, 4000))
+        hi = 7.5 if kind in ("int8", "fp8") else 9.0
+        yield i, kind, rows, cols, round(float(rng.uniform(1.5, hi)), 3)
+
+
+@pytest.mark.parametrize("case", list(_random_targets(8, 31)), ids=lambda c: f"{c[1]}_{c[2]}x{c[3]}_t{c[4]}")
+def test_device_stream_random_targets(case):
+    """Seeded random shapes, containers and targets through rate selection:
+    the GPU encoder's stream equals the oracle's."""
+    i, kind, rows, cols, target = case
+    if kind in ("bf16", "fp16"):
+        x = W.rowscale_gaussian(rows, cols, 3100 + i, dtype=torch.bfloat16 if kind == "bf16" else torch.float16)
+    else:
+        x = W.absmax_codes(rows, cols, 3100 + i, kind)
+    try:
+        ref, rc, _ = oracle.compress(x, target)
+    except oracle.OracleError as e:  # a target this shape cannot reach: the device encoder must refuse it too
+        with pytest.raises(ep.EPError) as d:
+            ep.compress_device(x.cuda(), target)
+        assert d.value.code == e.rc
+        return
+    dev = ep.compress_device(x.cuda(), target)
+    assert dev.status == rc
+    assert np.array_equal(dev.blob, ref)

@@ -126,3 +126,38 @@ def test_extreme_inputs(name):
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{len(bad)} elements differ, first {bad[:4].tolist()}: " \
                           f"{[hex(int(got[tuple(i)])) for i in bad[:4]]} vs {[hex(int(ref[tuple(i)])) for i in bad[:4]]}"
+
+
+def _random_multitile(n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    kinds = ["bf16", "fp16", "int8", "fp8"]
+    for i in range(n):
+        kind = kinds[i % 4]
+        rows, cols = int(rng.integers(2100, 2600)), int(rng.integers(8100, 9000))
+        hi = 7.5 if kind in ("int8", "fp8") else 8.0
+        yield i, kind, rows, cols, round(float(rng.uniform(1.0, hi)), 3)
+
+
+@pytest.mark.parametrize("case", list(_random_multitile(4, 55)), ids=lambda c: f"{c[1]}_{c[2]}x{c[3]}_t{c[4]}")
+def test_random_multitile_streams(case):
+    """Seeded random shapes of 2100-2600 x 8100-9000 (more than one round of
+    workgroups: the multi-tile kernel, uneven tile counts per CU, padded
+    columns), containers and targets: symbols and values equal the oracle's."""
+    i, kind, rows, cols, target = case
+    if kind in ("bf16", "fp16"):
+        x = W.t4_outliers(rows, cols, 5500 + i, dtype=torch.bfloat16 if kind == "bf16" else torch.float16)
+    else:
+        x = W.absmax_codes(rows, cols, 5500 + i, kind)
+    blob, rc, _ = oracle.compress(x, target)
+    p = ep.from_blob(blob).to("cuda")
+    y = ep.decompress(p)
+    torch.cuda.synchronize()
+    got = y.cpu().view(torch.int16 if x.element_size() == 2 else torch.int8).numpy().view(np.uint8)
+    if rc == oracle.WARN_RAW:  # outliers beyond the stream's value range at this rate: raw container
+        assert np.array_equal(got, x.view(torch.int16 if x.element_size() == 2 else torch.int8).numpy().view(np.uint8))
+        return
+    assert rc == 0
+    v = ep.decode_symbols(p)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.cpu().numpy(), oracle.decode_symbols(blob))
+    assert np.array_equal(got, oracle.decompress_raw(blob).view(np.uint8))
