@@ -120,7 +120,9 @@ __device__ __forceinline__ uint32_t lds_u8(uint32_t byte) {
   return *(__attribute__((address_space(3))) const uint8_t *)(uintptr_t)byte;
 }
 
-// hides a value from constant folding so that address arithmetic stays one v_and_or_b32
+// hides a value from the compiler's folding: a table address stays one
+// v_and_or_b32 with the context base in the lookup's offset, and an f32
+// product stays rounded before it is narrowed
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   asm volatile("" : "+v"(v));
   return v;
