@@ -598,7 +598,19 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   const uint32_t nwaves = A.waves;
 
   // ---- 1. global loads, all unconditional so that each wait is exact ----
-  // the first 256 frequencies of this wave's first context (first: they need
+  const uint32_t tile = blockIdx.x * nwaves + wave;
+  const bool has_tile = tile < A.n_tiles;
+  const uint32_t tc = has_tile ? tile : A.n_tiles - 1u;  // waves without a tile load a valid one and drop it
+  // The workgroup's tiles are consecutive, so their words are one range of
+  // the stream.  The tile offsets the wave needs come first, from one vector
+  // load (lane 0: its tile's first word, lane 1: the tile's end, lanes 2 and
+  // 3: the workgroup's range): scalar loads would share their counter with
+  // the table build's LDS accesses, whose waits would then wait for them too.
+  const uint32_t g0 = blockIdx.x * nwaves;
+  const uint32_t gend = g0 + nwaves < A.n_tiles ? g0 + nwaves : A.n_tiles;
+  const uint32_t oi = lane == 0u ? tc : lane == 1u ? tc + 1u : lane == 2u ? g0 : gend;
+  const uint32_t ov = reinterpret_cast<const uint32_t *>(A.blob + A.off_tile_offsets)[oi];
+  // the first 256 frequencies of this wave's first context (they need
   // nothing but the kernel arguments)
   const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
   const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
@@ -612,9 +624,6 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
       fpre[i] = s < n0 ? v : 0u;
     }
   }
-  const uint32_t tile = blockIdx.x * nwaves + wave;
-  const bool has_tile = tile < A.n_tiles;
-  const uint32_t tc = has_tile ? tile : A.n_tiles - 1u;  // waves without a tile load a valid one and drop it
   const uint32_t x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tc * 64u + lane];
   float gs[16];
   {
@@ -628,22 +637,19 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // the loads above go out before anything waits
-  // the tile's word range, read through the constant address space so that
-  // the loads are scalar and their wait leaves the vector loads above alone
-  typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
-  const cptr_u32 toff = (cptr_u32)(A.blob + A.off_tile_offsets);
-  const uint32_t w_begin = toff[tc], w_end = toff[tc + 1u];
-  // The workgroup's tiles are consecutive, so their words are one range of the
-  // stream: the last wave copies it into LDS with global_load_lds (1 KB per
-  // instruction, lanes past the end re-read the last 16 bytes).  Its waits
-  // are conservative about LDS written this way; the other waves never touch
-  // these loads, so the table build keeps exact waits.
-  const uint32_t g0 = blockIdx.x * nwaves;
-  const uint64_t gbyte0 = (A.off_words + 2ull * toff[g0]) & ~15ull;  // 16-byte aligned start of the range
-  const uint32_t wt = A.words_off + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);  // LDS address of this tile's first word
+  // ---- 2. one wave per context: the tables --------------------------------
+  build_tables<WIDE>(A, lds, wave, lane, nwaves, fpre);
+
+  // The last wave (which builds no table when the workgroup has eight waves)
+  // copies the workgroup's words into LDS with global_load_lds (1 KB per
+  // instruction, lanes past the end re-read the last 16 bytes).  This comes
+  // after the table build: where the copying branch rejoins, the compiler
+  // waits for every load, so before the build that wait would hold every
+  // builder until its tile's states and scales had landed.
   if (wave == nwaves - 1u) {
-    const uint32_t gend = g0 + nwaves < A.n_tiles ? g0 + nwaves : A.n_tiles;
-    const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * toff[gend] + 15ull) & ~15ull) - gbyte0) >> 4);
+    const uint64_t gbyte0 = (A.off_words + 2ull * __builtin_amdgcn_readlane(ov, 2)) & ~15ull;
+    const uint32_t nchunks =
+        (uint32_t)((((A.off_words + 2ull * __builtin_amdgcn_readlane(ov, 3) + 15ull) & ~15ull) - gbyte0) >> 4);
     const gbyte_t src = (gbyte_t)(A.blob + gbyte0);
     // whole kilobytes first: no per-lane clamp, so each load issues right
     // after the last one
@@ -658,8 +664,6 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
     }
   }
 
-  // ---- 2. one wave per context: the tables --------------------------------
-  build_tables<WIDE>(A, lds, wave, lane, nwaves, fpre);
   __builtin_amdgcn_s_waitcnt(0);  // the loader's words have landed in LDS
   __syncthreads();
 
@@ -667,6 +671,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   if (!has_tile) return;
   const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
   const uint32_t X = x0 << 3;
+  const uint32_t w_begin = __builtin_amdgcn_readlane(ov, 0), w_end = __builtin_amdgcn_readlane(ov, 1);
+  const uint64_t gbyte0 = (A.off_words + 2ull * __builtin_amdgcn_readlane(ov, 2)) & ~15ull;  // 16-byte aligned start of the range
+  const uint32_t wt = A.words_off + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);  // LDS address of this tile's first word
   const uint32_t we = wt + 2u * (w_end - w_begin);
   if (n == 1024u)
     decode_tile<OUT, WIDE, PADDED, false>(A, wt, we, X, tile, n, gs, lane);
