@@ -203,7 +203,8 @@ __device__ __forceinline__ void table_read(uint32_t a, uint32_t &d0, uint32_t &d
 // one rANS decode step of every active lane: decodes this step's symbol,
 // issues the lookup for the next step (context base BASE + nb) and, in
 // refilling lanes, the read of the following word; returns this step's entry.
-template <bool WIDE, uint32_t BASE>
+// BOP3 forms the lookup address with v_bitop3 instead of v_and_or.
+template <bool WIDE, uint32_t BASE, bool BOP3>
 __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active) {
   const uint32_t e = L.d0;
   uint32_t x;
@@ -220,8 +221,12 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   const bool need = active && x < 0x10000u;
   const uint64_t m = __ballot(need);
   const uint32_t X = select_mask(m, x, (x << 16) | r8);  // next state: refilling lanes shift the held word in
-  // opaque: keeps BASE in the lookup's offset instead of an add into nb
-  table_read<BASE>(opaque((X & 0x1ff8u) | nb), L.d0, L.d1);
+  // the address (X & 0x1ff8) | nb; opaque keeps BASE in the lookup's offset
+  // instead of an add into nb
+  if constexpr (BOP3)
+    table_read<BASE>(opaque(__builtin_amdgcn_bitop3_b32(X, 0x1ff8u, nb, 0xea)), L.d0, L.d1);  // truth table of (a & b) | c
+  else
+    table_read<BASE>(opaque((X & 0x1ff8u) | nb), L.d0, L.d1);
   __builtin_amdgcn_sched_barrier(0);  // the next lookup goes out before the refill
   if (need) {  // refilling lanes only: read the following word
     L.r = lds_u16(L.p + 2u);
@@ -361,7 +366,14 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
 // decodes one tile; PARTIAL handles the last tile of a stream (n < 1024).
 // wb and we are the LDS byte addresses of the tile's first word and of its
 // end; X is 8 * the start state.
-template <int OUT, bool WIDE, bool PADDED, bool PARTIAL>
+//
+// BOP3: the lookup address by v_bitop3 rather than v_and_or.  On gfx950 the
+// first issues faster (about 1.9 against 2.8 SIMD cycles per instruction with
+// four waves per SIMD) at the same dependent latency; it measured 1.5-2%
+// faster in the single-round kernel and for 8-bit outputs, but 1-2.5% slower
+// for 16-bit outputs in the multi-tile kernel, whose code differs in that
+// instruction alone, so each kernel takes the faster form.
+template <int OUT, bool WIDE, bool PADDED, bool PARTIAL, bool BOP3>
 __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t we, uint32_t X, uint32_t tile,
                                             uint32_t n, const float (&gs)[16], uint32_t lane) {
   Lane L;
@@ -384,17 +396,17 @@ __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t
     uint32_t e[8];
     // C_b at LDS context 1 + b; the coset bit is in the entry of coordinate 0
     const uint32_t cb = __builtin_amdgcn_ubfe(L.d0, kBitB, 1u) << 13;
-    e[0] = rans_step<WIDE, kC>(L, cb, act);
+    e[0] = rans_step<WIDE, kC, BOP3>(L, cb, act);
 #pragma unroll
-    for (int j = 1; j < 6; ++j) e[j] = rans_step<WIDE, kC>(L, cb, act);
+    for (int j = 1; j < 6; ++j) e[j] = rans_step<WIDE, kC, BOP3>(L, cb, act);
     // the XOR's copy of v's bit 0 is b (all eight coordinates share it), its
     // copy of bit 1 is p
     uint32_t acc = __builtin_amdgcn_bitop3_b32(e[0], e[1], e[2], 0x96);
     acc = __builtin_amdgcn_bitop3_b32(acc, e[3], e[4], 0x96);
     acc = __builtin_amdgcn_bitop3_b32(acc, e[5], L.d0, 0x96);
     const uint32_t eb = __builtin_amdgcn_ubfe(acc, kBitB, 2u) << 13;
-    e[6] = rans_step<WIDE, kE>(L, eb, act);
-    e[7] = rans_step<WIDE, 0u>(L, 0u, act);
+    e[6] = rans_step<WIDE, kE, BOP3>(L, eb, act);
+    e[7] = rans_step<WIDE, 0u, BOP3>(L, 0u, act);
     if (act) emit_vector<OUT, WIDE, PADDED>(A, opaque_s(tile_out + s * kStepBytes), tile, s * 64u + lane, lane, e, gs[s]);
   }
 }
@@ -543,6 +555,7 @@ __global__ void __launch_bounds__(64 * kMaxTileWaves) decode_waves_kernel(Args A
   const uint32_t k = A.waves;
   const uint32_t end = wg_first(A, blockIdx.x + 1u);
   const uint32_t buf = A.words_off + wave * A.wbuf;  // this wave's word buffer
+  constexpr bool kNarrowOut = OUT == EP_FP8_E4M3FN || OUT == EP_INT8;  // lookup address by v_bitop3
 
   // ---- 1. the first context's frequencies ----------------------------------
   const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
@@ -577,9 +590,9 @@ __global__ void __launch_bounds__(64 * kMaxTileWaves) decode_waves_kernel(Args A
     __builtin_amdgcn_s_waitcnt(0);  // the tile's states, scales and words have landed
     const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
     if (n == 1024u)
-      decode_tile<OUT, WIDE, PADDED, false>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
+      decode_tile<OUT, WIDE, PADDED, false, kNarrowOut>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
     else
-      decode_tile<OUT, WIDE, PADDED, true>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
+      decode_tile<OUT, WIDE, PADDED, true, kNarrowOut>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
     tile += k;
     if (tile < end) {
       __builtin_amdgcn_s_waitcnt(0);  // every read of the finished tile's words is done before they are overwritten
@@ -676,9 +689,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   const uint32_t wt = A.words_off + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);  // LDS address of this tile's first word
   const uint32_t we = wt + 2u * (w_end - w_begin);
   if (n == 1024u)
-    decode_tile<OUT, WIDE, PADDED, false>(A, wt, we, X, tile, n, gs, lane);
+    decode_tile<OUT, WIDE, PADDED, false, true>(A, wt, we, X, tile, n, gs, lane);
   else
-    decode_tile<OUT, WIDE, PADDED, true>(A, wt, we, X, tile, n, gs, lane);
+    decode_tile<OUT, WIDE, PADDED, true, true>(A, wt, we, X, tile, n, gs, lane);
 }
 
 typedef void (*KernelFn)(Args);
