@@ -522,10 +522,10 @@ int encode_at(const Problem &P, double a, double target, Blob &blob, std::string
   if (rc < 0) return rc;
   if (rc == 1) return EP_WARN_RAW;
   Tables tb;
-  if (!build_tables(hist, tb)) {
-    err = "frequency normalization failed";
-    return EP_ERR_TARGET;
-  }
+  // a context that needs more than 2^10 symbols cannot be coded: an encoding
+  // failure, like values outside the stream's range (the sampled estimate may
+  // have seen fewer symbols than the whole matrix holds)
+  if (!build_tables(hist, tb)) return EP_WARN_RAW;
   std::vector<uint32_t> states, tile_first;
   rc = P.be->encode_tiles(g, tb, states, tile_first, err);
   if (rc < 0) return rc;
@@ -682,7 +682,7 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, do
   if (rc == EP_WARN_RAW) {
     const int rr = raw_stream(P, target, blob, err);
     if (rr < 0) return rr;
-    err = "lattice coding failed (values out of range or no gain); stored the raw container";
+    err = "lattice coding failed (values out of range, a context beyond 2^10 symbols, or no gain); stored the raw container";
   }
   return rc;
 }

@@ -557,6 +557,10 @@ static int compress_at(const double *x, const or_geom *g, int dtype, double a, d
     for (int j = 0; j < 8; j++) h->cnt[ctx[j]][sym[j] + OR_SYM_OFF]++;
   }
   rc = tables_from_hist(h, g->prob_bits, &t);
+  /* a context that needs more than 2^prob_bits symbols cannot be coded: an
+   * encoding failure, like values outside the stream's range (the sampled
+   * estimate may have seen fewer symbols than the whole matrix holds) */
+  if (rc == OR_ERR_TARGET) rc = OR_WARN_RAW;
   if (rc) goto done;
   for (int64_t tile = 0; tile < g->T; tile++) {
     if (ws.n > 0xffffffffu) { rc = OR_ERR_SHAPE; goto done; }

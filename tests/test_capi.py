@@ -132,6 +132,16 @@ def test_raw_fallback_matches_oracle():
     assert ep.blob_info(p.blob)["method"] == 1
 
 
+def test_alphabet_overflow_fallback_matches_oracle():
+    """A context beyond 2^10 symbols at the chosen resolution: the product
+    warns and stores the raw container, byte for byte as the oracle does."""
+    x = W.rowscale_gaussian(1024, 4096, 6100)
+    p = ep.compress(x, 9.0)
+    blob, rc, _ = oracle.compress(x, 9.0)
+    assert p.status == ep.WARN_RAW == rc
+    assert np.array_equal(p.blob, blob)
+
+
 def test_device_compress_argument_errors_before_any_device_work():
     """ep_compress_device checks its arguments on the host before touching a
     device, so these run without a GPU."""

@@ -71,6 +71,16 @@ def test_device_raw_fallback_and_errors():
     assert e.value.code == ep.ERR_TARGET
 
 
+def test_device_alphabet_overflow_falls_back_to_raw():
+    """At 9.0 bpp a context of this matrix needs more than 2^10 symbols: the
+    GPU encoder warns and stores the raw container, as the oracle does."""
+    x = W.rowscale_gaussian(1024, 4096, 6100)
+    ref, rc, _ = oracle.compress(x, 9.0)
+    assert rc == oracle.WARN_RAW
+    p = ep.compress_device(x.cuda(), 9.0)
+    assert p.status == ep.WARN_RAW and np.array_equal(p.blob, ref)
+
+
 @pytest.mark.parametrize("name", list(extreme_cases()))
 def test_device_stream_at_format_extremes(name):
     """The GPU encoder at the ends of the formats (tiny and huge BF16, FP16

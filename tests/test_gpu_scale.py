@@ -161,3 +161,23 @@ def test_random_multitile_streams(case):
     torch.cuda.synchronize()
     assert np.array_equal(v.cpu().numpy(), oracle.decode_symbols(blob))
     assert np.array_equal(got, oracle.decompress_raw(blob).view(np.uint8))
+
+
+def test_multitile_lds_limited_waves():
+    """A 4096 x 10240 BF16 stream at 8.0 bpp (wide tables): a tile's words
+    take about 8 KB, so beside the 56 KB of tables the LDS holds fewer than
+    16 word buffers, and each CU's run of 20 tiles takes two passes of its
+    waves.  Symbols and values equal the oracle's."""
+    x = W.rowscale_gaussian(4096, 10240, 6100)
+    blob, rc, _ = oracle.compress(x, 8.0)
+    assert rc == 0
+    inf = oracle.info(blob)
+    tile_bytes = 2 * inf["n_words"] / inf["n_tiles"]
+    assert 16 * tile_bytes + 7 * 8192 > 160 * 1024  # sixteen buffers cannot fit
+    assert inf["n_tiles"] > 16 * 256  # more tiles per CU than waves (256 CUs)
+    p = ep.from_blob(blob).to("cuda")
+    v = ep.decode_symbols(p)
+    y = ep.decompress(p)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.cpu().numpy(), oracle.decode_symbols(blob))
+    assert np.array_equal(y.cpu().view(torch.int16).numpy().view(np.uint16), oracle.decompress_raw(blob).view(np.uint16))

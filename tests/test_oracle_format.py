@@ -19,6 +19,7 @@ import torch
 
 import oracle
 from decode_tile_interleaved_amd import workloads as W
+from decode_tile_interleaved_amd import workloads as W
 
 PAGES = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")))
 E8C = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "e8_constants.json")))
@@ -167,6 +168,22 @@ def test_raw_fallback_when_values_overflow():
     assert oracle.info(blob)["method"] == 1
     assert torch.equal(oracle.decompress(blob), t)
     assert 8 * blob.size / t.numel() >= 16
+
+
+def test_raw_fallback_when_a_context_overflows():
+    """At 9.0 bpp a 1024 x 4096 Gaussian matrix needs more than 2^10 symbols
+    in a context of the whole matrix, although the sampled estimate sees fewer
+    and picks that resolution: the tables cannot be normalized, which is an
+    encoding failure, so the oracle warns and stores the raw container (API
+    reference, "compress")."""
+    x = W.rowscale_gaussian(1024, 4096, 6100)
+    blob, rc, _ = oracle.compress(x, 9.0)
+    assert rc == oracle.WARN_RAW
+    assert oracle.info(blob)["method"] == 1
+    assert torch.equal(oracle.decompress(blob), x)
+    # just below, the same matrix still codes as a lattice stream
+    blob, rc, _ = oracle.compress(x, 8.5)
+    assert rc == 0 and abs(8 * blob.size / x.numel() - 8.5) <= 0.02 * 8.5
 
 
 def test_conversions_match_torch():
