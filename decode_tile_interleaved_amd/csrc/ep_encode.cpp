@@ -477,8 +477,9 @@ double estimate_bpp(const Problem &P, double a, int64_t S, std::string &err, int
       if (n) info += (double)n * ((double)kProbBits - std::log2((double)tb.freq[c][i]));
     }
   const double scale = S >= P.S.n_vec ? 1.0 : (double)P.S.n_vec / (double)S;
-  double bits = info * scale + kStateBits * (double)(kStatesPerTile * P.S.tiles) +
-                8.0 * (double)metadata_bytes(P.S, tb.total_symbols());
+  const double n_states = (double)(kStatesPerTile * P.S.tiles);
+  const double asymptotic = info * scale + kStateBits * n_states, least = kStateMinBits * n_states;
+  double bits = (asymptotic > least ? asymptotic : least) + 8.0 * (double)metadata_bytes(P.S, tb.total_symbols());
   return bits / ((double)P.S.R * (double)P.S.C);
 }
 
@@ -645,9 +646,10 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, do
     return EP_ERR_TARGET;
   }
   double a = fixed_a;
+  double goal = target;  // the sampled estimate the last selection aimed at
   if (!(fixed_a > 0.0)) {
     const double floor_bpp =
-        (kStateBits * (double)(kStatesPerTile * S.tiles) + 8.0 * (double)metadata_bytes(S, kContexts)) /
+        (kStateMinBits * (double)(kStatesPerTile * S.tiles) + 8.0 * (double)metadata_bytes(S, kContexts)) /
         ((double)S.R * (double)S.C);
     if (target < 1.02 * floor_bpp) {
       err = "target_bpp below this stream's fixed per-tile overhead (" + std::to_string(floor_bpp) + " bpp)";
@@ -666,17 +668,48 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, do
     // The sample misses rare symbols that the full tables must still give a
     // frequency of at least 1.  One histogram of the whole matrix at the chosen
     // scale (no entropy coding) measures that bias; beyond 0.5% the sampled
-    // bisection runs again toward the target minus the bias.
-    const double full = estimate_bpp(P, a, S.n_vec, err, status);
+    // bisection runs again toward the target minus the bias.  The bias changes
+    // with the scale, so this repeats (at most three bisections) until the
+    // whole-matrix estimate is within 0.5% of the target.
+    double full = estimate_bpp(P, a, S.n_vec, err, status);
     if (status < 0) return status;
     if (std::isfinite(full) && !(std::fabs(full - target) <= 0.005 * target)) {
-      double ignored;
-      a = choose_scale(P, target - (full - closest), &ignored, err, status);
-      if (status < 0) return status;
+      double est = closest;
+      for (int it = 0; it < 3; ++it) {
+        goal = target - (full - est);
+        a = choose_scale(P, goal, &est, err, status);
+        if (status < 0) return status;
+        if (it == 2) break;
+        full = estimate_bpp(P, a, S.n_vec, err, status);
+        if (status < 0) return status;
+        if (!std::isfinite(full) || std::fabs(full - target) <= 0.005 * target) break;
+      }
     }
   }
   int rc = encode_at(P, a, target, blob, err);
   if (rc < 0) return rc;
+  // The estimate's state part is exact only at its extremes: at low rates a
+  // state's cost steps by a whole word, so the encoded size can still miss the
+  // target.  Then the selection aims again, moved by the encoded size's miss,
+  // at most twice, and the stream closer to the target is kept.
+  if (rc == EP_OK && !(fixed_a > 0.0)) {
+    const double numel = (double)S.R * (double)S.C;
+    for (int it = 0; it < 2; ++it) {
+      const double actual = 8.0 * (double)blob.size() / numel;
+      if (std::fabs(actual - target) <= 0.01 * target) break;
+      double est;
+      int status = 0;
+      goal -= actual - target;
+      const double a2 = choose_scale(P, goal, &est, err, status);
+      if (status < 0) return status;
+      Blob b2;
+      const int rc2 = encode_at(P, a2, target, b2, err);
+      if (rc2 < 0) return rc2;
+      if (rc2 != EP_OK) break;
+      if (!(std::fabs(8.0 * (double)b2.size() / numel - target) < std::fabs(actual - target))) break;
+      blob.swap(b2);
+    }
+  }
   const uint64_t raw_total = kHeaderBytes + align16((uint64_t)S.R * (uint64_t)S.C * elem_bytes(S.dtype));
   if (rc == EP_OK && !(fixed_a > 0.0) && blob.size() >= raw_total) rc = EP_WARN_RAW;
   if (rc == EP_WARN_RAW) {

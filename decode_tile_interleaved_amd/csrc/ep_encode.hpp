@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "ep.h"
@@ -39,6 +40,10 @@ class Blob {
   }
   uint8_t *data() { return p_; }
   size_t size() const { return n_; }
+  void swap(Blob &o) {
+    std::swap(p_, o.p_);
+    std::swap(n_, o.n_);
+  }
   uint8_t *release() {
     uint8_t *p = p_;
     p_ = nullptr;

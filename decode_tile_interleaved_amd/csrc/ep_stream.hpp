@@ -35,6 +35,10 @@ constexpr int kCountWords = 32;            // words of per-state count bytes at 
 // estimate counts them: the fixed final state L (13), the unused high bits of
 // the stored start state (11 on average) and the count byte (8)
 constexpr double kStateBits = 32.0;
+// A state absorbs up to 16 bits of information before it emits a word, so it
+// never costs less than its stored 32 bits and count byte: the estimate's
+// state part is max(40 * states, information + 32 * states).
+constexpr double kStateMinBits = 40.0;
 constexpr int kTileVecs = 1024;            // E8 vectors (8 coordinates) per tile
 constexpr int kStatesPerTile = 64;         // interleaved rANS states per tile (2 count bytes per word)
 constexpr int kValueMin = -2048, kValueMax = 2047;  // lattice coordinates the stream can hold (12-bit field)

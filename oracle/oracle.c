@@ -46,6 +46,7 @@
 #define OR_MAGIC 0x314B5045u /* "EPK1" little-endian */
 #define OR_VERSION 1
 #define OR_STATE_BITS 32.0  /* estimated stream bits per rANS state beyond its symbols' information */
+#define OR_STATE_MIN_BITS 40.0 /* stored bits of a state that emits no word: its 32-bit state and count byte */
 #define OR_STATE_L 8192u     /* rANS lower state bound L = 2^13; states lie in [L, 2^29); words are 16 bits */
 
 static int esize_of(int dt) { return (dt == OR_BF16 || dt == OR_FP16) ? 2 : 1; }
@@ -590,9 +591,18 @@ done:
 /*        + 8 * (header, tables, scales, tile offsets).                      */
 /* 32 bits per state: 13 for the fixed final state L, on average 11 unused   */
 /* high bits of the stored 32-bit start state (log-uniform in [2^13, 2^29)), */
+/* A state absorbs up to 16 bits of information before it emits a word, so  */
+/* it never costs less than its 32 stored bits and count byte: the state     */
+/* part of the estimate is max(40 * states, information + 32 * states).      */
 /* and the state's 8-bit word count.  Out-of-range lattice values give +inf. */
 /* ------------------------------------------------------------------------ */
 #define OR_SAMPLE_VECS 65536
+
+/* information bits plus the states' overhead, for n states */
+static double state_part(double info, double n) {
+  const double asymptotic = info + OR_STATE_BITS * n, least = OR_STATE_MIN_BITS * n;
+  return asymptotic > least ? asymptotic : least;
+}
 
 double or_estimate_bpp_rows(const double *x, const double *rms, const or_geom *g, double a) {
   int64_t S = g->n_vec < OR_SAMPLE_VECS ? g->n_vec : OR_SAMPLE_VECS;
@@ -619,7 +629,7 @@ double or_estimate_bpp_rows(const double *x, const double *rms, const or_geom *g
       uint64_t cnt = (t.smin[c] + s + OR_SYM_OFF < OR_SYM_SPAN) ? h->cnt[c][t.smin[c] + s + OR_SYM_OFF] : 0;
       if (cnt) info += (double)cnt * ((double)g->prob_bits - log2((double)t.freq[c][s]));
     }
-  double bits = info * ((double)g->n_vec / (double)S) + OR_STATE_BITS * (double)(g->S * g->T) +
+  double bits = state_part(info * ((double)g->n_vec / (double)S), (double)(g->S * g->T)) +
                 8.0 * (double)meta_bytes(g, tables_total_nsym(&t));
   tables_free(&t);
   free(h);
@@ -653,7 +663,7 @@ static double estimate_bpp_full(const double *x, const or_geom *g, double a) {
         uint64_t cnt = (t.smin[c] + s + OR_SYM_OFF < OR_SYM_SPAN) ? h->cnt[c][t.smin[c] + s + OR_SYM_OFF] : 0;
         if (cnt) info += (double)cnt * ((double)g->prob_bits - log2((double)t.freq[c][s]));
       }
-    double bits = info + OR_STATE_BITS * (double)(g->S * g->T) + 8.0 * (double)meta_bytes(g, tables_total_nsym(&t));
+    double bits = state_part(info, (double)(g->S * g->T)) + 8.0 * (double)meta_bytes(g, tables_total_nsym(&t));
     result = bits / ((double)g->R * (double)g->C);
   }
 done:
@@ -761,21 +771,24 @@ int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, in
   or_geom g;
   geom_init(&g, R, C, n_states, prob_bits);
   double a = fixed_a;
+  double *rms = NULL;         /* row RMS, kept for every rate selection below */
+  double goal = target;       /* the sampled estimate the last selection aimed at */
+  or_sel_ctx sc = {x, NULL, &g, dtype, target};
   if (!(fixed_a > 0.0)) {
-    double *rms = (double *)malloc(sizeof(double) * (size_t)R);
+    rms = (double *)malloc(sizeof(double) * (size_t)R);
     if (!rms) return OR_ERR_NOMEM;
     for (int64_t r = 0; r < R; r++) rms[r] = row_rms(x + r * C, C);
-    or_sel_ctx sc = {x, rms, &g, dtype, target};
+    sc.rms = rms;
     /* targets below the fixed per-tile overhead cannot be met */
-    double floor_bpp = (OR_STATE_BITS * (double)(g.S * g.T) + 8.0 * (double)meta_bytes(&g, OR_NCTX)) /
+    double floor_bpp = (OR_STATE_MIN_BITS * (double)(g.S * g.T) + 8.0 * (double)meta_bytes(&g, OR_NCTX)) /
                        ((double)R * (double)C);
     if (target < 1.02 * floor_bpp) { free(rms); return OR_ERR_TARGET; }
     double best_est = INFINITY;
     a = select_scale(exact_select ? rate_exact : rate_sampled, &sc, target, &best_est);
-    free(rms);
     /* no resolution reaches the target within 2% (the lattice values would
      * leave the stream's value range first): an encoding failure */
     if (!(fabs(best_est - target) <= 0.02 * target)) {
+      free(rms);
       if (a_out) *a_out = a;
       if (!src_bytes) return OR_ERR_ARG;
       rc = write_raw_blob(R, C, dtype, target, src_bytes, blob, nbytes);
@@ -784,22 +797,49 @@ int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, in
     /* the sample misses rare symbols that the full tables must still give a
      * frequency of at least 1; one histogram of the whole matrix at the chosen
      * scale (no entropy coding) measures that bias, and when it exceeds 0.5%
-     * the sampled bisection runs again toward the target minus the bias */
+     * the sampled bisection runs again toward the target minus the bias.  The
+     * bias changes with the scale, so this repeats (at most three bisections)
+     * until the whole-matrix estimate is within 0.5% of the target. */
     if (!exact_select) {
       double full = estimate_bpp_full(x, &g, a);
       if (isfinite(full) && !(fabs(full - target) <= 0.005 * target)) {
-        double ignored;
-        double *rms2 = (double *)malloc(sizeof(double) * (size_t)R);
-        if (!rms2) return OR_ERR_NOMEM;
-        for (int64_t r = 0; r < R; r++) rms2[r] = row_rms(x + r * C, C);
-        or_sel_ctx sc2 = {x, rms2, &g, dtype, target};
-        a = select_scale(rate_sampled, &sc2, target - (full - best_est), &ignored);
-        free(rms2);
+        double est = best_est;
+        for (int it = 0; it < 3; it++) {
+          goal = target - (full - est);
+          a = select_scale(rate_sampled, &sc, goal, &est);
+          if (it == 2) break;
+          full = estimate_bpp_full(x, &g, a);
+          if (!isfinite(full) || fabs(full - target) <= 0.005 * target) break;
+        }
       }
     }
   }
   if (a_out) *a_out = a;
   rc = compress_at(x, &g, dtype, a, target, blob, nbytes);
+  /* The estimate's state part is exact only at its extremes: at low rates a
+   * state's cost steps by a whole word, so the encoded size can still miss the
+   * target.  Then the selection aims again, moved by the encoded size's miss,
+   * at most twice, and the stream closer to the target is kept. */
+  if (rc == OR_OK && rms && !exact_select) {
+    const double numel = (double)R * (double)C;
+    for (int it = 0; it < 2; it++) {
+      const double actual = 8.0 * (double)*nbytes / numel;
+      if (fabs(actual - target) <= 0.01 * target) break;
+      double est;
+      goal -= actual - target;
+      const double a2 = select_scale(rate_sampled, &sc, goal, &est);
+      uint8_t *b2 = NULL;
+      size_t n2 = 0;
+      if (compress_at(x, &g, dtype, a2, target, &b2, &n2) != OR_OK) { free(b2); break; }
+      if (!(fabs(8.0 * (double)n2 / numel - target) < fabs(actual - target))) { free(b2); break; }
+      free(*blob);
+      *blob = b2;
+      *nbytes = n2;
+      a = a2;
+      if (a_out) *a_out = a;
+    }
+  }
+  free(rms);
   uint64_t raw_total = OR_HDR + pad16((uint64_t)R * (uint64_t)C * (uint64_t)esize_of(dtype));
   /* with the resolution chosen from the target, a lattice stream no smaller
    * than the raw container is an encoding failure; a fixed resolution keeps

@@ -122,3 +122,19 @@ def test_device_stream_random_targets(case):
     dev = ep.compress_device(x.cuda(), target)
     assert dev.status == rc
     assert np.array_equal(dev.blob, ref)
+
+
+@pytest.mark.parametrize("target", [0.36, 0.4, 7.0])
+def test_device_stream_rate_corrections(target):
+    """Targets where the rate selection corrects itself: at 0.36 and 0.4 bpp
+    from the encoded size (a state's cost steps by a whole word there), at
+    7.0 bpp on heavy tails by repeated whole-matrix bias corrections.  The
+    GPU encoder's stream equals the oracle's."""
+    if target < 1.0:
+        x = W.rowscale_gaussian(512, 4096, 7001)
+    else:
+        x = W.t4_outliers(384, 6144, 7002, dtype=torch.bfloat16)
+    ref, rc, _ = oracle.compress(x, target)
+    p = ep.compress_device(x.cuda(), target)
+    assert p.status == rc == 0 and np.array_equal(p.blob, ref)
+    assert abs(8 * ref.size / x.numel() - target) <= 0.02 * target
