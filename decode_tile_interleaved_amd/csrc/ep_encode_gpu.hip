@@ -65,37 +65,41 @@ struct Shape {
   int64_t R, C, C8, vpr, n_vec, tiles;
 };
 
-// one thread per row: sum of squares in column order, and whether every
-// element is finite.  VEC: rows start on 16-byte boundaries and hold whole
-// 16-byte pieces, read one piece per load (the sum still runs element by
-// element, in column order).
-template <bool VEC>
-__global__ void row_sums_kernel(Shape S, double *sums, uint32_t *nonfinite) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= S.R) return;
+// One wave per row: the sum of squares in column order, and whether every
+// element is finite.  The lanes widen and square a chunk of the row into LDS
+// (the squares are the same wherever they are computed), then lane 0 adds
+// them in column order, so the f64 sum is the host's, add for add.
+constexpr int kSumChunk = 2048;  // f64 squares staged per pass (16 KB of LDS)
+
+__global__ void __launch_bounds__(64) row_sums_kernel(Shape S, double *sums, uint32_t *nonfinite) {
+  __shared__ double sq[kSumChunk];
+  const int64_t r = blockIdx.x;
+  const uint32_t lane = threadIdx.x;
   double acc = 0.0;
   bool bad = false;
-  if (VEC) {
-    const uint32_t eb = S.dtype <= EP_FP16 ? 2u : 1u, per = 16u / eb;
-    const uint4 *row = (const uint4 *)((const uint8_t *)S.src + (uint64_t)r * (uint64_t)S.C * eb);
-    for (int64_t i = 0; i < S.C / per; ++i) {
-      const uint4 q = row[i];
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-      for (uint32_t k = 0; k < per; ++k) {
-        const uint32_t bits = eb == 2u ? (w[k >> 1] >> (16u * (k & 1u))) & 0xffffu : (w[k >> 2] >> (8u * (k & 3u))) & 0xffu;
-        const double x = widen_bits(bits, S.dtype);
-        bad |= !isfinite(x);
-        acc += x * x;
-      }
-    }
-  } else {
-    for (int64_t c = 0; c < S.C; ++c) {
-      const double x = widen_d(S.src, S.dtype, r * S.C + c);
+  for (int64_t c0 = 0; c0 < S.C; c0 += kSumChunk) {
+    const int64_t n = S.C - c0 < kSumChunk ? S.C - c0 : kSumChunk;
+    for (int64_t j = lane; j < n; j += 64) {
+      const double x = widen_d(S.src, S.dtype, r * S.C + c0 + j);
       bad |= !isfinite(x);
-      acc += x * x;
+      sq[j] = x * x;
     }
+    __syncthreads();
+    if (lane == 0) {
+      // whole groups of 16 first, so that their LDS reads go out together
+      int64_t j = 0;
+      for (; j + 16 <= n; j += 16) {
+        double v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = sq[j + u];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc += v[u];
+      }
+      for (; j < n; ++j) acc += sq[j];
+    }
+    __syncthreads();  // the squares are read before the next chunk overwrites them
   }
-  sums[r] = acc;
+  if (lane == 0) sums[r] = acc;
   if (bad) atomicOr(nonfinite, 1u);
 }
 
@@ -342,10 +346,7 @@ class GpuBackend final : public EncodeBackend {
   int row_rms(std::vector<double> &rms, std::string &err) override {
     if (!sums_.reserve((size_t)es_.R) || !flag_.reserve(1)) return nomem(err);
     if (hipMemsetAsync(flag_.p, 0, sizeof(uint32_t), stream_) != hipSuccess) return device(err, "hipMemsetAsync");
-    const uint64_t row_bytes = (uint64_t)es_.C * elem_bytes(es_.dtype);
-    const bool vec = ((uintptr_t)S_.src & 15u) == 0 && row_bytes % 16 == 0;
-    hipLaunchKernelGGL(vec ? row_sums_kernel<true> : row_sums_kernel<false>, dim3((unsigned)((es_.R + 63) / 64)), dim3(64),
-                       0, stream_, S_, sums_.p, flag_.p);
+    hipLaunchKernelGGL(row_sums_kernel, dim3((unsigned)es_.R), dim3(64), 0, stream_, S_, sums_.p, flag_.p);
     if (hipGetLastError() != hipSuccess) return device(err, "row sums launch");
     std::vector<double> sums((size_t)es_.R);
     uint32_t bad = 0;
