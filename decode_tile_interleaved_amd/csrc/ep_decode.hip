@@ -11,15 +11,15 @@
 // (16 bytes for BF16/FP16, 8 bytes for FP8/INT8).
 //
 // Per workgroup (up to 8 waves, one workgroup per CU):
-//   1. every wave starts its global loads: one context's frequencies, its
-//      tile's start states and row scales (vector loads, which need only the
-//      kernel arguments), then its tile's word offset (scalar loads); the last
-//      wave copies the words of all the workgroup's tiles (one range of the
-//      stream) into LDS with global_load_lds;
+//   1. every wave starts its global loads, all vector loads that need only the
+//      kernel arguments: the tile offsets it needs, one context's frequencies,
+//      its tile's start states and row scales;
 //   2. one wave per context prefix-sums the frequencies (DPP scan), lists the
 //      used symbols, sets a bitmap of the slots where a symbol starts, and
 //      expands the context's table 64 slots at a time: a slot's symbol is the
 //      number of starts up to it, which v_mbcnt counts from the row's bitmap;
+//      the last wave copies the words of all the workgroup's tiles (one range
+//      of the stream) into LDS with global_load_lds;
 //   3. each wave decodes its tile.
 // Streams with more tiles than one such round of workgroups covers take the
 // multi-tile kernel instead: one workgroup of up to 16 waves per CU builds
@@ -35,10 +35,10 @@
 //
 // The step is software-pipelined around its one serial dependence, table
 // lookup -> multiply-add -> compare -> select -> address -> next lookup (on
-// gfx950 a dependent VALU op costs about fourteen cycles, an eight-byte LDS
-// lookup about sixty).  The refilled state (x' with the held word shifted in)
-// is formed in parallel with the compare, one v_cndmask selects the next
-// state, one v_and_or makes its address, and the next lookup leaves.  Only
+// gfx950 a dependent VALU op costs ten-odd cycles, an eight-byte LDS lookup
+// about sixty).  The refilled state (x' with the held word shifted in) is
+// formed in parallel with the compare, one v_cndmask selects the next state,
+// one v_bitop3 or v_and_or makes its address, and the next lookup leaves.  Only
 // then do the refilling lanes, under the exec mask, read their following
 // word, which is first needed one step later.  Eight VALU instructions per
 // step: the chain is one instruction longer than with both candidate
@@ -121,7 +121,7 @@ __device__ __forceinline__ uint32_t lds_u8(uint32_t byte) {
 }
 
 // hides a value from the compiler's folding: a table address stays one
-// v_and_or_b32 with the context base in the lookup's offset, and an f32
+// instruction with the context base in the lookup's offset, and an f32
 // product stays rounded before it is narrowed
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   asm volatile("" : "+v"(v));
@@ -503,7 +503,8 @@ struct TileIn {
 // Issues a tile's loads: start states and row scales (vector loads), word
 // offsets (scalar loads), and the copy of its words into LDS at buf with
 // global_load_lds (1 KB per instruction; lanes past the end of the last,
-// partial kilobyte re-read its last 16 bytes).  Nothing here waits for them.
+// partial kilobyte re-read its last 16 bytes).  Only the copy's addresses
+// wait, for the word offsets; nothing waits for the rest.
 __device__ __forceinline__ TileIn issue_tile(const Args &A, uint8_t *lds, uint32_t tile, uint32_t buf, uint32_t lane) {
   TileIn T;
   T.x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tile * 64u + lane];
