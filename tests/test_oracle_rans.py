@@ -71,6 +71,27 @@ def test_uniform_table_costs_exactly_k_bits(k):
         assert np.array_equal(dec, syms)
 
 
+def test_state_absorbs_under_16_bits_without_a_word():
+    """The rate estimate's floor of 40 bits per state: a state whose symbols
+    carry fewer than 16 bits in total emits no word, and its stored state
+    holds their information (log2 x0 - log2 L equals it up to the coder's
+    rounding), so storing it costs its 32 bits and count byte whatever it
+    holds; past 16 bits the first word appears."""
+    f = np.array([M - 8, 8], np.uint32)  # symbol 1 carries 7 bits, symbol 0 about 0.01
+    for ones in (0, 1, 2):
+        syms = np.zeros(128, np.int32)
+        syms[:ones] = 1
+        info = float(np.sum(np.log2(M / f[syms].astype(np.float64))))
+        states, words = oracle.rans_encode(f, syms, 1)
+        assert words.size == 0
+        assert abs(np.log2(float(states[0])) - np.log2(L) - info) < 0.1
+    syms = np.zeros(128, np.int32)
+    syms[:3] = 1  # about 22.4 bits: one word, the rest in the state
+    states, words = oracle.rans_encode(f, syms, 1)
+    assert words.size == 1
+    assert abs(16 + np.log2(float(states[0])) - np.log2(L) - 22.414) < 0.1
+
+
 def test_size_matches_information():
     """16W + sum(log2 x0) - nstates*log2 L equals sum -log2(f/M) up to the
     coder's small approximation loss (well under 0.5%)."""
