@@ -181,3 +181,31 @@ def test_multitile_lds_limited_waves():
     torch.cuda.synchronize()
     assert np.array_equal(v.cpu().numpy(), oracle.decode_symbols(blob))
     assert np.array_equal(y.cpu().view(torch.int16).numpy().view(np.uint16), oracle.decompress_raw(blob).view(np.uint16))
+
+
+@pytest.mark.parametrize("rows,cols", [(512, 4096), (3072, 8192)], ids=["one_round", "multi_tile"])
+def test_corrupt_words_decode_within_bounds(rows, cols):
+    """The host checks a stream's header, tables and tile offsets but not its
+    words and count bytes (that would mean decoding it).  With the whole word
+    section overwritten by random bytes the decoder still completes: a lane's
+    word pointer starts at most at its tile's end and moves at most 128 words
+    on, inside the LDS padding, and table addresses are masked into the
+    tables.  Every decoded coordinate stays in the stream's value range, and
+    a clean decode right after is exact."""
+    x = W.rowscale_gaussian(rows, cols, 8100)
+    blob, rc, _ = oracle.compress(x, 4.0)
+    assert rc == 0
+    n_words = ep.blob_info(blob)["n_words"]
+    o_w = blob.size - (2 * n_words + 15) // 16 * 16  # the word section ends the stream
+    bad = blob.copy()
+    bad[o_w:o_w + 2 * n_words] = np.random.default_rng(8101).integers(0, 256, 2 * n_words, dtype=np.uint8)
+    pb = ep.from_blob(bad).to("cuda")
+    v = ep.decode_symbols(pb)
+    y = ep.decompress(pb)
+    torch.cuda.synchronize()
+    assert int(v.abs().max()) <= 2047
+    assert bool(torch.isfinite(y.float()).all())
+    p = ep.from_blob(blob).to("cuda")
+    y2 = ep.decompress(p)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().view(torch.int16).numpy().view(np.uint16), oracle.decompress_raw(blob).view(np.uint16))
