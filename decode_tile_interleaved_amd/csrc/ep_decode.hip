@@ -363,9 +363,21 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
   }
 }
 
-// decodes one tile; PARTIAL handles the last tile of a stream (n < 1024).
-// wb and we are the LDS byte addresses of the tile's first word and of its
-// end; X is 8 * the start state.
+// the row scale of vector vec (the last row's for vectors past the end)
+__device__ __forceinline__ float row_scale(const Args &A, uint32_t vec) {
+  const float *scales = reinterpret_cast<const float *>(A.blob + A.off_scales);
+  const uint32_t last = A.rows - 1u, one = A.vpr == 1u ? 0xffffffffu : 0u;
+  const uint32_t r = ((__umulhi(vec, A.row_magic) >> A.row_shift) & ~one) | (vec & one);
+  return scales[r < last ? r : last];
+}
+
+// decodes one tile of NS states; PARTIAL handles the last tile of a stream
+// (n < 1024).  wb and we are the LDS byte addresses of the tile's first word
+// and of its end; X is 8 * the start state.  Lane q < NS decodes vectors q,
+// q + NS, ...; with NS = 64, gs holds the row scale of each of its 16
+// vectors, with fewer states the scales of each group of 16 steps are loaded
+// as the group starts, and lanes from NS on only follow along (they never
+// refill or store).
 //
 // BOP3: the lookup address by v_bitop3 rather than v_and_or.  On gfx950 the
 // first issues faster (about 1.9 against 2.8 SIMD cycles per instruction with
@@ -373,41 +385,59 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
 // faster in the single-round kernel and for 8-bit outputs, but 1-2.5% slower
 // for 16-bit outputs in the multi-tile kernel, whose code differs in that
 // instruction alone, so each kernel takes the faster form.
-template <int OUT, bool WIDE, bool PADDED, bool PARTIAL, bool BOP3>
+template <int OUT, bool WIDE, bool PADDED, bool PARTIAL, bool BOP3, int NS>
 __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t we, uint32_t X, uint32_t tile,
                                             uint32_t n, const float (&gs)[16], uint32_t lane) {
+  static_assert(NS == 64 || NS == 16, "states per tile");
+  constexpr uint32_t kNs = (uint32_t)NS;
+  constexpr uint32_t kGroups = 1024u / kNs / 16u;  // groups of 16 steps
+  const bool mine = NS == 64 || lane < kNs;        // this lane holds one of the tile's states
   Lane L;
   table_read<0u>(X & 0x1ff8u, L.d0, L.d1);  // context F
   L.q = X >> 13;
-  // this state's words follow the count bytes of the states before it; the
-  // clamp keeps every read of a corrupt tile inside the LDS allocation
-  const uint32_t cnt = lds_u8(wb + lane);
-  const uint32_t p = wb + 2u * kCountWords + 2u * (wave_inclusive_sum(cnt) - cnt);
+  // this state's words follow the NS count bytes and the words of the states
+  // before it; the clamp keeps every read of a corrupt tile inside the LDS
+  // allocation
+  const uint32_t cnt = mine ? lds_u8(wb + lane) : 0u;
+  const uint32_t p = wb + kNs + 2u * (wave_inclusive_sum(cnt) - cnt);
   L.p = p < we ? p : we;
   L.r = lds_u16(L.p);
   constexpr uint32_t kC = kCtxBytes, kE = 3u * kCtxBytes;  // LDS bases of C_0 and E_{0,0}
   constexpr uint32_t kBitB = WIDE ? 16u : 24u;  // where bit 0 of v sits in d0
-  constexpr uint32_t kStepBytes = 64u * ((OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u);
-  const gbyte_t tile_out = (gbyte_t)A.out + (uint64_t)tile * (16u * kStepBytes);
+  constexpr uint32_t kVecBytes = (OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u;
+  constexpr uint32_t kStepBytes = kNs * kVecBytes;
+  const gbyte_t tile_out = (gbyte_t)A.out + (uint64_t)tile * (1024u * kVecBytes);
+#pragma unroll 1
+  for (uint32_t grp = 0; grp < kGroups; ++grp) {
+    if (PARTIAL && grp * 16u * kNs >= n) break;
+    float gl[16];
+    if constexpr (NS != 64) {
 #pragma unroll
-  for (uint32_t s = 0; s < 16; ++s) {
-    const bool act = PARTIAL ? (s * 64 + lane < n) : true;
-    if (PARTIAL && s * 64 >= n) break;
-    uint32_t e[8];
-    // C_b at LDS context 1 + b; the coset bit is in the entry of coordinate 0
-    const uint32_t cb = __builtin_amdgcn_ubfe(L.d0, kBitB, 1u) << 13;
-    e[0] = rans_step<WIDE, kC, BOP3>(L, cb, act);
+      for (uint32_t s = 0; s < 16; ++s) gl[s] = row_scale(A, tile * 1024u + (grp * 16u + s) * kNs + (mine ? lane : 0u));
+    }
 #pragma unroll
-    for (int j = 1; j < 6; ++j) e[j] = rans_step<WIDE, kC, BOP3>(L, cb, act);
-    // the XOR's copy of v's bit 0 is b (all eight coordinates share it), its
-    // copy of bit 1 is p
-    uint32_t acc = __builtin_amdgcn_bitop3_b32(e[0], e[1], e[2], 0x96);
-    acc = __builtin_amdgcn_bitop3_b32(acc, e[3], e[4], 0x96);
-    acc = __builtin_amdgcn_bitop3_b32(acc, e[5], L.d0, 0x96);
-    const uint32_t eb = __builtin_amdgcn_ubfe(acc, kBitB, 2u) << 13;
-    e[6] = rans_step<WIDE, kE, BOP3>(L, eb, act);
-    e[7] = rans_step<WIDE, 0u, BOP3>(L, 0u, act);
-    if (act) emit_vector<OUT, WIDE, PADDED>(A, opaque_s(tile_out + s * kStepBytes), tile, s * 64u + lane, lane, e, gs[s]);
+    for (uint32_t s = 0; s < 16; ++s) {
+      const uint32_t t = grp * 16u + s;  // step
+      const bool act = mine && (PARTIAL ? (t * kNs + lane < n) : true);
+      if (PARTIAL && t * kNs >= n) break;
+      uint32_t e[8];
+      // C_b at LDS context 1 + b; the coset bit is in the entry of coordinate 0
+      const uint32_t cb = __builtin_amdgcn_ubfe(L.d0, kBitB, 1u) << 13;
+      e[0] = rans_step<WIDE, kC, BOP3>(L, cb, act);
+#pragma unroll
+      for (int j = 1; j < 6; ++j) e[j] = rans_step<WIDE, kC, BOP3>(L, cb, act);
+      // the XOR's copy of v's bit 0 is b (all eight coordinates share it), its
+      // copy of bit 1 is p
+      uint32_t acc = __builtin_amdgcn_bitop3_b32(e[0], e[1], e[2], 0x96);
+      acc = __builtin_amdgcn_bitop3_b32(acc, e[3], e[4], 0x96);
+      acc = __builtin_amdgcn_bitop3_b32(acc, e[5], L.d0, 0x96);
+      const uint32_t eb = __builtin_amdgcn_ubfe(acc, kBitB, 2u) << 13;
+      e[6] = rans_step<WIDE, kE, BOP3>(L, eb, act);
+      e[7] = rans_step<WIDE, 0u, BOP3>(L, 0u, act);
+      if (act)
+        emit_vector<OUT, WIDE, PADDED>(A, opaque_s(tile_out + t * kStepBytes), tile, t * kNs + lane, lane, e,
+                                       NS == 64 ? gs[s] : gl[s]);
+    }
   }
 }
 
@@ -505,10 +535,11 @@ struct TileIn {
 // global_load_lds (1 KB per instruction; lanes past the end of the last,
 // partial kilobyte re-read its last 16 bytes).  Only the copy's addresses
 // wait, for the word offsets; nothing waits for the rest.
+template <int NS>
 __device__ __forceinline__ TileIn issue_tile(const Args &A, uint8_t *lds, uint32_t tile, uint32_t buf, uint32_t lane) {
   TileIn T;
-  T.x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tile * 64u + lane];
-  {
+  T.x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tile * (uint32_t)NS + (lane < (uint32_t)NS ? lane : 0u)];
+  if constexpr (NS == 64) {
     const float *scales = reinterpret_cast<const float *>(A.blob + A.off_scales);
     const uint32_t last = A.rows - 1u, one = A.vpr == 1u ? 0xffffffffu : 0u;
 #pragma unroll
@@ -548,7 +579,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // no wave waits for another: while one waits for its next tile's loads, the
 // other waves of its SIMD keep the VALU busy (four waves per SIMD cover the
 // decode chain's latency).
-template <int OUT, bool WIDE, bool PADDED>
+template <int OUT, bool WIDE, bool PADDED, int NS>
 __global__ void __launch_bounds__(64 * kMaxTileWaves) decode_waves_kernel(Args A) {
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lane = threadIdx.x & 63u;
@@ -579,11 +610,11 @@ __global__ void __launch_bounds__(64 * kMaxTileWaves) decode_waves_kernel(Args A
   // every copy into LDS before the next LDS access) delays a table.
   const bool builder = wave < (uint32_t)kContexts;
   TileIn T;
-  if (!builder) T = issue_tile(A, lds, tc, buf, lane);
+  if (!builder) T = issue_tile<NS>(A, lds, tc, buf, lane);
 
   // ---- 2. the tables -------------------------------------------------------
   build_tables<WIDE>(A, lds, wave, lane, k, fpre);
-  if (builder) T = issue_tile(A, lds, tc, buf, lane);
+  if (builder) T = issue_tile<NS>(A, lds, tc, buf, lane);
   lds_barrier();  // tables built (every wave's LDS writes done)
 
   // ---- 3. this wave's tiles --------------------------------------------------
@@ -591,20 +622,20 @@ __global__ void __launch_bounds__(64 * kMaxTileWaves) decode_waves_kernel(Args A
     __builtin_amdgcn_s_waitcnt(0);  // the tile's states, scales and words have landed
     const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
     if (n == 1024u)
-      decode_tile<OUT, WIDE, PADDED, false, kNarrowOut>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
+      decode_tile<OUT, WIDE, PADDED, false, kNarrowOut, NS>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
     else
-      decode_tile<OUT, WIDE, PADDED, true, kNarrowOut>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
+      decode_tile<OUT, WIDE, PADDED, true, kNarrowOut, NS>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
     tile += k;
     if (tile < end) {
       __builtin_amdgcn_s_waitcnt(0);  // every read of the finished tile's words is done before they are overwritten
-      T = issue_tile(A, lds, tile, buf, lane);
+      T = issue_tile<NS>(A, lds, tile, buf, lane);
     }
   }
 }
 
 // Streams that one round of workgroups covers: workgroups of up to 8 waves,
 // one tile each.
-template <int OUT, bool WIDE, bool PADDED>
+template <int OUT, bool WIDE, bool PADDED, int NS>
 __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lane = threadIdx.x & 63u;
@@ -638,9 +669,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
       fpre[i] = s < n0 ? v : 0u;
     }
   }
-  const uint32_t x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tc * 64u + lane];
+  const uint32_t x0 =
+      reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tc * (uint32_t)NS + (lane < (uint32_t)NS ? lane : 0u)];
   float gs[16];
-  {
+  if constexpr (NS == 64) {
     const float *scales = reinterpret_cast<const float *>(A.blob + A.off_scales);
     const uint32_t last = A.rows - 1u, one = A.vpr == 1u ? 0xffffffffu : 0u;
 #pragma unroll
@@ -690,31 +722,33 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   const uint32_t wt = A.words_off + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);  // LDS address of this tile's first word
   const uint32_t we = wt + 2u * (w_end - w_begin);
   if (n == 1024u)
-    decode_tile<OUT, WIDE, PADDED, false, true>(A, wt, we, X, tile, n, gs, lane);
+    decode_tile<OUT, WIDE, PADDED, false, true, NS>(A, wt, we, X, tile, n, gs, lane);
   else
-    decode_tile<OUT, WIDE, PADDED, true, true>(A, wt, we, X, tile, n, gs, lane);
+    decode_tile<OUT, WIDE, PADDED, true, true, NS>(A, wt, we, X, tile, n, gs, lane);
 }
 
 typedef void (*KernelFn)(Args);
 
 template <int OUT, bool WIDE, bool PADDED>
-KernelFn pick3(bool multi) {
-  return multi ? decode_waves_kernel<OUT, WIDE, PADDED> : decode_kernel<OUT, WIDE, PADDED>;
+KernelFn pick3(bool multi, bool low) {
+  if (low) return multi ? decode_waves_kernel<OUT, WIDE, PADDED, kStatesLow> : decode_kernel<OUT, WIDE, PADDED, kStatesLow>;
+  return multi ? decode_waves_kernel<OUT, WIDE, PADDED, kStatesPerTile> : decode_kernel<OUT, WIDE, PADDED, kStatesPerTile>;
 }
 
 template <int OUT>
-KernelFn pick(bool wide, bool padded, bool multi) {
-  if (wide) return padded ? pick3<OUT, true, true>(multi) : pick3<OUT, true, false>(multi);
-  return padded ? pick3<OUT, false, true>(multi) : pick3<OUT, false, false>(multi);
+KernelFn pick(bool wide, bool padded, bool multi, bool low) {
+  if (wide) return padded ? pick3<OUT, true, true>(multi, low) : pick3<OUT, true, false>(multi, low);
+  return padded ? pick3<OUT, false, true>(multi, low) : pick3<OUT, false, false>(multi, low);
 }
 
-KernelFn pick_kernel(int out, bool wide, bool padded, bool multi) {
+// low: the stream has kStatesLow states per tile
+KernelFn pick_kernel(int out, bool wide, bool padded, bool multi, bool low) {
   switch (out) {
-    case EP_BF16: return pick<EP_BF16>(wide, padded, multi);
-    case EP_FP16: return pick<EP_FP16>(wide, padded, multi);
-    case EP_FP8_E4M3FN: return pick<EP_FP8_E4M3FN>(wide, padded, multi);
-    case EP_INT8: return pick<EP_INT8>(wide, padded, multi);
-    default: return pick<kOutSym>(wide, false, multi);
+    case EP_BF16: return pick<EP_BF16>(wide, padded, multi, low);
+    case EP_FP16: return pick<EP_FP16>(wide, padded, multi, low);
+    case EP_FP8_E4M3FN: return pick<EP_FP8_E4M3FN>(wide, padded, multi, low);
+    case EP_INT8: return pick<EP_INT8>(wide, padded, multi, low);
+    default: return pick<kOutSym>(wide, false, multi, low);
   }
 }
 
@@ -768,7 +802,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   const uint8_t *toff = hb + s.off_tile_offsets;
   for (int64_t t = 0; t < s.tiles; ++t) {
     const uint32_t b = rd<uint32_t>(toff + 4 * t), e = rd<uint32_t>(toff + 4 * t + 4);
-    if (e < b || e > s.n_words || e - b < (uint32_t)kCountWords) {
+    if (e < b || e > s.n_words || e - b < (uint32_t)s.states / 2u) {
       set_error("corrupt tile offsets");
       return EP_ERR_FORMAT;
     }
@@ -885,7 +919,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   A.n_vec = (uint32_t)s.n_vec;
   A.n_tiles = (uint32_t)s.tiles;
   const bool padded = out != kOutSym && (s.cols % 8) != 0;
-  KernelFn fn = pick_kernel(out, wide, padded, multi);
+  KernelFn fn = pick_kernel(out, wide, padded, multi, s.states == kStatesLow);
   static std::mutex mu;
   static std::vector<KernelFn> configured;
   {

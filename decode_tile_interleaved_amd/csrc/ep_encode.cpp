@@ -242,8 +242,9 @@ static bool build_tables(const std::vector<uint64_t> &h, Tables &t) {
 // the passes over the matrix on host threads
 // ---------------------------------------------------------------------------
 struct TileOut {
-  uint32_t states[kStatesPerTile];
+  uint32_t states[kStatesPerTile];  // the first shape.states are used
   std::vector<uint16_t> words;
+  bool overflow = false;            // a state's word count does not fit its count byte
 };
 
 class HostBackend final : public EncodeBackend {
@@ -310,11 +311,12 @@ class HostBackend final : public EncodeBackend {
     parallel_for(S_.tiles, std::max(1, threads_), [&](int64_t b, int64_t e) {
       for (int64_t t = b; t < e; ++t) encode_tile(tb, t, tiles_[(size_t)t]);
     });
-    states.resize((size_t)S_.tiles * kStatesPerTile);
+    const int ns = states_;
+    states.resize((size_t)S_.tiles * ns);
     tile_first.resize((size_t)S_.tiles + 1);
     uint64_t w = 0;
     for (int64_t t = 0; t < S_.tiles; ++t) {
-      std::memcpy(&states[(size_t)t * kStatesPerTile], tiles_[(size_t)t].states, 4 * kStatesPerTile);
+      std::memcpy(&states[(size_t)t * ns], tiles_[(size_t)t].states, 4 * (size_t)ns);
       tile_first[(size_t)t] = (uint32_t)w;
       w += tiles_[(size_t)t].words.size();
       if (w > 0xffffffffull) {
@@ -323,6 +325,8 @@ class HostBackend final : public EncodeBackend {
       }
     }
     tile_first[(size_t)S_.tiles] = (uint32_t)w;
+    for (const TileOut &to : tiles_)
+      if (to.overflow) return 1;
     return 0;
   }
 
@@ -397,17 +401,18 @@ class HostBackend final : public EncodeBackend {
       fc[(size_t)(i * 8 + j) * 2 + 1] = tb.cum[c][s];
     }
   }
+  const int S = states_;
   uint32_t x[kStatesPerTile];
-  for (int q = 0; q < kStatesPerTile; ++q) x[q] = kStateLow;
+  for (int q = 0; q < S; ++q) x[q] = kStateLow;
   std::vector<uint16_t> emitted;   // emission order (reverse of consumption)
   std::vector<uint8_t> who;        // state that emitted each word
   emitted.reserve((size_t)n * 3);
   who.reserve((size_t)n * 3);
-  const int steps = kTileVecs / kStatesPerTile;
+  const int steps = kTileVecs / S;
   for (int s = steps - 1; s >= 0; --s)
     for (int j = 7; j >= 0; --j)
-      for (int q = kStatesPerTile - 1; q >= 0; --q) {
-        int i = s * kStatesPerTile + q;
+      for (int q = S - 1; q >= 0; --q) {
+        int i = s * S + q;
         if (i >= n) continue;
         uint32_t f = fc[(size_t)(i * 8 + j) * 2], c = fc[(size_t)(i * 8 + j) * 2 + 1];
         uint32_t st = x[q];
@@ -418,15 +423,18 @@ class HostBackend final : public EncodeBackend {
         }
         x[q] = (st / f) * kProbTotal + st % f + c;
       }
-  std::memcpy(out.states, x, sizeof(x));
+  std::memcpy(out.states, x, sizeof(uint32_t) * (size_t)S);
   // per-state words in consumption order
-  std::vector<std::vector<uint16_t>> lane(kStatesPerTile);
+  std::vector<std::vector<uint16_t>> lane((size_t)S);
   for (size_t k = emitted.size(); k-- > 0;) lane[who[k]].push_back(emitted[k]);
   out.words.clear();
-  out.words.reserve(emitted.size() + kCountWords);
-  for (int q = 0; q < kStatesPerTile; q += 2)  // at most 8 words per vector: every count fits a byte
-    out.words.push_back((uint16_t)(lane[q].size() | lane[q + 1].size() << 8));
-  for (int q = 0; q < kStatesPerTile; ++q) out.words.insert(out.words.end(), lane[q].begin(), lane[q].end());
+  out.words.reserve(emitted.size() + (size_t)S / 2);
+  out.overflow = false;
+  for (int q = 0; q < S; q += 2) {  // 64 states: at most 8 words per vector, so every count fits a byte
+    out.overflow |= lane[q].size() > 255 || lane[q + 1].size() > 255;
+    out.words.push_back((uint16_t)((lane[q].size() & 0xff) | (lane[q + 1].size() & 0xff) << 8));
+  }
+  for (int q = 0; q < S; ++q) out.words.insert(out.words.end(), lane[q].begin(), lane[q].end());
 }
 
 
@@ -477,7 +485,7 @@ double estimate_bpp(const Problem &P, double a, int64_t S, std::string &err, int
       if (n) info += (double)n * ((double)kProbBits - std::log2((double)tb.freq[c][i]));
     }
   const double scale = S >= P.S.n_vec ? 1.0 : (double)P.S.n_vec / (double)S;
-  const double n_states = (double)(kStatesPerTile * P.S.tiles);
+  const double n_states = (double)((int64_t)P.S.states * P.S.tiles);
   const double asymptotic = info * scale + kStateBits * n_states, least = kStateMinBits * n_states;
   double bits = (asymptotic > least ? asymptotic : least) + 8.0 * (double)metadata_bytes(P.S, tb.total_symbols());
   return bits / ((double)P.S.R * (double)P.S.C);
@@ -530,12 +538,13 @@ int encode_at(const Problem &P, double a, double target, Blob &blob, std::string
   std::vector<uint32_t> states, tile_first;
   rc = P.be->encode_tiles(g, tb, states, tile_first, err);
   if (rc < 0) return rc;
+  if (rc == 1) return EP_WARN_RAW;  // a count byte cannot hold a state's words: an encoding failure
   const uint64_t n_words = tile_first.back();
   const int nsum = tb.total_symbols();
   const uint64_t o_tab = kHeaderBytes;
   const uint64_t o_sc = o_tab + align16(4 * kContexts + 2 * (uint64_t)nsum);
   const uint64_t o_st = o_sc + align16(4 * (uint64_t)S.R);
-  const uint64_t o_to = o_st + align16(4 * (uint64_t)S.tiles * kStatesPerTile);
+  const uint64_t o_to = o_st + align16(4 * (uint64_t)S.tiles * (uint64_t)S.states);
   const uint64_t o_w = o_to + align16(4 * (uint64_t)(S.tiles + 1));
   const uint64_t total = o_w + align16(2 * n_words);
   if (!blob.alloc(total)) {
@@ -553,7 +562,7 @@ int encode_at(const Problem &P, double a, double target, Blob &blob, std::string
   b[hdr::prob_bits] = kProbBits;
   b[hdr::contexts] = kContexts;
   wr<uint32_t>(b + hdr::tile_vecs, kTileVecs);
-  wr<uint32_t>(b + hdr::states, kStatesPerTile);
+  wr<uint32_t>(b + hdr::states, (uint32_t)S.states);
   wr<uint32_t>(b + hdr::tiles, (uint32_t)S.tiles);
   wr<uint64_t>(b + hdr::rows, (uint64_t)S.R);
   wr<uint64_t>(b + hdr::cols, (uint64_t)S.C);
@@ -638,6 +647,15 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, do
                   Blob &blob, std::string &err) {
   Problem P{shape, &be, {}};
   const EncodeShape &S = P.S;
+  {
+    // 64 states per tile, or 16 when a target-selected stream's target lies
+    // below the overhead of 64 (40 bits per state plus the metadata)
+    const double floor64 =
+        (kStateMinBits * (double)(kStatesPerTile * S.tiles) + 8.0 * (double)metadata_bytes(S, kContexts)) /
+        ((double)S.R * (double)S.C);
+    P.S.states = (!(fixed_a > 0.0) && target < 1.1 * floor64) ? kStatesLow : kStatesPerTile;
+    be.set_states(P.S.states);
+  }
   // finiteness and row RMS (sequential sum per row)
   if (const int rc = be.row_rms(P.rms, err); rc != 0) return rc;
   const bool eight_bit = elem_bytes(S.dtype) == 1;
@@ -649,7 +667,7 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, do
   double goal = target;  // the sampled estimate the last selection aimed at
   if (!(fixed_a > 0.0)) {
     const double floor_bpp =
-        (kStateMinBits * (double)(kStatesPerTile * S.tiles) + 8.0 * (double)metadata_bytes(S, kContexts)) /
+        (kStateMinBits * (double)((int64_t)S.states * S.tiles) + 8.0 * (double)metadata_bytes(S, kContexts)) /
         ((double)S.R * (double)S.C);
     if (target < 1.02 * floor_bpp) {
       err = "target_bpp below this stream's fixed per-tile overhead (" + std::to_string(floor_bpp) + " bpp)";

@@ -59,6 +59,7 @@ class Blob {
 struct EncodeShape {
   int dtype = 0;
   int64_t R = 0, C = 0, C8 = 0, vpr = 0, n_vec = 0, tiles = 0;
+  int states = kStatesPerTile;  // rANS states per tile: kStatesPerTile or kStatesLow
 };
 
 // Normalized frequencies of each context over its symbol range
@@ -81,6 +82,8 @@ struct Tables {
 class EncodeBackend {
  public:
   virtual ~EncodeBackend() = default;
+  // rANS states per tile for encode_tiles (kStatesPerTile or kStatesLow)
+  void set_states(int states) { states_ = states; }
   // RMS of every row (f64 sum of squares in column order).  Returns 0,
   // EP_ERR_NONFINITE if the input holds NaN or Inf, or another negative
   // ep_status.
@@ -89,16 +92,20 @@ class EncodeBackend {
   // (S >= n_vec: every vector), quantized at row scales g.  Returns 0, 1 if a
   // coordinate leaves [-2048, 2047], or a negative ep_status.
   virtual int histogram(const std::vector<float> &g, int64_t S, std::vector<uint64_t> &hist, std::string &err) = 0;
-  // Every tile at row scales g with tables t: start states (kStatesPerTile
+  // Every tile at row scales g with tables t: start states (set_states
   // per tile) and the index of each tile's first word (tiles + 1 entries;
   // the last is the word count).  The words stay with the backend until
-  // copy_words.  Returns 0 or a negative ep_status.
+  // copy_words.  Returns 0, 1 if a state's word count does not fit its count
+  // byte (possible with kStatesLow only), or a negative ep_status.
   virtual int encode_tiles(const std::vector<float> &g, const Tables &t, std::vector<uint32_t> &states,
                            std::vector<uint32_t> &tile_first, std::string &err) = 0;
   // The word section of the last encode_tiles, to dst.
   virtual int copy_words(uint16_t *dst, std::string &err) = 0;
   // The container elements, row-major (rows * cols * element bytes).
   virtual int copy_input(uint8_t *dst, std::string &err) = 0;
+
+ protected:
+  int states_ = kStatesPerTile;
 };
 
 // The encoder on a backend: row normalization, rate selection from sampled

@@ -237,25 +237,27 @@ struct DevTables {
   uint32_t base[kContexts];  // index of each context's first entry in fc
 };
 
-constexpr int kWordsPerState = 128;  // at most one word per symbol: 16 vectors x 8 coordinates
+// words a state's slot holds: at most one per symbol, 8 per vector
+__host__ __device__ constexpr int words_per_state(int states) { return 8 * (kTileVecs / states); }
 
-// One wave per tile, lane q = state q: its vectors q, q + 64, ... quantized
-// again at the same scales, their symbols encoded backwards (vector 15 down
-// to 0, coordinate 7 down to 0).  Words go to the lane's slot in emission
-// order; the count and the final state are kept.
-__global__ void __launch_bounds__(64) encode_tiles_kernel(Shape S, const float *g, DevTables T, const uint32_t *fc,
-                                                          uint16_t *slots, uint8_t *counts, uint32_t *states,
-                                                          uint32_t *fault) {
+// One wave per tile, lane q = state q of ns: its vectors q, q + ns, ...
+// quantized again at the same scales, their symbols encoded backwards (last
+// vector first, coordinate 7 down to 0).  Words go to the lane's slot in
+// emission order; the count and the final state are kept.
+__global__ void __launch_bounds__(64) encode_tiles_kernel(Shape S, int ns, const float *g, DevTables T,
+                                                          const uint32_t *fc, uint16_t *slots, uint16_t *counts,
+                                                          uint32_t *states, uint32_t *fault) {
   const int64_t tile = blockIdx.x;
   const int q = threadIdx.x;
   const int64_t first = tile * kTileVecs;
   const int n = (int)min((int64_t)kTileVecs, S.n_vec - first);
-  uint16_t *slot = slots + ((size_t)tile * kStatesPerTile + q) * kWordsPerState;
+  const int wps = words_per_state(ns);
+  uint16_t *slot = slots + ((size_t)tile * ns + q) * wps;
   uint32_t x = kStateLow;
   int emitted = 0;
   bool bad = false;
-  for (int s = kTileVecs / kStatesPerTile - 1; s >= 0; --s) {
-    const int i = s * kStatesPerTile + q;
+  for (int s = kTileVecs / ns - 1; s >= 0; --s) {
+    const int i = s * ns + q;
     if (i >= n) continue;
     const int64_t vid = first + i;
     int32_t v[8], ctx[8], sym[8];
@@ -275,16 +277,16 @@ __global__ void __launch_bounds__(64) encode_tiles_kernel(Shape S, const float *
         continue;
       }
       if ((uint64_t)x >= ((uint64_t)f << (29 - kProbBits))) {
-        if (emitted < kWordsPerState) slot[emitted] = (uint16_t)x;
+        if (emitted < wps) slot[emitted] = (uint16_t)x;
         ++emitted;
         x >>= 16;
       }
       x = (x / f) * kProbTotal + x % f + cum;
     }
   }
-  if (emitted > kWordsPerState) bad = true;
-  counts[tile * kStatesPerTile + q] = (uint8_t)min(emitted, kWordsPerState);
-  states[tile * kStatesPerTile + q] = x;
+  if (emitted > wps) bad = true;
+  counts[tile * ns + q] = (uint16_t)min(emitted, wps);
+  states[tile * ns + q] = x;
   if (bad) atomicOr(fault, 1u);
 }
 
@@ -297,19 +299,20 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t v, int lane) {
   return v;
 }
 
-// One wave per tile: the count words (state 2w in the low byte, 2w + 1 in
-// the high), then each state's words in the order the decoder consumes them
-// (the reverse of emission), at the tile's first word.
-__global__ void __launch_bounds__(64) lay_out_kernel(const uint16_t *slots, const uint8_t *counts,
+// One wave per tile, lane q = state q of ns: the ns / 2 count words (state
+// 2w in the low byte, 2w + 1 in the high; every count fits a byte, which the
+// host checked), then each state's words in the order the decoder consumes
+// them (the reverse of emission), at the tile's first word.
+__global__ void __launch_bounds__(64) lay_out_kernel(int ns, const uint16_t *slots, const uint16_t *counts,
                                                      const uint32_t *tile_first, uint16_t *words) {
   const int64_t tile = blockIdx.x;
   const int q = threadIdx.x;
-  const uint32_t cnt = counts[tile * kStatesPerTile + q];
+  const uint32_t cnt = counts[tile * ns + q];
   const uint32_t before = wave_scan(cnt, q) - cnt;
   uint16_t *w = words + tile_first[tile];
-  if (q < kCountWords) w[q] = (uint16_t)(counts[tile * kStatesPerTile + 2 * q] | counts[tile * kStatesPerTile + 2 * q + 1] << 8);
-  const uint16_t *slot = slots + ((size_t)tile * kStatesPerTile + q) * kWordsPerState;
-  uint16_t *mine = w + kCountWords + before;
+  if (q < ns / 2) w[q] = (uint16_t)(counts[tile * ns + 2 * q] | counts[tile * ns + 2 * q + 1] << 8);
+  const uint16_t *slot = slots + ((size_t)tile * ns + q) * words_per_state(ns);
+  uint16_t *mine = w + ns / 2 + before;
   for (uint32_t k = 0; k < cnt; ++k) mine[k] = slot[cnt - 1u - k];
 }
 
@@ -394,21 +397,22 @@ class GpuBackend final : public EncodeBackend {
       T.base[c] = (uint32_t)fc.size();
       for (int i = 0; i < tb.nsym[c]; ++i) fc.push_back(tb.freq[c][(size_t)i] | tb.cum[c][(size_t)i] << 16);
     }
-    const size_t nt = (size_t)es_.tiles, ns = nt * kStatesPerTile;
-    if (!fc_.reserve(fc.size()) || !slots_.reserve(ns * kWordsPerState) || !counts_.reserve(ns) ||
-        !states_.reserve(ns) || !first_.reserve(nt + 1) || !flag_.reserve(1))
+    const int sp = states_;  // states per tile
+    const size_t nt = (size_t)es_.tiles, ns = nt * (size_t)sp;
+    if (!fc_.reserve(fc.size()) || !slots_.reserve(ns * (size_t)words_per_state(sp)) || !counts_.reserve(ns) ||
+        !dstates_.reserve(ns) || !first_.reserve(nt + 1) || !flag_.reserve(1))
       return nomem(err);
     if (hipMemcpyAsync(fc_.p, fc.data(), 4 * fc.size(), hipMemcpyHostToDevice, stream_) != hipSuccess ||
         hipMemsetAsync(flag_.p, 0, sizeof(uint32_t), stream_) != hipSuccess)
       return device(err, "table upload");
-    hipLaunchKernelGGL(encode_tiles_kernel, dim3((unsigned)nt), dim3(kStatesPerTile), 0, stream_, S_, g_.p, T, fc_.p,
-                       slots_.p, counts_.p, states_.p, flag_.p);
+    hipLaunchKernelGGL(encode_tiles_kernel, dim3((unsigned)nt), dim3(sp), 0, stream_, S_, sp, g_.p, T, fc_.p,
+                       slots_.p, counts_.p, dstates_.p, flag_.p);
     if (hipGetLastError() != hipSuccess) return device(err, "tile encode launch");
-    std::vector<uint8_t> counts(ns);
+    std::vector<uint16_t> counts(ns);
     uint32_t fault = 0;
     states.resize(ns);
-    if (hipMemcpyAsync(counts.data(), counts_.p, ns, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
-        hipMemcpyAsync(states.data(), states_.p, 4 * ns, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+    if (hipMemcpyAsync(counts.data(), counts_.p, 2 * ns, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipMemcpyAsync(states.data(), dstates_.p, 4 * ns, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
         hipMemcpyAsync(&fault, flag_.p, 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
         hipStreamSynchronize(stream_) != hipSuccess)
       return device(err, "tile encode");
@@ -421,8 +425,11 @@ class GpuBackend final : public EncodeBackend {
     uint64_t w = 0;
     for (size_t t = 0; t < nt; ++t) {
       tile_first[t] = (uint32_t)w;
-      w += kCountWords;
-      for (int q = 0; q < kStatesPerTile; ++q) w += counts[t * kStatesPerTile + q];
+      w += (uint64_t)sp / 2;
+      for (int q = 0; q < sp; ++q) {
+        if (counts[t * sp + q] > 255) return 1;  // a count byte cannot hold this state's words
+        w += counts[t * sp + q];
+      }
       if (w > 0xffffffffull) {
         err = "stream too large for 32-bit tile offsets";
         return EP_ERR_SHAPE;
@@ -432,7 +439,7 @@ class GpuBackend final : public EncodeBackend {
     if (!words_.reserve((size_t)w)) return nomem(err);
     if (hipMemcpyAsync(first_.p, tile_first.data(), 4 * (nt + 1), hipMemcpyHostToDevice, stream_) != hipSuccess)
       return device(err, "tile offsets upload");
-    hipLaunchKernelGGL(lay_out_kernel, dim3((unsigned)nt), dim3(kStatesPerTile), 0, stream_, slots_.p, counts_.p, first_.p,
+    hipLaunchKernelGGL(lay_out_kernel, dim3((unsigned)nt), dim3(sp), 0, stream_, sp, slots_.p, counts_.p, first_.p,
                        words_.p);
     if (hipGetLastError() != hipSuccess) return device(err, "layout launch");
     n_words_ = (size_t)w;
@@ -476,9 +483,9 @@ class GpuBackend final : public EncodeBackend {
   DevBuf<double> sums_;
   DevBuf<float> g_;
   DevBuf<uint64_t> hist_;
-  DevBuf<uint32_t> flag_, fc_, states_, first_;
+  DevBuf<uint32_t> flag_, fc_, dstates_, first_;
   DevBuf<uint16_t> slots_, words_;
-  DevBuf<uint8_t> counts_;
+  DevBuf<uint16_t> counts_;
   size_t n_words_ = 0;
 };
 

@@ -30,7 +30,6 @@ constexpr int kContexts = 7;
 constexpr int kProbBits = 10;
 constexpr uint32_t kProbTotal = 1u << kProbBits;
 constexpr uint32_t kStateLow = 1u << 13;   // rANS states live in [2^13, 2^29)
-constexpr int kCountWords = 32;            // words of per-state count bytes at the start of a tile
 // stream bits per state beyond its symbols' information, as the rate
 // estimate counts them: the fixed final state L (13), the unused high bits of
 // the stored start state (11 on average) and the count byte (8)
@@ -41,6 +40,9 @@ constexpr double kStateBits = 32.0;
 constexpr double kStateMinBits = 40.0;
 constexpr int kTileVecs = 1024;            // E8 vectors (8 coordinates) per tile
 constexpr int kStatesPerTile = 64;         // interleaved rANS states per tile (2 count bytes per word)
+// states per tile when the target lies below the overhead of kStatesPerTile
+// (the stream's header says which); a tile starts with states / 2 count words
+constexpr int kStatesLow = 16;
 constexpr int kValueMin = -2048, kValueMax = 2047;  // lattice coordinates the stream can hold (12-bit field)
 
 enum Method : uint8_t { kLattice = 0, kRaw = 1 };
@@ -104,9 +106,9 @@ inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
   }
   s.prob_bits = b[hdr::prob_bits];
   if (s.prob_bits != kProbBits || b[hdr::contexts] != kContexts) return "unsupported model parameters";
-  if (rd<uint32_t>(b + hdr::tile_vecs) != kTileVecs || rd<uint32_t>(b + hdr::states) != kStatesPerTile)
+  s.states = (int)rd<uint32_t>(b + hdr::states);
+  if (rd<uint32_t>(b + hdr::tile_vecs) != kTileVecs || (s.states != kStatesPerTile && s.states != kStatesLow))
     return "unsupported tile geometry";
-  s.states = kStatesPerTile;
   s.cols8 = (int64_t)rd<uint64_t>(b + hdr::cols8);
   if (s.cols8 != (s.cols + 7) / 8 * 8) return "bad padded column count";
   s.n_vec = s.rows * (s.cols8 / 8);
@@ -130,7 +132,7 @@ inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
   s.off_freq = s.off_tables + 4 * kContexts;
   const uint64_t T = (uint64_t)s.tiles;
   if (s.off_scales < s.off_freq + 2 * nsum || (s.off_scales & 15) || s.off_states < s.off_scales + 4 * (uint64_t)s.rows ||
-      (s.off_states & 15) || s.off_tile_offsets < s.off_states + 4 * T * kStatesPerTile || (s.off_tile_offsets & 15) ||
+      (s.off_states & 15) || s.off_tile_offsets < s.off_states + 4 * T * (uint64_t)s.states || (s.off_tile_offsets & 15) ||
       s.off_words < s.off_tile_offsets + 4 * (T + 1) || (s.off_words & 15) || s.off_words + 2 * s.n_words > n)
     return "section table out of bounds";
   if (n - s.off_words < align16(2 * s.n_words)) return "word section not padded";

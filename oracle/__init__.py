@@ -149,9 +149,11 @@ def e8_nearest(u) -> np.ndarray:
     return v
 
 
-def compress(t, target_bpp: float, fixed_a: float = 0.0, n_states: int = N_STATES, prob_bits: int = PROB_BITS,
+def compress(t, target_bpp: float, fixed_a: float = 0.0, n_states: int = 0, prob_bits: int = PROB_BITS,
              exact_select: bool = False):
-    """Returns (blob bytes as np.uint8, status, chosen lattice scale a)."""
+    """Returns (blob bytes as np.uint8, status, chosen lattice scale a).
+    n_states = 0 picks the state count per tile as the product does: 64, or
+    16 when a target-selected stream's target is below the overhead of 64."""
     dt, x, raw = _as_container(t)
     if x.ndim != 2:
         raise OracleError(ERR_SHAPE, "compress")
@@ -178,7 +180,7 @@ def compress_status(x: np.ndarray, dtype: int, target_bpp: float) -> int:
     a = ctypes.c_double(0.0)
     raw = np.zeros(max(1, x.size * 2), np.uint8)
     rc = lib().or_compress(_ptr(x, ctypes.c_double), raw.ctypes.data_as(ctypes.c_void_p), R, C, dtype,
-                           float(target_bpp), 0.0, N_STATES, PROB_BITS, 0, ctypes.byref(out), ctypes.byref(nb),
+                           float(target_bpp), 0.0, 0, PROB_BITS, 0, ctypes.byref(out), ctypes.byref(nb),
                            ctypes.byref(a))
     if rc >= 0:
         lib().or_free(out)

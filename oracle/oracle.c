@@ -46,6 +46,8 @@
 #define OR_MAGIC 0x314B5045u /* "EPK1" little-endian */
 #define OR_VERSION 1
 #define OR_STATE_BITS 32.0  /* estimated stream bits per rANS state beyond its symbols' information */
+#define OR_STATES_DEFAULT 64 /* rANS states per tile */
+#define OR_STATES_LOW 16     /* per tile when the target is below the overhead of 64 */
 #define OR_STATE_MIN_BITS 40.0 /* stored bits of a state that emits no word: its 32-bit state and count byte */
 #define OR_STATE_L 8192u     /* rANS lower state bound L = 2^13; states lie in [L, 2^29); words are 16 bits */
 
@@ -436,7 +438,7 @@ static int encode_tile(const or_geom *g, const or_tables *t, const int32_t *v, i
   /* count bytes, then the per-state lists back to back */
   for (int64_t q = 0; q < g->S; q += 2) {
     int64_t hi = q + 1 < g->S ? cnt[q + 1] : 0;
-    if (cnt[q] > 255 || hi > 255) { rc = OR_ERR_SHAPE; goto done; }
+    if (cnt[q] > 255 || hi > 255) { rc = OR_WARN_RAW; goto done; } /* a count byte cannot hold it: encoding failure */
     if ((rc = words_push(out, (uint16_t)(cnt[q] | (hi << 8))))) goto done;
   }
   for (uint64_t k = 0; k < rev.n; k++)
@@ -766,9 +768,17 @@ int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, in
                 double *a_out) {
   int rc = check_input(x, R, C, dtype, target);
   if (rc) return rc;
-  if (n_states < 1 || n_states > 1024 || prob_bits < 8 || prob_bits > 12 || !blob || !nbytes)
+  if (n_states < 0 || n_states > 1024 || prob_bits < 8 || prob_bits > 12 || !blob || !nbytes)
     return OR_ERR_ARG;
   or_geom g;
+  if (n_states == 0) {
+    /* 64 states per tile, or 16 when a target-selected stream's target lies
+     * below the overhead of 64 (its 40 bits per state plus the metadata) */
+    geom_init(&g, R, C, OR_STATES_DEFAULT, prob_bits);
+    const double floor64 = (OR_STATE_MIN_BITS * (double)(g.S * g.T) + 8.0 * (double)meta_bytes(&g, OR_NCTX)) /
+                           ((double)R * (double)C);
+    n_states = (!(fixed_a > 0.0) && target < 1.1 * floor64) ? OR_STATES_LOW : OR_STATES_DEFAULT;
+  }
   geom_init(&g, R, C, n_states, prob_bits);
   double a = fixed_a;
   double *rms = NULL;         /* row RMS, kept for every rate selection below */

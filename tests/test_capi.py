@@ -168,15 +168,16 @@ def test_device_compress_argument_errors_before_any_device_work():
 
 
 @pytest.mark.parametrize("kind,targets", [
-    ("bf16", [0.001, 0.3, 0.36, 0.45, 0.6, 1.5, 3.3, 5.7, 7.0, 8.5, 9.0, 10.5, 11.0]),
-    ("int8", [0.3, 0.36, 0.5, 2.5, 4.5, 7.5]),
+    ("bf16", [0.001, 0.05, 0.12, 0.3, 0.36, 0.45, 0.6, 1.5, 3.3, 5.7, 7.0, 8.5, 9.0, 10.5, 11.0]),
+    ("int8", [0.05, 0.2, 0.3, 0.36, 0.5, 2.5, 4.5, 7.5]),
 ])
 def test_target_range_sweep_matches_oracle(kind, targets):
     """Across the whole target range the product and the oracle agree byte for
     byte and status for status; a lattice stream lands within 2% of the
     target (within 6% and not above it just over the fixed overhead, where a
-    state's cost steps by a whole word); targets under the overhead are
-    errors and the top of the 16-bit range falls back to the raw container
+    state's cost steps by a whole word), with 16 states per tile below the
+    overhead of 64; targets under the overhead of 16 are errors and the top
+    of the 16-bit range falls back to the raw container
     (README, "Direct tensor compression"; API reference, "compress")."""
     x = W.rowscale_gaussian(512, 4096, 7001) if kind == "bf16" else W.absmax_codes(512, 2048, 7004, "int8")
     seen = set()

@@ -138,3 +138,14 @@ def test_device_stream_rate_corrections(target):
     p = ep.compress_device(x.cuda(), target)
     assert p.status == rc == 0 and np.array_equal(p.blob, ref)
     assert abs(8 * ref.size / x.numel() - target) <= 0.02 * target
+
+
+@pytest.mark.parametrize("target", [0.15, 0.3])
+def test_device_16_state_streams(target):
+    """Below the overhead of 64 states per tile the GPU encoder writes the
+    oracle's 16-state stream, byte for byte."""
+    x = W.rowscale_gaussian(512, 4096, 7001)
+    ref, rc, _ = oracle.compress(x, target)
+    assert rc == 0 and oracle.info(ref)["n_states"] == 16
+    p = ep.compress_device(x.cuda(), target)
+    assert p.status == 0 and np.array_equal(p.blob, ref)

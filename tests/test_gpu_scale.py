@@ -209,3 +209,32 @@ def test_corrupt_words_decode_within_bounds(rows, cols):
     y2 = ep.decompress(p)
     torch.cuda.synchronize()
     assert np.array_equal(y2.cpu().view(torch.int16).numpy().view(np.uint16), oracle.decompress_raw(blob).view(np.uint16))
+
+
+def _low_rate_cases():
+    yield "bf16_one_round", W.rowscale_gaussian(512, 4096, 8200), 0.2
+    yield "bf16_multi_tile", W.rowscale_gaussian(3072, 8192, 8201), 0.15
+    yield "t4_bf16", W.t4_outliers(384, 6144, 8202, dtype=torch.bfloat16), 0.3
+    yield "fp16_padded", W.rowscale_gaussian(300, 1000, 8203).to(torch.float16), 0.2
+    yield "int8_codes", W.absmax_codes(512, 2048, 8204, "int8"), 0.3
+    yield "fp8_padded", W.absmax_codes(256, 3000, 8205, "fp8"), 0.25
+
+
+@pytest.mark.parametrize("case", list(_low_rate_cases()), ids=lambda c: c[0])
+def test_low_rate_16_state_streams(case):
+    """Targets below the overhead of 64 states per tile take 16 (40 bits per
+    state): a lane decodes 64 vectors, lanes 16-63 only follow along, and the
+    row scales are loaded per group of 16 steps.  Symbols and values equal
+    the oracle's in the single-round and the multi-tile kernel, for every
+    container."""
+    _, x, target = case
+    blob, rc, _ = oracle.compress(x, target)
+    assert rc == 0 and oracle.info(blob)["n_states"] == 16
+    assert abs(8 * blob.size / x.numel() - target) <= 0.02 * target
+    p = ep.from_blob(blob).to("cuda")
+    v = ep.decode_symbols(p)
+    y = ep.decompress(p)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.cpu().numpy(), oracle.decode_symbols(blob))
+    got = y.cpu().view(torch.int16 if x.element_size() == 2 else torch.int8).numpy().view(np.uint8)
+    assert np.array_equal(got, oracle.decompress_raw(blob).view(np.uint8))
