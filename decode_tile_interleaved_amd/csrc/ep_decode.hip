@@ -8,7 +8,9 @@
 // Work mapping: one wavefront per tile of 1024 E8 vectors; lane q owns rANS
 // state q and decodes local vectors q, q+64, ..., so every step's 64 vectors
 // are contiguous and each lane writes one 8-coordinate vector per step
-// (16 bytes for BF16/FP16, 8 bytes for FP8/INT8).
+// (16 bytes for BF16/FP16, 8 bytes for FP8/INT8).  Streams for targets below
+// the overhead of 64 states have 16 per tile: lanes 0..15 decode vectors q,
+// q+16, ..., and lanes 16..63 follow along without refilling or storing.
 //
 // Per workgroup (up to 8 waves, one workgroup per CU):
 //   1. every wave starts its global loads, all vector loads that need only the

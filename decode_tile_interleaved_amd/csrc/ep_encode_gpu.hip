@@ -12,8 +12,8 @@
 //   * E8 nearest point per 8-vector (the same D8 / D8 + 1/2 rounding, parity
 //     fix and tie rule), then the 7-context model; counts in LDS, added to a
 //     global histogram;
-//   * one wave per tile, lane q = rANS state q, walking its 16 vectors and 8
-//     coordinates backwards; each lane writes its words into a slot of its
+//   * one wave per tile, lane q = rANS state q, walking its vectors (16 with
+//     64 states per tile, 64 with 16) and their 8 coordinates backwards; each lane writes its words into a slot of its
 //     own, and a second kernel lays them out in the order the decoder
 //     consumes them, behind the count bytes.
 #include <hip/hip_runtime.h>

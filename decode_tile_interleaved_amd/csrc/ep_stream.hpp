@@ -10,8 +10,8 @@
 //   scales           float32 g_r per row
 //   states           uint32 initial decoder state per (tile, state)
 //   tile offsets     uint32 word index of each tile's first word, plus the end
-//   words            uint16 words, tile after tile: 32 words of count bytes
-//                    (byte q = number of words state q consumes), then each
+//   words            uint16 words, tile after tile: states / 2 words of count
+//                    bytes (byte q = number of words state q consumes), then each
 //                    state's words in consumption order, states ascending
 // A raw stream (method 1) is the header followed by the container bytes.
 #pragma once
