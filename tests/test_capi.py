@@ -200,3 +200,29 @@ def test_target_range_sweep_matches_oracle(kind, targets):
     assert {ep.OK, ep.ERR_TARGET} <= seen
     if kind == "bf16":
         assert ep.WARN_RAW in seen
+
+
+def test_concurrent_compressions_match():
+    """Entry points are thread-safe: four threads compressing different
+    matrices at once get the streams each gets alone, and a failing call's
+    error text stays on its own thread."""
+    import threading
+    mats = [W.rowscale_gaussian(64, 1024, 8400 + i) for i in range(4)]
+    alone = [ep.compress(m, 3.0).blob for m in mats]
+    got = [None] * 4
+    errs = [None] * 4
+
+    def work(i):
+        got[i] = ep.compress(mats[i], 3.0).blob
+        try:
+            ep.compress(mats[i], float("nan"))
+        except ep.EPError as e:
+            errs[i] = e.code
+
+    th = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert all(np.array_equal(a, b) for a, b in zip(alone, got))
+    assert errs == [ep.ERR_TARGET] * 4

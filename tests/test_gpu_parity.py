@@ -165,3 +165,32 @@ def test_device_argument_errors():
                            ctypes.c_void_p(out.data_ptr()), -1, None)
     assert rc == ep.ERR_FORMAT
     torch.cuda.synchronize()
+
+
+def test_decode_replays_from_a_graph():
+    """ep_decompress enqueues kernels only (no allocation, no memset, no
+    synchronization), so it can be captured in a HIP graph: five replays,
+    with eager decodes and synchronizations between them, each equal the
+    eager result, for the single-round and the multi-tile kernel."""
+    for rows, cols in ((512, 4096), (3072, 8192)):
+        x = W.rowscale_gaussian(rows, cols, 8300)
+        p = ep.compress(x, 4.0).to("cuda")
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            ref = ep.decompress(p, stream=s)
+            out = torch.empty_like(ref)
+            ep.decompress(p, out=out, stream=s)  # warm-up outside the capture
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            ep.decompress(p, out=out, stream=s)
+        for _ in range(5):
+            out.zero_()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(s):
+                g.replay()
+            s.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+            with torch.cuda.stream(s):
+                ep.decompress(p, stream=s)  # eager work between replays
+            s.synchronize()
