@@ -37,6 +37,7 @@ METRIC = "decoded Gparams/s + achieved HBM GB/s vs peak, 4096x4096 BF16 @ 4.0 bp
 PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ep_decode_bf16_4096x4096_traffic.json")
+DEFAULT_WORKLOAD = "rowscale4096_bf16_4.0"  # the workload the counters in TRAFFIC_FILE were taken on
 KERNEL_SRC = os.path.join(ROOT, "decode_tile_interleaved_amd", "csrc", "ep_decode.hip")
 
 
@@ -44,9 +45,12 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(per_launch_algorithmic: float):
+def measured_traffic(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source."""
+    were taken on the current kernel source and on this workload (the
+    counters cover the default 4096x4096 BF16 workload only)."""
+    if workload != DEFAULT_WORKLOAD:
+        return None
     try:
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -85,7 +89,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="rowscale4096_bf16_4.0")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed decodes after the warmup steps until the clocks settle (milliseconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -241,7 +245,7 @@ def main() -> int:
         rel_l2_weights = ((ref.double() * scale.double().to(dev) - wd).norm() / wd.norm()).item()
 
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
-    traffic = measured_traffic(alg_bytes)
+    traffic = measured_traffic(args.workload)
     line = {
         "metric": METRIC,
         "value": round(numel / (ms_per_step * 1e-3) / 1e9, 3),
@@ -257,7 +261,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "rows": rows, "cols": cols, "container": str(x.dtype).split(".")[-1],
                    "target_bpp": target, "actual_bpp": round(p.actual_bpp, 5), "stream_bytes": p.nbytes,
-                   "tile": "1024 E8 vectors (8x1024 coords), 64 rANS states", "mall_rotation_copies": copies},
+                   "tile": f"1024 E8 vectors (8x1024 coords), {ep.blob_info(p.blob)['n_states']} rANS states", "mall_rotation_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
         "kernel_us": round(kernel_ms * 1e3, 3),

@@ -65,7 +65,7 @@ def ulp_diff(a: np.ndarray, b: np.ndarray, dtype) -> int:
 
 
 WORKLOADS = ["gauss256_bf16_3.5", "rowscale4096_bf16_4.0", "t4outlier3072x12288_bf16_2.75", "absmax8192_int8_3.0",
-             "absmax8192_fp8_3.0"]
+             "absmax8192_fp8_3.0", "rowscale4096_bf16_0.2"]
 RAGGED = ["ragged_1_8_bf16_0.3", "ragged_3_5_bf16_0.3", "ragged_7_13_fp16_0.2", "ragged_3_2736_bf16_0.5",
           "ragged_129_64_bf16_0.05", "ragged_64_1032_fp16_1.0", "ragged_5_4100_bf16_2.0", "ragged_1030_8_bf16_0.3",
           # more tiles than one round of workgroups covers (the multi-tile
