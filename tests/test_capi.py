@@ -226,3 +226,18 @@ def test_concurrent_compressions_match():
         t.join()
     assert all(np.array_equal(a, b) for a, b in zip(alone, got))
     assert errs == [ep.ERR_TARGET] * 4
+
+
+def test_bench_traffic_only_for_the_profiled_workload():
+    """bench.py reports counter-measured HBM traffic only for the workload the
+    committed counters were taken on, and only for the kernel source they
+    were taken on."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(os.path.dirname(__file__), "..", "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    assert bench.measured_traffic("t4outlier3072x12288_bf16_2.75") is None
+    assert bench.measured_traffic("rowscale4096_bf16_0.2") is None
+    t = bench.measured_traffic(bench.DEFAULT_WORKLOAD)
+    assert t is None or t > 0
