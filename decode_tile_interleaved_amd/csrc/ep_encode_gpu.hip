@@ -319,6 +319,27 @@ __global__ void __launch_bounds__(64) lay_out_kernel(int ns, const uint16_t *slo
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// pinned host memory, kept for the encoder's lifetime
+struct PinnedBuf {
+  void *p = nullptr;
+  size_t n = 0;
+  ~PinnedBuf() {
+    if (p) (void)hipHostFree(p);
+  }
+  bool reserve(size_t bytes) {
+    if (bytes <= n && p) return true;
+    if (p) (void)hipHostFree(p);
+    p = nullptr;
+    n = 0;
+    if (hipHostMalloc(&p, bytes, hipHostMallocDefault) != hipSuccess) {
+      p = nullptr;
+      return false;
+    }
+    n = bytes;
+    return true;
+  }
+};
+
 template <class T>
 struct DevBuf {
   T *p = nullptr;
@@ -376,13 +397,17 @@ class GpuBackend final : public EncodeBackend {
     const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4096));
     hipLaunchKernelGGL(histogram_kernel, dim3(blocks), dim3(256), 0, stream_, S_, g_.p, nsamp, hist_.p, flag_.p);
     if (hipGetLastError() != hipSuccess) return device(err, "histogram launch");
-    hist.assign((size_t)kContexts * kSymSpan, 0);
-    uint32_t over = 0;
-    if (hipMemcpyAsync(hist.data(), hist_.p, 8 * hist.size(), hipMemcpyDeviceToHost, stream_) != hipSuccess ||
-        hipMemcpyAsync(&over, flag_.p, 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+    // through pinned host memory: each rate probe copies the whole histogram
+    const size_t nh = (size_t)kContexts * kSymSpan;
+    if (!pin_.reserve(8 * nh + 8)) return nomem(err);
+    uint64_t *ph = static_cast<uint64_t *>(pin_.p);
+    uint32_t *pf = reinterpret_cast<uint32_t *>(ph + nh);
+    if (hipMemcpyAsync(ph, hist_.p, 8 * nh, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
+        hipMemcpyAsync(pf, flag_.p, 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
         hipStreamSynchronize(stream_) != hipSuccess)
       return device(err, "histogram");
-    return over ? 1 : 0;
+    hist.assign(ph, ph + nh);
+    return *pf ? 1 : 0;
   }
 
   int encode_tiles(const std::vector<float> &g, const Tables &tb, std::vector<uint32_t> &states,
@@ -486,6 +511,7 @@ class GpuBackend final : public EncodeBackend {
   DevBuf<uint32_t> flag_, fc_, dstates_, first_;
   DevBuf<uint16_t> slots_, words_;
   DevBuf<uint16_t> counts_;
+  PinnedBuf pin_;
   size_t n_words_ = 0;
 };
 
