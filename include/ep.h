@@ -69,6 +69,10 @@ struct ep_options {
  * Returns EP_OK, EP_WARN_RAW (lattice coding could not meet the target: the
  * stream holds the raw container), or a negative error (nothing allocated).
  * Input rules (API reference, "compress"): non-empty 2-D, finite values.
+ * Tiles carry 64 rANS states, or 16 when the target lies below the overhead
+ * of 64 (40 bits per state plus metadata; ep_blob_info reports which); the
+ * README's low targets need the smaller overhead, whose streams decode about
+ * 3.7x slower.
  */
 int ep_compress(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
                 uint8_t **blob_out, size_t *nbytes_out);
