@@ -10,14 +10,19 @@ Prints one JSON line.
 Timing:
   * warmup: W untimed decodes, then untimed decodes for --settle-ms (default
     300 ms) so that the GPU clocks have ramped up before the timed region;
-  * steps: K decodes captured in one HIP graph and replayed; the decodes
-    rotate over enough stream/output copies (> 2x the 256 MB MALL) that each
-    decode reads and writes HBM, not the Infinity Cache;
-  * kernel duration (roofline): HIP events on the launch stream around the
-    K replayed decodes, divided by K;
+  * steps: K decodes captured in one HIP graph and replayed once between
+    device synchronizations; `value` is numel * K / that wall time (whole-job
+    throughput, host launch included).  The decodes rotate over enough
+    stream/output copies (> 2x the 256 MB MALL) that each decode reads and
+    writes HBM, not the Infinity Cache;
+  * kernel duration (roofline): HIP events on the launch stream around
+    back-to-back replays of that graph, at least --roofline-launches (200)
+    launches in all, divided by the launch count.  One replay of a few
+    launches would also time the gap before the graph's first kernel, which
+    rocprof's per-kernel durations do not contain;
   * cpu_baseline: the CPU oracle's decoder on the same stream, tiles split
-    over every host core the process may use (and on one thread, as
-    cpu_baseline_1thread).
+    over the host cores the process may use, at most the 16 a GPU's share of
+    the host holds (and on one thread, as cpu_baseline_1thread).
 """
 from __future__ import annotations
 
@@ -65,7 +70,8 @@ def cpu_baseline(blob, numel: int):
     use (tiles split into contiguous ranges, one thread each), and on one
     thread.  Median of 3 whole-stream decodes each, reconstruction included."""
     import oracle
-    cores = min(16, len(os.sched_getaffinity(0)))  # at most the CPU share one GPU's host gets
+    available = len(os.sched_getaffinity(0))
+    cores = min(16, available)  # the host cores one GPU's share of the box holds
 
     def median_s(fn):
         runs = []
@@ -79,7 +85,7 @@ def cpu_baseline(blob, numel: int):
     t_one = median_s(lambda: oracle.decompress_raw(blob))
     sample = f"whole stream ({numel} params), median of 3 decodes incl. reconstruction"
     return ({"value": round(numel / t_all / 1e9, 5), "unit": "Gparams/s", "cores": cores, "kind": "oracle",
-             "sample": sample + f", tiles split over {cores} threads"},
+             "cores_available": available, "sample": sample + f", tiles split over {cores} threads"},
             {"value": round(numel / t_one / 1e9, 5), "unit": "Gparams/s", "cores": 1, "kind": "oracle",
              "sample": sample + ", one thread"})
 
@@ -92,6 +98,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed decodes after the warmup steps until the clocks settle (milliseconds)")
+    ap.add_argument("--roofline-launches", type=int, default=200,
+                    help="launches timed back to back for the roofline's kernel duration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager-only", action="store_true", help="skip the graph replay (profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -206,7 +214,22 @@ def main() -> int:
             t_end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    kernel_ms = t_start.elapsed_time(t_end) / args.steps  # average launch duration over the timed region
+    region_kernel_ms = t_start.elapsed_time(t_end) / args.steps  # includes the gap before the graph's first kernel
+    # roofline: the same graph replayed back to back until at least
+    # --roofline-launches decodes have run between one pair of events
+    kernel_ms = region_kernel_ms
+    launches = args.steps
+    if not args.eager_only:
+        reps = max(1, math.ceil(args.roofline_launches / args.steps))
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            r0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            r1.record(stream)
+        torch.cuda.synchronize()
+        launches = reps * args.steps
+        kernel_ms = r0.elapsed_time(r1) / launches
     ms_per_step = wall * 1e3 / args.steps
 
     # context only: the same decodes on one resident stream/output (warm
@@ -265,6 +288,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
         "kernel_us": round(kernel_ms * 1e3, 3),
+        "kernel_us_launches": launches,
+        "kernel_us_timed_region": round(region_kernel_ms * 1e3, 3),
         "kernel_us_eager_events": round(eager_ms * 1e3, 3),
         "kernel_us_warm": round(warm_ms * 1e3, 3) if warm_ms is not None else None,
         "clock_settle_s": round(settle_s, 3),

@@ -81,8 +81,13 @@ struct StreamView {
   uint64_t off_freq = 0;                // byte offset of the frequency array
 };
 
+// true if [off, off + size) lies inside [0, n); no addition can wrap
+inline bool inside(uint64_t off, uint64_t size, uint64_t n) { return off <= n && size <= n - off; }
+
 // Parses and bounds-checks the header and table directory.  Returns an empty
-// string on success, else a description of the problem.
+// string on success, else a description of the problem.  Every bound is
+// written as off <= n && size <= n - off and every product is taken on
+// values capped first, so no header, however corrupt, makes a check wrap.
 inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
   if (!b) return "null stream";
   if (n < kHeaderBytes) return "stream shorter than its header";
@@ -94,14 +99,17 @@ inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
   if (s.method > 1 || s.dtype > 3) return "bad method or dtype";
   s.rows = (int64_t)rd<uint64_t>(b + hdr::rows);
   s.cols = (int64_t)rd<uint64_t>(b + hdr::cols);
-  if (s.rows <= 0 || s.cols <= 0 || s.rows > (int64_t(1) << 40) || s.cols > (int64_t(1) << 40)) return "bad shape";
+  // both below 2^31 and their product below 2^40: every product below fits 64 bits
+  if (s.rows <= 0 || s.cols <= 0 || s.rows >= (int64_t(1) << 31) || s.cols >= (int64_t(1) << 31) ||
+      (uint64_t)s.rows * (uint64_t)s.cols >= (uint64_t(1) << 40))
+    return "bad shape";
   s.total = rd<uint64_t>(b + hdr::total);
   if (s.total != n) return "stream length does not match its header";
   s.target = rd<double>(b + hdr::target);
   if (s.method == kRaw) {
     s.off_words = rd<uint64_t>(b + hdr::off_words);
-    uint64_t payload = (uint64_t)s.rows * (uint64_t)s.cols * elem_bytes(s.dtype);
-    if (s.off_words != kHeaderBytes || kHeaderBytes + payload > n) return "raw payload out of bounds";
+    const uint64_t payload = (uint64_t)s.rows * (uint64_t)s.cols * elem_bytes(s.dtype);
+    if (s.off_words != kHeaderBytes || !inside(kHeaderBytes, payload, n)) return "raw payload out of bounds";
     return "";
   }
   s.prob_bits = b[hdr::prob_bits];
@@ -112,6 +120,7 @@ inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
   s.cols8 = (int64_t)rd<uint64_t>(b + hdr::cols8);
   if (s.cols8 != (s.cols + 7) / 8 * 8) return "bad padded column count";
   s.n_vec = s.rows * (s.cols8 / 8);
+  if (s.n_vec >= (int64_t(1) << 31)) return "stream too large";
   s.tiles = rd<uint32_t>(b + hdr::tiles);
   if (s.tiles != (s.n_vec + kTileVecs - 1) / kTileVecs) return "bad tile count";
   s.scale_a = rd<double>(b + hdr::scale_a);
@@ -121,7 +130,7 @@ inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
   s.off_tile_offsets = rd<uint64_t>(b + hdr::off_tile_offsets);
   s.off_words = rd<uint64_t>(b + hdr::off_words);
   s.n_words = rd<uint64_t>(b + hdr::n_words);
-  if (s.off_tables != kHeaderBytes) return "bad table offset";
+  if (s.off_tables != kHeaderBytes || !inside(s.off_tables, 4 * kContexts, n)) return "bad table offset";
   uint64_t nsum = 0;
   for (int c = 0; c < kContexts; ++c) {
     s.smin[c] = rd<int16_t>(b + s.off_tables + 4 * c);
@@ -130,10 +139,15 @@ inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
     nsum += s.nsym[c];
   }
   s.off_freq = s.off_tables + 4 * kContexts;
-  const uint64_t T = (uint64_t)s.tiles;
-  if (s.off_scales < s.off_freq + 2 * nsum || (s.off_scales & 15) || s.off_states < s.off_scales + 4 * (uint64_t)s.rows ||
-      (s.off_states & 15) || s.off_tile_offsets < s.off_states + 4 * T * (uint64_t)s.states || (s.off_tile_offsets & 15) ||
-      s.off_words < s.off_tile_offsets + 4 * (T + 1) || (s.off_words & 15) || s.off_words + 2 * s.n_words > n)
+  const uint64_t T = (uint64_t)s.tiles;  // below 2^22: every size below is small
+  // sections in order, each inside the stream and 16-byte aligned, none
+  // overlapping the one before it
+  if (!inside(s.off_freq, 2 * nsum, n) || s.off_scales < s.off_freq + 2 * nsum || (s.off_scales & 15) ||
+      !inside(s.off_scales, 4 * (uint64_t)s.rows, n) || s.off_states < s.off_scales + 4 * (uint64_t)s.rows ||
+      (s.off_states & 15) || !inside(s.off_states, 4 * T * (uint64_t)s.states, n) ||
+      s.off_tile_offsets < s.off_states + 4 * T * (uint64_t)s.states || (s.off_tile_offsets & 15) ||
+      !inside(s.off_tile_offsets, 4 * (T + 1), n) || s.off_words < s.off_tile_offsets + 4 * (T + 1) ||
+      (s.off_words & 15) || s.n_words > n || !inside(s.off_words, 2 * s.n_words, n))
     return "section table out of bounds";
   if (n - s.off_words < align16(2 * s.n_words)) return "word section not padded";
   return "";

@@ -903,29 +903,37 @@ typedef struct {
   uint64_t o_tab, o_sc, o_st, o_to, o_w, n_words, total;
 } or_header;
 
+/* [off, off + size) inside [0, nb), written so that no sum can wrap */
+static int span_ok(uint64_t off, uint64_t size, uint64_t nb) { return off <= nb && size <= nb - off; }
+
+/* Header and section table.  Rows and columns are capped below 2^31 (and
+ * their product below 2^40) before any product is formed, and every section
+ * bound is checked as an offset and a size against the stream length, so a
+ * corrupt header cannot make a check overflow. */
 static int parse_header(const uint8_t *b, size_t nb, or_header *h) {
   if (!b || nb < OR_HDR) return OR_ERR_FORMAT;
   if (get_u32(b) != OR_MAGIC || get_u16(b + 4) != OR_VERSION || get_u16(b + 6) != OR_HDR) return OR_ERR_FORMAT;
   h->method = b[8];
   h->dtype = b[9];
   if (h->dtype > 3 || h->method > 1) return OR_ERR_FORMAT;
-  int64_t R = (int64_t)get_u64(b + 24), C = (int64_t)get_u64(b + 32);
-  if (R <= 0 || C <= 0) return OR_ERR_FORMAT;
+  uint64_t R = get_u64(b + 24), C = get_u64(b + 32);
+  if (R == 0 || C == 0 || R >= ((uint64_t)1 << 31) || C >= ((uint64_t)1 << 31) || R * C >= ((uint64_t)1 << 40))
+    return OR_ERR_FORMAT;
   h->total = get_u64(b + 112);
   if (h->total != nb) return OR_ERR_FORMAT;
   h->target = get_f64(b + 56);
   if (h->method == 1) {
-    geom_init(&h->g, R, C, 64, 11);
+    geom_init(&h->g, (int64_t)R, (int64_t)C, 64, 11);
     h->o_w = get_u64(b + 96);
-    if (h->o_w != OR_HDR || OR_HDR + (uint64_t)R * (uint64_t)C * (uint64_t)esize_of(h->dtype) > nb)
-      return OR_ERR_FORMAT;
+    if (h->o_w != OR_HDR || !span_ok(OR_HDR, R * C * (uint64_t)esize_of(h->dtype), nb)) return OR_ERR_FORMAT;
     return OR_OK;
   }
   int pb = b[10];
   if (pb < 8 || pb > 12 || b[11] != OR_NCTX) return OR_ERR_FORMAT;
   int64_t S = get_u32(b + 16);
   if (get_u32(b + 12) != 1024 || S < 1 || S > 1024) return OR_ERR_FORMAT;
-  geom_init(&h->g, R, C, S, pb);
+  if (R * ((C + 7) / 8) >= ((uint64_t)1 << 31)) return OR_ERR_FORMAT;
+  geom_init(&h->g, (int64_t)R, (int64_t)C, S, pb);
   if ((int64_t)get_u64(b + 40) != h->g.Cp || (int64_t)get_u32(b + 20) != h->g.T) return OR_ERR_FORMAT;
   h->a = get_f64(b + 48);
   h->o_tab = get_u64(b + 64);
@@ -934,9 +942,12 @@ static int parse_header(const uint8_t *b, size_t nb, or_header *h) {
   h->o_to = get_u64(b + 88);
   h->o_w = get_u64(b + 96);
   h->n_words = get_u64(b + 104);
-  if (h->o_tab != OR_HDR || h->o_sc < h->o_tab + 4 * OR_NCTX || h->o_st < h->o_sc + 4 * (uint64_t)R ||
-      h->o_to < h->o_st + 4 * (uint64_t)(h->g.T * S) || h->o_w < h->o_to + 4 * (uint64_t)(h->g.T + 1) ||
-      h->o_w + 2 * h->n_words > nb)
+  uint64_t T = (uint64_t)h->g.T; /* below 2^21 here */
+  if (h->o_tab != OR_HDR || !span_ok(h->o_tab, 4 * OR_NCTX, nb)) return OR_ERR_FORMAT;
+  if (!span_ok(h->o_sc, 4 * R, nb) || h->o_sc < h->o_tab + 4 * OR_NCTX ||
+      !span_ok(h->o_st, 4 * T * (uint64_t)S, nb) || h->o_st < h->o_sc + 4 * R ||
+      !span_ok(h->o_to, 4 * (T + 1), nb) || h->o_to < h->o_st + 4 * T * (uint64_t)S ||
+      h->n_words > nb || !span_ok(h->o_w, 2 * h->n_words, nb) || h->o_w < h->o_to + 4 * (T + 1))
     return OR_ERR_FORMAT;
   return OR_OK;
 }

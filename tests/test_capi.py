@@ -241,3 +241,48 @@ def test_bench_traffic_only_for_the_profiled_workload():
     assert bench.measured_traffic("rowscale4096_bf16_0.2") is None
     t = bench.measured_traffic(bench.DEFAULT_WORKLOAD)
     assert t is None or t > 0
+
+
+def _forged(blob, n=None, **fields):
+    """A copy of `blob` (truncated or zero-extended to n bytes) with header
+    fields overwritten: name -> (byte offset, numpy dtype, value); the total
+    field is set to the new length."""
+    n = blob.size if n is None else n
+    out = np.zeros(n, np.uint8)
+    out[:min(n, blob.size)] = blob[:min(n, blob.size)]
+    out[112:120] = np.array([n], np.uint64).view(np.uint8)
+    for off, dt, val in fields.values():
+        out[off:off + np.dtype(dt).itemsize] = np.array([val], dt).view(np.uint8)
+    return out
+
+
+def test_malformed_headers_rejected_without_overreads():
+    """Headers whose fields would make an unchecked reader run past the
+    stream: a lattice header with nothing after it (the table directory lies
+    beyond the 128 bytes), a word section whose offset plus size wraps 64 bits,
+    raw and lattice shapes whose element counts overflow.  Both the library
+    and the oracle report a format error; neither reads past the buffer (the
+    checks are written as offset <= n and size <= n - offset)."""
+    x, target = W.make("gauss256_bf16_3.5")
+    p = ep.compress(x, target)
+    b = p.blob
+    cases = {
+        "header_only": _forged(b, 128),
+        "word_section_wraps": _forged(b, 4096, off_words=(96, np.uint64, (1 << 40) + 272),
+                                      n_words=(104, np.uint64, (1 << 64) - (1 << 39))),
+        "words_past_end": _forged(b, n_words=(104, np.uint64, b.size)),
+        "raw_count_overflows": _forged(b, 4096, method=(8, np.uint8, 1), rows=(24, np.uint64, 1 << 33),
+                                       cols=(32, np.uint64, 1 << 33), off_words=(96, np.uint64, 128)),
+        "lattice_count_overflows": _forged(b, rows=(24, np.uint64, (1 << 62) + 1)),
+        "scales_past_end": _forged(b, off_scales=(72, np.uint64, (1 << 64) - 16)),
+    }
+    for name, bad in cases.items():
+        with pytest.raises(ep.EPError) as e:
+            ep.blob_info(bad)
+        assert e.value.code == ep.ERR_FORMAT, name
+        assert np.isnan(ep.lib().ep_actual_bpp(bad.ctypes.data, bad.size)), name
+        # the decode entry point rejects it on the host, before any device work
+        assert ep.lib().ep_decompress(bad.ctypes.data, bad.size, None, None, -1, None) == ep.ERR_FORMAT, name
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.info(bad)
+        assert e.value.rc == oracle.ERR_FORMAT, name
