@@ -44,12 +44,32 @@
 #define OR_NCTX 7
 #define OR_HDR 128
 #define OR_MAGIC 0x314B5045u /* "EPK1" little-endian */
-#define OR_VERSION 1
-#define OR_STATE_BITS 32.0  /* estimated stream bits per rANS state beyond its symbols' information */
+#define OR_VERSION 2
 #define OR_STATES_DEFAULT 64 /* rANS states per tile */
 #define OR_STATES_LOW 16     /* per tile when the target is below the overhead of 64 */
-#define OR_STATE_MIN_BITS 40.0 /* stored bits of a state that emits no word: its 32-bit state and count byte */
-#define OR_STATE_L 8192u     /* rANS lower state bound L = 2^13; states lie in [L, 2^29); words are 16 bits */
+#define OR_STATE_L 2048u     /* rANS lower state bound L = 2^11; states lie in [L, 2^27); words are 16 bits */
+#define OR_STATE_TOP 27      /* log2(L) + 16: the encoder emits a word while x >= f * 2^(27 - prob_bits) */
+/*
+ * Stream bits a state costs beyond the information of its symbols, as the
+ * rate estimate counts them.  A tile stores per state half a pair-count byte
+ * and a 4-bit length code (8 bits), and the start state x_f at its bit length
+ * W less its implicit leading one: W - 1 = floor(log2 x_f) bits.  The symbols'
+ * information equals the words plus log2(x_f / L), so the state's own cost is
+ * 8 + 11 + floor(log2 x_f) - log2 x_f, on average 18.5 bits; a state that
+ * codes nothing costs 19.
+ */
+#define OR_STATE_BITS 18.5
+#define OR_STATE_MIN_BITS 19.0
+/* the start bits of a tile end on a whole word (7.5 bits of padding on
+ * average), and the word section ends on 16 bytes (60 bits on average) */
+#define OR_TILE_PAD_BITS 7.5
+#define OR_WORDS_PAD_BITS 60.0
+/* matrices of fewer E8 vectors than this get 512-vector tiles when they have
+ * 64 states per tile (twice the tiles, so twice the parallel rANS states),
+ * larger ones 1024-vector tiles */
+#define OR_SMALL_MATRIX_VECS 4194304
+/* stride sample of the rate estimate, vectors */
+#define OR_SAMPLE_VECS 65536
 
 static int esize_of(int dt) { return (dt == OR_BF16 || dt == OR_FP16) ? 2 : 1; }
 
@@ -312,28 +332,42 @@ typedef struct {
   int64_t R, C, Cp;    /* rows, columns, columns padded to a multiple of 8 */
   int64_t vpr;         /* vectors per row */
   int64_t n_vec;
-  int64_t tile_vecs;
-  int64_t S;           /* rANS states per tile */
+  int64_t tile_vecs;   /* E8 vectors per tile: a multiple of S */
+  int64_t S;           /* rANS states per tile (16 or 64) */
   int64_t T;           /* tiles */
   int prob_bits;
 } or_geom;
 
-static void geom_init(or_geom *g, int64_t R, int64_t C, int64_t S, int prob_bits) {
+static void geom_init(or_geom *g, int64_t R, int64_t C, int64_t S, int64_t tile_vecs, int prob_bits) {
   g->R = R;
   g->C = C;
   g->Cp = (C + 7) / 8 * 8;
   g->vpr = g->Cp / 8;
   g->n_vec = R * g->vpr;
-  g->tile_vecs = 1024;
+  g->tile_vecs = tile_vecs;
   g->S = S;
   g->T = (g->n_vec + g->tile_vecs - 1) / g->tile_vecs;
   g->prob_bits = prob_bits;
 }
 
-/* bytes of everything except states and words, with section padding */
+/* bytes of everything except the word section, with section padding */
 static uint64_t meta_bytes(const or_geom *g, int nsym_total) {
   return OR_HDR + pad16(4 * OR_NCTX + 2 * (uint64_t)nsym_total) + pad16(4 * (uint64_t)g->R) +
          pad16(4 * (uint64_t)(g->T + 1));
+}
+
+/* estimated stream bits: the symbols' information plus every state's cost
+ * plus the padding and the metadata */
+static double stream_bits(const or_geom *g, double info, int nsym_total) {
+  return info + OR_STATE_BITS * (double)(g->S * g->T) + OR_TILE_PAD_BITS * (double)g->T + OR_WORDS_PAD_BITS +
+         8.0 * (double)meta_bytes(g, nsym_total);
+}
+
+/* the least a stream of this geometry can cost, in bits per element: every
+ * state coding nothing */
+static double floor_bpp(const or_geom *g) {
+  return (OR_STATE_MIN_BITS * (double)(g->S * g->T) + 8.0 * (double)meta_bytes(g, OR_NCTX)) /
+         ((double)g->R * (double)g->C);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -353,15 +387,23 @@ static int quantize_all(const double *x, const or_geom *g, const float *gs, int3
 /* ------------------------------------------------------------------------ */
 /* Interleaved rANS over one tile.                                           */
 /* Decode order: step s, coordinate j, state q (ascending), for local vector */
-/* i = s*S + q when i < n.  The first min(n, S) states are active.           */
+/* i = s*S + q when i < n (steps = tile_vecs / S vectors per state).         */
 /* Decode: slot = x mod M; x = f*(x >> prob_bits) + slot - c;                */
 /*         if x < L: x = (x << 16) | w, w = state q's next word.             */
-/* Encode: if x >= f * 2^(29 - prob_bits): emit x & 0xffff, x >>= 16;       */
+/* Encode (every state starts at x = L, walking the decode order backwards): */
+/*         if x >= f * 2^(27 - prob_bits): emit x & 0xffff, x >>= 16;       */
 /*         x = (x / f) * M + (x mod f) + c.                                  */
-/* Tile word layout: one count byte per state (the number of words it        */
-/* consumes; states ascending, two to a 16-bit word, the last word padded    */
-/* with 0), then every state's words in the order it consumes them, states   */
-/* ascending.                                                                */
+/* The final encoder state is the decoder's start state, in [2^11, 2^27).    */
+/*                                                                           */
+/* Tile word layout (16-bit words, little-endian):                          */
+/*   S/4 words of pair counts: byte k = words in the region of states 2k,   */
+/*     2k+1;                                                                 */
+/*   S/4 words of length codes: nibble q (word q/4, bits 4(q%4)..) = W - 12, */
+/*     W the bit length of state q's start state;                           */
+/*   the start states' low W - 1 bits (the leading one is implied), states  */
+/*     ascending, least significant bit first, zero-padded to a whole word; */
+/*   region k: state 2k's words in the order it consumes them, then state   */
+/*     2k+1's words in reverse order (it reads its region from the end).    */
 /* ------------------------------------------------------------------------ */
 typedef struct {
   uint16_t *w;
@@ -380,28 +422,48 @@ static int words_push(or_words *ws, uint16_t w) {
   return OR_OK;
 }
 
-/* v: the matrix's lattice coordinates; appends the tile's words to out */
-static int encode_tile(const or_geom *g, const or_tables *t, const int32_t *v, int64_t tile,
-                       uint32_t *states, or_words *out) {
+static int bit_length(uint32_t x) {
+  int n = 0;
+  while (x) { n++; x >>= 1; }
+  return n;
+}
+
+/* A bit string of at most 64 states x 26 bits, least significant bit first. */
+typedef struct {
+  uint16_t w[OR_STATES_DEFAULT * 2];
+  int nbits;
+} or_bitbuf;
+
+static void bits_put(or_bitbuf *bb, uint32_t value, int nbits) {
+  for (int i = 0; i < nbits; i++) {
+    if ((value >> i) & 1u) bb->w[bb->nbits >> 4] |= (uint16_t)(1u << (bb->nbits & 15));
+    bb->nbits++;
+  }
+}
+
+/* v: the matrix's lattice coordinates; appends the tile's words to out.
+ * Returns OR_WARN_RAW if a pair's word count does not fit its byte. */
+static int encode_tile(const or_geom *g, const or_tables *t, const int32_t *v, int64_t tile, or_words *out) {
   int64_t first = tile * g->tile_vecs;
   int64_t n = g->n_vec - first;
   if (n > g->tile_vecs) n = g->tile_vecs;
-  int64_t steps = (g->tile_vecs + g->S - 1) / g->S;
+  int64_t steps = g->tile_vecs / g->S;
   uint32_t M = 1u << g->prob_bits;
+  int S = (int)g->S;
   int rc = OR_OK;
+  uint32_t x[OR_STATES_DEFAULT];
   or_words rev = {0, 0, 0};
-  int32_t *owner = NULL;            /* state that emitted each reversed word */
+  int32_t *owner = NULL; /* state that emitted each reversed word */
   uint64_t owner_cap = 0;
-  int64_t *cnt = (int64_t *)calloc((size_t)g->S, sizeof(int64_t));
-  int64_t *start = (int64_t *)calloc((size_t)g->S + 1, sizeof(int64_t));
-  int64_t *cur = (int64_t *)calloc((size_t)g->S, sizeof(int64_t));
+  int64_t cnt[OR_STATES_DEFAULT], start[OR_STATES_DEFAULT + 1], cur[OR_STATES_DEFAULT];
   uint16_t *lane_words = NULL;
-  if (!cnt || !start || !cur) { rc = OR_ERR_NOMEM; goto done; }
-  for (int64_t q = 0; q < g->S; q++) states[q] = OR_STATE_L;
+  or_bitbuf bb;
+  memset(&bb, 0, sizeof(bb));
+  for (int q = 0; q < S; q++) { x[q] = OR_STATE_L; cnt[q] = 0; cur[q] = 0; }
   for (int64_t s = steps - 1; s >= 0; s--)
     for (int j = 7; j >= 0; j--)
-      for (int64_t q = g->S - 1; q >= 0; q--) {
-        int64_t i = s * g->S + q;
+      for (int q = S - 1; q >= 0; q--) {
+        int64_t i = s * S + q;
         if (i >= n) continue;
         int64_t vid = first + i;
         int64_t r = vid / g->vpr, k = vid % g->vpr;
@@ -410,62 +472,77 @@ static int encode_tile(const or_geom *g, const or_tables *t, const int32_t *v, i
         vector_symbols(v + r * g->Cp + 8 * k, ctx, sym);
         int si = sym[j] - t->smin[ctx[j]];
         uint32_t f = t->freq[ctx[j]][si], c = t->cum[ctx[j]][si];
-        uint32_t x = states[q];
-        if ((uint64_t)x >= ((uint64_t)f << (29 - g->prob_bits))) {
-          if ((rc = words_push(&rev, (uint16_t)(x & 0xffffu)))) goto done;
+        uint32_t xs = x[q];
+        if ((uint64_t)xs >= ((uint64_t)f << (OR_STATE_TOP - g->prob_bits))) {
+          if ((rc = words_push(&rev, (uint16_t)(xs & 0xffffu)))) goto done;
           if (rev.n > owner_cap) {
             owner_cap = rev.cap;
             int32_t *no = (int32_t *)realloc(owner, owner_cap * sizeof(int32_t));
             if (!no) { rc = OR_ERR_NOMEM; goto done; }
             owner = no;
           }
-          owner[rev.n - 1] = (int32_t)q;
-          x >>= 16;
+          owner[rev.n - 1] = q;
+          xs >>= 16;
         }
-        x = (x / f) * M + (x % f) + c;
-        states[q] = x;
+        x[q] = (xs / f) * M + (xs % f) + c;
       }
-  /* standard (consumption) order is the reverse of emission order; split it
-   * into per-state word lists */
+  /* consumption order is the reverse of emission order; split it into
+   * per-state lists */
   for (uint64_t k = 0; k < rev.n; k++) cnt[owner[k]]++;
-  for (int64_t q = 0; q < g->S; q++) start[q + 1] = start[q] + cnt[q];
+  start[0] = 0;
+  for (int q = 0; q < S; q++) start[q + 1] = start[q] + cnt[q];
   lane_words = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(rev.n + 1));
   if (!lane_words) { rc = OR_ERR_NOMEM; goto done; }
   for (uint64_t k = rev.n; k > 0; k--) {
     int32_t q = owner[k - 1];
     lane_words[start[q] + cur[q]++] = rev.w[k - 1];
   }
-  /* count bytes, then the per-state lists back to back */
-  for (int64_t q = 0; q < g->S; q += 2) {
-    int64_t hi = q + 1 < g->S ? cnt[q + 1] : 0;
-    if (cnt[q] > 255 || hi > 255) { rc = OR_WARN_RAW; goto done; } /* a count byte cannot hold it: encoding failure */
-    if ((rc = words_push(out, (uint16_t)(cnt[q] | (hi << 8))))) goto done;
+  /* pair counts */
+  for (int q = 0; q < S; q += 4) {
+    int64_t lo = cnt[q] + cnt[q + 1], hi = cnt[q + 2] + cnt[q + 3];
+    if (lo > 255 || hi > 255) { rc = OR_WARN_RAW; goto done; } /* a count byte cannot hold it: encoding failure */
+    if ((rc = words_push(out, (uint16_t)(lo | (hi << 8))))) goto done;
   }
-  for (uint64_t k = 0; k < rev.n; k++)
-    if ((rc = words_push(out, lane_words[k]))) goto done;
+  /* length codes */
+  for (int q = 0; q < S; q += 4) {
+    uint32_t w = 0;
+    for (int i = 0; i < 4; i++) w |= (uint32_t)(bit_length(x[q + i]) - 12) << (4 * i);
+    if ((rc = words_push(out, (uint16_t)w))) goto done;
+  }
+  /* start states below their leading one */
+  for (int q = 0; q < S; q++) {
+    int W = bit_length(x[q]);
+    bits_put(&bb, x[q], W - 1);
+  }
+  for (int k = 0; k < (bb.nbits + 15) / 16; k++)
+    if ((rc = words_push(out, bb.w[k]))) goto done;
+  /* pair regions */
+  for (int q = 0; q < S; q += 2) {
+    for (int64_t k = 0; k < cnt[q]; k++)
+      if ((rc = words_push(out, lane_words[start[q] + k]))) goto done;
+    for (int64_t k = cnt[q + 1] - 1; k >= 0; k--)
+      if ((rc = words_push(out, lane_words[start[q + 1] + k]))) goto done;
+  }
 done:
   free(rev.w);
   free(owner);
-  free(cnt);
-  free(start);
-  free(cur);
   free(lane_words);
   return rc;
 }
 
 /* ------------------------------------------------------------------------ */
 /* Stream writer.                                                            */
-/* header(128) | tables | scales f32[R] | states u32[T*S] |                  */
-/* tile word offsets u32[T+1] | words u16[n_words]; sections 16-aligned.     */
+/* header(128) | tables | scales f32[R] | tile word offsets u32[T+1] |       */
+/* words u16[n_words]; sections 16-aligned.  The header's states-section    */
+/* offset (byte 80) is 0: start states live in the tiles.                   */
 /* ------------------------------------------------------------------------ */
 static int write_lattice_blob(const or_geom *g, int dtype, double a, double target, const or_tables *t,
-                              const float *gs, const uint32_t *states, const uint32_t *toff,
-                              const or_words *ws, uint8_t **blob, size_t *nbytes) {
+                              const float *gs, const uint32_t *toff, const or_words *ws, uint8_t **blob,
+                              size_t *nbytes) {
   int nsym = tables_total_nsym(t);
   uint64_t o_tab = OR_HDR;
   uint64_t o_sc = o_tab + pad16(4 * OR_NCTX + 2 * (uint64_t)nsym);
-  uint64_t o_st = o_sc + pad16(4 * (uint64_t)g->R);
-  uint64_t o_to = o_st + pad16(4 * (uint64_t)(g->T * g->S));
+  uint64_t o_to = o_sc + pad16(4 * (uint64_t)g->R);
   uint64_t o_w = o_to + pad16(4 * (uint64_t)(g->T + 1));
   uint64_t total = o_w + pad16(2 * ws->n);
   uint8_t *b = (uint8_t *)calloc(total, 1);
@@ -487,7 +564,7 @@ static int write_lattice_blob(const or_geom *g, int dtype, double a, double targ
   put_f64(b + 56, target);
   put_u64(b + 64, o_tab);
   put_u64(b + 72, o_sc);
-  put_u64(b + 80, o_st);
+  put_u64(b + 80, 0);
   put_u64(b + 88, o_to);
   put_u64(b + 96, o_w);
   put_u64(b + 104, ws->n);
@@ -504,7 +581,6 @@ static int write_lattice_blob(const or_geom *g, int dtype, double a, double targ
       p += 2;
     }
   for (int64_t r = 0; r < g->R; r++) put_f32(b + o_sc + 4 * r, gs[r]);
-  for (int64_t i = 0; i < g->T * g->S; i++) put_u32(b + o_st + 4 * i, states[i]);
   for (int64_t i = 0; i <= g->T; i++) put_u32(b + o_to + 4 * i, toff[i]);
   for (uint64_t i = 0; i < ws->n; i++) put_u16(b + o_w + 2 * i, ws->w[i]);
   *blob = b;
@@ -538,18 +614,20 @@ static int write_raw_blob(int64_t R, int64_t C, int dtype, double target, const 
 /* ------------------------------------------------------------------------ */
 /* Full compression at a fixed lattice scale a.                              */
 /* ------------------------------------------------------------------------ */
+static long or_encodes; /* full encodes (compress_at calls) since the last or_compress began */
+
 static int compress_at(const double *x, const or_geom *g, int dtype, double a, double target,
                        uint8_t **blob, size_t *nbytes) {
   int rc;
+  or_encodes++;
   float *gs = (float *)malloc(sizeof(float) * (size_t)g->R);
   int32_t *v = (int32_t *)malloc(sizeof(int32_t) * (size_t)(g->R * g->Cp));
-  uint32_t *states = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(g->T * g->S));
   uint32_t *toff = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(g->T + 1));
   or_hist *h = (or_hist *)calloc(1, sizeof(or_hist));
   or_tables t;
   memset(&t, 0, sizeof(t));
   or_words ws = {0, 0, 0};
-  if (!gs || !v || !states || !toff || !h) { rc = OR_ERR_NOMEM; goto done; }
+  if (!gs || !v || !toff || !h) { rc = OR_ERR_NOMEM; goto done; }
   for (int64_t r = 0; r < g->R; r++) gs[r] = stored_scale(row_rms(x + r * g->C, g->C), a);
   rc = quantize_all(x, g, gs, v);
   if (rc) goto done;
@@ -568,16 +646,15 @@ static int compress_at(const double *x, const or_geom *g, int dtype, double a, d
   for (int64_t tile = 0; tile < g->T; tile++) {
     if (ws.n > 0xffffffffu) { rc = OR_ERR_SHAPE; goto done; }
     toff[tile] = (uint32_t)ws.n;
-    rc = encode_tile(g, &t, v, tile, states + tile * g->S, &ws);
+    rc = encode_tile(g, &t, v, tile, &ws);
     if (rc) goto done;
   }
   if (ws.n > 0xffffffffu) { rc = OR_ERR_SHAPE; goto done; }
   toff[g->T] = (uint32_t)ws.n;
-  rc = write_lattice_blob(g, dtype, a, target, &t, gs, states, toff, &ws, blob, nbytes);
+  rc = write_lattice_blob(g, dtype, a, target, &t, gs, toff, &ws, blob, nbytes);
 done:
   free(gs);
   free(v);
-  free(states);
   free(toff);
   free(h);
   free(ws.w);
@@ -587,31 +664,45 @@ done:
 
 /* ------------------------------------------------------------------------ */
 /* Sampled storage estimate (the pages' resolution selection without         */
-/* repeated full-stream encoding).  S = min(n_vec, 65536) vectors at indices */
-/* floor(k * n_vec / S); tables are built from the sample alone;             */
-/* bits = (n_vec/S) * sum c_s (prob_bits - log2 f_s) + 32 * states           */
-/*        + 8 * (header, tables, scales, tile offsets).                      */
-/* 32 bits per state: 13 for the fixed final state L, on average 11 unused   */
-/* high bits of the stored 32-bit start state (log-uniform in [2^13, 2^29)), */
-/* A state absorbs up to 16 bits of information before it emits a word, so  */
-/* it never costs less than its 32 stored bits and count byte: the state     */
-/* part of the estimate is max(40 * states, information + 32 * states).      */
-/* and the state's 8-bit word count.  Out-of-range lattice values give +inf. */
+/* repeated full-stream encoding).  n = min(n_vec, sample_vecs) vectors at   */
+/* indices floor(k * n_vec / n) + phase, phase = seed mod floor(n_vec / n);  */
+/* tables are built from the sample alone;                                   */
+/* bits = (n_vec / n) * sum_s c_s (prob_bits - log2 f_s)                     */
+/*        + 18.5 per state + padding + 8 * (header, tables, scales, offsets) */
+/* (stream_bits above).  Out-of-range lattice values give +inf.             */
 /* ------------------------------------------------------------------------ */
-#define OR_SAMPLE_VECS 65536
+typedef struct {
+  int64_t vecs;  /* sample size (vectors) */
+  uint64_t seed; /* sample phase */
+} or_sample;
 
-/* information bits plus the states' overhead, for n states */
-static double state_part(double info, double n) {
-  const double asymptotic = info + OR_STATE_BITS * n, least = OR_STATE_MIN_BITS * n;
-  return asymptotic > least ? asymptotic : least;
+static int64_t sample_size(const or_geom *g, const or_sample *sp) {
+  return g->n_vec < sp->vecs ? g->n_vec : sp->vecs;
 }
 
-double or_estimate_bpp_rows(const double *x, const double *rms, const or_geom *g, double a) {
-  int64_t S = g->n_vec < OR_SAMPLE_VECS ? g->n_vec : OR_SAMPLE_VECS;
+/* vector index of sample k of n */
+static int64_t sample_vid(const or_geom *g, const or_sample *sp, int64_t k, int64_t n) {
+  uint64_t stride = (uint64_t)g->n_vec / (uint64_t)n;
+  uint64_t phase = sp->seed % stride;
+  return (int64_t)(((uint64_t)k * (uint64_t)g->n_vec) / (uint64_t)n + phase);
+}
+
+static double info_bits(const or_hist *h, const or_tables *t, int prob_bits) {
+  double info = 0.0;
+  for (int c = 0; c < OR_NCTX; c++)
+    for (int s = 0; s < t->nsym[c]; s++) {
+      uint64_t cnt = (t->smin[c] + s + OR_SYM_OFF < OR_SYM_SPAN) ? h->cnt[c][t->smin[c] + s + OR_SYM_OFF] : 0;
+      if (cnt) info += (double)cnt * ((double)prob_bits - log2((double)t->freq[c][s]));
+    }
+  return info;
+}
+
+double or_estimate_bpp_rows(const double *x, const double *rms, const or_geom *g, const or_sample *sp, double a) {
+  int64_t n = sample_size(g, sp);
   or_hist *h = (or_hist *)calloc(1, sizeof(or_hist));
   if (!h) return NAN;
-  for (int64_t k = 0; k < S; k++) {
-    int64_t vid = (int64_t)(((uint64_t)k * (uint64_t)g->n_vec) / (uint64_t)S);
+  for (int64_t k = 0; k < n; k++) {
+    int64_t vid = sample_vid(g, sp, k, n);
     int64_t r = vid / g->vpr, kk = vid % g->vpr;
     int32_t v[8];
     int ctx[8];
@@ -625,14 +716,8 @@ double or_estimate_bpp_rows(const double *x, const double *rms, const or_geom *g
   or_tables t;
   int rc = tables_from_hist(h, g->prob_bits, &t);
   if (rc) { tables_free(&t); free(h); return INFINITY; }
-  double info = 0.0;
-  for (int c = 0; c < OR_NCTX; c++)
-    for (int s = 0; s < t.nsym[c]; s++) {
-      uint64_t cnt = (t.smin[c] + s + OR_SYM_OFF < OR_SYM_SPAN) ? h->cnt[c][t.smin[c] + s + OR_SYM_OFF] : 0;
-      if (cnt) info += (double)cnt * ((double)g->prob_bits - log2((double)t.freq[c][s]));
-    }
-  double bits = state_part(info * ((double)g->n_vec / (double)S), (double)(g->S * g->T)) +
-                8.0 * (double)meta_bytes(g, tables_total_nsym(&t));
+  double info = info_bits(h, &t, g->prob_bits) * ((double)g->n_vec / (double)n);
+  double bits = stream_bits(g, info, tables_total_nsym(&t));
   tables_free(&t);
   free(h);
   return bits / ((double)g->R * (double)g->C);
@@ -658,16 +743,7 @@ static double estimate_bpp_full(const double *x, const or_geom *g, double a) {
     for (int j = 0; j < 8; j++) h->cnt[ctx[j]][sym[j] + OR_SYM_OFF]++;
   }
   if (tables_from_hist(h, g->prob_bits, &t) != OR_OK) { result = INFINITY; goto done; }
-  {
-    double info = 0.0;
-    for (int c = 0; c < OR_NCTX; c++)
-      for (int s = 0; s < t.nsym[c]; s++) {
-        uint64_t cnt = (t.smin[c] + s + OR_SYM_OFF < OR_SYM_SPAN) ? h->cnt[c][t.smin[c] + s + OR_SYM_OFF] : 0;
-        if (cnt) info += (double)cnt * ((double)g->prob_bits - log2((double)t.freq[c][s]));
-      }
-    double bits = state_part(info, (double)(g->S * g->T)) + 8.0 * (double)meta_bytes(g, tables_total_nsym(&t));
-    result = bits / ((double)g->R * (double)g->C);
-  }
+  result = stream_bits(g, info_bits(h, &t, g->prob_bits), tables_total_nsym(&t)) / ((double)g->R * (double)g->C);
 done:
   tables_free(&t);
   free(gs);
@@ -721,13 +797,14 @@ typedef struct {
   const double *x;
   const double *rms;
   const or_geom *g;
+  const or_sample *sp;
   int dtype;
   double target;
 } or_sel_ctx;
 
 static double rate_sampled(void *vctx, double a) {
   or_sel_ctx *c = (or_sel_ctx *)vctx;
-  return or_estimate_bpp_rows(c->x, c->rms, c->g, a);
+  return or_estimate_bpp_rows(c->x, c->rms, c->g, c->sp, a);
 }
 
 /* exact rate: a full compression per probe (slow; used to pin the estimate) */
@@ -760,41 +837,62 @@ static int check_input(const double *x, int64_t R, int64_t C, int dtype, double 
 /*
  * Compress an R x C matrix given as f64 values (widened exactly from the
  * container dtype) plus the container's own bytes (for a raw fallback).
- * fixed_a > 0 skips resolution selection; exact_select != 0 selects with
- * full encodes instead of sampled estimates.
+ *   fixed_a > 0      : this lattice resolution, no rate selection;
+ *   n_states         : 0 (choose), 16 or 64 rANS states per tile;
+ *   tile_vecs        : 0 (choose), 512 or 1024 E8 vectors per tile;
+ *   sample_vecs      : 0 (65536) or the rate estimate's sample size;
+ *   seed             : the sample's phase (vectors past each stride point);
+ *   exact_select != 0: select with a full encode per probe instead of the
+ *                      sampled estimate (slow; pins the estimate).
+ * With the state count chosen, tiles have 64 states, or 16 when a
+ * target-selected stream's target is less than 4x the least a 64-state stream
+ * costs (64 states would spend over a quarter of the bits on their overhead).  With the tile size chosen, 64-state tiles hold 512 vectors in
+ * matrices of fewer than 2^22 vectors (twice the tiles, so twice the states
+ * decoding in parallel) and 1024 in larger ones; 16-state tiles hold 512, or
+ * 1024 when the target lies below 1.1x the least 512 allow.
+ * Exactly one full encode runs for a lattice stream (or_last_encode_count).
  */
 int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, int dtype, double target,
-                double fixed_a, int n_states, int prob_bits, int exact_select, uint8_t **blob, size_t *nbytes,
-                double *a_out) {
+                double fixed_a, int n_states, int64_t tile_vecs, int64_t sample_vecs, uint64_t seed, int prob_bits,
+                int exact_select, uint8_t **blob, size_t *nbytes, double *a_out) {
+  or_encodes = 0;
   int rc = check_input(x, R, C, dtype, target);
   if (rc) return rc;
-  if (n_states < 0 || n_states > 1024 || prob_bits < 8 || prob_bits > 12 || !blob || !nbytes)
+  if ((n_states != 0 && n_states != 16 && n_states != 64) ||
+      (tile_vecs != 0 && tile_vecs != 512 && tile_vecs != 1024) || sample_vecs < 0 || prob_bits < 8 ||
+      prob_bits > 11 || !blob || !nbytes)
     return OR_ERR_ARG;
+  if (R * ((C + 7) / 8) >= ((int64_t)1 << 31)) return OR_ERR_SHAPE;
+  const int chosen = !(fixed_a > 0.0);
   or_geom g;
   if (n_states == 0) {
-    /* 64 states per tile, or 16 when a target-selected stream's target lies
-     * below the overhead of 64 (its 40 bits per state plus the metadata) */
-    geom_init(&g, R, C, OR_STATES_DEFAULT, prob_bits);
-    const double floor64 = (OR_STATE_MIN_BITS * (double)(g.S * g.T) + 8.0 * (double)meta_bytes(&g, OR_NCTX)) /
-                           ((double)R * (double)C);
-    n_states = (!(fixed_a > 0.0) && target < 1.1 * floor64) ? OR_STATES_LOW : OR_STATES_DEFAULT;
+    int64_t tv = tile_vecs ? tile_vecs : (R * ((C + 7) / 8) < OR_SMALL_MATRIX_VECS ? 512 : 1024);
+    geom_init(&g, R, C, OR_STATES_DEFAULT, tv, prob_bits);
+    n_states = (chosen && target < 4.0 * floor_bpp(&g)) ? OR_STATES_LOW : OR_STATES_DEFAULT;
   }
-  geom_init(&g, R, C, n_states, prob_bits);
+  if (tile_vecs == 0) {
+    if (n_states == OR_STATES_DEFAULT) {
+      tile_vecs = R * ((C + 7) / 8) < OR_SMALL_MATRIX_VECS ? 512 : 1024;
+    } else {
+      geom_init(&g, R, C, n_states, 512, prob_bits);
+      tile_vecs = (chosen && target < 1.1 * floor_bpp(&g)) ? 1024 : 512;
+    }
+  }
+  geom_init(&g, R, C, n_states, tile_vecs, prob_bits);
+  or_sample sp = {sample_vecs ? sample_vecs : OR_SAMPLE_VECS, seed};
   double a = fixed_a;
-  double *rms = NULL;         /* row RMS, kept for every rate selection below */
-  double goal = target;       /* the sampled estimate the last selection aimed at */
-  or_sel_ctx sc = {x, NULL, &g, dtype, target};
-  if (!(fixed_a > 0.0)) {
+  double *rms = NULL;
+  or_sel_ctx sc = {x, NULL, &g, &sp, dtype, target};
+  if (chosen) {
     rms = (double *)malloc(sizeof(double) * (size_t)R);
     if (!rms) return OR_ERR_NOMEM;
     for (int64_t r = 0; r < R; r++) rms[r] = row_rms(x + r * C, C);
     sc.rms = rms;
-    /* targets below the fixed per-tile overhead cannot be met */
-    double floor_bpp = (OR_STATE_MIN_BITS * (double)(g.S * g.T) + 8.0 * (double)meta_bytes(&g, OR_NCTX)) /
-                       ((double)R * (double)C);
-    if (target < 1.02 * floor_bpp) { free(rms); return OR_ERR_TARGET; }
+    /* targets below the fixed per-state overhead cannot be met */
+    if (target < 1.02 * floor_bpp(&g)) { free(rms); return OR_ERR_TARGET; }
     double best_est = INFINITY;
     a = select_scale(exact_select ? rate_exact : rate_sampled, &sc, target, &best_est);
+    if (exact_select) or_encodes = 0; /* the probes' encodes are the exact selection's, not the stream's */
     /* no resolution reaches the target within 2% (the lattice values would
      * leave the stream's value range first): an encoding failure */
     if (!(fabs(best_est - target) <= 0.02 * target)) {
@@ -815,8 +913,7 @@ int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, in
       if (isfinite(full) && !(fabs(full - target) <= 0.005 * target)) {
         double est = best_est;
         for (int it = 0; it < 3; it++) {
-          goal = target - (full - est);
-          a = select_scale(rate_sampled, &sc, goal, &est);
+          a = select_scale(rate_sampled, &sc, target - (full - est), &est);
           if (it == 2) break;
           full = estimate_bpp_full(x, &g, a);
           if (!isfinite(full) || fabs(full - target) <= 0.005 * target) break;
@@ -826,35 +923,12 @@ int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, in
   }
   if (a_out) *a_out = a;
   rc = compress_at(x, &g, dtype, a, target, blob, nbytes);
-  /* The estimate's state part is exact only at its extremes: at low rates a
-   * state's cost steps by a whole word, so the encoded size can still miss the
-   * target.  Then the selection aims again, moved by the encoded size's miss,
-   * at most twice, and the stream closer to the target is kept. */
-  if (rc == OR_OK && rms && !exact_select) {
-    const double numel = (double)R * (double)C;
-    for (int it = 0; it < 2; it++) {
-      const double actual = 8.0 * (double)*nbytes / numel;
-      if (fabs(actual - target) <= 0.01 * target) break;
-      double est;
-      goal -= actual - target;
-      const double a2 = select_scale(rate_sampled, &sc, goal, &est);
-      uint8_t *b2 = NULL;
-      size_t n2 = 0;
-      if (compress_at(x, &g, dtype, a2, target, &b2, &n2) != OR_OK) { free(b2); break; }
-      if (!(fabs(8.0 * (double)n2 / numel - target) < fabs(actual - target))) { free(b2); break; }
-      free(*blob);
-      *blob = b2;
-      *nbytes = n2;
-      a = a2;
-      if (a_out) *a_out = a;
-    }
-  }
   free(rms);
   uint64_t raw_total = OR_HDR + pad16((uint64_t)R * (uint64_t)C * (uint64_t)esize_of(dtype));
   /* with the resolution chosen from the target, a lattice stream no smaller
    * than the raw container is an encoding failure; a fixed resolution keeps
    * the lattice stream */
-  if (rc == OR_OK && !(fixed_a > 0.0) && (uint64_t)*nbytes >= raw_total) {
+  if (rc == OR_OK && chosen && (uint64_t)*nbytes >= raw_total) {
     free(*blob);
     *blob = NULL;
     rc = OR_WARN_RAW;
@@ -867,13 +941,19 @@ int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, in
   return rc;
 }
 
-double or_estimate_bpp(const double *x, int64_t R, int64_t C, double a, int n_states, int prob_bits) {
+/* full encodes the last or_compress ran (1 for a lattice stream, also after
+ * an exact selection, whose probes are not counted) */
+long or_last_encode_count(void) { return or_encodes; }
+
+double or_estimate_bpp(const double *x, int64_t R, int64_t C, double a, int n_states, int64_t tile_vecs,
+                       int64_t sample_vecs, uint64_t seed, int prob_bits) {
   or_geom g;
-  geom_init(&g, R, C, n_states, prob_bits);
+  geom_init(&g, R, C, n_states, tile_vecs, prob_bits);
+  or_sample sp = {sample_vecs ? sample_vecs : OR_SAMPLE_VECS, seed};
   double *rms = (double *)malloc(sizeof(double) * (size_t)R);
   if (!rms) return NAN;
   for (int64_t r = 0; r < R; r++) rms[r] = row_rms(x + r * C, C);
-  double e = or_estimate_bpp_rows(x, rms, &g, a);
+  double e = or_estimate_bpp_rows(x, rms, &g, &sp, a);
   free(rms);
   return e;
 }
@@ -886,7 +966,7 @@ int or_quantize_matrix(const double *x, int64_t R, int64_t C, double a, int prob
                        int32_t *v_out) {
   if (!x || R <= 0 || C <= 0 || !g_out || !v_out) return OR_ERR_ARG;
   or_geom g;
-  geom_init(&g, R, C, 64, prob_bits);
+  geom_init(&g, R, C, 64, 1024, prob_bits);
   for (int64_t r = 0; r < R; r++) g_out[r] = stored_scale(row_rms(x + r * C, C), a);
   for (int64_t r = 0; r < R; r++)
     for (int64_t k = 0; k < g.vpr; k++) quantize_vector(x + r * C, C, k, g_out[r], v_out + r * g.Cp + 8 * k);
@@ -900,7 +980,7 @@ typedef struct {
   int method, dtype;
   or_geom g;
   double a, target;
-  uint64_t o_tab, o_sc, o_st, o_to, o_w, n_words, total;
+  uint64_t o_tab, o_sc, o_to, o_w, n_words, total;
 } or_header;
 
 /* [off, off + size) inside [0, nb), written so that no sum can wrap */
@@ -923,30 +1003,28 @@ static int parse_header(const uint8_t *b, size_t nb, or_header *h) {
   if (h->total != nb) return OR_ERR_FORMAT;
   h->target = get_f64(b + 56);
   if (h->method == 1) {
-    geom_init(&h->g, (int64_t)R, (int64_t)C, 64, 11);
+    geom_init(&h->g, (int64_t)R, (int64_t)C, 64, 1024, 10);
     h->o_w = get_u64(b + 96);
     if (h->o_w != OR_HDR || !span_ok(OR_HDR, R * C * (uint64_t)esize_of(h->dtype), nb)) return OR_ERR_FORMAT;
     return OR_OK;
   }
   int pb = b[10];
-  if (pb < 8 || pb > 12 || b[11] != OR_NCTX) return OR_ERR_FORMAT;
-  int64_t S = get_u32(b + 16);
-  if (get_u32(b + 12) != 1024 || S < 1 || S > 1024) return OR_ERR_FORMAT;
+  if (pb < 8 || pb > 11 || b[11] != OR_NCTX) return OR_ERR_FORMAT;
+  int64_t S = get_u32(b + 16), TV = get_u32(b + 12);
+  if ((S != 16 && S != 64) || (TV != 512 && TV != 1024)) return OR_ERR_FORMAT;
   if (R * ((C + 7) / 8) >= ((uint64_t)1 << 31)) return OR_ERR_FORMAT;
-  geom_init(&h->g, (int64_t)R, (int64_t)C, S, pb);
+  geom_init(&h->g, (int64_t)R, (int64_t)C, S, TV, pb);
   if ((int64_t)get_u64(b + 40) != h->g.Cp || (int64_t)get_u32(b + 20) != h->g.T) return OR_ERR_FORMAT;
   h->a = get_f64(b + 48);
   h->o_tab = get_u64(b + 64);
   h->o_sc = get_u64(b + 72);
-  h->o_st = get_u64(b + 80);
   h->o_to = get_u64(b + 88);
   h->o_w = get_u64(b + 96);
   h->n_words = get_u64(b + 104);
-  uint64_t T = (uint64_t)h->g.T; /* below 2^21 here */
-  if (h->o_tab != OR_HDR || !span_ok(h->o_tab, 4 * OR_NCTX, nb)) return OR_ERR_FORMAT;
+  uint64_t T = (uint64_t)h->g.T; /* below 2^22 here */
+  if (h->o_tab != OR_HDR || !span_ok(h->o_tab, 4 * OR_NCTX, nb) || get_u64(b + 80) != 0) return OR_ERR_FORMAT;
   if (!span_ok(h->o_sc, 4 * R, nb) || h->o_sc < h->o_tab + 4 * OR_NCTX ||
-      !span_ok(h->o_st, 4 * T * (uint64_t)S, nb) || h->o_st < h->o_sc + 4 * R ||
-      !span_ok(h->o_to, 4 * (T + 1), nb) || h->o_to < h->o_st + 4 * T * (uint64_t)S ||
+      !span_ok(h->o_to, 4 * (T + 1), nb) || h->o_to < h->o_sc + 4 * R ||
       h->n_words > nb || !span_ok(h->o_w, 2 * h->n_words, nb) || h->o_w < h->o_to + 4 * (T + 1))
     return OR_ERR_FORMAT;
   return OR_OK;
@@ -979,37 +1057,46 @@ static int decode_lattice_tiles(const uint8_t *b, const or_header *h, int32_t *v
   int rc = read_tables(b, h, &t);
   if (rc) { tables_free(&t); return rc; }
   const or_geom *g = &h->g;
+  const int S = (int)g->S;
   uint32_t M = 1u << g->prob_bits;
-  int64_t steps = (g->tile_vecs + g->S - 1) / g->S;
-  uint32_t *x = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)g->S);
-  uint64_t *pos = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)g->S); /* next word of each state */
-  uint64_t *end = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)g->S); /* end of each state's words */
-  int32_t *vb = (int32_t *)malloc(sizeof(int32_t) * (size_t)g->S);     /* coset bit per state */
-  int32_t *zp = (int32_t *)malloc(sizeof(int32_t) * (size_t)g->S);     /* running z sum per state */
-  if (!x || !pos || !end || !vb || !zp) { rc = OR_ERR_NOMEM; goto done; }
+  int64_t steps = g->tile_vecs / S;
+  uint32_t x[OR_STATES_DEFAULT];
+  int64_t fwd[OR_STATES_DEFAULT / 2], bwd[OR_STATES_DEFAULT / 2]; /* next word of states 2k and 2k+1 */
+  int32_t vb[OR_STATES_DEFAULT], zp[OR_STATES_DEFAULT];           /* coset bit, running z sum */
+  const uint8_t *words = b + h->o_w;
   for (int64_t tile = t0; tile < t1; tile++) {
     int64_t first = tile * g->tile_vecs;
     int64_t n = g->n_vec - first;
     if (n > g->tile_vecs) n = g->tile_vecs;
-    int64_t n_act = n < g->S ? n : g->S;
-    uint64_t wp = get_u32(b + h->o_to + 4 * tile);
-    uint64_t wend = get_u32(b + h->o_to + 4 * (tile + 1));
-    uint64_t ncw = (uint64_t)(g->S + 1) / 2; /* words holding the count bytes */
-    if (wend < wp || wend > h->n_words || wend - wp < ncw) { rc = OR_ERR_FORMAT; goto done; }
-    for (int64_t q = 0; q < g->S; q++) x[q] = get_u32(b + h->o_st + 4 * (tile * g->S + q));
-    uint64_t next = wp + ncw;
-    for (int64_t q = 0; q < g->S; q++) {
-      uint64_t c = b[h->o_w + 2 * wp + (uint64_t)q];
-      if (q >= n_act && c != 0) { rc = OR_ERR_FORMAT; goto done; }
-      pos[q] = next;
-      next += c;
-      end[q] = next;
+    int64_t wp = get_u32(b + h->o_to + 4 * tile);
+    int64_t wend = get_u32(b + h->o_to + 4 * (tile + 1));
+    int64_t hw = S / 2; /* words of pair counts and length codes */
+    if (wend < wp || wend > (int64_t)h->n_words || wend - wp < hw) { rc = OR_ERR_FORMAT; goto done; }
+    /* start states: length codes, then the bits below each leading one */
+    int64_t bitpos = 0, bit0 = 2 * (wp + hw);
+    for (int q = 0; q < S; q++) {
+      int W = (int)((get_u16(words + 2 * (wp + S / 4 + q / 4)) >> (4 * (q % 4))) & 15u) + 12;
+      uint32_t val = 1u << (W - 1);
+      for (int i = 0; i < W - 1; i++, bitpos++) {
+        int64_t byte = bit0 + bitpos / 8;
+        if (byte >= 2 * wend) { rc = OR_ERR_FORMAT; goto done; }
+        if ((words[byte] >> (bitpos % 8)) & 1u) val |= 1u << i;
+      }
+      x[q] = val;
     }
-    if (next != wend) { rc = OR_ERR_FORMAT; goto done; }
+    /* pair regions after the start bits' whole words */
+    int64_t r0 = wp + hw + (bitpos + 15) / 16;
+    for (int k = 0; k < S / 2; k++) {
+      int64_t cnt = words[2 * wp + k];
+      fwd[k] = r0;
+      r0 += cnt;
+      bwd[k] = r0 - 1;
+    }
+    if (r0 != wend) { rc = OR_ERR_FORMAT; goto done; }
     for (int64_t s = 0; s < steps; s++)
       for (int j = 0; j < 8; j++) {
-        for (int64_t q = 0; q < g->S; q++) {
-          int64_t i = s * g->S + q;
+        for (int q = 0; q < S; q++) {
+          int64_t i = s * S + q;
           if (i >= n) continue;
           int ctx;
           if (j == 0) ctx = 0;
@@ -1021,8 +1108,10 @@ static int decode_lattice_tiles(const uint8_t *b, const or_header *h, int32_t *v
           while (!(t.cum[ctx][si] <= slot && slot < t.cum[ctx][si + 1])) si++;
           x[q] = t.freq[ctx][si] * (x[q] >> g->prob_bits) + slot - t.cum[ctx][si];
           if (x[q] < OR_STATE_L) {
-            if (pos[q] >= end[q]) { rc = OR_ERR_FORMAT; goto done; }
-            x[q] = (x[q] << 16) | get_u16(b + h->o_w + 2 * (pos[q]++));
+            int k = q / 2;
+            if (fwd[k] > bwd[k]) { rc = OR_ERR_FORMAT; goto done; } /* the pair's region is used up */
+            int64_t at = (q % 2 == 0) ? fwd[k]++ : bwd[k]--;
+            x[q] = (x[q] << 16) | get_u16(words + 2 * at);
           }
           int32_t sym = t.smin[ctx] + si;
           int64_t vid = first + i;
@@ -1037,15 +1126,14 @@ static int decode_lattice_tiles(const uint8_t *b, const or_header *h, int32_t *v
           }
         }
       }
-    for (int64_t q = 0; q < n_act; q++)
-      if (x[q] != OR_STATE_L || pos[q] != end[q]) { rc = OR_ERR_FORMAT; goto done; }
+    /* every state ends at L (states without vectors start there), and every
+     * pair has used its whole region */
+    for (int q = 0; q < S; q++)
+      if (x[q] != OR_STATE_L) { rc = OR_ERR_FORMAT; goto done; }
+    for (int k = 0; k < S / 2; k++)
+      if (fwd[k] != bwd[k] + 1) { rc = OR_ERR_FORMAT; goto done; }
   }
 done:
-  free(x);
-  free(pos);
-  free(end);
-  free(vb);
-  free(zp);
   tables_free(&t);
   return rc;
 }
@@ -1214,7 +1302,7 @@ int or_reconstruct(const int32_t *v, const float *g, int64_t R, int64_t C, int d
   return OR_OK;
 }
 
-/* header fields for tests: rows, cols, method, dtype, S, T, prob_bits, n_words, a */
+/* header fields for tests: rows, cols, method, dtype, S, T, prob_bits, n_words, tile_vecs, a */
 int or_blob_info(const uint8_t *b, size_t nb, int64_t *i64_out, double *a_out) {
   or_header h;
   int rc = parse_header(b, nb, &h);
@@ -1227,6 +1315,7 @@ int or_blob_info(const uint8_t *b, size_t nb, int64_t *i64_out, double *a_out) {
   i64_out[5] = h.g.T;
   i64_out[6] = h.g.prob_bits;
   i64_out[7] = (int64_t)h.n_words;
+  i64_out[8] = h.g.tile_vecs;
   *a_out = h.a;
   return OR_OK;
 }
@@ -1238,7 +1327,8 @@ int or_blob_info(const uint8_t *b, size_t nb, int64_t *i64_out, double *a_out) {
 /* ------------------------------------------------------------------------ */
 int or_rans_encode(const uint32_t *freq, int nsym, int prob_bits, const int32_t *syms, int64_t n, int nstates,
                    uint32_t *states_out, uint16_t *words_out, int64_t *nwords_out, int64_t words_cap) {
-  if (!freq || nsym <= 0 || !syms || nstates <= 0 || !states_out || !nwords_out) return OR_ERR_ARG;
+  if (!freq || nsym <= 0 || !syms || nstates <= 0 || !states_out || !nwords_out || prob_bits < 1 || prob_bits > 11)
+    return OR_ERR_ARG;
   uint32_t *cum = (uint32_t *)calloc((size_t)nsym + 1, sizeof(uint32_t));
   if (!cum) return OR_ERR_NOMEM;
   for (int s = 0; s < nsym; s++) cum[s + 1] = cum[s] + freq[s];
@@ -1251,7 +1341,7 @@ int or_rans_encode(const uint32_t *freq, int nsym, int prob_bits, const int32_t 
     int s = syms[k];
     if (s < 0 || s >= nsym || freq[s] == 0) { free(cum); free(rev.w); return OR_ERR_ARG; }
     uint32_t f = freq[s], x = states_out[q];
-    if ((uint64_t)x >= ((uint64_t)f << (29 - prob_bits))) {
+    if ((uint64_t)x >= ((uint64_t)f << (OR_STATE_TOP - prob_bits))) {
       if (words_push(&rev, (uint16_t)(x & 0xffffu))) { free(cum); free(rev.w); return OR_ERR_NOMEM; }
       x >>= 16;
     }
@@ -1267,7 +1357,8 @@ int or_rans_encode(const uint32_t *freq, int nsym, int prob_bits, const int32_t 
 
 int or_rans_decode(const uint32_t *freq, int nsym, int prob_bits, const uint32_t *states_in, int nstates,
                    const uint16_t *words, int64_t nwords, int64_t n, int32_t *syms_out, uint32_t *final_states) {
-  if (!freq || nsym <= 0 || !states_in || nstates <= 0 || !syms_out) return OR_ERR_ARG;
+  if (!freq || nsym <= 0 || !states_in || nstates <= 0 || !syms_out || prob_bits < 1 || prob_bits > 11)
+    return OR_ERR_ARG;
   uint32_t *cum = (uint32_t *)calloc((size_t)nsym + 1, sizeof(uint32_t));
   uint32_t *x = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)nstates);
   if (!cum || !x) { free(cum); free(x); return OR_ERR_NOMEM; }

@@ -49,7 +49,7 @@ def test_closed_form_ragged_shapes(shape):
     blob, rc, a = oracle.compress(t, 4.0, fixed_a=0.3)
     assert rc == 0
     d, v = check_closed_form(t, blob)
-    assert d["n_tiles"] == math.ceil(shape[0] * ((shape[1] + 7) // 8) / 1024)
+    assert d["n_tiles"] == math.ceil(shape[0] * ((shape[1] + 7) // 8) / d["tile_vecs"])
     # the reconstruction drops pad coordinates
     assert oracle.decompress(blob).shape == t.shape
 
@@ -110,8 +110,10 @@ def test_rate_within_two_percent_rowscale4096():
     d = oracle.info(blob)
     y = oracle.decompress(blob)
     e = rel_l2(y, t)
-    # payload rate: everything but the per-state overhead (32 bits each) and metadata
-    meta_bits = 8 * (128 + 4 * t.shape[0] + 4 * (d["n_tiles"] + 1) + 28) + 32 * 64 * d["n_tiles"]
+    # payload rate: everything but the per-state overhead (18.5 bits each on
+    # average: 8 of pair count and length code, 11 of the final state L, less
+    # half a bit of the start state's implied leading one) and metadata
+    meta_bits = 8 * (128 + 4 * t.shape[0] + 4 * (d["n_tiles"] + 1) + 28) + 18.5 * 64 * d["n_tiles"]
     r_pay = (8 * blob.size - meta_bits) / t.numel()
     G = E8C["normalized_second_moment_num"] / E8C["normalized_second_moment_den"]
     theory = math.sqrt(2 * math.pi * math.e * G) * 2 ** (-r_pay)
@@ -228,38 +230,94 @@ def test_corrupt_streams_rejected():
         pass
 
 
-def tile_words(blob):
-    """(count bytes, word lists) of every tile, read straight from the layout:
-    tile offsets u32[T+1] at header byte 88, words at header byte 96."""
+def read_tiles(blob):
+    """Every tile of a stream, read straight from the layout without the
+    oracle: tile offsets u32[T+1] at the header's byte 88, words at byte 96.
+    A tile of S states holds S/2 pair-count bytes, S/2 length-code nibbles
+    (W - 12, W a start state's bit length), the start states' low W - 1 bits
+    (least significant bit first, whole words), then pair k's region: state
+    2k's words, then state 2k+1's words reversed.  Returns per tile a dict of
+    pair counts, start states and per-state word lists in consumption order
+    (state 2k+1's taken from the region's end), whose split between the two
+    states is unknown to a reader and is taken from the oracle's decode."""
     hdr = blob[:128].view(np.uint64)
     o_to, o_w, n_words = int(hdr[11]), int(hdr[12]), int(hdr[13])
     d = oracle.info(blob)
+    S = d["n_states"]
     toff = blob[o_to:o_to + 4 * (d["n_tiles"] + 1)].view(np.uint32)
     words = blob[o_w:o_w + 2 * n_words].view(np.uint16)
     assert toff[0] == 0 and toff[-1] == n_words
-    return [(words[b:e][:32].view(np.uint8).astype(np.int64), words[b:e][32:]) for b, e in zip(toff[:-1], toff[1:])]
+    tiles = []
+    for b, e in zip(toff[:-1], toff[1:]):
+        tw = words[b:e]
+        pc = tw[:S // 4].view(np.uint8).astype(np.int64)
+        nib = tw[S // 4:S // 2]
+        W = np.array([(int(nib[q // 4]) >> (4 * (q % 4)) & 15) + 12 for q in range(S)])
+        bits = np.unpackbits(tw[S // 2:].view(np.uint8), bitorder="little")
+        x, pos = [], 0
+        for q in range(S):
+            low = bits[pos:pos + W[q] - 1]
+            x.append((1 << (int(W[q]) - 1)) | int(sum(int(bit) << i for i, bit in enumerate(low))))
+            pos += int(W[q]) - 1
+        nbw = (pos + 15) // 16
+        regions = tw[S // 2 + nbw:]
+        tiles.append({"pair_counts": pc, "W": W, "x": np.array(x, np.int64), "start_bits": pos,
+                      "start_words": nbw, "regions": regions})
+    return d, tiles
 
 
-@pytest.mark.parametrize("shape", [(8, 8), (129, 64), (96, 1024)])
+@pytest.mark.parametrize("shape", [(8, 8), (129, 64), (96, 1024), (40, 8200)])
 def test_tile_word_layout(shape):
-    """Each tile: 64 count bytes (a state consumes at most one word per symbol,
-    so at most 16 * 8 = 128), then the states' word lists back to back; states
-    without vectors in a partial tile consume nothing."""
+    """Each tile: S/2 pair-count bytes, S/2 length nibbles, the start bits on
+    whole words, then the regions, and nothing else (the counts add up to the
+    tile's words).  Start states lie in [2^11, 2^27); states without vectors
+    in a partial tile start at L exactly and their pair holds no words
+    beyond its partner's."""
     t = W.gaussian(*shape, 0.02, seed=3 + shape[0])
     blob, rc, _ = oracle.compress(t, 4.0, fixed_a=0.3)
     assert rc == 0
+    d, tiles = read_tiles(blob)
     n_vec = shape[0] * ((shape[1] + 7) // 8)
-    for k, (cnt, rest) in enumerate(tile_words(blob)):
-        n = min(1024, n_vec - 1024 * k)
-        assert cnt.sum() == rest.size
-        assert cnt.max() <= 8 * math.ceil(n / 64)
-        assert np.all(cnt[min(n, 64):] == 0)
-        assert np.all(cnt[: min(n, 64)] > 0)  # at 4 bpp every state refills
+    TV, S = d["tile_vecs"], d["n_states"]
+    for k, tl in enumerate(tiles):
+        n = min(TV, n_vec - TV * k)
+        assert tl["pair_counts"].sum() == tl["regions"].size
+        assert np.all((tl["x"] >= oracle.STATE_L) & (tl["x"] < (1 << 27)))
+        assert np.all(tl["W"] == [int(v).bit_length() for v in tl["x"]])
+        # at most one word per symbol: 8 per vector a state decodes
+        per_state = 8 * math.ceil(n / S) if n >= S else 8
+        assert tl["pair_counts"].max() <= 2 * per_state
+        if n < S:  # states n.. have no vectors
+            assert np.all(tl["x"][n:] == oracle.STATE_L)
+            empty_pairs = np.arange(S // 2)[2 * np.arange(S // 2) >= n]
+            assert np.all(tl["pair_counts"][empty_pairs] == 0)
+        else:
+            assert np.all(tl["pair_counts"] > 0)  # at 4 bpp every state refills
 
 
-def test_count_bytes_decide_word_ownership():
-    """Moving one word from state 0's list to state 1's (count bytes only) is
-    caught: state 0 runs out of words or a state ends off its list."""
+def test_start_state_overhead_matches_the_estimate():
+    """The rate estimate prices a state at 18.5 bits beyond its symbols'
+    information: 8 for its pair-count share and length nibble, and its start
+    state stored as W - 1 bits although it carries log2(x / L) bits of
+    information, i.e. 11 bits for the final state L less the fractional part
+    of log2 x, on average one half.  The mean over many states agrees."""
+    t = W.rowscale_gaussian(256, 4096, seed=21)
+    blob, rc, _ = oracle.compress(t, 3.0)
+    assert rc == 0
+    _, tiles = read_tiles(blob)
+    x = np.concatenate([tl["x"] for tl in tiles]).astype(np.float64)
+    W_ = np.concatenate([tl["W"] for tl in tiles])
+    slack = (W_ - 1) - (np.log2(x) - np.log2(oracle.STATE_L))
+    assert abs(slack.mean() - 10.5) < 0.1, slack.mean()
+    # the tiles' bytes: 8 bits per state of counts and codes, the start bits
+    # padded to a word, the regions
+    for tl in tiles:
+        assert tl["start_words"] == (int((tl["W"] - 1).sum()) + 15) // 16
+
+
+def test_pair_counts_decide_word_ownership():
+    """Moving one word from pair 0's region to pair 1's (count bytes only) is
+    caught: a pair runs out of words or does not use its region up."""
     t = W.gaussian(64, 1024, 0.02, seed=77)
     blob, rc, _ = oracle.compress(t, 4.0, fixed_a=0.3)
     assert rc == 0
@@ -270,6 +328,33 @@ def test_count_bytes_decide_word_ownership():
     bad[o_w + 1] += 1
     with pytest.raises(oracle.OracleError):
         oracle.decode_symbols(bad)
+
+
+def test_a_flipped_start_bit_is_caught():
+    """A start state with one bit flipped decodes to something else or ends
+    off L: the end-state check rejects the stream or the symbols differ."""
+    t = W.gaussian(64, 1024, 0.02, seed=78)
+    blob, rc, _ = oracle.compress(t, 4.0, fixed_a=0.3)
+    o_w = int(blob[:128].view(np.uint64)[12])
+    d = oracle.info(blob)
+    good = oracle.decode_symbols(blob)
+    bad = blob.copy()
+    bad[o_w + d["n_states"] + 3] ^= 0x10  # inside the first tile's start bits
+    try:
+        assert not np.array_equal(oracle.decode_symbols(bad), good)
+    except oracle.OracleError:
+        pass
+
+
+@pytest.mark.parametrize("n_states,tile_vecs", [(16, 512), (16, 1024), (64, 512), (64, 1024)])
+def test_every_tile_geometry_round_trips(n_states, tile_vecs):
+    """The four geometries the format allows decode to the closed form."""
+    t = W.rowscale_gaussian(70, 1000, seed=n_states + tile_vecs)
+    blob, rc, _ = oracle.compress(t, 2.0, n_states=n_states, tile_vecs=tile_vecs)
+    assert rc == 0
+    d, _ = check_closed_form(t, blob)
+    assert (d["n_states"], d["tile_vecs"]) == (n_states, tile_vecs)
+    assert oracle.last_encode_count() == 1
 
 
 @pytest.mark.parametrize("shape", [(129, 64), (7, 13), (64, 1032)])
@@ -288,3 +373,37 @@ def test_tile_range_decode_matches_whole(shape):
     for t0 in range(0, T, 2):
         oracle.decompress_tile_range(blob, t0, min(T, t0 + 2), out=out)
     assert np.array_equal(out, whole)
+
+
+@pytest.mark.parametrize("kind", ["gauss", "t4"])
+def test_one_full_encode_per_call_across_targets(kind):
+    """The abstract: sampled storage estimates select the resolution without
+    repeated full-stream encoding.  Each call encodes the stream once (a
+    whole-matrix histogram may correct the sample's bias; it codes nothing)
+    and lands within 2% of the target from 0.1 bpp up, across the switch
+    from 16 to 64 states per tile."""
+    m = W.rowscale_gaussian(256, 2048, 11) if kind == "gauss" else W.t4_outliers(192, 3072, 12)
+    for target in (0.1, 0.25, 0.5, 0.9, 1.3, 2.0, 3.0, 4.5, 6.0):
+        blob, rc, _ = oracle.compress(m, target)
+        assert rc == 0, target
+        assert oracle.last_encode_count() == 1, target
+        actual = 8 * blob.size / m.numel()
+        assert abs(actual - target) <= 0.02 * target, (target, actual)
+
+
+def test_sample_options():
+    """sample_vecs sets the estimate's sample size (the whole matrix when it
+    is at least n_vec) and seed its phase; either way the stream is a valid
+    one within 2% of the target."""
+    m = W.rowscale_gaussian(128, 2048, 13)
+    n_vec = 128 * 256
+    est_all = oracle.estimate_bpp(m, 0.3, tile_vecs=512, sample_vecs=n_vec)
+    est_big = oracle.estimate_bpp(m, 0.3, tile_vecs=512, sample_vecs=10 * n_vec)
+    assert est_all == est_big
+    e0 = oracle.estimate_bpp(m, 0.3, tile_vecs=512, sample_vecs=1000, seed=0)
+    e1 = oracle.estimate_bpp(m, 0.3, tile_vecs=512, sample_vecs=1000, seed=5)
+    assert e0 != e1 and abs(e0 - e1) / e0 < 0.05
+    for sv, seed in ((2000, 0), (2000, 17), (n_vec, 3)):
+        blob, rc, _ = oracle.compress(m, 3.0, sample_vecs=sv, seed=seed)
+        assert rc == 0 and abs(8 * blob.size / m.numel() - 3.0) <= 0.06
+        check_closed_form(m, blob)

@@ -39,7 +39,7 @@ def test_round_trip_and_end_state(nsym, nstates, n):
     f = random_table(rng, nsym, with_ones=nsym > 3)
     syms = draw(rng, f, n)
     states, words = oracle.rans_encode(f, syms, nstates)
-    assert all(L <= s < (1 << 29) for s in states)
+    assert all(L <= s < (1 << 27) for s in states)
     dec, final = oracle.rans_decode(f, states, words, n)
     assert np.array_equal(dec, syms)
     assert np.all(final == L)
@@ -58,7 +58,9 @@ def test_rare_and_dominant_symbols():
 @pytest.mark.parametrize("k", [1, 3, 6, 10])
 def test_uniform_table_costs_exactly_k_bits(k):
     """f = M / 2^k for 2^k symbols: each symbol inserts exactly k bits, so
-    16 * words + sum(bitlen(x0) - bitlen(L)) == n * k exactly."""
+    16 * words + sum(bitlen(x0) - bitlen(L)) == n * k exactly.  A stream
+    stores each start state in bitlen(x0) - 1 bits, so a state's stored bits
+    are exactly 11 + (its symbols) * k."""
     rng = np.random.default_rng(k)
     f = np.full(1 << k, M >> k, np.uint32)
     for nstates in (1, 64):
@@ -72,11 +74,11 @@ def test_uniform_table_costs_exactly_k_bits(k):
 
 
 def test_state_absorbs_under_16_bits_without_a_word():
-    """The rate estimate's floor of 40 bits per state: a state whose symbols
-    carry fewer than 16 bits in total emits no word, and its stored state
-    holds their information (log2 x0 - log2 L equals it up to the coder's
-    rounding), so storing it costs its 32 bits and count byte whatever it
-    holds; past 16 bits the first word appears."""
+    """A state whose symbols carry fewer than 16 bits in total emits no word:
+    its start state holds their information (log2 x0 - log2 L equals it up
+    to the coder's rounding), which the stream stores at its bit length; past
+    16 bits the first word appears.  This is what makes a state's cost its
+    information plus a constant (the rate estimate's 18.5 bits)."""
     f = np.array([M - 8, 8], np.uint32)  # symbol 1 carries 7 bits, symbol 0 about 0.01
     for ones in (0, 1, 2):
         syms = np.zeros(128, np.int32)
@@ -84,12 +86,14 @@ def test_state_absorbs_under_16_bits_without_a_word():
         info = float(np.sum(np.log2(M / f[syms].astype(np.float64))))
         states, words = oracle.rans_encode(f, syms, 1)
         assert words.size == 0
-        assert abs(np.log2(float(states[0])) - np.log2(L) - info) < 0.1
+        # near L = 2^11 the state's integer steps are coarse: 128 symbols of
+        # probability 1016/1024 move it by 1.23 bits for their 1.45
+        assert abs(np.log2(float(states[0])) - np.log2(L) - info) < 0.25
     syms = np.zeros(128, np.int32)
     syms[:3] = 1  # about 22.4 bits: one word, the rest in the state
     states, words = oracle.rans_encode(f, syms, 1)
     assert words.size == 1
-    assert abs(16 + np.log2(float(states[0])) - np.log2(L) - 22.414) < 0.1
+    assert abs(16 + np.log2(float(states[0])) - np.log2(L) - 22.414) < 0.25
 
 
 def test_size_matches_information():
