@@ -268,6 +268,7 @@ def main() -> int:
         rel_l2_weights = ((ref.double() * scale.double().to(dev) - wd).norm() / wd.norm()).item()
 
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    info = ep.blob_info(p.blob)
     traffic = measured_traffic(args.workload)
     line = {
         "metric": METRIC,
@@ -284,7 +285,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "rows": rows, "cols": cols, "container": str(x.dtype).split(".")[-1],
                    "target_bpp": target, "actual_bpp": round(p.actual_bpp, 5), "stream_bytes": p.nbytes,
-                   "tile": f"1024 E8 vectors (8x1024 coords), {ep.blob_info(p.blob)['n_states']} rANS states", "mall_rotation_copies": copies},
+                   "tile": f"{info['tile_vecs']} E8 vectors ({8 * info['tile_vecs']} coords), {info['n_states']} rANS states",
+                   "mall_rotation_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
         "kernel_us": round(kernel_ms * 1e3, 3),

@@ -17,6 +17,32 @@ void set_error(const std::string &msg) { g_error = msg; }
 
 namespace {
 
+// ep_options to EncodeOptions; 0 or EP_ERR_ARG (with the error text set)
+int read_options(const struct ep_options *opt, ep::EncodeOptions &eo, int &threads) {
+  if (!opt) return 0;
+  for (int r : opt->reserved)
+    if (r != 0) {
+      ep::set_error("ep_options.reserved must be zero");
+      return EP_ERR_ARG;
+    }
+  eo.fixed_a = opt->fixed_scale;
+  eo.n_states = opt->n_states;
+  eo.tile_vecs = opt->tile_vecs;
+  eo.sample_vecs = opt->sample_vecs;
+  eo.seed = opt->seed;
+  threads = opt->n_threads;
+  if (!(eo.fixed_a >= 0.0) || std::isinf(eo.fixed_a)) {
+    ep::set_error("fixed_scale must be finite and >= 0");
+    return EP_ERR_ARG;
+  }
+  if ((eo.n_states != 0 && eo.n_states != 16 && eo.n_states != 64) ||
+      (eo.tile_vecs != 0 && eo.tile_vecs != 512 && eo.tile_vecs != 1024) || eo.sample_vecs < 0) {
+    ep::set_error("n_states must be 0, 16 or 64, tile_vecs 0, 512 or 1024, sample_vecs >= 0");
+    return EP_ERR_ARG;
+  }
+  return 0;
+}
+
 // option checks, the call, and the copy of the stream into malloc'ed memory
 template <class F>
 int compress_entry(const struct ep_options *opt, uint8_t **blob_out, size_t *nbytes_out, F &&run) {
@@ -25,26 +51,14 @@ int compress_entry(const struct ep_options *opt, uint8_t **blob_out, size_t *nby
     ep::set_error("null output pointer");
     return EP_ERR_ARG;
   }
-  double fixed_a = 0.0;
+  ep::EncodeOptions eo;
   int threads = 0;
-  if (opt) {
-    for (int r : opt->reserved)
-      if (r != 0) {
-        ep::set_error("ep_options.reserved must be zero");
-        return EP_ERR_ARG;
-      }
-    fixed_a = opt->fixed_scale;
-    threads = opt->n_threads;
-    if (!(fixed_a >= 0.0) || std::isinf(fixed_a)) {
-      ep::set_error("fixed_scale must be finite and >= 0");
-      return EP_ERR_ARG;
-    }
-  }
+  if (const int rc = read_options(opt, eo, threads); rc != 0) return rc;
   ep::Blob blob;
   std::string err;
   int rc;
   try {
-    rc = run(fixed_a, threads, blob, err);
+    rc = run(eo, threads, blob, err);
   } catch (const std::bad_alloc &) {
     ep::set_error("host allocation failed");
     return EP_ERR_NOMEM;
@@ -65,17 +79,17 @@ extern "C" {
 
 int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
                    const struct ep_options *opt, uint8_t **blob_out, size_t *nbytes_out) {
-  return compress_entry(opt, blob_out, nbytes_out, [&](double fixed_a, int threads, ep::Blob &blob,
+  return compress_entry(opt, blob_out, nbytes_out, [&](const ep::EncodeOptions &eo, int threads, ep::Blob &blob,
                                                         std::string &err) {
-    return ep::compress(host_src, dtype, rows, cols, target_bpp, fixed_a, threads, blob, err);
+    return ep::compress(host_src, dtype, rows, cols, target_bpp, eo, threads, blob, err);
   });
 }
 
 int ep_compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
                        const struct ep_options *opt, void *hip_stream, uint8_t **blob_out, size_t *nbytes_out) {
-  return compress_entry(opt, blob_out, nbytes_out, [&](double fixed_a, int, ep::Blob &blob,
+  return compress_entry(opt, blob_out, nbytes_out, [&](const ep::EncodeOptions &eo, int, ep::Blob &blob,
                                                         std::string &err) {
-    return ep::compress_device(dev_src, dtype, rows, cols, target_bpp, fixed_a, hip_stream, blob, err);
+    return ep::compress_device(dev_src, dtype, rows, cols, target_bpp, eo, hip_stream, blob, err);
   });
 }
 
@@ -103,6 +117,7 @@ int ep_blob_info(const uint8_t *blob, size_t nbytes, struct ep_info *info) {
   info->dtype = s.dtype;
   info->method = s.method;
   info->n_states = s.states;
+  info->tile_vecs = s.tile_vecs;
   info->prob_bits = s.prob_bits;
   info->n_tiles = s.tiles;
   info->n_words = (int64_t)s.n_words;
@@ -132,5 +147,7 @@ int64_t ep_storage_nbytes(const uint8_t *blob, size_t nbytes, int include_header
 }
 
 const char *ep_last_error(void) { return ep::g_error.c_str(); }
+
+int64_t ep_last_encode_count(void) { return ep::last_encode_count(); }
 
 }  // extern "C"

@@ -5,35 +5,44 @@
 // are entropy-coded in independently decodable tiles so that symbol decoding
 // and numerical reconstruction fuse on the GPU.  This file is that pass.
 //
-// Work mapping: one wavefront per tile of 1024 E8 vectors; lane q owns rANS
-// state q and decodes local vectors q, q+64, ..., so every step's 64 vectors
-// are contiguous and each lane writes one 8-coordinate vector per step
-// (16 bytes for BF16/FP16, 8 bytes for FP8/INT8).  Streams for targets below
-// the overhead of 64 states have 16 per tile: lanes 0..15 decode vectors q,
-// q+16, ..., and lanes 16..63 follow along without refilling or storing.
+// Work mapping.  A wave decodes one unit of 64 rANS states: one tile of 64
+// states, or four tiles of 16 (lanes 16r..16r+15 hold tile r's states, one
+// tile per DPP row).  Lane q of a tile owns state q and decodes the tile's
+// local vectors q, q + S, q + 2S, ... (S states per tile): V = tile_vecs / S
+// vectors per lane, 8, 16, 32 or 64.  Each step's vectors of a tile are
+// contiguous, so a lane writes one 8-coordinate vector per step (16 bytes
+// for BF16/FP16, 8 for FP8/INT8) next to its neighbours'.
 //
-// Per workgroup (up to 8 waves, one workgroup per CU):
+// Per workgroup (up to 16 waves, one workgroup per CU):
 //   1. every wave starts its global loads, all vector loads that need only the
-//      kernel arguments: the tile offsets it needs, one context's frequencies,
-//      its tile's start states and row scales;
+//      kernel arguments: its tiles' word offsets, one context's frequencies,
+//      the row scales of its first 8 vectors per lane;
 //   2. one wave per context prefix-sums the frequencies (DPP scan), lists the
 //      used symbols, sets a bitmap of the slots where a symbol starts, and
 //      expands the context's table 64 slots at a time: a slot's symbol is the
 //      number of starts up to it, which v_mbcnt counts from the row's bitmap;
-//      the last wave copies the words of all the workgroup's tiles (one range
+//      the other waves copy the words of all the workgroup's tiles (one range
 //      of the stream) into LDS with global_load_lds;
-//   3. each wave decodes its tile.
+//   3. each wave reads its tiles' start states and word pointers from LDS
+//      and decodes.
 // Streams with more tiles than one such round of workgroups covers take the
 // multi-tile kernel instead: one workgroup of up to 16 waves per CU builds
-// the tables once, and each wave then loads and decodes one tile after
+// the tables once, and each wave then loads and decodes one unit after
 // another on its own.
 //
-// Decode step for state x in [2^13, 2^29), kept as X = 8x so that the table
+// A tile in the stream: S/2 pair-count bytes (words in the region of states
+// 2k and 2k+1), S length nibbles (W - 12, W the bit length of a start
+// state), the start states' bits below their leading one, bit-packed, then
+// region k: state 2k's words front to back, state 2k+1's back to front.  A
+// lane finds its start state from the nibbles' prefix sum (DPP) and three
+// 16-bit reads, and its first word from the pair counts' prefix sum; it then
+// walks its words with a private pointer and a step of +2 or -2 bytes and
+// always holds its next word in a register.
+//
+// Decode step for state x in [2^11, 2^27), kept as X = 8x so that the table
 // address is one AND-OR:  8*slot = X & 0x1ff8;  e = table[ctx][slot];
-//   x' = f * (x >> 10) + (slot - cum);  if x' < 2^13: x = x' << 16 | w
-// where w is the state's next word.  A tile stores each state's words
-// together (behind one count byte per state), so a lane walks its own word
-// list with a private pointer and always holds its next word in a register.
+//   x' = f * (x >> 10) + (slot - cum);  if x' < 2^11: x = x' << 16 | w
+// where w is the state's next word.
 //
 // The step is software-pipelined around its one serial dependence, table
 // lookup -> multiply-add -> compare -> select -> address -> next lookup (on
@@ -43,10 +52,7 @@
 // one v_bitop3 or v_and_or makes its address, and the next lookup leaves.  Only
 // then do the refilling lanes, under the exec mask, read their following
 // word, which is first needed one step later.  Eight VALU instructions per
-// step: the chain is one instruction longer than with both candidate
-// addresses formed before the select, but the step is one instruction
-// shorter, which pays where the VALU is the bound (more than two waves per
-// SIMD).
+// step.
 //
 // Table entries (2^10 slots of 8 bytes per context; one ds_read_b64 meets
 // fewer LDS bank conflicts than two dword reads), d1 = 8 (slot - cum) and
@@ -78,25 +84,32 @@
 namespace ep {
 namespace {
 
-constexpr int kMaxWaves = 8;        // decoding waves per workgroup, single-round kernel
-constexpr int kMaxTileWaves = 16;  // multi-tile kernel: four per SIMD cover the decode chain
+constexpr int kMaxWaves = 16;      // waves per workgroup (four per SIMD cover the decode chain)
 constexpr uint32_t kCtxBytes = kProbTotal * 8;             // 8 KB per context
 constexpr uint32_t kTableBytes = kContexts * kCtxBytes;     // 57344
 constexpr uint32_t kRows = kProbTotal / 64;                // 16 rows of 64 slots per context
 constexpr uint32_t kMarkWords = kProbTotal / 32;           // 32 bitmap words per context
 constexpr uint32_t kLdsLimit = 160 * 1024;
-// slack after the last word buffer: a lane of a corrupt tile reads at most
-// 128 words past its clamped start, i.e. 258 bytes past the tile's end
-constexpr uint32_t kLdsPad = 512;
+constexpr uint32_t kMaxVecsPerLane = kTileVecsLarge / kStatesLow;  // 64
+// Slack after the last word buffer.  A lane's pointer starts clamped to its
+// tile's words and moves by at most one word per decoded symbol, 8 per
+// vector, so even in a corrupt tile it stays within 16 V bytes past the tile
+// (forward) or before it (backward, where the tables lie below the buffers);
+// the start-state reads of a corrupt tile reach at most 64 + 2 + 208 + 6
+// bytes past its start.
+constexpr uint32_t kLdsPad = 16 * kMaxVecsPerLane + 16;
+static_assert(kLdsPad >= 16 * kMaxVecsPerLane + 6 && kLdsPad >= 280, "LDS slack below a lane's worst overrun");
+static_assert(kTableBytes >= 16 * kMaxVecsPerLane, "a backward lane's worst underrun stays inside the tables");
 constexpr int kOutSym = 4;         // int16 lattice coordinates; 0..3 are the container dtypes
 
 static_assert(kProbBits == 10, "table addressing below assumes 2^10 slots per context");
+static_assert(kStateLow == (1u << 11) && kStateTop == 27, "X = 8x must fit 32 bits and refill below 8 L");
 
 // Kernel arguments.  The fields the first global loads need come first, so
 // that they arrive with the first batch of scalar loads.
 struct Args {
   const uint8_t *blob;
-  uint64_t off_freq, off_tile_offsets, off_states, off_scales, off_words;
+  uint64_t off_freq, off_tile_offsets, off_scales, off_words;
   uint32_t nsym[kContexts];
   uint32_t fidx[kContexts];
   uint32_t nzbase[kContexts];
@@ -105,9 +118,9 @@ struct Args {
   uint64_t cols;                  // columns of the output (padded layouts only)
   uint32_t rows, vpr;             // rows; vectors per row
   uint32_t row_magic, row_shift;  // vec / vpr = umulhi(vec, row_magic) >> row_shift  (vpr > 1)
-  uint32_t n_vec, n_tiles, waves;
+  uint32_t n_vec, n_tiles, n_units, waves;  // units: groups of 64 / states consecutive tiles, one per wave
   uint32_t rec_off, mark_off, words_off;  // LDS byte offsets
-  uint32_t wg_q, wg_rem;  // multi-tile kernel: workgroup b decodes wg_q tiles, one more if b < wg_rem
+  uint32_t wg_q, wg_rem;  // multi-tile kernel: workgroup b decodes wg_q units, one more if b < wg_rem
   uint32_t wbuf;          // multi-tile kernel: bytes of each wave's word buffer
 };
 
@@ -188,6 +201,7 @@ struct Lane {
   uint32_t q;       // X >> 13 of this step's state
   uint32_t r;       // the state's next word (its read may be in flight when a step starts)
   uint32_t p;       // LDS byte address of that word
+  uint32_t dp;      // +2 (even states read their region forward) or -2 (odd states, backward)
 };
 
 // BASE: the fixed part of the context's LDS address, folded into the
@@ -220,7 +234,7 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
   // of the refill block
   uint32_t r8;
   asm volatile("v_lshlrev_b32 %0, 3, %1" : "=v"(r8) : "v"(L.r), "v"(x));
-  const bool need = active && x < 0x10000u;
+  const bool need = active && x < (kStateLow << 3);  // x' < L, in units of X = 8x
   const uint64_t m = __ballot(need);
   const uint32_t X = select_mask(m, x, (x << 16) | r8);  // next state: refilling lanes shift the held word in
   // the address (X & 0x1ff8) | nb; opaque keeps BASE in the lookup's offset
@@ -231,8 +245,8 @@ __device__ __forceinline__ uint32_t rans_step(Lane &L, uint32_t nb, bool active)
     table_read<BASE>(opaque((X & 0x1ff8u) | nb), L.d0, L.d1);
   __builtin_amdgcn_sched_barrier(0);  // the next lookup goes out before the refill
   if (need) {  // refilling lanes only: read the following word
-    L.r = lds_u16(L.p + 2u);
-    L.p += 2u;
+    L.p += L.dp;
+    L.r = lds_u16(L.p);
   }
   L.q = X >> 13;
   return e;
@@ -292,20 +306,18 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
 }
 
-// writes one decoded vector.  row is the wave-uniform address of this step's
-// 64 vectors (unpadded layouts); local is the vector's index in the tile.
+// writes one decoded vector: at dst (unpadded layouts), or, with PADDED,
+// the C mod 8 leading elements of global vector vec element by element
 template <int OUT, bool WIDE, bool PADDED>
-__device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t tile, uint32_t local,
-                                            uint32_t lane, const uint32_t (&e)[8], float g) {
-  constexpr uint32_t kVecBytes = (OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u;
-  const uint32_t lane_off = kVecBytes * lane;
+__device__ __forceinline__ void emit_vector(const Args &A, gbyte_t dst, uint32_t vec, const uint32_t (&e)[8],
+                                            float g) {
   if constexpr (OUT == kOutSym) {
     uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       w[k] = ((uint32_t)entry_value<WIDE>(e[2 * k]) & 0xffffu) | ((uint32_t)entry_value<WIDE>(e[2 * k + 1]) << 16);
     const u32x4 pk = {w[0], w[1], w[2], w[3]};
-    __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x4 *)(row + lane_off));
+    __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x4 *)dst);
     return;
   } else {
     float y[8];
@@ -314,7 +326,7 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
     if constexpr (!PADDED) {
       if constexpr (OUT == EP_BF16 || OUT == EP_FP16) {
         const u32x4 pk = {pack2<OUT>(y[0], y[1]), pack2<OUT>(y[2], y[3]), pack2<OUT>(y[4], y[5]), pack2<OUT>(y[6], y[7])};
-        __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x4 *)(row + lane_off));
+        __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x4 *)dst);
       } else if constexpr (OUT == EP_FP8_E4M3FN) {
         // the first conversion of each word fills its low half; the high half
         // it keeps (here the first input's bits) is overwritten by the second,
@@ -325,7 +337,7 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
         int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c4, fp8_clamp(y[5]), __float_as_int(c4), false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(y[6]), fp8_clamp(y[7]), hi, true);
         const u32x2 pk = {(uint32_t)lo, (uint32_t)hi};
-        __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x2 *)(row + lane_off));
+        __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x2 *)dst);
       } else {
         const float magic = 12582912.0f;
         uint32_t lo = 0, hi = 0;
@@ -338,10 +350,9 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t row, uint32_t
         lo = int8_into<3>(lo, y[3], magic);
         hi = int8_into<3>(hi, y[7], magic);
         const u32x2 pk = {lo, hi};
-        __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x2 *)(row + lane_off));
+        __builtin_nontemporal_store(pk, (__attribute__((address_space(1))) u32x2 *)dst);
       }
     } else {
-      const uint32_t vec = tile * 1024u + local;
       const uint32_t r = vec / A.vpr, k = vec - r * A.vpr;
       const uint64_t base = (uint64_t)r * A.cols + 8ull * k;
       const uint32_t left = (uint32_t)(A.cols - 8ull * k);
@@ -373,55 +384,87 @@ __device__ __forceinline__ float row_scale(const Args &A, uint32_t vec) {
   return scales[r < last ? r : last];
 }
 
-// decodes one tile of NS states; PARTIAL handles the last tile of a stream
-// (n < 1024).  wb and we are the LDS byte addresses of the tile's first word
-// and of its end; X is 8 * the start state.  Lane q < NS decodes vectors q,
-// q + NS, ...; with NS = 64, gs holds the row scale of each of its 16
-// vectors, with fewer states the scales of each group of 16 steps are loaded
-// as the group starts, and lanes from NS on only follow along (they never
-// refill or store).
-//
-// BOP3: the lookup address by v_bitop3 rather than v_and_or.  On gfx950 the
-// first issues faster (about 1.9 against 2.8 SIMD cycles per instruction with
-// four waves per SIMD) at the same dependent latency; it measured 1.5-2%
-// faster in the single-round kernel and for 8-bit outputs, but 1-2.5% slower
-// for 16-bit outputs in the multi-tile kernel, whose code differs in that
-// instruction alone, so each kernel takes the faster form.
-template <int OUT, bool WIDE, bool PADDED, bool PARTIAL, bool BOP3, int NS>
-__device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t we, uint32_t X, uint32_t tile,
-                                            uint32_t n, const float (&gs)[16], uint32_t lane) {
-  static_assert(NS == 64 || NS == 16, "states per tile");
-  constexpr uint32_t kNs = (uint32_t)NS;
-  constexpr uint32_t kGroups = 1024u / kNs / 16u;  // groups of 16 steps
-  const bool mine = NS == 64 || lane < kNs;        // this lane holds one of the tile's states
+// The lanes of a wave's unit: unit u holds tiles u * 64/NS .. (64/NS tiles of
+// NS states; lanes 16r.. hold tile r's states when NS = 16).
+struct UnitLane {
+  uint32_t tile;  // the lane's tile (the stream's last for a tile past its end)
+  uint32_t q;     // the lane's state in its tile
+  uint32_t n;     // vectors in the lane's tile (0 past the stream's end)
+};
+
+template <int NS, int V>
+__device__ __forceinline__ UnitLane unit_lane(const Args &A, uint32_t unit, uint32_t lane) {
+  constexpr uint32_t kTv = (uint32_t)(NS * V);
+  UnitLane u;
+  const uint32_t t = unit * (64u / NS) + lane / NS;
+  u.q = lane % NS;
+  const bool have = t < A.n_tiles;
+  u.tile = have ? t : A.n_tiles - 1u;
+  u.n = have ? min(kTv, A.n_vec - t * kTv) : 0u;
+  return u;
+}
+
+// the row scales of lane's vectors 8g .. 8g + 7 (lanes past the end read the
+// last row; their values are unused)
+template <int NS, int V>
+__device__ __forceinline__ void group_scales(const Args &A, const UnitLane &u, uint32_t g, float (&gs)[8]) {
+  constexpr uint32_t kTv = (uint32_t)(NS * V);
+#pragma unroll
+  for (uint32_t s = 0; s < 8; ++s) gs[s] = row_scale(A, u.tile * kTv + (8u * g + s) * NS + u.q);
+}
+
+// Decodes a wave's unit.  wt, we: LDS byte addresses of the first word of
+// the lane's tile and of its end; gs: the row scales of the lane's first 8
+// vectors.  The lane reads its start state (length nibble, bit offset by a
+// prefix sum over its tile's states, three 16-bit reads) and its first word
+// (pair counts' prefix sum; odd states start at their region's end and read
+// backwards), then decodes V vectors in groups of 8, each group's row scales
+// loaded during the group before.  PARTIAL: some lane's tile holds fewer
+// vectors than a full one (the stream's last unit).
+template <int OUT, bool WIDE, bool PADDED, bool PARTIAL, bool BOP3, int NS, int V>
+__device__ __forceinline__ void decode_unit(const Args &A, const UnitLane &u, uint32_t wt, uint32_t we,
+                                            const float (&gs0)[8], uint32_t lane) {
+  static_assert((NS == 64 && (V == 8 || V == 16)) || (NS == 16 && (V == 32 || V == 64)), "tile geometry");
+  constexpr uint32_t kNs = (uint32_t)NS, kTv = (uint32_t)(NS * V), kGroups = (uint32_t)V / 8u;
+  const uint32_t q = u.q;
+  // ---- start state: W - 1 bits after the bits of the states before it
+  const uint32_t nb = ((lds_u8(wt + kNs / 2u + (q >> 1)) >> ((q & 1u) << 2)) & 15u) + 11u;
+  const uint32_t bincl = NS == 64 ? wave_inclusive_sum(nb) : row16_inclusive_sum(nb);
+  const uint32_t bo = bincl - nb;
+  const uint32_t btotal = NS == 64 ? (uint32_t)__builtin_amdgcn_readlane((int)bincl, 63)
+                                   : (uint32_t)__builtin_amdgcn_ds_bpermute((int)((lane | 15u) << 2), (int)bincl);
+  const uint32_t wa = wt + kNs + ((bo >> 4) << 1);
+  const uint32_t lo = lds_u16(wa) | (lds_u16(wa + 2u) << 16), hi = lds_u16(wa + 4u);
+  const uint32_t x = (__builtin_amdgcn_alignbit(hi, lo, bo & 15u) & ((1u << nb) - 1u)) | (1u << nb);
+  // ---- first word: pair k's region starts after the regions before it
+  const uint32_t pc = (q & 1u) ? 0u : lds_u8(wt + (q >> 1));
+  const uint32_t pincl = NS == 64 ? wave_inclusive_sum(pc) : row16_inclusive_sum(pc);
+  const uint32_t region = wt + kNs + (((btotal + 15u) >> 4) << 1);
+  uint32_t p = (q & 1u) ? region + 2u * pincl - 2u : region + 2u * (pincl - pc);
+  p = p < wt ? wt : (p > we ? we : p);  // a corrupt tile's pointers stay inside it
   Lane L;
+  L.dp = (q & 1u) ? 0xfffffffeu : 2u;
+  L.p = p;
+  L.r = lds_u16(p);
+  const uint32_t X = x << 3;
   table_read<0u>(X & 0x1ff8u, L.d0, L.d1);  // context F
   L.q = X >> 13;
-  // this state's words follow the NS count bytes and the words of the states
-  // before it; the clamp keeps every read of a corrupt tile inside the LDS
-  // allocation
-  const uint32_t cnt = mine ? lds_u8(wb + lane) : 0u;
-  const uint32_t p = wb + kNs + 2u * (wave_inclusive_sum(cnt) - cnt);
-  L.p = p < we ? p : we;
-  L.r = lds_u16(L.p);
   constexpr uint32_t kC = kCtxBytes, kE = 3u * kCtxBytes;  // LDS bases of C_0 and E_{0,0}
   constexpr uint32_t kBitB = WIDE ? 16u : 24u;  // where bit 0 of v sits in d0
   constexpr uint32_t kVecBytes = (OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u;
-  constexpr uint32_t kStepBytes = kNs * kVecBytes;
-  const gbyte_t tile_out = (gbyte_t)A.out + (uint64_t)tile * (1024u * kVecBytes);
+  const uint32_t tile = u.tile, n = u.n;
+  float gs[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) gs[s] = gs0[s];
 #pragma unroll 1
   for (uint32_t grp = 0; grp < kGroups; ++grp) {
-    if (PARTIAL && grp * 16u * kNs >= n) break;
-    float gl[16];
-    if constexpr (NS != 64) {
+    float gn[8];
+    if (grp + 1u < kGroups) group_scales<NS, V>(A, u, grp + 1u, gn);
 #pragma unroll
-      for (uint32_t s = 0; s < 16; ++s) gl[s] = row_scale(A, tile * 1024u + (grp * 16u + s) * kNs + (mine ? lane : 0u));
-    }
-#pragma unroll
-    for (uint32_t s = 0; s < 16; ++s) {
-      const uint32_t t = grp * 16u + s;  // step
-      const bool act = mine && (PARTIAL ? (t * kNs + lane < n) : true);
-      if (PARTIAL && t * kNs >= n) break;
+    for (uint32_t s8 = 0; s8 < 8; ++s8) {
+      const uint32_t s = grp * 8u + s8;  // step
+      const uint32_t i = s * kNs + q;    // the lane's vector in its tile
+      const bool act = PARTIAL ? i < n : true;
       uint32_t e[8];
       // C_b at LDS context 1 + b; the coset bit is in the entry of coordinate 0
       const uint32_t cb = __builtin_amdgcn_ubfe(L.d0, kBitB, 1u) << 13;
@@ -436,9 +479,20 @@ __device__ __forceinline__ void decode_tile(const Args &A, uint32_t wb, uint32_t
       const uint32_t eb = __builtin_amdgcn_ubfe(acc, kBitB, 2u) << 13;
       e[6] = rans_step<WIDE, kE, BOP3>(L, eb, act);
       e[7] = rans_step<WIDE, 0u, BOP3>(L, 0u, act);
-      if (act)
-        emit_vector<OUT, WIDE, PADDED>(A, opaque_s(tile_out + t * kStepBytes), tile, t * kNs + lane, lane, e,
-                                       NS == 64 ? gs[s] : gl[s]);
+      if (act) {
+        // one tile per wave: the step's 64 vectors are one run at a
+        // wave-uniform address; four tiles: each row's 16 vectors are one
+        gbyte_t dst;
+        if constexpr (NS == 64)
+          dst = opaque_s((gbyte_t)A.out + ((uint64_t)tile * kTv + s * kNs) * kVecBytes) + kVecBytes * lane;
+        else
+          dst = (gbyte_t)A.out + ((uint64_t)tile * kTv + i) * kVecBytes;
+        emit_vector<OUT, WIDE, PADDED>(A, dst, tile * kTv + i, e, gs[s8]);
+      }
+    }
+    if (grp + 1u < kGroups) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) gs[s] = gn[s];
     }
   }
 }
@@ -518,55 +572,55 @@ __device__ __forceinline__ void build_tables(const Args &A, uint8_t *lds, uint32
   }
 }
 
-// Multi-tile kernel: workgroup b decodes the consecutive tiles
-// [wg_first(b), wg_first(b + 1)); the counts differ by at most one tile.
+// Multi-tile kernel: workgroup b decodes the consecutive units
+// [wg_first(b), wg_first(b + 1)); the counts differ by at most one unit.
 __device__ __forceinline__ uint32_t wg_first(const Args &A, uint32_t b) {
   return b * A.wg_q + (b < A.wg_rem ? b : A.wg_rem);
 }
 
-// What a wave needs in registers to decode one tile: its start states, the
-// row scale of each of its lane's vectors, and where its words land in LDS.
-struct TileIn {
-  uint32_t x0;
-  float gs[16];
-  uint32_t wt, we;  // LDS byte addresses of the tile's first word and of its end
+// What a wave needs to decode one unit: its lanes' tiles, the row scales of
+// each lane's first 8 vectors, and where the lane's tile's words land in LDS.
+struct UnitIn {
+  UnitLane u;
+  float gs[8];
+  uint32_t wt, we;  // LDS byte addresses of the lane's tile's first word and of its end
 };
 
-// Issues a tile's loads: start states and row scales (vector loads), word
-// offsets (scalar loads), and the copy of its words into LDS at buf with
-// global_load_lds (1 KB per instruction; lanes past the end of the last,
-// partial kilobyte re-read its last 16 bytes).  Only the copy's addresses
-// wait, for the word offsets; nothing waits for the rest.
-template <int NS>
-__device__ __forceinline__ TileIn issue_tile(const Args &A, uint8_t *lds, uint32_t tile, uint32_t buf, uint32_t lane) {
-  TileIn T;
-  T.x0 = reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tile * (uint32_t)NS + (lane < (uint32_t)NS ? lane : 0u)];
-  if constexpr (NS == 64) {
-    const float *scales = reinterpret_cast<const float *>(A.blob + A.off_scales);
-    const uint32_t last = A.rows - 1u, one = A.vpr == 1u ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const uint32_t vec = tile * 1024u + 64u * s + lane;
-      const uint32_t r = ((__umulhi(vec, A.row_magic) >> A.row_shift) & ~one) | (vec & one);
-      T.gs[s] = scales[r < last ? r : last];  // lanes past the end read the last row; their values are unused
-    }
-  }
-  typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
-  const cptr_u32 toff = (cptr_u32)(A.blob + A.off_tile_offsets);
-  const uint32_t w_begin = toff[tile], w_end = toff[tile + 1u];
-  const uint64_t gbyte0 = (A.off_words + 2ull * w_begin) & ~15ull;
-  const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * w_end + 15ull) & ~15ull) - gbyte0) >> 4);
+// Copies the words [w_lo, w_hi) of the stream into LDS at buf: 16-byte
+// pieces from the 16-byte boundary at or below w_lo, 1 KB per instruction;
+// lanes past the end of the last, partial kilobyte re-read its last piece.
+// Returns that 16-byte aligned start (a byte offset in the stream).  Blocks
+// k0, k0 + dk, ... are this wave's share.
+__device__ __forceinline__ uint64_t copy_words(const Args &A, uint8_t *lds, uint32_t w_lo, uint32_t w_hi,
+                                               uint32_t buf, uint32_t lane, uint32_t k0, uint32_t dk) {
+  const uint64_t gbyte0 = (A.off_words + 2ull * w_lo) & ~15ull;
+  const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * w_hi + 15ull) & ~15ull) - gbyte0) >> 4);
   const gbyte_t src = (gbyte_t)(A.blob + gbyte0);
-  uint32_t i = 0;
-  for (; 64u * i + 64u <= nchunks; ++i)
-    __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + buf + 1024u * i), 16, 0, 0);
-  if (64u * i < nchunks) {
-    const uint32_t ch = lane + 64u * i;
+  for (uint32_t i = k0; 64u * i < nchunks; i += dk) {
+    const uint32_t ch = 64u * i + lane;
     __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (ch < nchunks ? ch : nchunks - 1u)),
                                      (lptr_t)(lds + buf + 1024u * i), 16, 0, 0);
   }
-  T.wt = buf + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);
-  T.we = T.wt + 2u * (w_end - w_begin);
+  return gbyte0;
+}
+
+// Issues a unit's loads: its lanes' tile offsets and row scales (vector
+// loads), the unit's word range (scalar loads), and the copy of its words
+// into LDS at buf.  Only the copy's addresses wait, for the word range.
+template <int NS, int V>
+__device__ __forceinline__ UnitIn issue_unit(const Args &A, uint8_t *lds, uint32_t unit, uint32_t buf,
+                                             uint32_t lane) {
+  UnitIn T;
+  T.u = unit_lane<NS, V>(A, unit, lane);
+  group_scales<NS, V>(A, T.u, 0u, T.gs);
+  const uint32_t *toffv = reinterpret_cast<const uint32_t *>(A.blob + A.off_tile_offsets);
+  const uint32_t tb = toffv[T.u.tile], te = toffv[T.u.tile + 1u];
+  typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
+  const cptr_u32 toff = (cptr_u32)(A.blob + A.off_tile_offsets);
+  const uint32_t t0 = unit * (64u / NS), t1 = min(t0 + 64u / NS, A.n_tiles);
+  const uint64_t gbyte0 = copy_words(A, lds, toff[t0], toff[t1], buf, lane, 0u, 1u);
+  T.wt = buf + (uint32_t)(A.off_words + 2ull * tb - gbyte0);
+  T.we = T.wt + 2u * (te - tb);
   return T;
 }
 
@@ -574,15 +628,39 @@ __device__ __forceinline__ TileIn issue_tile(const Args &A, uint8_t *lds, uint32
 // completed, none after it has started
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Streams with more tiles than one round of workgroups covers: one
+// the first 256 frequencies of this wave's first context, which need
+// nothing but the kernel arguments
+__device__ __forceinline__ void first_frequencies(const Args &A, uint32_t wave, uint32_t lane, uint32_t (&fpre)[4]) {
+  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
+  const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
+  const uint32_t n0 = pick(A.nsym, c0), f0 = pick(A.fidx, c0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t s = 64u * i + lane;
+    const uint32_t v = freq[f0 + (s < n0 ? s : 0u)];
+    fpre[i] = s < n0 ? v : 0u;
+  }
+}
+
+template <int OUT, bool WIDE, bool PADDED, bool BOP3, int NS, int V>
+__device__ __forceinline__ void decode_unit_any(const Args &A, const UnitLane &u, uint32_t wt, uint32_t we,
+                                                const float (&gs)[8], uint32_t lane) {
+  constexpr uint32_t kTv = (uint32_t)(NS * V);
+  if (__ballot(u.n != kTv) == 0)
+    decode_unit<OUT, WIDE, PADDED, false, BOP3, NS, V>(A, u, wt, we, gs, lane);
+  else
+    decode_unit<OUT, WIDE, PADDED, true, BOP3, NS, V>(A, u, wt, we, gs, lane);
+}
+
+// Streams with more units than one round of workgroups covers: one
 // workgroup per CU builds the tables once, then each of its k waves decodes
-// tiles first + wave, first + wave + k, ... of the workgroup's run on its
-// own, copying each tile's words into a buffer of its own.  After the tables
-// no wave waits for another: while one waits for its next tile's loads, the
+// units first + wave, first + wave + k, ... of the workgroup's run on its
+// own, copying each unit's words into a buffer of its own.  After the tables
+// no wave waits for another: while one waits for its next unit's loads, the
 // other waves of its SIMD keep the VALU busy (four waves per SIMD cover the
 // decode chain's latency).
-template <int OUT, bool WIDE, bool PADDED, int NS>
-__global__ void __launch_bounds__(64 * kMaxTileWaves) decode_waves_kernel(Args A) {
+template <int OUT, bool WIDE, bool PADDED, int NS, int V>
+__global__ void __launch_bounds__(64 * kMaxWaves) decode_waves_kernel(Args A) {
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -591,166 +669,112 @@ __global__ void __launch_bounds__(64 * kMaxTileWaves) decode_waves_kernel(Args A
   const uint32_t buf = A.words_off + wave * A.wbuf;  // this wave's word buffer
   constexpr bool kNarrowOut = OUT == EP_FP8_E4M3FN || OUT == EP_INT8;  // lookup address by v_bitop3
 
-  // ---- 1. the first context's frequencies ----------------------------------
-  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
-  const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
   uint32_t fpre[4];
-  {
-    const uint32_t n0 = pick(A.nsym, c0), f0 = pick(A.fidx, c0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t s = 64u * i + lane;
-      const uint32_t v = freq[f0 + (s < n0 ? s : 0u)];
-      fpre[i] = s < n0 ? v : 0u;
-    }
-  }
-  uint32_t tile = wg_first(A, blockIdx.x) + wave;
-  const uint32_t tc = tile < end ? tile : end - 1u;  // waves without a tile load a valid one and drop it
-  // Waves that build no table issue their first tile's loads now and start
+  first_frequencies(A, wave, lane, fpre);
+  uint32_t unit = wg_first(A, blockIdx.x) + wave;
+  const uint32_t uc = unit < end ? unit : end - 1u;  // waves without a unit load a valid one and drop it
+  // Waves that build no table issue their first unit's loads now and start
   // decoding right after the barrier; the table builders issue theirs after
-  // their table, so that no wait for a tile's loads (the compiler waits for
+  // their table, so that no wait for a unit's loads (the compiler waits for
   // every copy into LDS before the next LDS access) delays a table.
   const bool builder = wave < (uint32_t)kContexts;
-  TileIn T;
-  if (!builder) T = issue_tile<NS>(A, lds, tc, buf, lane);
-
-  // ---- 2. the tables -------------------------------------------------------
+  UnitIn T;
+  if (!builder) T = issue_unit<NS, V>(A, lds, uc, buf, lane);
   build_tables<WIDE>(A, lds, wave, lane, k, fpre);
-  if (builder) T = issue_tile<NS>(A, lds, tc, buf, lane);
+  if (builder) T = issue_unit<NS, V>(A, lds, uc, buf, lane);
   lds_barrier();  // tables built (every wave's LDS writes done)
 
-  // ---- 3. this wave's tiles --------------------------------------------------
-  while (tile < end) {
-    __builtin_amdgcn_s_waitcnt(0);  // the tile's states, scales and words have landed
-    const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
-    if (n == 1024u)
-      decode_tile<OUT, WIDE, PADDED, false, kNarrowOut, NS>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
-    else
-      decode_tile<OUT, WIDE, PADDED, true, kNarrowOut, NS>(A, T.wt, T.we, T.x0 << 3, tile, n, T.gs, lane);
-    tile += k;
-    if (tile < end) {
-      __builtin_amdgcn_s_waitcnt(0);  // every read of the finished tile's words is done before they are overwritten
-      T = issue_tile<NS>(A, lds, tile, buf, lane);
+  while (unit < end) {
+    __builtin_amdgcn_s_waitcnt(0);  // the unit's offsets, scales and words have landed
+    decode_unit_any<OUT, WIDE, PADDED, kNarrowOut, NS, V>(A, T.u, T.wt, T.we, T.gs, lane);
+    unit += k;
+    if (unit < end) {
+      __builtin_amdgcn_s_waitcnt(0);  // every read of the finished unit's words is done before they are overwritten
+      T = issue_unit<NS, V>(A, lds, unit, buf, lane);
     }
   }
 }
 
-// Streams that one round of workgroups covers: workgroups of up to 8 waves,
-// one tile each.
-template <int OUT, bool WIDE, bool PADDED, int NS>
+// Streams that one round of workgroups covers: workgroups of up to 16 waves,
+// one unit each.
+template <int OUT, bool WIDE, bool PADDED, int NS, int V>
 __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
   extern __shared__ __align__(16) uint8_t lds[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t nwaves = A.waves;
+  constexpr uint32_t kTpw = 64u / NS;
 
   // ---- 1. global loads, all unconditional so that each wait is exact ----
-  const uint32_t tile = blockIdx.x * nwaves + wave;
-  const bool has_tile = tile < A.n_tiles;
-  const uint32_t tc = has_tile ? tile : A.n_tiles - 1u;  // waves without a tile load a valid one and drop it
+  const uint32_t unit = blockIdx.x * nwaves + wave;
+  const bool has_unit = unit < A.n_units;
+  const UnitLane u = unit_lane<NS, V>(A, has_unit ? unit : A.n_units - 1u, lane);
   // The workgroup's tiles are consecutive, so their words are one range of
-  // the stream.  The tile offsets the wave needs come first, from one vector
-  // load (lane 0: its tile's first word, lane 1: the tile's end, lanes 2 and
-  // 3: the workgroup's range): scalar loads would share their counter with
-  // the table build's LDS accesses, whose waits would then wait for them too.
-  const uint32_t g0 = blockIdx.x * nwaves;
-  const uint32_t gend = g0 + nwaves < A.n_tiles ? g0 + nwaves : A.n_tiles;
-  const uint32_t oi = lane == 0u ? tc : lane == 1u ? tc + 1u : lane == 2u ? g0 : gend;
-  const uint32_t ov = reinterpret_cast<const uint32_t *>(A.blob + A.off_tile_offsets)[oi];
-  // the first 256 frequencies of this wave's first context (they need
-  // nothing but the kernel arguments)
-  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
-  const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
+  // the stream.  Every lane loads its tile's first and end word and the
+  // range's first word; copying waves also its end.  These are vector loads:
+  // scalar loads would share their counter with the table build's LDS
+  // accesses, whose waits would then wait for them too.
+  const uint32_t *toff = reinterpret_cast<const uint32_t *>(A.blob + A.off_tile_offsets);
+  const uint32_t g0 = blockIdx.x * nwaves * kTpw;
+  const uint32_t gend = min(g0 + nwaves * kTpw, A.n_tiles);
+  const uint32_t tb = toff[u.tile], te = toff[u.tile + 1u];
+  const uint32_t w_lo = toff[g0];
   uint32_t fpre[4];
-  {
-    const uint32_t n0 = pick(A.nsym, c0), f0 = pick(A.fidx, c0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t s = 64u * i + lane;
-      const uint32_t v = freq[f0 + (s < n0 ? s : 0u)];
-      fpre[i] = s < n0 ? v : 0u;
-    }
-  }
-  const uint32_t x0 =
-      reinterpret_cast<const uint32_t *>(A.blob + A.off_states)[tc * (uint32_t)NS + (lane < (uint32_t)NS ? lane : 0u)];
-  float gs[16];
-  if constexpr (NS == 64) {
-    const float *scales = reinterpret_cast<const float *>(A.blob + A.off_scales);
-    const uint32_t last = A.rows - 1u, one = A.vpr == 1u ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const uint32_t vec = tc * 1024u + 64u * s + lane;
-      const uint32_t r = ((__umulhi(vec, A.row_magic) >> A.row_shift) & ~one) | (vec & one);
-      gs[s] = scales[r < last ? r : last];  // lanes past the end read the last row; their values are unused
-    }
-  }
+  first_frequencies(A, wave, lane, fpre);
+  float gs[8];
+  group_scales<NS, V>(A, u, 0u, gs);
   __builtin_amdgcn_sched_barrier(0);  // the loads above go out before anything waits
-  // ---- 2. one wave per context: the tables --------------------------------
-  build_tables<WIDE>(A, lds, wave, lane, nwaves, fpre);
-
-  // The last wave (which builds no table when the workgroup has eight waves)
-  // copies the workgroup's words into LDS with global_load_lds (1 KB per
-  // instruction, lanes past the end re-read the last 16 bytes).  This comes
-  // after the table build: where the copying branch rejoins, the compiler
-  // waits for every load, so before the build that wait would hold every
-  // builder until its tile's states and scales had landed.
-  if (wave == nwaves - 1u) {
-    const uint64_t gbyte0 = (A.off_words + 2ull * __builtin_amdgcn_readlane(ov, 2)) & ~15ull;
-    const uint32_t nchunks =
-        (uint32_t)((((A.off_words + 2ull * __builtin_amdgcn_readlane(ov, 3) + 15ull) & ~15ull) - gbyte0) >> 4);
-    const gbyte_t src = (gbyte_t)(A.blob + gbyte0);
-    // whole kilobytes first: no per-lane clamp, so each load issues right
-    // after the last one
-    uint32_t i = 0;
-    for (; 64u * i + 64u <= nchunks; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(src + 1024u * i + 16u * lane), (lptr_t)(lds + A.words_off + 1024u * i),
-                                       16, 0, 0);
-    if (64u * i < nchunks) {
-      const uint32_t ch = lane + 64u * i;
-      __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (ch < nchunks ? ch : nchunks - 1u)),
-                                       (lptr_t)(lds + A.words_off + 1024u * i), 16, 0, 0);
-    }
+  // ---- 2. the tables (waves 0..6) and the word copy (the others) ----------
+  const uint32_t builders = nwaves < (uint32_t)kContexts + 1u ? nwaves : (uint32_t)kContexts;
+  if (wave < builders) build_tables<WIDE>(A, lds, wave, lane, builders, fpre);
+  // With eight or more waves the waves past the builders copy the
+  // workgroup's words into LDS with global_load_lds (1 KB per instruction),
+  // each taking every (waves - 7)th kilobyte; with fewer the last wave copies
+  // them after its table.  Where the copying branch rejoins, the compiler
+  // waits for every load, so a builder that copied before its table would
+  // wait for its states and scales first.
+  if (wave >= builders || (builders == nwaves && wave == nwaves - 1u)) {
+    const uint32_t w_hi = toff[gend];
+    const uint32_t k0 = wave >= builders ? wave - builders : 0u, dk = wave >= builders ? nwaves - builders : 1u;
+    (void)copy_words(A, lds, __builtin_amdgcn_readfirstlane(w_lo), __builtin_amdgcn_readfirstlane(w_hi),
+                     A.words_off, lane, k0, dk);
   }
-
-  __builtin_amdgcn_s_waitcnt(0);  // the loader's words have landed in LDS
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
   __syncthreads();
 
   // ---- 3. decode ---------------------------------------------------------
-  if (!has_tile) return;
-  const uint32_t n = min(1024u, A.n_vec - tile * 1024u);
-  const uint32_t X = x0 << 3;
-  const uint32_t w_begin = __builtin_amdgcn_readlane(ov, 0), w_end = __builtin_amdgcn_readlane(ov, 1);
-  const uint64_t gbyte0 = (A.off_words + 2ull * __builtin_amdgcn_readlane(ov, 2)) & ~15ull;  // 16-byte aligned start of the range
-  const uint32_t wt = A.words_off + (uint32_t)(A.off_words + 2ull * w_begin - gbyte0);  // LDS address of this tile's first word
-  const uint32_t we = wt + 2u * (w_end - w_begin);
-  if (n == 1024u)
-    decode_tile<OUT, WIDE, PADDED, false, true, NS>(A, wt, we, X, tile, n, gs, lane);
-  else
-    decode_tile<OUT, WIDE, PADDED, true, true, NS>(A, wt, we, X, tile, n, gs, lane);
+  if (!has_unit) return;
+  const uint64_t gbyte0 = (A.off_words + 2ull * w_lo) & ~15ull;  // 16-byte aligned start of the range
+  const uint32_t wt = A.words_off + (uint32_t)(A.off_words + 2ull * tb - gbyte0);  // LDS address of the tile's first word
+  const uint32_t we = wt + 2u * (te - tb);
+  decode_unit_any<OUT, WIDE, PADDED, true, NS, V>(A, u, wt, we, gs, lane);
 }
 
 typedef void (*KernelFn)(Args);
 
 template <int OUT, bool WIDE, bool PADDED>
-KernelFn pick3(bool multi, bool low) {
-  if (low) return multi ? decode_waves_kernel<OUT, WIDE, PADDED, kStatesLow> : decode_kernel<OUT, WIDE, PADDED, kStatesLow>;
-  return multi ? decode_waves_kernel<OUT, WIDE, PADDED, kStatesPerTile> : decode_kernel<OUT, WIDE, PADDED, kStatesPerTile>;
+KernelFn pick4(bool multi, int ns, int tv) {
+  if (ns == kStatesLow) {
+    if (tv == kTileVecsSmall) return multi ? decode_waves_kernel<OUT, WIDE, PADDED, 16, 32> : decode_kernel<OUT, WIDE, PADDED, 16, 32>;
+    return multi ? decode_waves_kernel<OUT, WIDE, PADDED, 16, 64> : decode_kernel<OUT, WIDE, PADDED, 16, 64>;
+  }
+  if (tv == kTileVecsSmall) return multi ? decode_waves_kernel<OUT, WIDE, PADDED, 64, 8> : decode_kernel<OUT, WIDE, PADDED, 64, 8>;
+  return multi ? decode_waves_kernel<OUT, WIDE, PADDED, 64, 16> : decode_kernel<OUT, WIDE, PADDED, 64, 16>;
 }
 
 template <int OUT>
-KernelFn pick(bool wide, bool padded, bool multi, bool low) {
-  if (wide) return padded ? pick3<OUT, true, true>(multi, low) : pick3<OUT, true, false>(multi, low);
-  return padded ? pick3<OUT, false, true>(multi, low) : pick3<OUT, false, false>(multi, low);
+KernelFn pick(bool wide, bool padded, bool multi, int ns, int tv) {
+  if (wide) return padded ? pick4<OUT, true, true>(multi, ns, tv) : pick4<OUT, true, false>(multi, ns, tv);
+  return padded ? pick4<OUT, false, true>(multi, ns, tv) : pick4<OUT, false, false>(multi, ns, tv);
 }
 
-// low: the stream has kStatesLow states per tile
-KernelFn pick_kernel(int out, bool wide, bool padded, bool multi, bool low) {
+KernelFn pick_kernel(int out, bool wide, bool padded, bool multi, int ns, int tv) {
   switch (out) {
-    case EP_BF16: return pick<EP_BF16>(wide, padded, multi, low);
-    case EP_FP16: return pick<EP_FP16>(wide, padded, multi, low);
-    case EP_FP8_E4M3FN: return pick<EP_FP8_E4M3FN>(wide, padded, multi, low);
-    case EP_INT8: return pick<EP_INT8>(wide, padded, multi, low);
-    default: return pick<kOutSym>(wide, false, multi, low);
+    case EP_BF16: return pick<EP_BF16>(wide, padded, multi, ns, tv);
+    case EP_FP16: return pick<EP_FP16>(wide, padded, multi, ns, tv);
+    case EP_FP8_E4M3FN: return pick<EP_FP8_E4M3FN>(wide, padded, multi, ns, tv);
+    case EP_INT8: return pick<EP_INT8>(wide, padded, multi, ns, tv);
+    default: return pick<kOutSym>(wide, false, multi, ns, tv);
   }
 }
 
@@ -796,20 +820,18 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     set_error("device buffers must be 16-byte aligned");
     return EP_ERR_ARG;
   }
-  if (s.n_vec >= (int64_t(1) << 31) || s.rows >= (int64_t(1) << 31)) {
-    set_error("stream too large");
-    return EP_ERR_FORMAT;
-  }
-  // tile offsets: monotone, inside the word section, room for the count bytes
+  // tile offsets: monotone, inside the word section, room for the pair counts
+  // and length codes
   const uint8_t *toff = hb + s.off_tile_offsets;
+  auto first_word = [&](int64_t t) { return rd<uint32_t>(toff + 4 * t); };
   for (int64_t t = 0; t < s.tiles; ++t) {
-    const uint32_t b = rd<uint32_t>(toff + 4 * t), e = rd<uint32_t>(toff + 4 * t + 4);
+    const uint32_t b = first_word(t), e = first_word(t + 1);
     if (e < b || e > s.n_words || e - b < (uint32_t)s.states / 2u) {
       set_error("corrupt tile offsets");
       return EP_ERR_FORMAT;
     }
   }
-  if (rd<uint32_t>(toff + 4 * s.tiles) != s.n_words) {
+  if (first_word(s.tiles) != s.n_words) {
     set_error("corrupt tile offsets");
     return EP_ERR_FORMAT;
   }
@@ -840,31 +862,37 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
       return EP_ERR_FORMAT;
     }
   }
-  // LDS layout: tables | records | bitmap | words | pad.  The
-  // words of a workgroup's consecutive tiles are one range; with k waves per
-  // workgroup the buffer holds the longest such range, in whole 1 KB copies.
+  // LDS layout: tables | records | bitmap | words | pad.  A wave decodes a
+  // unit of 64 / states consecutive tiles; the words of a workgroup's
+  // consecutive units are one range, copied in whole kilobytes from a 16-byte
+  // boundary.
+  const int64_t tpw = 64 / s.states;
+  const int64_t units = (s.tiles + tpw - 1) / tpw;
   uint32_t off = kTableBytes;
   A.rec_off = off;
   off += 8 * nz_total;
   A.mark_off = off;
   off = (uint32_t)align16(off + 4 * kContexts * kMarkWords);
   A.words_off = off;
-  auto span_for = [&](uint32_t k) {
+  // bytes the copy of tiles [t0, t1) takes
+  auto copy_bytes = [&](int64_t t0, int64_t t1) {
+    const uint64_t a0 = (s.off_words + 2ull * first_word(t0)) & ~15ull;
+    const uint64_t a1 = (s.off_words + 2ull * first_word(t1) + 15ull) & ~15ull;
+    return (a1 - a0 + 1023ull) & ~1023ull;
+  };
+  // the largest copy of k consecutive units
+  auto span_for = [&](int64_t k) {
     uint64_t span = 0;
-    for (int64_t t = 0; t < s.tiles; t += k) {
-      const int64_t e = std::min<int64_t>(t + k, s.tiles);
-      const uint64_t a0 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t)) & ~15ull;
-      const uint64_t a1 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * e) + 15ull) & ~15ull;
-      span = std::max<uint64_t>(span, a1 - a0);
-    }
-    return (span + 1023ull) & ~1023ull;
+    for (int64_t u0 = 0; u0 < units; u0 += k)
+      span = std::max<uint64_t>(span, copy_bytes(u0 * tpw, std::min<int64_t>((u0 + k) * tpw, s.tiles)));
+    return span;
   };
   uint32_t waves = 0;
   uint64_t span = 0;
-  for (uint32_t k = kMaxWaves; k >= 1; --k) {
+  for (int64_t k = std::min<int64_t>(kMaxWaves, units); k >= 1; --k) {
     span = span_for(k);
     if (off + span + kLdsPad <= kLdsLimit) {
-      waves = k;
+      waves = (uint32_t)k;
       break;
     }
   }
@@ -873,33 +901,24 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     return EP_ERR_FORMAT;
   }
   uint32_t lds_bytes = off + (uint32_t)span + kLdsPad;
-  uint32_t grid = (uint32_t)((s.tiles + waves - 1) / waves);
+  uint32_t grid = (uint32_t)((units + waves - 1) / waves);
   // More workgroups than compute units: the multi-tile kernel instead, with
   // one workgroup per CU that builds the tables once.
   const bool multi = (int64_t)grid > num_cus();
   if (multi) {
-    // One workgroup per CU, each with a run of consecutive tiles (counts that
-    // differ by at most one); its k waves take the run's tiles in turn.  k is
+    // One workgroup per CU, each with a run of consecutive units (counts that
+    // differ by at most one); its k waves take the run's units in turn.  k is
     // as many waves as the run and the LDS allow (at most 16, four per SIMD).
-    // Measured on runs of 17 to 40 tiles, no smaller k with fewer or evener
-    // passes does better: 18 tiles per CU take 15% less time as 16 waves (two
-    // of them with a second tile) than as 9 waves of two tiles each.  Every
-    // wave has a buffer for one tile's words, copied in whole kilobytes from
-    // a 16-byte aligned start.
-    uint64_t wbuf = 0;
-    for (int64_t t = 0; t < s.tiles; ++t) {
-      const uint64_t a0 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t)) & ~15ull;
-      const uint64_t a1 = (s.off_words + 2ull * rd<uint32_t>(toff + 4 * t + 4) + 15ull) & ~15ull;
-      wbuf = std::max<uint64_t>(wbuf, (a1 - a0 + 1023ull) & ~1023ull);
-    }
+    // Every wave has a buffer for one unit's words.
+    const uint64_t wbuf = span_for(1);
     const uint64_t room = kLdsLimit - std::min<uint64_t>(kLdsLimit, (uint64_t)A.words_off + kLdsPad);
-    const int64_t kmax = std::min<int64_t>(kMaxTileWaves, (int64_t)(room / wbuf));
+    const int64_t kmax = std::min<int64_t>(kMaxWaves, (int64_t)(room / wbuf));
     if (kmax < 1) {
       set_error("tile too large for the decoder's LDS budget");
       return EP_ERR_FORMAT;
     }
-    const int64_t g = std::min<int64_t>(s.tiles, num_cus());
-    const int64_t q = s.tiles / g, rem = s.tiles % g, qmax = q + (rem ? 1 : 0);
+    const int64_t g = std::min<int64_t>(units, num_cus());
+    const int64_t q = units / g, rem = units % g, qmax = q + (rem ? 1 : 0);
     waves = (uint32_t)std::min<int64_t>(kmax, qmax);
     grid = (uint32_t)g;
     A.wg_q = (uint32_t)q;
@@ -911,7 +930,6 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   A.out = dev_out;
   A.off_freq = s.off_freq;
   A.off_scales = s.off_scales;
-  A.off_states = s.off_states;
   A.off_tile_offsets = s.off_tile_offsets;
   A.off_words = s.off_words;
   A.cols = (uint64_t)s.cols;
@@ -920,8 +938,9 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   if (A.vpr > 1) row_divider(A.vpr, A.row_magic, A.row_shift);
   A.n_vec = (uint32_t)s.n_vec;
   A.n_tiles = (uint32_t)s.tiles;
+  A.n_units = (uint32_t)units;
   const bool padded = out != kOutSym && (s.cols % 8) != 0;
-  KernelFn fn = pick_kernel(out, wide, padded, multi, s.states == kStatesLow);
+  KernelFn fn = pick_kernel(out, wide, padded, multi, s.states, s.tile_vecs);
   static std::mutex mu;
   static std::vector<KernelFn> configured;
   {

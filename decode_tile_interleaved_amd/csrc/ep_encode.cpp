@@ -5,8 +5,9 @@
 // Arbitrary Bitrates" (arXiv abstract, mlsanity index page).  The pages give
 // the steps, not their internals; the choices made here (RMS row scale, a
 // 7-context model built on E8's coset bit and even-sum parity, 10-bit
-// frequencies, 64 interleaved states per 1024-vector tile, each state's words
-// stored together behind a count byte) define the stream that ep_decode.hip
+// frequencies, 64 or 16 interleaved states per 512- or 1024-vector tile,
+// start states bit-packed at their length, each pair of states sharing one
+// word region read from both ends) define the stream that ep_decode.hip
 // reads.
 #include <algorithm>
 #include <atomic>
@@ -242,9 +243,8 @@ static bool build_tables(const std::vector<uint64_t> &h, Tables &t) {
 // the passes over the matrix on host threads
 // ---------------------------------------------------------------------------
 struct TileOut {
-  uint32_t states[kStatesPerTile];  // the first shape.states are used
-  std::vector<uint16_t> words;
-  bool overflow = false;            // a state's word count does not fit its count byte
+  std::vector<uint16_t> words;  // the tile as the stream stores it
+  bool overflow = false;        // a pair's word count does not fit its count byte
 };
 
 class HostBackend final : public EncodeBackend {
@@ -270,7 +270,8 @@ class HostBackend final : public EncodeBackend {
     return EP_ERR_NONFINITE;
   }
 
-  int histogram(const std::vector<float> &g, int64_t S, std::vector<uint64_t> &hist, std::string &) override {
+  int histogram(const std::vector<float> &g, int64_t S, uint64_t seed, std::vector<uint64_t> &hist,
+                std::string &) override {
     if (S >= S_.n_vec) return full_pass(g, hist);
     const int nt = std::max(1, std::min(threads_, 16));
     std::vector<std::vector<uint64_t>> part(nt, std::vector<uint64_t>((size_t)kContexts * kSymSpan, 0));
@@ -280,7 +281,7 @@ class HostBackend final : public EncodeBackend {
       pool.emplace_back([&, t]() {
         int32_t v[8];
         for (int64_t k = t * S / nt; k < (t + 1) * S / nt; ++k) {
-          int64_t vid = (int64_t)(((uint64_t)k * (uint64_t)S_.n_vec) / (uint64_t)S);
+          int64_t vid = sample_vid(S_.n_vec, k, S, seed);
           int64_t r = vid / S_.vpr;
           if (!quantize(src_, S_.dtype, S_.C, r, vid % S_.vpr, g[(size_t)r], v)) {
             overflow = true;
@@ -298,8 +299,8 @@ class HostBackend final : public EncodeBackend {
     return 0;
   }
 
-  int encode_tiles(const std::vector<float> &g, const Tables &tb, std::vector<uint32_t> &states,
-                   std::vector<uint32_t> &tile_first, std::string &err) override {
+  int encode_tiles(const std::vector<float> &g, const Tables &tb, std::vector<uint32_t> &tile_first,
+                   std::string &err) override {
     if (V_.empty() || Vg_ != g) {  // the lattice vectors of the last full pass, if it was at these scales
       std::vector<uint64_t> ignored;
       if (full_pass(g, ignored) != 0) {
@@ -307,16 +308,14 @@ class HostBackend final : public EncodeBackend {
         return EP_ERR_ARG;
       }
     }
-    tiles_.assign((size_t)S_.tiles, TileOut{});
-    parallel_for(S_.tiles, std::max(1, threads_), [&](int64_t b, int64_t e) {
+    const int64_t tiles = (S_.n_vec + tile_vecs_ - 1) / tile_vecs_;
+    tiles_.assign((size_t)tiles, TileOut{});
+    parallel_for(tiles, std::max(1, threads_), [&](int64_t b, int64_t e) {
       for (int64_t t = b; t < e; ++t) encode_tile(tb, t, tiles_[(size_t)t]);
     });
-    const int ns = states_;
-    states.resize((size_t)S_.tiles * ns);
-    tile_first.resize((size_t)S_.tiles + 1);
+    tile_first.resize((size_t)tiles + 1);
     uint64_t w = 0;
-    for (int64_t t = 0; t < S_.tiles; ++t) {
-      std::memcpy(&states[(size_t)t * ns], tiles_[(size_t)t].states, 4 * (size_t)ns);
+    for (int64_t t = 0; t < tiles; ++t) {
       tile_first[(size_t)t] = (uint32_t)w;
       w += tiles_[(size_t)t].words.size();
       if (w > 0xffffffffull) {
@@ -324,7 +323,7 @@ class HostBackend final : public EncodeBackend {
         return EP_ERR_SHAPE;
       }
     }
-    tile_first[(size_t)S_.tiles] = (uint32_t)w;
+    tile_first[(size_t)tiles] = (uint32_t)w;
     for (const TileOut &to : tiles_)
       if (to.overflow) return 1;
     return 0;
@@ -384,59 +383,81 @@ class HostBackend final : public EncodeBackend {
     return 0;
   }
 
-  // one tile: interleaved rANS in reverse order, then the count bytes and
-  // each state's words in the order the decoder consumes them
+  // one tile: interleaved rANS in reverse decode order from x = L, then the
+  // tile as the stream stores it (pair counts, length codes, start bits,
+  // pair regions)
   void encode_tile(const Tables &tb, int64_t tile, TileOut &out) const {
-  const int64_t first = tile * kTileVecs;
-  const int n = (int)std::min<int64_t>(kTileVecs, S_.n_vec - first);
-  // (frequency, cumulative) of every coordinate, vector-major
-  std::vector<uint32_t> fc((size_t)n * 8 * 2);
-  for (int i = 0; i < n; ++i) {
-    int64_t vid = first + i;
-    const int32_t *v = &V_[(size_t)((vid / S_.vpr) * S_.C8 + 8 * (vid % S_.vpr))];
-    Coded cd = model(v);
-    for (int j = 0; j < 8; ++j) {
-      int c = cd.ctx[j], s = cd.sym[j] - tb.smin[c];
-      fc[(size_t)(i * 8 + j) * 2] = tb.freq[c][s];
-      fc[(size_t)(i * 8 + j) * 2 + 1] = tb.cum[c][s];
+    const int64_t first = tile * tile_vecs_;
+    const int n = (int)std::min<int64_t>(tile_vecs_, S_.n_vec - first);
+    // (frequency, cumulative) of every coordinate, vector-major
+    std::vector<uint32_t> fc((size_t)n * 8 * 2);
+    for (int i = 0; i < n; ++i) {
+      int64_t vid = first + i;
+      const int32_t *v = &V_[(size_t)((vid / S_.vpr) * S_.C8 + 8 * (vid % S_.vpr))];
+      Coded cd = model(v);
+      for (int j = 0; j < 8; ++j) {
+        int c = cd.ctx[j], s = cd.sym[j] - tb.smin[c];
+        fc[(size_t)(i * 8 + j) * 2] = tb.freq[c][s];
+        fc[(size_t)(i * 8 + j) * 2 + 1] = tb.cum[c][s];
+      }
+    }
+    const int S = states_;
+    uint32_t x[kStatesPerTile];
+    for (int q = 0; q < S; ++q) x[q] = kStateLow;
+    std::vector<uint16_t> emitted;  // emission order (reverse of consumption)
+    std::vector<uint8_t> who;       // state that emitted each word
+    emitted.reserve((size_t)n * 3);
+    who.reserve((size_t)n * 3);
+    const int steps = tile_vecs_ / S;
+    for (int s = steps - 1; s >= 0; --s)
+      for (int j = 7; j >= 0; --j)
+        for (int q = S - 1; q >= 0; --q) {
+          int i = s * S + q;
+          if (i >= n) continue;
+          uint32_t f = fc[(size_t)(i * 8 + j) * 2], c = fc[(size_t)(i * 8 + j) * 2 + 1];
+          uint32_t st = x[q];
+          if ((uint64_t)st >= ((uint64_t)f << (kStateTop - kProbBits))) {
+            emitted.push_back((uint16_t)st);
+            who.push_back((uint8_t)q);
+            st >>= 16;
+          }
+          x[q] = (st / f) * kProbTotal + st % f + c;
+        }
+    // per-state words in consumption order
+    std::vector<std::vector<uint16_t>> lane((size_t)S);
+    for (size_t k = emitted.size(); k-- > 0;) lane[who[k]].push_back(emitted[k]);
+    std::vector<uint16_t> &w = out.words;
+    w.clear();
+    w.reserve(emitted.size() + (size_t)S + 8);
+    out.overflow = false;
+    for (int q = 0; q < S; q += 4) {  // pair counts, two pairs to a word
+      const size_t lo = lane[q].size() + lane[q + 1].size(), hi = lane[q + 2].size() + lane[q + 3].size();
+      out.overflow |= lo > 255 || hi > 255;
+      w.push_back((uint16_t)((lo & 0xff) | (hi & 0xff) << 8));
+    }
+    int bits[kStatesPerTile];
+    for (int q = 0; q < S; ++q) bits[q] = 32 - __builtin_clz(x[q]);  // in [12, 27]
+    for (int q = 0; q < S; q += 4)  // length codes, four to a word
+      w.push_back((uint16_t)((bits[q] - 12) | (bits[q + 1] - 12) << 4 | (bits[q + 2] - 12) << 8 |
+                             (bits[q + 3] - 12) << 12));
+    // start states below their leading bit, least significant bit first
+    uint64_t acc = 0;
+    int nacc = 0;
+    for (int q = 0; q < S; ++q) {
+      acc |= (uint64_t)(x[q] & ((1u << (bits[q] - 1)) - 1u)) << nacc;
+      nacc += bits[q] - 1;
+      while (nacc >= 16) {
+        w.push_back((uint16_t)acc);
+        acc >>= 16;
+        nacc -= 16;
+      }
+    }
+    if (nacc > 0) w.push_back((uint16_t)acc);
+    for (int q = 0; q < S; q += 2) {  // region of states q, q + 1
+      w.insert(w.end(), lane[q].begin(), lane[q].end());
+      w.insert(w.end(), lane[q + 1].rbegin(), lane[q + 1].rend());
     }
   }
-  const int S = states_;
-  uint32_t x[kStatesPerTile];
-  for (int q = 0; q < S; ++q) x[q] = kStateLow;
-  std::vector<uint16_t> emitted;   // emission order (reverse of consumption)
-  std::vector<uint8_t> who;        // state that emitted each word
-  emitted.reserve((size_t)n * 3);
-  who.reserve((size_t)n * 3);
-  const int steps = kTileVecs / S;
-  for (int s = steps - 1; s >= 0; --s)
-    for (int j = 7; j >= 0; --j)
-      for (int q = S - 1; q >= 0; --q) {
-        int i = s * S + q;
-        if (i >= n) continue;
-        uint32_t f = fc[(size_t)(i * 8 + j) * 2], c = fc[(size_t)(i * 8 + j) * 2 + 1];
-        uint32_t st = x[q];
-        if ((uint64_t)st >= ((uint64_t)f << (29 - kProbBits))) {
-          emitted.push_back((uint16_t)st);
-          who.push_back((uint8_t)q);
-          st >>= 16;
-        }
-        x[q] = (st / f) * kProbTotal + st % f + c;
-      }
-  std::memcpy(out.states, x, sizeof(uint32_t) * (size_t)S);
-  // per-state words in consumption order
-  std::vector<std::vector<uint16_t>> lane((size_t)S);
-  for (size_t k = emitted.size(); k-- > 0;) lane[who[k]].push_back(emitted[k]);
-  out.words.clear();
-  out.words.reserve(emitted.size() + (size_t)S / 2);
-  out.overflow = false;
-  for (int q = 0; q < S; q += 2) {  // 64 states: at most 8 words per vector, so every count fits a byte
-    out.overflow |= lane[q].size() > 255 || lane[q + 1].size() > 255;
-    out.words.push_back((uint16_t)((lane[q].size() & 0xff) | (lane[q + 1].size() & 0xff) << 8));
-  }
-  for (int q = 0; q < S; ++q) out.words.insert(out.words.end(), lane[q].begin(), lane[q].end());
-}
-
 
   const void *src_;
   EncodeShape S_;
@@ -451,15 +472,26 @@ class HostBackend final : public EncodeBackend {
 // ---------------------------------------------------------------------------
 namespace {
 
+thread_local int64_t g_encodes = 0;  // full encodes of the current compress call
+
 struct Problem {
   EncodeShape S;
   EncodeBackend *be;
   std::vector<double> rms;
+  int64_t sample = kSampleVecs;
+  uint64_t seed = 0;
 };
 
 uint64_t metadata_bytes(const EncodeShape &S, int total_symbols) {
   return kHeaderBytes + align16(4 * kContexts + 2 * (uint64_t)total_symbols) + align16(4 * (uint64_t)S.R) +
          align16(4 * (uint64_t)(S.tiles + 1));
+}
+
+// the least a stream of this shape and geometry costs (every state coding
+// nothing), bits per element
+double floor_bpp(const EncodeShape &S) {
+  return (kStateMinBits * (double)((int64_t)S.states * S.tiles) + 8.0 * (double)metadata_bytes(S, kContexts)) /
+         ((double)S.R * (double)S.C);
 }
 
 std::vector<float> row_scales(const Problem &P, double a) {
@@ -469,11 +501,12 @@ std::vector<float> row_scales(const Problem &P, double a) {
 }
 
 // storage estimate (bits per element) at lattice scale a from the tables of
-// S vectors (S >= n_vec: the whole matrix, no entropy coding); infinite if a
-// coordinate leaves the value range
+// S vectors (S >= n_vec: the whole matrix, no entropy coding): the symbols'
+// information, 18.5 bits per state, the padding and the metadata; infinite
+// if a coordinate leaves the value range
 double estimate_bpp(const Problem &P, double a, int64_t S, std::string &err, int &status) {
   std::vector<uint64_t> hist;
-  const int rc = P.be->histogram(row_scales(P, a), S, hist, err);
+  const int rc = P.be->histogram(row_scales(P, a), S, P.seed, hist, err);
   if (rc < 0) status = rc;
   if (rc != 0) return INFINITY;
   Tables tb;
@@ -486,15 +519,15 @@ double estimate_bpp(const Problem &P, double a, int64_t S, std::string &err, int
     }
   const double scale = S >= P.S.n_vec ? 1.0 : (double)P.S.n_vec / (double)S;
   const double n_states = (double)((int64_t)P.S.states * P.S.tiles);
-  const double asymptotic = info * scale + kStateBits * n_states, least = kStateMinBits * n_states;
-  double bits = (asymptotic > least ? asymptotic : least) + 8.0 * (double)metadata_bytes(P.S, tb.total_symbols());
+  const double bits = info * scale + kStateBits * n_states + kTilePadBits * (double)P.S.tiles + kWordsPadBits +
+                      8.0 * (double)metadata_bytes(P.S, tb.total_symbols());
   return bits / ((double)P.S.R * (double)P.S.C);
 }
 
 // bisection on log2(a) over sampled estimates; returns the probed a whose
 // estimate is closest to the target
 double choose_scale(const Problem &P, double target, double *closest, std::string &err, int &status) {
-  const int64_t S = std::min(P.S.n_vec, kSampleVecs);
+  const int64_t S = std::min(P.S.n_vec, P.sample);
   const double la0 = 0.5 * std::log2(17.079468445347132) - target;  // high-rate guess sqrt(2 pi e) 2^-target
   double lo = la0 - 1.0, hi = la0 + 1.0;
   double best_la = la0, best_gap = INFINITY, best_e = INFINITY;
@@ -524,10 +557,11 @@ double choose_scale(const Problem &P, double target, double *closest, std::strin
 
 // the full stream at resolution a
 int encode_at(const Problem &P, double a, double target, Blob &blob, std::string &err) {
+  ++g_encodes;
   const EncodeShape &S = P.S;
   const std::vector<float> g = row_scales(P, a);
   std::vector<uint64_t> hist;
-  int rc = P.be->histogram(g, S.n_vec, hist, err);
+  int rc = P.be->histogram(g, S.n_vec, 0, hist, err);
   if (rc < 0) return rc;
   if (rc == 1) return EP_WARN_RAW;
   Tables tb;
@@ -535,16 +569,15 @@ int encode_at(const Problem &P, double a, double target, Blob &blob, std::string
   // failure, like values outside the stream's range (the sampled estimate may
   // have seen fewer symbols than the whole matrix holds)
   if (!build_tables(hist, tb)) return EP_WARN_RAW;
-  std::vector<uint32_t> states, tile_first;
-  rc = P.be->encode_tiles(g, tb, states, tile_first, err);
+  std::vector<uint32_t> tile_first;
+  rc = P.be->encode_tiles(g, tb, tile_first, err);
   if (rc < 0) return rc;
-  if (rc == 1) return EP_WARN_RAW;  // a count byte cannot hold a state's words: an encoding failure
+  if (rc == 1) return EP_WARN_RAW;  // a count byte cannot hold a pair's words: an encoding failure
   const uint64_t n_words = tile_first.back();
   const int nsum = tb.total_symbols();
   const uint64_t o_tab = kHeaderBytes;
   const uint64_t o_sc = o_tab + align16(4 * kContexts + 2 * (uint64_t)nsum);
-  const uint64_t o_st = o_sc + align16(4 * (uint64_t)S.R);
-  const uint64_t o_to = o_st + align16(4 * (uint64_t)S.tiles * (uint64_t)S.states);
+  const uint64_t o_to = o_sc + align16(4 * (uint64_t)S.R);
   const uint64_t o_w = o_to + align16(4 * (uint64_t)(S.tiles + 1));
   const uint64_t total = o_w + align16(2 * n_words);
   if (!blob.alloc(total)) {
@@ -561,7 +594,7 @@ int encode_at(const Problem &P, double a, double target, Blob &blob, std::string
   b[hdr::dtype] = (uint8_t)S.dtype;
   b[hdr::prob_bits] = kProbBits;
   b[hdr::contexts] = kContexts;
-  wr<uint32_t>(b + hdr::tile_vecs, kTileVecs);
+  wr<uint32_t>(b + hdr::tile_vecs, (uint32_t)S.tile_vecs);
   wr<uint32_t>(b + hdr::states, (uint32_t)S.states);
   wr<uint32_t>(b + hdr::tiles, (uint32_t)S.tiles);
   wr<uint64_t>(b + hdr::rows, (uint64_t)S.R);
@@ -571,7 +604,7 @@ int encode_at(const Problem &P, double a, double target, Blob &blob, std::string
   wr<double>(b + hdr::target, target);
   wr<uint64_t>(b + hdr::off_tables, o_tab);
   wr<uint64_t>(b + hdr::off_scales, o_sc);
-  wr<uint64_t>(b + hdr::off_states, o_st);
+  wr<uint64_t>(b + hdr::off_states, 0);
   wr<uint64_t>(b + hdr::off_tile_offsets, o_to);
   wr<uint64_t>(b + hdr::off_words, o_w);
   wr<uint64_t>(b + hdr::n_words, n_words);
@@ -586,7 +619,6 @@ int encode_at(const Problem &P, double a, double target, Blob &blob, std::string
     }
   }
   std::memcpy(b + o_sc, g.data(), 4 * (size_t)S.R);
-  std::memcpy(b + o_st, states.data(), 4 * states.size());
   std::memcpy(b + o_to, tile_first.data(), 4 * tile_first.size());
   return P.be->copy_words(reinterpret_cast<uint16_t *>(b + o_w), err);
 }
@@ -617,6 +649,8 @@ int raw_stream(const Problem &P, double target, Blob &blob, std::string &err) {
 
 }  // namespace
 
+int64_t last_encode_count() { return g_encodes; }
+
 bool make_shape(int dtype, int64_t rows, int64_t cols, EncodeShape &S, int &status, std::string &err) {
   if (dtype < 0 || dtype > 3) {
     err = "unknown container dtype";
@@ -625,6 +659,11 @@ bool make_shape(int dtype, int64_t rows, int64_t cols, EncodeShape &S, int &stat
   }
   if (rows <= 0 || cols <= 0) {
     err = "input must be a non-empty 2-D matrix";
+    status = EP_ERR_SHAPE;
+    return false;
+  }
+  if (rows >= (int64_t(1) << 31) || cols >= (int64_t(1) << 31)) {
+    err = "matrix too large for one stream";
     status = EP_ERR_SHAPE;
     return false;
   }
@@ -639,23 +678,45 @@ bool make_shape(int dtype, int64_t rows, int64_t cols, EncodeShape &S, int &stat
     status = EP_ERR_SHAPE;
     return false;
   }
-  S.tiles = (S.n_vec + kTileVecs - 1) / kTileVecs;
+  S.set_tiles(kStatesPerTile, S.n_vec < kSmallMatrixVecs ? kTileVecsSmall : kTileVecsLarge);
   return true;
 }
 
-int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, double fixed_a,
+int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, const EncodeOptions &opt,
                   Blob &blob, std::string &err) {
-  Problem P{shape, &be, {}};
-  const EncodeShape &S = P.S;
-  {
-    // 64 states per tile, or 16 when a target-selected stream's target lies
-    // below the overhead of 64 (40 bits per state plus the metadata)
-    const double floor64 =
-        (kStateMinBits * (double)(kStatesPerTile * S.tiles) + 8.0 * (double)metadata_bytes(S, kContexts)) /
-        ((double)S.R * (double)S.C);
-    P.S.states = (!(fixed_a > 0.0) && target < 1.1 * floor64) ? kStatesLow : kStatesPerTile;
-    be.set_states(P.S.states);
+  g_encodes = 0;
+  if ((opt.n_states != 0 && opt.n_states != kStatesLow && opt.n_states != kStatesPerTile) ||
+      (opt.tile_vecs != 0 && opt.tile_vecs != kTileVecsSmall && opt.tile_vecs != kTileVecsLarge) ||
+      opt.sample_vecs < 0 || !(opt.fixed_a >= 0.0) || std::isinf(opt.fixed_a)) {
+    err = "invalid ep_options";
+    return EP_ERR_ARG;
   }
+  Problem P{shape, &be, {}, opt.sample_vecs ? opt.sample_vecs : kSampleVecs, opt.seed};
+  EncodeShape &S = P.S;
+  const bool chosen = !(opt.fixed_a > 0.0);
+  // Tile geometry.  64 states per tile, or 16 when a target-selected
+  // stream's target is less than 4x the least a 64-state stream costs (64
+  // would spend over a quarter of the bits on their overhead).  64-state
+  // tiles hold 512 vectors in matrices of fewer than 2^22 vectors (twice the
+  // states decoding in parallel), else 1024; 16-state tiles hold 512, or
+  // 1024 when the target lies below 1.1x the least 512 allow.
+  const int tv64 = opt.tile_vecs ? opt.tile_vecs : (S.n_vec < kSmallMatrixVecs ? kTileVecsSmall : kTileVecsLarge);
+  int states = opt.n_states;
+  if (!states) {
+    S.set_tiles(kStatesPerTile, tv64);
+    states = (chosen && target < 4.0 * floor_bpp(S)) ? kStatesLow : kStatesPerTile;
+  }
+  int tile_vecs = opt.tile_vecs;
+  if (!tile_vecs) {
+    if (states == kStatesPerTile) {
+      tile_vecs = tv64;
+    } else {
+      S.set_tiles(kStatesLow, kTileVecsSmall);
+      tile_vecs = (chosen && target < 1.1 * floor_bpp(S)) ? kTileVecsLarge : kTileVecsSmall;
+    }
+  }
+  S.set_tiles(states, tile_vecs);
+  be.set_geometry(states, tile_vecs);
   // finiteness and row RMS (sequential sum per row)
   if (const int rc = be.row_rms(P.rms, err); rc != 0) return rc;
   const bool eight_bit = elem_bytes(S.dtype) == 1;
@@ -663,14 +724,11 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, do
     err = "target_bpp outside the supported range for this container";
     return EP_ERR_TARGET;
   }
-  double a = fixed_a;
-  double goal = target;  // the sampled estimate the last selection aimed at
-  if (!(fixed_a > 0.0)) {
-    const double floor_bpp =
-        (kStateMinBits * (double)((int64_t)S.states * S.tiles) + 8.0 * (double)metadata_bytes(S, kContexts)) /
-        ((double)S.R * (double)S.C);
-    if (target < 1.02 * floor_bpp) {
-      err = "target_bpp below this stream's fixed per-tile overhead (" + std::to_string(floor_bpp) + " bpp)";
+  double a = opt.fixed_a;
+  if (chosen) {
+    const double fl = floor_bpp(S);
+    if (target < 1.02 * fl) {
+      err = "target_bpp below this stream's fixed per-tile overhead (" + std::to_string(fl) + " bpp)";
       return EP_ERR_TARGET;
     }
     int status = 0;
@@ -694,8 +752,7 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, do
     if (std::isfinite(full) && !(std::fabs(full - target) <= 0.005 * target)) {
       double est = closest;
       for (int it = 0; it < 3; ++it) {
-        goal = target - (full - est);
-        a = choose_scale(P, goal, &est, err, status);
+        a = choose_scale(P, target - (full - est), &est, err, status);
         if (status < 0) return status;
         if (it == 2) break;
         full = estimate_bpp(P, a, S.n_vec, err, status);
@@ -704,42 +761,22 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, do
       }
     }
   }
+  // the one full encode
   int rc = encode_at(P, a, target, blob, err);
   if (rc < 0) return rc;
-  // The estimate's state part is exact only at its extremes: at low rates a
-  // state's cost steps by a whole word, so the encoded size can still miss the
-  // target.  Then the selection aims again, moved by the encoded size's miss,
-  // at most twice, and the stream closer to the target is kept.
-  if (rc == EP_OK && !(fixed_a > 0.0)) {
-    const double numel = (double)S.R * (double)S.C;
-    for (int it = 0; it < 2; ++it) {
-      const double actual = 8.0 * (double)blob.size() / numel;
-      if (std::fabs(actual - target) <= 0.01 * target) break;
-      double est;
-      int status = 0;
-      goal -= actual - target;
-      const double a2 = choose_scale(P, goal, &est, err, status);
-      if (status < 0) return status;
-      Blob b2;
-      const int rc2 = encode_at(P, a2, target, b2, err);
-      if (rc2 < 0) return rc2;
-      if (rc2 != EP_OK) break;
-      if (!(std::fabs(8.0 * (double)b2.size() / numel - target) < std::fabs(actual - target))) break;
-      blob.swap(b2);
-    }
-  }
   const uint64_t raw_total = kHeaderBytes + align16((uint64_t)S.R * (uint64_t)S.C * elem_bytes(S.dtype));
-  if (rc == EP_OK && !(fixed_a > 0.0) && blob.size() >= raw_total) rc = EP_WARN_RAW;
+  if (rc == EP_OK && chosen && blob.size() >= raw_total) rc = EP_WARN_RAW;
   if (rc == EP_WARN_RAW) {
     const int rr = raw_stream(P, target, blob, err);
     if (rr < 0) return rr;
-    err = "lattice coding failed (values out of range, a context beyond 2^10 symbols, or no gain); stored the raw container";
+    err = "lattice coding failed (values out of range, a context beyond 2^10 symbols, a pair's words beyond its "
+          "count byte, or no gain); stored the raw container";
   }
   return rc;
 }
 
-int compress(const void *src, int dtype, int64_t rows, int64_t cols, double target, double fixed_a, int threads,
-             Blob &blob, std::string &err) {
+int compress(const void *src, int dtype, int64_t rows, int64_t cols, double target, const EncodeOptions &opt,
+             int threads, Blob &blob, std::string &err) {
   EncodeShape S;
   int status = 0;
   if (!make_shape(dtype, rows, cols, S, status, err)) return status;
@@ -748,7 +785,7 @@ int compress(const void *src, int dtype, int64_t rows, int64_t cols, double targ
     return EP_ERR_ARG;
   }
   HostBackend be(src, S, threads > 0 ? threads : (int)std::max(1u, std::thread::hardware_concurrency()));
-  return compress_with(be, S, target, fixed_a, blob, err);
+  return compress_with(be, S, target, opt, blob, err);
 }
 
 }  // namespace ep

@@ -12,15 +12,18 @@
 //   * E8 nearest point per 8-vector (the same D8 / D8 + 1/2 rounding, parity
 //     fix and tie rule), then the 7-context model; counts in LDS, added to a
 //     global histogram;
-//   * one wave per tile, lane q = rANS state q, walking its vectors (16 with
-//     64 states per tile, 64 with 16) and their 8 coordinates backwards; each lane writes its words into a slot of its
-//     own, and a second kernel lays them out in the order the decoder
-//     consumes them, behind the count bytes.
+//   * one wave per tile, lane q = rANS state q, walking its vectors
+//     (tile_vecs / states of them) and their 8 coordinates backwards; each
+//     lane writes its words into a slot of its own, and a second kernel lays
+//     the tile out as the stream stores it: pair counts, length codes, the
+//     bit-packed start states, then each pair's region.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -197,10 +200,10 @@ __device__ __forceinline__ void bin_symbol(int b, int &c, int &sym) {
   }
 }
 
-// counts of (context, symbol) over vectors floor(k * n_vec / S), k < S
-// (S >= n_vec: every vector); hist is kContexts x kSymSpan u64
-__global__ void __launch_bounds__(256) histogram_kernel(Shape S, const float *g, int64_t nsamp, uint64_t *hist,
-                                                        uint32_t *overflow) {
+// counts of (context, symbol) over vectors sample_vid(n_vec, k, S, seed),
+// k < S (S >= n_vec: every vector); hist is kContexts x kSymSpan u64
+__global__ void __launch_bounds__(256) histogram_kernel(Shape S, const float *g, int64_t nsamp, uint64_t seed,
+                                                        uint64_t *hist, uint32_t *overflow) {
   __shared__ uint32_t bins[kLdsBins];
   for (int b = threadIdx.x; b < kLdsBins; b += blockDim.x) bins[b] = 0u;
   __syncthreads();
@@ -208,7 +211,7 @@ __global__ void __launch_bounds__(256) histogram_kernel(Shape S, const float *g,
   const int64_t n = all ? S.n_vec : nsamp;
   bool bad = false;
   for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t vid = all ? k : (int64_t)(((uint64_t)k * (uint64_t)S.n_vec) / (uint64_t)nsamp);
+    const int64_t vid = all ? k : sample_vid(S.n_vec, k, nsamp, seed);
     int32_t v[8], ctx[8], sym[8];
     if (!quantize_d(S, vid, g[vid / S.vpr], v)) {
       bad = true;
@@ -238,25 +241,25 @@ struct DevTables {
 };
 
 // words a state's slot holds: at most one per symbol, 8 per vector
-__host__ __device__ constexpr int words_per_state(int states) { return 8 * (kTileVecs / states); }
+__host__ __device__ constexpr int words_per_state(int states, int tile_vecs) { return 8 * (tile_vecs / states); }
 
 // One wave per tile, lane q = state q of ns: its vectors q, q + ns, ...
 // quantized again at the same scales, their symbols encoded backwards (last
-// vector first, coordinate 7 down to 0).  Words go to the lane's slot in
-// emission order; the count and the final state are kept.
-__global__ void __launch_bounds__(64) encode_tiles_kernel(Shape S, int ns, const float *g, DevTables T,
+// vector first, coordinate 7 down to 0) from x = 2^11.  Words go to the
+// lane's slot in emission order; the count and the final state are kept.
+__global__ void __launch_bounds__(64) encode_tiles_kernel(Shape S, int ns, int tv, const float *g, DevTables T,
                                                           const uint32_t *fc, uint16_t *slots, uint16_t *counts,
                                                           uint32_t *states, uint32_t *fault) {
   const int64_t tile = blockIdx.x;
   const int q = threadIdx.x;
-  const int64_t first = tile * kTileVecs;
-  const int n = (int)min((int64_t)kTileVecs, S.n_vec - first);
-  const int wps = words_per_state(ns);
+  const int64_t first = tile * tv;
+  const int n = (int)min((int64_t)tv, S.n_vec - first);
+  const int wps = words_per_state(ns, tv);
   uint16_t *slot = slots + ((size_t)tile * ns + q) * wps;
   uint32_t x = kStateLow;
   int emitted = 0;
   bool bad = false;
-  for (int s = kTileVecs / ns - 1; s >= 0; --s) {
+  for (int s = tv / ns - 1; s >= 0; --s) {
     const int i = s * ns + q;
     if (i >= n) continue;
     const int64_t vid = first + i;
@@ -276,7 +279,7 @@ __global__ void __launch_bounds__(64) encode_tiles_kernel(Shape S, int ns, const
         bad = true;
         continue;
       }
-      if ((uint64_t)x >= ((uint64_t)f << (29 - kProbBits))) {
+      if ((uint64_t)x >= ((uint64_t)f << (kStateTop - kProbBits))) {
         if (emitted < wps) slot[emitted] = (uint16_t)x;
         ++emitted;
         x >>= 16;
@@ -299,21 +302,51 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t v, int lane) {
   return v;
 }
 
-// One wave per tile, lane q = state q of ns: the ns / 2 count words (state
-// 2w in the low byte, 2w + 1 in the high; every count fits a byte, which the
-// host checked), then each state's words in the order the decoder consumes
-// them (the reverse of emission), at the tile's first word.
-__global__ void __launch_bounds__(64) lay_out_kernel(int ns, const uint16_t *slots, const uint16_t *counts,
-                                                     const uint32_t *tile_first, uint16_t *words) {
+// One wave per tile, lane q = state q of ns (lanes past ns hold nothing):
+// the tile at its first word as the stream stores it.  The pair counts fit a
+// byte each (the host checked).  The start bits are OR-ed together in LDS
+// (a state's bits straddle at most two dwords), then written out as words.
+__global__ void __launch_bounds__(64) lay_out_kernel(int ns, int tv, const uint16_t *slots, const uint16_t *counts,
+                                                     const uint32_t *states, const uint32_t *tile_first,
+                                                     uint16_t *words) {
+  __shared__ uint32_t bitbuf[kStatesPerTile];  // 64 states x at most 26 bits < 64 dwords
   const int64_t tile = blockIdx.x;
   const int q = threadIdx.x;
-  const uint32_t cnt = counts[tile * ns + q];
-  const uint32_t before = wave_scan(cnt, q) - cnt;
+  const bool mine = q < ns;
+  const uint32_t cnt = mine ? counts[tile * ns + q] : 0u;
+  const uint32_t x = mine ? states[tile * ns + q] : 0u;
+  const uint32_t nb = mine ? 31u - (uint32_t)__builtin_clz(x) : 0u;  // bits below the leading one: W - 1
+  const uint32_t words_before = wave_scan(cnt, q) - cnt;
+  const uint32_t bits_incl = wave_scan(nb, q), bits_before = bits_incl - nb;
+  const uint32_t total_bits = __shfl(bits_incl, 63, 64);
   uint16_t *w = words + tile_first[tile];
-  if (q < ns / 2) w[q] = (uint16_t)(counts[tile * ns + 2 * q] | counts[tile * ns + 2 * q + 1] << 8);
-  const uint16_t *slot = slots + ((size_t)tile * ns + q) * words_per_state(ns);
-  uint16_t *mine = w + ns / 2 + before;
-  for (uint32_t k = 0; k < cnt; ++k) mine[k] = slot[cnt - 1u - k];
+  // pair counts (two pairs to a word) and length codes (four to a word)
+  const uint32_t c1 = __shfl_down(cnt, 1, 64), c2 = __shfl_down(cnt, 2, 64), c3 = __shfl_down(cnt, 3, 64);
+  const uint32_t n1 = __shfl_down(nb, 1, 64), n2 = __shfl_down(nb, 2, 64), n3 = __shfl_down(nb, 3, 64);
+  if (mine && (q & 3) == 0) {
+    w[q / 4] = (uint16_t)((cnt + c1) | (c2 + c3) << 8);
+    w[ns / 4 + q / 4] = (uint16_t)((nb - 11u) | (n1 - 11u) << 4 | (n2 - 11u) << 8 | (n3 - 11u) << 12);
+  }
+  bitbuf[q] = 0u;
+  __syncthreads();
+  if (mine) {
+    const uint64_t v = (uint64_t)(x & ((1u << nb) - 1u)) << (bits_before & 31u);
+    atomicOr(&bitbuf[bits_before >> 5], (uint32_t)v);
+    if (v >> 32) atomicOr(&bitbuf[(bits_before >> 5) + 1u], (uint32_t)(v >> 32));
+  }
+  __syncthreads();
+  const uint32_t nbw = (total_bits + 15u) / 16u;
+  for (uint32_t k = (uint32_t)q; k < nbw; k += 64u) w[ns / 2 + k] = (uint16_t)(bitbuf[k / 2] >> (16u * (k & 1u)));
+  // regions: state 2k's words in consumption order (the reverse of emission),
+  // then state 2k+1's in emission order
+  if (mine) {
+    const uint16_t *slot = slots + ((size_t)tile * ns + q) * words_per_state(ns, tv);
+    uint16_t *mine_w = w + ns / 2 + nbw + words_before;
+    if ((q & 1) == 0)
+      for (uint32_t k = 0; k < cnt; ++k) mine_w[k] = slot[cnt - 1u - k];
+    else
+      for (uint32_t k = 0; k < cnt; ++k) mine_w[k] = slot[k];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -340,15 +373,24 @@ struct PinnedBuf {
   }
 };
 
+// A device buffer: from hipMalloc (grown on demand, freed with the
+// backend), or a fixed piece of the no-alloc scratch array (never grown).
 template <class T>
 struct DevBuf {
   T *p = nullptr;
   size_t n = 0;
+  bool owned = true;
   ~DevBuf() {
-    if (p) (void)hipFree(p);
+    if (p && owned) (void)hipFree(p);
+  }
+  void attach(T *q, size_t count) {
+    p = q;
+    n = count;
+    owned = false;
   }
   bool reserve(size_t count) {
     if (count <= n && p) return true;
+    if (!owned) return false;  // a scratch piece is sized for the largest use up front
     if (p) (void)hipFree(p);
     p = nullptr;
     n = 0;
@@ -361,10 +403,42 @@ struct DevBuf {
   }
 };
 
+// Carves 256-byte aligned pieces off a device region, front to back.
+struct Arena {
+  uint8_t *base = nullptr;
+  size_t cap = 0, used = 0;
+  template <class T>
+  bool take(DevBuf<T> &b, size_t count) {
+    const size_t start = (used + 255) & ~size_t(255), bytes = sizeof(T) * (count ? count : 1);
+    if (start > cap || bytes > cap - start) return false;
+    b.attach(reinterpret_cast<T *>(base + start), count);
+    used = start + bytes;
+    return true;
+  }
+};
+
 class GpuBackend final : public EncodeBackend {
  public:
   GpuBackend(const void *dev_src, const EncodeShape &S, hipStream_t stream) : es_(S), stream_(stream) {
     S_ = Shape{dev_src, S.dtype, S.R, S.C, S.C8, S.vpr, S.n_vec, S.tiles};
+  }
+
+  // Every buffer from `arena`, at the most any geometry of this shape needs
+  // (tiles of 512 vectors with 64 states); false if the arena is too small.
+  bool use_arena(Arena &arena) {
+    const size_t tiles = (size_t)((es_.n_vec + kTileVecsSmall - 1) / kTileVecsSmall);
+    const size_t states = tiles * kStatesPerTile;
+    // one word slot per symbol of every whole tile: 8 tile_vecs words per
+    // tile, which whole 1024-vector tiles bound for either tile size
+    const size_t slot_words = (size_t)((es_.n_vec + kTileVecsLarge - 1) / kTileVecsLarge) * 8 * kTileVecsLarge;
+    // a tile's words: its states' words plus pair counts, codes and start bits
+    const size_t words = slot_words + tiles * (kStatesPerTile / 2 + (kStatesPerTile * 26 + 15) / 16);
+    host_copies_ = true;
+    return arena.take(sums_, (size_t)es_.R) && arena.take(g_, (size_t)es_.R) &&
+           arena.take(hist_, (size_t)kContexts * kSymSpan) && arena.take(flag_, 1) &&
+           arena.take(fc_, (size_t)kContexts * kSymSpan) && arena.take(slots_, slot_words) &&
+           arena.take(counts_, states) && arena.take(dstates_, states) && arena.take(first_, tiles + 1) &&
+           arena.take(words_, words);
   }
 
   int row_rms(std::vector<double> &rms, std::string &err) override {
@@ -387,7 +461,8 @@ class GpuBackend final : public EncodeBackend {
     return 0;
   }
 
-  int histogram(const std::vector<float> &g, int64_t nsamp, std::vector<uint64_t> &hist, std::string &err) override {
+  int histogram(const std::vector<float> &g, int64_t nsamp, uint64_t seed, std::vector<uint64_t> &hist,
+                std::string &err) override {
     if (const int rc = upload_scales(g, err); rc != 0) return rc;
     if (!hist_.reserve((size_t)kContexts * kSymSpan) || !flag_.reserve(1)) return nomem(err);
     if (hipMemsetAsync(hist_.p, 0, 8 * hist_.n, stream_) != hipSuccess ||
@@ -395,23 +470,35 @@ class GpuBackend final : public EncodeBackend {
       return device(err, "hipMemsetAsync");
     const int64_t n = nsamp >= es_.n_vec ? es_.n_vec : nsamp;
     const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4096));
-    hipLaunchKernelGGL(histogram_kernel, dim3(blocks), dim3(256), 0, stream_, S_, g_.p, nsamp, hist_.p, flag_.p);
+    hipLaunchKernelGGL(histogram_kernel, dim3(blocks), dim3(256), 0, stream_, S_, g_.p, nsamp, seed, hist_.p,
+                       flag_.p);
     if (hipGetLastError() != hipSuccess) return device(err, "histogram launch");
-    // through pinned host memory: each rate probe copies the whole histogram
+    // through pinned host memory (each rate probe copies the whole
+    // histogram), or straight into pageable memory where nothing may be
+    // allocated on the device side
     const size_t nh = (size_t)kContexts * kSymSpan;
-    if (!pin_.reserve(8 * nh + 8)) return nomem(err);
-    uint64_t *ph = static_cast<uint64_t *>(pin_.p);
-    uint32_t *pf = reinterpret_cast<uint32_t *>(ph + nh);
+    uint64_t *ph;
+    uint32_t *pf;
+    if (host_copies_) {
+      hist.resize(nh);
+      ph = hist.data();
+      pf = &flag_host_;
+    } else {
+      if (!pin_.reserve(8 * nh + 8)) return nomem(err);
+      ph = static_cast<uint64_t *>(pin_.p);
+      pf = reinterpret_cast<uint32_t *>(ph + nh);
+    }
     if (hipMemcpyAsync(ph, hist_.p, 8 * nh, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
         hipMemcpyAsync(pf, flag_.p, 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
         hipStreamSynchronize(stream_) != hipSuccess)
       return device(err, "histogram");
+    if (host_copies_) return *pf ? 1 : 0;
     hist.assign(ph, ph + nh);
     return *pf ? 1 : 0;
   }
 
-  int encode_tiles(const std::vector<float> &g, const Tables &tb, std::vector<uint32_t> &states,
-                   std::vector<uint32_t> &tile_first, std::string &err) override {
+  int encode_tiles(const std::vector<float> &g, const Tables &tb, std::vector<uint32_t> &tile_first,
+                   std::string &err) override {
     if (const int rc = upload_scales(g, err); rc != 0) return rc;
     // tables: frequency | cumulative << 16 per symbol, contexts one after another
     DevTables T{};
@@ -422,20 +509,20 @@ class GpuBackend final : public EncodeBackend {
       T.base[c] = (uint32_t)fc.size();
       for (int i = 0; i < tb.nsym[c]; ++i) fc.push_back(tb.freq[c][(size_t)i] | tb.cum[c][(size_t)i] << 16);
     }
-    const int sp = states_;  // states per tile
-    const size_t nt = (size_t)es_.tiles, ns = nt * (size_t)sp;
-    if (!fc_.reserve(fc.size()) || !slots_.reserve(ns * (size_t)words_per_state(sp)) || !counts_.reserve(ns) ||
+    const int sp = states_, tv = tile_vecs_;  // states and vectors per tile
+    const size_t nt = (size_t)((es_.n_vec + tv - 1) / tv), ns = nt * (size_t)sp;
+    if (!fc_.reserve(fc.size()) || !slots_.reserve(ns * (size_t)words_per_state(sp, tv)) || !counts_.reserve(ns) ||
         !dstates_.reserve(ns) || !first_.reserve(nt + 1) || !flag_.reserve(1))
       return nomem(err);
     if (hipMemcpyAsync(fc_.p, fc.data(), 4 * fc.size(), hipMemcpyHostToDevice, stream_) != hipSuccess ||
         hipMemsetAsync(flag_.p, 0, sizeof(uint32_t), stream_) != hipSuccess)
       return device(err, "table upload");
-    hipLaunchKernelGGL(encode_tiles_kernel, dim3((unsigned)nt), dim3(sp), 0, stream_, S_, sp, g_.p, T, fc_.p,
+    hipLaunchKernelGGL(encode_tiles_kernel, dim3((unsigned)nt), dim3(sp), 0, stream_, S_, sp, tv, g_.p, T, fc_.p,
                        slots_.p, counts_.p, dstates_.p, flag_.p);
     if (hipGetLastError() != hipSuccess) return device(err, "tile encode launch");
     std::vector<uint16_t> counts(ns);
+    std::vector<uint32_t> states(ns);
     uint32_t fault = 0;
-    states.resize(ns);
     if (hipMemcpyAsync(counts.data(), counts_.p, 2 * ns, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
         hipMemcpyAsync(states.data(), dstates_.p, 4 * ns, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
         hipMemcpyAsync(&fault, flag_.p, 4, hipMemcpyDeviceToHost, stream_) != hipSuccess ||
@@ -445,27 +532,32 @@ class GpuBackend final : public EncodeBackend {
       err = "the tile encoder met a symbol outside the tables";
       return EP_ERR_DEVICE;
     }
-    // each tile's first word: the count words plus its states' words
+    // each tile's first word: pair counts and length codes, the start bits
+    // on whole words, the states' words
     tile_first.resize(nt + 1);
     uint64_t w = 0;
+    bool overflow = false;
     for (size_t t = 0; t < nt; ++t) {
       tile_first[t] = (uint32_t)w;
-      w += (uint64_t)sp / 2;
+      uint64_t bits = 0;
       for (int q = 0; q < sp; ++q) {
-        if (counts[t * sp + q] > 255) return 1;  // a count byte cannot hold this state's words
+        bits += 31u - (uint32_t)__builtin_clz(states[t * sp + q]);
         w += counts[t * sp + q];
+        if (q & 1) overflow |= counts[t * sp + q - 1] + counts[t * sp + q] > 255;
       }
+      w += (uint64_t)sp / 2 + (bits + 15) / 16;
       if (w > 0xffffffffull) {
         err = "stream too large for 32-bit tile offsets";
         return EP_ERR_SHAPE;
       }
     }
     tile_first[nt] = (uint32_t)w;
+    if (overflow) return 1;  // a count byte cannot hold a pair's words
     if (!words_.reserve((size_t)w)) return nomem(err);
     if (hipMemcpyAsync(first_.p, tile_first.data(), 4 * (nt + 1), hipMemcpyHostToDevice, stream_) != hipSuccess)
       return device(err, "tile offsets upload");
-    hipLaunchKernelGGL(lay_out_kernel, dim3((unsigned)nt), dim3(sp), 0, stream_, sp, slots_.p, counts_.p, first_.p,
-                       words_.p);
+    hipLaunchKernelGGL(lay_out_kernel, dim3((unsigned)nt), dim3(64), 0, stream_, sp, tv, slots_.p, counts_.p,
+                       dstates_.p, first_.p, words_.p);
     if (hipGetLastError() != hipSuccess) return device(err, "layout launch");
     n_words_ = (size_t)w;
     return 0;
@@ -513,12 +605,14 @@ class GpuBackend final : public EncodeBackend {
   DevBuf<uint16_t> counts_;
   PinnedBuf pin_;
   size_t n_words_ = 0;
+  bool host_copies_ = false;  // scratch mode: histograms go to pageable memory
+  uint32_t flag_host_ = 0;
 };
 
 }  // namespace
 
-int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target, double fixed_a,
-                    void *stream, Blob &blob, std::string &err) {
+int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target,
+                    const EncodeOptions &opt, void *stream, Blob &blob, std::string &err) {
   EncodeShape S;
   int status = 0;
   if (!make_shape(dtype, rows, cols, S, status, err)) return status;
@@ -527,7 +621,7 @@ int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, 
     return EP_ERR_ARG;
   }
   GpuBackend be(dev_src, S, reinterpret_cast<hipStream_t>(stream));
-  return compress_with(be, S, target, fixed_a, blob, err);
+  return compress_with(be, S, target, opt, blob, err);
 }
 
 }  // namespace ep

@@ -1,18 +1,27 @@
 // ep_stream.hpp -- byte layout of a lattice-rANS stream and its host-side reader.
 //
 // Layout (little-endian; every section starts on a 16-byte boundary):
-//   header   128 B   magic "EPK1", version, method, container dtype, prob_bits,
-//                    context count, tile_vecs, states per tile, tiles, rows,
-//                    cols, padded cols, lattice scale a, target bpp, section
-//                    offsets, word count, total bytes
+//   header   128 B   magic "EPK1", version 2, method, container dtype,
+//                    prob_bits, context count, tile_vecs, states per tile,
+//                    tiles, rows, cols, padded cols, lattice scale a, target
+//                    bpp, section offsets (the states-section field is 0),
+//                    word count, total bytes
 //   tables           7 x {int16 smin, uint16 nsym} then every context's
 //                    uint16 frequencies back to back
 //   scales           float32 g_r per row
-//   states           uint32 initial decoder state per (tile, state)
 //   tile offsets     uint32 word index of each tile's first word, plus the end
-//   words            uint16 words, tile after tile: states / 2 words of count
-//                    bytes (byte q = number of words state q consumes), then each
-//                    state's words in consumption order, states ascending
+//   words            uint16 words, tile after tile.  A tile of S states:
+//                      S/4 words of pair counts (byte k: words in the region
+//                        of states 2k and 2k+1),
+//                      S/4 words of length codes (nibble q, least significant
+//                        first: W - 12, W the bit length of state q's start
+//                        state, which lies in [2^11, 2^27)),
+//                      the start states' bits below their leading one,
+//                        states ascending, least significant bit first, on
+//                        whole words,
+//                      region k: state 2k's words in the order it consumes
+//                        them, then state 2k+1's in reverse order (it reads
+//                        its region from the end)
 // A raw stream (method 1) is the header followed by the container bytes.
 #pragma once
 
@@ -24,25 +33,27 @@
 namespace ep {
 
 constexpr uint32_t kMagic = 0x314B5045u;  // "EPK1"
-constexpr uint16_t kVersion = 1;
+constexpr uint16_t kVersion = 2;
 constexpr uint32_t kHeaderBytes = 128;
 constexpr int kContexts = 7;
 constexpr int kProbBits = 10;
 constexpr uint32_t kProbTotal = 1u << kProbBits;
-constexpr uint32_t kStateLow = 1u << 13;   // rANS states live in [2^13, 2^29)
-// stream bits per state beyond its symbols' information, as the rate
-// estimate counts them: the fixed final state L (13), the unused high bits of
-// the stored start state (11 on average) and the count byte (8)
-constexpr double kStateBits = 32.0;
-// A state absorbs up to 16 bits of information before it emits a word, so it
-// never costs less than its stored 32 bits and count byte: the estimate's
-// state part is max(40 * states, information + 32 * states).
-constexpr double kStateMinBits = 40.0;
-constexpr int kTileVecs = 1024;            // E8 vectors (8 coordinates) per tile
-constexpr int kStatesPerTile = 64;         // interleaved rANS states per tile (2 count bytes per word)
-// states per tile when the target lies below the overhead of kStatesPerTile
-// (the stream's header says which); a tile starts with states / 2 count words
-constexpr int kStatesLow = 16;
+constexpr uint32_t kStateLow = 1u << 11;  // rANS states live in [2^11, 2^27)
+constexpr int kStateTop = 27;             // the encoder emits a word while x >= f << (27 - kProbBits)
+// Stream bits a state costs beyond its symbols' information, as the rate
+// estimate counts them: half a pair-count byte and a length nibble (8), and
+// the start state stored at its bit length less the implied leading one
+// while it carries log2(x / 2^11) bits: 11 bits less the fractional part of
+// log2 x, on average 10.5.  A state that codes nothing costs 19.
+constexpr double kStateBits = 18.5;
+constexpr double kStateMinBits = 19.0;
+constexpr double kTilePadBits = 7.5;   // a tile's start bits end on a whole word (on average)
+constexpr double kWordsPadBits = 60.0; // the word section ends on 16 bytes (on average)
+constexpr int kStatesPerTile = 64;     // interleaved rANS states per tile
+constexpr int kStatesLow = 16;         // per tile for low targets (the header says which)
+constexpr int kTileVecsSmall = 512;    // E8 vectors (8 coordinates) per tile ...
+constexpr int kTileVecsLarge = 1024;   // ... or, for 16-state tiles at the lowest targets and large matrices, 1024
+constexpr int64_t kSmallMatrixVecs = int64_t(1) << 22;  // 64-state tiles of fewer vectors hold 512
 constexpr int kValueMin = -2048, kValueMax = 2047;  // lattice coordinates the stream can hold (12-bit field)
 
 enum Method : uint8_t { kLattice = 0, kRaw = 1 };
@@ -70,10 +81,10 @@ inline void wr(uint8_t *p, T v) {
 }
 
 struct StreamView {
-  int method = 0, dtype = 0, prob_bits = 0, states = 0;
+  int method = 0, dtype = 0, prob_bits = 0, states = 0, tile_vecs = 0;
   int64_t rows = 0, cols = 0, cols8 = 0, tiles = 0, n_vec = 0;
   double scale_a = 0, target = 0;
-  uint64_t off_tables = 0, off_scales = 0, off_states = 0, off_tile_offsets = 0, off_words = 0;
+  uint64_t off_tables = 0, off_scales = 0, off_tile_offsets = 0, off_words = 0;
   uint64_t n_words = 0, total = 0;
   int16_t smin[kContexts] = {};
   uint16_t nsym[kContexts] = {};
@@ -115,21 +126,23 @@ inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
   s.prob_bits = b[hdr::prob_bits];
   if (s.prob_bits != kProbBits || b[hdr::contexts] != kContexts) return "unsupported model parameters";
   s.states = (int)rd<uint32_t>(b + hdr::states);
-  if (rd<uint32_t>(b + hdr::tile_vecs) != kTileVecs || (s.states != kStatesPerTile && s.states != kStatesLow))
+  s.tile_vecs = (int)rd<uint32_t>(b + hdr::tile_vecs);
+  if ((s.tile_vecs != kTileVecsSmall && s.tile_vecs != kTileVecsLarge) ||
+      (s.states != kStatesPerTile && s.states != kStatesLow))
     return "unsupported tile geometry";
   s.cols8 = (int64_t)rd<uint64_t>(b + hdr::cols8);
   if (s.cols8 != (s.cols + 7) / 8 * 8) return "bad padded column count";
   s.n_vec = s.rows * (s.cols8 / 8);
   if (s.n_vec >= (int64_t(1) << 31)) return "stream too large";
   s.tiles = rd<uint32_t>(b + hdr::tiles);
-  if (s.tiles != (s.n_vec + kTileVecs - 1) / kTileVecs) return "bad tile count";
+  if (s.tiles != (s.n_vec + s.tile_vecs - 1) / s.tile_vecs) return "bad tile count";
   s.scale_a = rd<double>(b + hdr::scale_a);
   s.off_tables = rd<uint64_t>(b + hdr::off_tables);
   s.off_scales = rd<uint64_t>(b + hdr::off_scales);
-  s.off_states = rd<uint64_t>(b + hdr::off_states);
   s.off_tile_offsets = rd<uint64_t>(b + hdr::off_tile_offsets);
   s.off_words = rd<uint64_t>(b + hdr::off_words);
   s.n_words = rd<uint64_t>(b + hdr::n_words);
+  if (rd<uint64_t>(b + hdr::off_states) != 0) return "states section present";
   if (s.off_tables != kHeaderBytes || !inside(s.off_tables, 4 * kContexts, n)) return "bad table offset";
   uint64_t nsum = 0;
   for (int c = 0; c < kContexts; ++c) {
@@ -143,9 +156,8 @@ inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
   // sections in order, each inside the stream and 16-byte aligned, none
   // overlapping the one before it
   if (!inside(s.off_freq, 2 * nsum, n) || s.off_scales < s.off_freq + 2 * nsum || (s.off_scales & 15) ||
-      !inside(s.off_scales, 4 * (uint64_t)s.rows, n) || s.off_states < s.off_scales + 4 * (uint64_t)s.rows ||
-      (s.off_states & 15) || !inside(s.off_states, 4 * T * (uint64_t)s.states, n) ||
-      s.off_tile_offsets < s.off_states + 4 * T * (uint64_t)s.states || (s.off_tile_offsets & 15) ||
+      !inside(s.off_scales, 4 * (uint64_t)s.rows, n) ||
+      s.off_tile_offsets < s.off_scales + 4 * (uint64_t)s.rows || (s.off_tile_offsets & 15) ||
       !inside(s.off_tile_offsets, 4 * (T + 1), n) || s.off_words < s.off_tile_offsets + 4 * (T + 1) ||
       (s.off_words & 15) || s.n_words > n || !inside(s.off_words, 2 * s.n_words, n))
     return "section table out of bounds";

@@ -27,8 +27,9 @@ ERR_ARG, ERR_SHAPE, ERR_NONFINITE, ERR_TARGET, ERR_FORMAT, ERR_DEVICE, ERR_NOMEM
 _DTYPE_CODE = {torch.bfloat16: BF16, torch.float16: FP16, torch.float8_e4m3fn: FP8_E4M3FN, torch.int8: INT8}
 _CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
 
-EXPORTS = ["ep_compress", "ep_compress_ex", "ep_compress_device", "ep_free", "ep_decompress", "ep_decode_symbols", "ep_actual_bpp",
-           "ep_storage_nbytes", "ep_blob_info", "ep_last_error"]
+EXPORTS = ["ep_compress", "ep_compress_ex", "ep_compress_device", "ep_free",
+           "ep_decompress", "ep_decode_symbols", "ep_actual_bpp", "ep_storage_nbytes", "ep_blob_info", "ep_last_error",
+           "ep_last_encode_count"]
 
 
 class EPError(RuntimeError):
@@ -38,13 +39,21 @@ class EPError(RuntimeError):
 
 
 class _Options(ctypes.Structure):
-    _fields_ = [("fixed_scale", ctypes.c_double), ("n_threads", ctypes.c_int), ("reserved", ctypes.c_int * 6)]
+    _fields_ = [("fixed_scale", ctypes.c_double), ("n_threads", ctypes.c_int), ("n_states", ctypes.c_int),
+                ("tile_vecs", ctypes.c_int), ("sample_vecs", ctypes.c_int), ("seed", ctypes.c_uint64),
+                ("reserved", ctypes.c_int * 4)]
 
 
 class _Info(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("dtype", ctypes.c_int), ("method", ctypes.c_int),
-                ("n_states", ctypes.c_int), ("prob_bits", ctypes.c_int), ("n_tiles", ctypes.c_int64),
-                ("n_words", ctypes.c_int64), ("scale_a", ctypes.c_double), ("target_bpp", ctypes.c_double)]
+                ("n_states", ctypes.c_int), ("tile_vecs", ctypes.c_int), ("prob_bits", ctypes.c_int),
+                ("n_tiles", ctypes.c_int64), ("n_words", ctypes.c_int64), ("scale_a", ctypes.c_double),
+                ("target_bpp", ctypes.c_double)]
+
+
+def _options(fixed_scale=0.0, n_threads=0, n_states=0, tile_vecs=0, sample_vecs=0, seed=0) -> _Options:
+    return _Options(float(fixed_scale), int(n_threads), int(n_states), int(tile_vecs), int(sample_vecs), int(seed),
+                    (ctypes.c_int * 4)())
 
 
 _lib = None
@@ -78,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.ep_blob_info.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(_Info)]
         L.ep_last_error.argtypes = []
         L.ep_last_error.restype = ctypes.c_char_p
+        L.ep_last_encode_count.argtypes = []
+        L.ep_last_encode_count.restype = ctypes.c_int64
         _lib = L
     return _lib
 
@@ -130,14 +141,16 @@ def _host_ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def compress(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, n_threads: int = 0) -> Packed:
-    """ep_compress_ex on a 2-D CPU tensor (BF16, FP16, FP8-E4M3FN or INT8)."""
+def compress(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, n_threads: int = 0, n_states: int = 0,
+             tile_vecs: int = 0, sample_vecs: int = 0, seed: int = 0) -> Packed:
+    """ep_compress_ex on a 2-D CPU tensor (BF16, FP16, FP8-E4M3FN or INT8);
+    the keyword arguments are the ep_options fields."""
     if t.dtype not in _DTYPE_CODE:
         raise EPError(ERR_ARG, "compress", f"unsupported dtype {t.dtype}")
     if t.dim() != 2:
         raise EPError(ERR_SHAPE, "compress", "input must be 2-D")
     t = t.detach().to("cpu").contiguous()
-    opt = _Options(float(fixed_scale), int(n_threads), (ctypes.c_int * 6)())
+    opt = _options(fixed_scale, n_threads, n_states, tile_vecs, sample_vecs, seed)
     out = ctypes.POINTER(ctypes.c_uint8)()
     nb = ctypes.c_size_t(0)
     src = t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16)
@@ -148,7 +161,8 @@ def compress(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, n_thr
     return Packed(blob=_take_blob(out, nb.value), status=rc, shape=tuple(t.shape), dtype=t.dtype)
 
 
-def compress_device(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, stream=None) -> Packed:
+def compress_device(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, stream=None, n_states: int = 0,
+                    tile_vecs: int = 0, sample_vecs: int = 0, seed: int = 0) -> Packed:
     """ep_compress_device on a 2-D tensor in GPU memory: the same stream as
     compress() of the same values, with the passes over the matrix on the GPU
     (on `stream`, default: the current stream, synchronized on return)."""
@@ -161,7 +175,7 @@ def compress_device(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0
     t = t.detach().contiguous()
     if stream is None:
         stream = torch.cuda.current_stream(t.device)
-    opt = _Options(float(fixed_scale), 0, (ctypes.c_int * 6)())
+    opt = _options(fixed_scale, 0, n_states, tile_vecs, sample_vecs, seed)
     out = ctypes.POINTER(ctypes.c_uint8)()
     nb = ctypes.c_size_t(0)
     with torch.cuda.device(t.device):
@@ -170,6 +184,11 @@ def compress_device(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0
                                       ctypes.c_void_p(stream.cuda_stream), ctypes.byref(out), ctypes.byref(nb))
     _check(rc, "ep_compress_device")
     return Packed(blob=_take_blob(out, nb.value), status=rc, shape=tuple(t.shape), dtype=t.dtype)
+
+
+def last_encode_count() -> int:
+    """ep_last_encode_count: full encodes of the last compress on this thread."""
+    return int(lib().ep_last_encode_count())
 
 
 def actual_bpp(blob: np.ndarray) -> float:

@@ -20,8 +20,7 @@ WORKLOADS = {
     "t4outlier3072x12288_bf16_2.75": (3072, 12288, torch.bfloat16, 2.75, 1003),
     "absmax8192_int8_3.0": (8192, 8192, torch.int8, 3.0, 1004),
     "absmax8192_fp8_3.0": (8192, 8192, torch.float8_e4m3fn, 3.0, 1004),
-    # the 4096x4096 matrix at a rate below the overhead of 64 states per tile
-    # (its stream has 16)
+    # the 4096x4096 matrix at a low rate (its stream has 16 states per tile)
     "rowscale4096_bf16_0.2": (4096, 4096, torch.bfloat16, 0.2, 1002),
 }
 

@@ -49,12 +49,22 @@ enum ep_status {
   EP_ERR_NOMEM = -7       /* host (or, for ep_compress_device, device) allocation failed */
 };
 
-/* Optional knobs for ep_compress_ex.  Zero-initialize and set what you need;
- * zero fields take the defaults. */
+/* Optional knobs for ep_compress_ex and ep_compress_device.  Zero-initialize
+ * and set what you need; zero fields take the defaults.  Invalid values give
+ * EP_ERR_ARG. */
 struct ep_options {
   double fixed_scale;  /* > 0: use this lattice resolution a, skip rate selection */
   int n_threads;       /* host encoder threads; 0 = all hardware threads */
-  int reserved[6];     /* must be zero */
+  int n_states;        /* rANS states per tile: 0 = chosen (64, or 16 when the
+                          target is under 4x what 64 states cost at least),
+                          16 or 64 */
+  int tile_vecs;       /* E8 vectors per tile: 0 = chosen (64-state tiles: 512
+                          below 2^22 vectors, else 1024; 16-state tiles: 512,
+                          or 1024 for the lowest targets), 512 or 1024 */
+  int sample_vecs;     /* vectors in the rate estimate's stride sample; 0 = 65536 */
+  uint64_t seed;       /* phase of that sample: vector floor(k n / S) + seed mod
+                          floor(n / S) for sample point k */
+  int reserved[4];     /* must be zero */
 };
 
 /*
@@ -69,10 +79,13 @@ struct ep_options {
  * Returns EP_OK, EP_WARN_RAW (lattice coding could not meet the target: the
  * stream holds the raw container), or a negative error (nothing allocated).
  * Input rules (API reference, "compress"): non-empty 2-D, finite values.
- * Tiles carry 64 rANS states, or 16 when the target lies below the overhead
- * of 64 (40 bits per state plus metadata; ep_blob_info reports which); the
- * README's low targets need the smaller overhead, whose streams decode about
- * 3.7x slower.
+ * Rate selection runs on sampled storage estimates (plus one whole-matrix
+ * histogram that codes nothing) and the stream is entropy-coded exactly once
+ * (arXiv abstract: no repeated full-stream encoding).  Tiles carry 64 rANS
+ * states, or 16 for low targets (ep_options; ep_blob_info reports which);
+ * a state costs its symbols' information plus about 18.5 bits.  A pair of
+ * states whose words exceed a count byte (only 16-state tiles at high rates)
+ * is an encoding failure: EP_WARN_RAW.
  */
 int ep_compress(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
                 uint8_t **blob_out, size_t *nbytes_out);
@@ -93,8 +106,8 @@ int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, 
  *   hip_stream : hipStream_t the work runs on (NULL = default stream); it is
  *                synchronized before the call returns.
  *   blob_out, nbytes_out : as for ep_compress (host memory; ep_free).
- * Allocates device scratch with hipMalloc for the call (about 16 KB per tile
- * of 1024 vectors, plus the word section) and frees it before returning.
+ * Allocates device scratch with hipMalloc for the call (word slots of 2 bytes
+ * per element, the word section, histograms) and frees it before returning.
  * Returns as ep_compress; EP_ERR_DEVICE if a HIP call fails, EP_ERR_NOMEM if
  * a device allocation does.
  */
@@ -149,6 +162,7 @@ struct ep_info {
   int dtype;         /* container */
   int method;        /* 0 = lattice-rANS, 1 = raw */
   int n_states;      /* rANS states per tile */
+  int tile_vecs;     /* E8 vectors per tile */
   int prob_bits;     /* log2 of the frequency total */
   int64_t n_tiles;
   int64_t n_words;   /* 16-bit words in the entropy-coded section */
@@ -159,6 +173,11 @@ int ep_blob_info(const uint8_t *blob, size_t nbytes, struct ep_info *info);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char *ep_last_error(void);
+
+/* Full entropy-coding passes the last ep_compress* call on this thread ran:
+ * 1 for a lattice stream (rate selection reads sampled estimates and
+ * histograms, never an encoded stream), 0 when it stopped before encoding. */
+int64_t ep_last_encode_count(void);
 
 #ifdef __cplusplus
 }

@@ -161,10 +161,14 @@ def test_device_compress_argument_errors_before_any_device_work():
     # null outputs and non-zero reserved options
     rc = L.ep_compress_device(ctypes.c_void_p(0x1000), ep.BF16, 64, 512, 4.0, None, None, None, ctypes.byref(nb))
     assert rc == ep.ERR_ARG
-    opt = ep._Options(0.0, 0, (ctypes.c_int * 6)(0, 1, 0, 0, 0, 0))
-    rc = L.ep_compress_device(ctypes.c_void_p(0x1000), ep.BF16, 64, 512, 4.0, ctypes.byref(opt), None,
-                              ctypes.byref(out), ctypes.byref(nb))
-    assert rc == ep.ERR_ARG
+    bad_options = [ep._options(n_states=32), ep._options(tile_vecs=768), ep._options(sample_vecs=-1),
+                   ep._options(fixed_scale=float("inf"))]
+    reserved = ep._options()
+    reserved.reserved[1] = 1
+    for opt in bad_options + [reserved]:
+        rc = L.ep_compress_device(ctypes.c_void_p(0x1000), ep.BF16, 64, 512, 4.0, ctypes.byref(opt), None,
+                                  ctypes.byref(out), ctypes.byref(nb))
+        assert rc == ep.ERR_ARG
 
 
 @pytest.mark.parametrize("kind,targets", [
@@ -286,3 +290,31 @@ def test_malformed_headers_rejected_without_overreads():
         with pytest.raises(oracle.OracleError) as e:
             oracle.info(bad)
         assert e.value.rc == oracle.ERR_FORMAT, name
+
+
+@pytest.mark.parametrize("n_states,tile_vecs,target", [(64, 1024, 0.3), (64, 0, 0.45), (16, 0, 4.0), (64, 1024, 4.0), (16, 1024, 2.0),
+                                                       (0, 0, 0.3), (0, 0, 4.0)])
+def test_forced_geometry_matches_oracle(n_states, tile_vecs, target):
+    """ep_options.n_states / tile_vecs force the tile geometry (a 64-state
+    stream at a low target, a 16-state one at a high target); the host
+    encoder writes the oracle's stream and encodes it once."""
+    x = W.rowscale_gaussian(160, 2048, 31)
+    p = ep.compress(x, target, n_states=n_states, tile_vecs=tile_vecs)
+    assert ep.last_encode_count() == 1
+    blob, rc, _ = oracle.compress(x, target, n_states=n_states, tile_vecs=tile_vecs)
+    assert p.status == rc == 0
+    assert np.array_equal(p.blob, blob)
+    d = ep.blob_info(p.blob)
+    if n_states:
+        assert d["n_states"] == n_states
+    if tile_vecs:
+        assert d["tile_vecs"] == tile_vecs
+    assert abs(p.actual_bpp - target) <= 0.02 * target
+
+
+def test_sample_options_match_oracle():
+    x = W.rowscale_gaussian(96, 1024, 32)
+    for sv, seed in ((1000, 0), (1000, 9), (3000, 2)):
+        p = ep.compress(x, 3.0, sample_vecs=sv, seed=seed)
+        blob, rc, _ = oracle.compress(x, 3.0, sample_vecs=sv, seed=seed)
+        assert np.array_equal(p.blob, blob), (sv, seed)

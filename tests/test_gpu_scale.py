@@ -14,11 +14,11 @@ from cases import extreme_cases
 pytestmark = pytest.mark.gpu
 
 
-def _tile_elements(tile: int, rows: int, cols: int):
+def _tile_elements(tile: int, rows: int, cols: int, tile_vecs: int):
     """(row, column) slices of the elements tile `tile` reconstructs."""
     vpr = (cols + 7) // 8
     out = []
-    v0, v1 = tile * 1024, min((tile + 1) * 1024, rows * vpr)
+    v0, v1 = tile * tile_vecs, min((tile + 1) * tile_vecs, rows * vpr)
     vid = v0
     while vid < v1:
         r, k = divmod(vid, vpr)
@@ -29,9 +29,10 @@ def _tile_elements(tile: int, rows: int, cols: int):
 
 
 def test_large_stream_sampled_tiles():
-    """24576 x 24576 BF16 (604M parameters, 73,728 tiles: the multi-tile
-    kernel, 288 tiles per CU in 18 passes of 16 waves): the host encoder's
-    stream, decoded on the GPU, against the oracle's decode of 24 tiles."""
+    """24576 x 24576 BF16 (604M parameters, 73,728 tiles of 1024 vectors: the
+    multi-tile kernel, 288 tiles per CU in 18 passes of 16 waves): the host
+    encoder's stream, decoded on the GPU, against the oracle's decode of 24
+    tiles."""
     rows = cols = 24576
     x = W.rowscale_gaussian(rows, cols, seed=4242)
     p = ep.compress(x, 4.0)
@@ -39,14 +40,14 @@ def test_large_stream_sampled_tiles():
     y = ep.decompress(p.to("cuda"))
     torch.cuda.synchronize()
     got = y.cpu().view(torch.int16).numpy()
-    T = p.info()["n_tiles"]
+    T, TV = p.info()["n_tiles"], p.info()["tile_vecs"]
     rng = np.random.default_rng(7)
     tiles = sorted(set([0, 1, T // 2, T - 2, T - 1] + rng.integers(0, T, 19).tolist()))
     ref = np.zeros((rows, cols), np.uint16)
     work = np.zeros((rows, cols), np.int32)
     for t in tiles:
         oracle.decompress_tile_range(p.blob, t, t + 1, out=ref, work=work)
-        for r, cs in _tile_elements(t, rows, cols):
+        for r, cs in _tile_elements(t, rows, cols, TV):
             assert np.array_equal(got[r, cs].view(np.uint16), ref[r, cs]), (t, r)
 
 
@@ -183,17 +184,23 @@ def test_multitile_lds_limited_waves():
     assert np.array_equal(y.cpu().view(torch.int16).numpy().view(np.uint16), oracle.decompress_raw(blob).view(np.uint16))
 
 
-@pytest.mark.parametrize("rows,cols", [(512, 4096), (3072, 8192)], ids=["one_round", "multi_tile"])
-def test_corrupt_words_decode_within_bounds(rows, cols):
+@pytest.mark.parametrize("rows,cols,target", [(512, 4096, 4.0), (3072, 8192, 4.0), (512, 4096, 0.2),
+                                              (3072, 8192, 0.15), (256, 8192, 0.06)],
+                         ids=["one_round", "multi_tile", "one_round_16", "multi_tile_16", "16_states_1024"])
+def test_corrupt_words_decode_within_bounds(rows, cols, target):
     """The host checks a stream's header, tables and tile offsets but not its
-    words and count bytes (that would mean decoding it).  With the whole word
-    section overwritten by random bytes the decoder still completes: a lane's
-    word pointer starts at most at its tile's end and moves at most 128 words
-    on, inside the LDS padding, and table addresses are masked into the
-    tables.  Every decoded coordinate stays in the stream's value range, and
-    a clean decode right after is exact."""
+    words (that would mean decoding it).  With the whole word section
+    overwritten by random bytes (pair counts, length codes and start bits
+    included) the decoder still completes: a lane's word pointer starts
+    clamped into its tile and moves at most one word per symbol (8 per vector,
+    64 vectors per lane at most), inside the LDS slack after the buffers or
+    the tables before them; start-state reads stay within 300 bytes of the
+    tile; table addresses are masked into the tables.  Every decoded
+    coordinate stays in the stream's value range, and a clean decode right
+    after is exact.  64-state and 16-state tiles (512 and 1024 vectors) in
+    the single-round and the multi-tile kernel."""
     x = W.rowscale_gaussian(rows, cols, 8100)
-    blob, rc, _ = oracle.compress(x, 4.0)
+    blob, rc, _ = oracle.compress(x, target)
     assert rc == 0
     n_words = ep.blob_info(blob)["n_words"]
     o_w = blob.size - (2 * n_words + 15) // 16 * 16  # the word section ends the stream
@@ -213,6 +220,7 @@ def test_corrupt_words_decode_within_bounds(rows, cols):
 
 def _low_rate_cases():
     yield "bf16_one_round", W.rowscale_gaussian(512, 4096, 8200), 0.2
+    yield "bf16_1024_vector_tiles", W.rowscale_gaussian(256, 8192, 8206), 0.06
     yield "bf16_multi_tile", W.rowscale_gaussian(3072, 8192, 8201), 0.15
     yield "t4_bf16", W.t4_outliers(384, 6144, 8202, dtype=torch.bfloat16), 0.3
     yield "fp16_padded", W.rowscale_gaussian(300, 1000, 8203).to(torch.float16), 0.2
@@ -222,16 +230,44 @@ def _low_rate_cases():
 
 @pytest.mark.parametrize("case", list(_low_rate_cases()), ids=lambda c: c[0])
 def test_low_rate_16_state_streams(case):
-    """Targets below the overhead of 64 states per tile take 16 (40 bits per
-    state): a lane decodes 64 vectors, lanes 16-63 only follow along, and the
-    row scales are loaded per group of 16 steps.  Symbols and values equal
-    the oracle's in the single-round and the multi-tile kernel, for every
-    container."""
+    """Low targets take 16 states per tile: a wave decodes four tiles, one per
+    16-lane DPP row, each lane 32 vectors (64 for 1024-vector tiles at the
+    lowest targets) in groups of 8 whose row scales load during the group
+    before.  Symbols and values equal the oracle's in the single-round and the
+    multi-tile kernel, for every container."""
     _, x, target = case
     blob, rc, _ = oracle.compress(x, target)
     assert rc == 0 and oracle.info(blob)["n_states"] == 16
     assert abs(8 * blob.size / x.numel() - target) <= 0.02 * target
     p = ep.from_blob(blob).to("cuda")
+    v = ep.decode_symbols(p)
+    y = ep.decompress(p)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.cpu().numpy(), oracle.decode_symbols(blob))
+    got = y.cpu().view(torch.int16 if x.element_size() == 2 else torch.int8).numpy().view(np.uint8)
+    assert np.array_equal(got, oracle.decompress_raw(blob).view(np.uint8))
+
+
+@pytest.mark.parametrize("n_states,tile_vecs,target,kind", [(64, 1024, 0.3, "bf16"), (16, 512, 4.0, "bf16"),
+                                                            (16, 1024, 2.0, "fp16"), (64, 512, 0.45, "int8"),
+                                                            (16, 512, 3.0, "fp8")])
+def test_forced_geometry_streams(n_states, tile_vecs, target, kind):
+    """ep_options force the tile geometry: a 64-state stream at a low target
+    and a 16-state stream at a high one (and the other pairings) decode on
+    the GPU to the oracle's symbols and values; the host encoder's stream is
+    the oracle's byte for byte."""
+    if kind in ("int8", "fp8"):
+        x = W.absmax_codes(384, 2048, 8300 + n_states, kind)
+    else:
+        x = W.rowscale_gaussian(384, 2056, 8300 + n_states)
+        if kind == "fp16":
+            x = x.to(torch.float16)
+    p = ep.compress(x, target, n_states=n_states, tile_vecs=tile_vecs)
+    blob, rc, _ = oracle.compress(x, target, n_states=n_states, tile_vecs=tile_vecs)
+    assert p.status == rc == 0 and np.array_equal(p.blob, blob)
+    d = ep.blob_info(blob)
+    assert (d["n_states"], d["tile_vecs"]) == (n_states, tile_vecs)
+    p.to("cuda")
     v = ep.decode_symbols(p)
     y = ep.decompress(p)
     torch.cuda.synchronize()
