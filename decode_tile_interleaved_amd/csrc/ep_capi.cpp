@@ -93,6 +93,41 @@ int ep_compress_device(const void *dev_src, int dtype, int64_t rows, int64_t col
   });
 }
 
+int ep_compress_device_noalloc(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
+                               const struct ep_options *opt, void *hip_stream, uint8_t *out, size_t capacity,
+                               size_t *nbytes_out) {
+  ep::set_error("");
+  if (!out || !nbytes_out) {
+    ep::set_error("null output pointer");
+    return EP_ERR_ARG;
+  }
+  ep::EncodeOptions eo;
+  int threads = 0;
+  if (const int rc = read_options(opt, eo, threads); rc != 0) return rc;
+  ep::Blob blob(out, capacity);
+  std::string err;
+  int rc;
+  try {
+    rc = ep::compress_device_noalloc(dev_src, dtype, rows, cols, target_bpp, eo, hip_stream, blob, err);
+  } catch (const std::bad_alloc &) {
+    ep::set_error("host allocation failed");
+    return EP_ERR_NOMEM;
+  }
+  if (rc == EP_ERR_NOMEM && blob.wanted() > capacity) {
+    *nbytes_out = blob.wanted();
+    ep::set_error("output buffer of " + std::to_string(capacity) + " bytes is too small: the stream needs " +
+                  std::to_string(blob.wanted()));
+    return EP_ERR_ARG;
+  }
+  if (rc < 0) {
+    ep::set_error(err);
+    return rc;
+  }
+  *nbytes_out = blob.size();
+  if (rc > 0) ep::set_error(err);
+  return rc;
+}
+
 int ep_compress(const void *host_src, int dtype, int64_t rows, int64_t cols, double target_bpp, uint8_t **blob_out,
                 size_t *nbytes_out) {
   return ep_compress_ex(host_src, dtype, rows, cols, target_bpp, nullptr, blob_out, nbytes_out);

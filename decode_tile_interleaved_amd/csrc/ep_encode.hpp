@@ -180,6 +180,14 @@ int compress(const void *src, int dtype, int64_t rows, int64_t cols, double targ
 int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target,
                     const EncodeOptions &opt, void *stream, Blob &blob, std::string &err);
 
+// compress_device with every device buffer taken from one file-scope array
+// per GPU instead of hipMalloc, and no pinned host memory: for matrices of at
+// most kNoAllocMaxElements padded elements (rows x cols rounded up to 8);
+// larger ones give EP_ERR_SHAPE.  Calls on one GPU take turns (a lock per
+// device): the array is shared.
+constexpr int64_t kNoAllocMaxElements = int64_t(1) << 22;
+int compress_device_noalloc(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target,
+                            const EncodeOptions &opt, void *stream, Blob &blob, std::string &err);
 
 // Per-thread error text shared by the C ABI functions.
 void set_error(const std::string &msg);

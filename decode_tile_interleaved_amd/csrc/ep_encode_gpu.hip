@@ -609,6 +609,59 @@ class GpuBackend final : public EncodeBackend {
   uint32_t flag_host_ = 0;
 };
 
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing takes its device buffers from one
+// array per GPU.  Its size covers the largest shape allowed,
+// kNoAllocMaxElements padded elements (rows x cols rounded up to 8): at most
+// 2^19 rows (12 bytes each: sums and scales), 2^19 vectors in whole tiles
+// (16 bytes of word slots and as much of stream words each), 1024 tiles of 64 states (6 bytes
+// per state, 136 header words per tile, 4 bytes of offset), the histogram
+// and tables (12 bytes per context symbol), and the pieces' alignment.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchRows = (size_t)(kNoAllocMaxElements / 8);
+constexpr size_t kScratchVecs = (size_t)(kNoAllocMaxElements / 8);
+constexpr size_t kScratchTiles = kScratchVecs / kTileVecsSmall;
+constexpr size_t kScratchBytes = 12 * kScratchRows + 16 * kScratchVecs +
+                                 2 * (8 * kScratchVecs + kScratchTiles * (kStatesPerTile / 2 + (kStatesPerTile * 26 + 15) / 16)) +
+                                 6 * kScratchTiles * kStatesPerTile + 4 * (kScratchTiles + 1) +
+                                 12 * (size_t)kContexts * kSymSpan + 4 + 16 * 256;
+
+// The array (about 24 MB on each GPU the library runs on, held until the
+// process ends).  Host code never passes its name to a kernel: that is a
+// host-side stand-in, not a device address.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct DeviceScratch {
+  void *ptr = nullptr;  // the array's address on this device
+  std::mutex call;      // calls on this device take turns: they share the array
+};
+
+// The current device's array, its address looked up once per device with
+// that device current.  nullptr (with err) if the lookup fails.
+DeviceScratch *device_scratch(std::string &err) {
+  static std::mutex mu;
+  static std::vector<std::unique_ptr<DeviceScratch>> per_device;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    err = "hipGetDevice failed";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)per_device.size() <= dev) per_device.resize((size_t)dev + 1);
+  if (!per_device[(size_t)dev]) per_device[(size_t)dev] = std::make_unique<DeviceScratch>();
+  DeviceScratch &d = *per_device[(size_t)dev];
+  if (!d.ptr) {
+    void *p = nullptr;
+    const hipError_t rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (rc != hipSuccess || !p) {
+      err = std::string("hipGetSymbolAddress of the scratch array failed: ") + hipGetErrorString(rc);
+      return nullptr;
+    }
+    d.ptr = p;
+  }
+  return &d;
+}
+
 }  // namespace
 
 int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target,
@@ -621,6 +674,32 @@ int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, 
     return EP_ERR_ARG;
   }
   GpuBackend be(dev_src, S, reinterpret_cast<hipStream_t>(stream));
+  return compress_with(be, S, target, opt, blob, err);
+}
+
+int compress_device_noalloc(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target,
+                            const EncodeOptions &opt, void *stream, Blob &blob, std::string &err) {
+  EncodeShape S;
+  int status = 0;
+  if (!make_shape(dtype, rows, cols, S, status, err)) return status;
+  if (!dev_src) {
+    err = "null input";
+    return EP_ERR_ARG;
+  }
+  if (S.R * S.C8 > kNoAllocMaxElements) {
+    err = "matrix too large for the scratch array: at most " + std::to_string(kNoAllocMaxElements) +
+          " elements (rows x cols rounded up to 8)";
+    return EP_ERR_SHAPE;
+  }
+  DeviceScratch *ds = device_scratch(err);
+  if (!ds) return EP_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(ds->call);
+  Arena arena{static_cast<uint8_t *>(ds->ptr), kScratchBytes, 0};
+  GpuBackend be(dev_src, S, reinterpret_cast<hipStream_t>(stream));
+  if (!be.use_arena(arena)) {
+    err = "the scratch array cannot hold this shape's buffers";
+    return EP_ERR_SHAPE;
+  }
   return compress_with(be, S, target, opt, blob, err);
 }
 

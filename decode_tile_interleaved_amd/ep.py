@@ -27,7 +27,7 @@ ERR_ARG, ERR_SHAPE, ERR_NONFINITE, ERR_TARGET, ERR_FORMAT, ERR_DEVICE, ERR_NOMEM
 _DTYPE_CODE = {torch.bfloat16: BF16, torch.float16: FP16, torch.float8_e4m3fn: FP8_E4M3FN, torch.int8: INT8}
 _CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
 
-EXPORTS = ["ep_compress", "ep_compress_ex", "ep_compress_device", "ep_free",
+EXPORTS = ["ep_compress", "ep_compress_ex", "ep_compress_device", "ep_compress_device_noalloc", "ep_free",
            "ep_decompress", "ep_decode_symbols", "ep_actual_bpp", "ep_storage_nbytes", "ep_blob_info", "ep_last_error",
            "ep_last_encode_count"]
 
@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.ep_compress_device.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_double, ctypes.POINTER(_Options), ctypes.c_void_p,
                                          ctypes.POINTER(u8p), ctypes.POINTER(ctypes.c_size_t)]
+        L.ep_compress_device_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.c_double, ctypes.POINTER(_Options), ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
         L.ep_free.argtypes = [u8p]
         L.ep_free.restype = None
         L.ep_decompress.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,

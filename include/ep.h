@@ -114,6 +114,33 @@ int ep_compress_ex(const void *host_src, int dtype, int64_t rows, int64_t cols, 
 int ep_compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
                        const struct ep_options *opt, void *hip_stream, uint8_t **blob_out, size_t *nbytes_out);
 
+/*
+ * ep_compress_device_noalloc -- ep_compress_device for callers that cannot
+ * allocate memory (serving loops and harnesses that forbid hipMalloc): no
+ * hipMalloc, hipFree, pinned host memory or other device allocation.  Its
+ * device scratch (row sums, histograms, per-state word slots, the word
+ * section) is one file-scope array of about 24 MB on each GPU the library
+ * runs on, held until the process ends; the encoder's host-side tables use
+ * ordinary heap memory.  The stream is the one ep_compress_device returns,
+ * byte for byte, written to the caller's host buffer.
+ *   dev_src, dtype, rows, cols, target_bpp, opt, hip_stream : as for
+ *                ep_compress_device (the stream is synchronized before return).
+ *   out        : caller-owned host buffer of `capacity` bytes for the stream.
+ *                A stream whose resolution is chosen from the target never
+ *                exceeds 128 + the container bytes rounded up to 16, so that
+ *                capacity always suffices.
+ *   nbytes_out : receives the stream length (or, with EP_ERR_ARG for a
+ *                too-small buffer, the length it needs).
+ * Matrices of more than 2^22 elements (rows x cols rounded up to a multiple
+ * of 8) give EP_ERR_SHAPE.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents (the histograms and flags are cleared
+ * before each use); overlapping calls would race on it, so the library makes
+ * calls on one GPU take turns (a lock per device).
+ */
+int ep_compress_device_noalloc(const void *dev_src, int dtype, int64_t rows, int64_t cols, double target_bpp,
+                               const struct ep_options *opt, void *hip_stream, uint8_t *out, size_t capacity,
+                               size_t *nbytes_out);
+
 /* Release a stream returned by ep_compress / ep_compress_ex / ep_compress_device.
  * NULL is a no-op. */
 void ep_free(uint8_t *blob);
