@@ -105,24 +105,28 @@ constexpr int kOutSym = 4;         // int16 lattice coordinates; 0..3 are the co
 static_assert(kProbBits == 10, "table addressing below assumes 2^10 slots per context");
 static_assert(kStateLow == (1u << 11) && kStateTop == 27, "X = 8x must fit 32 bits and refill below 8 L");
 
-// Kernel arguments.  The fields the first global loads need come first, so
-// that they arrive with the first batch of scalar loads.
+// Kernel arguments: section pointers computed on the host (the word
+// section is 16-byte aligned), then the fields the first loads need, all in
+// the first 80 bytes so that one round of scalar loads brings them.
 struct Args {
-  const uint8_t *blob;
-  uint64_t off_freq, off_tile_offsets, off_scales, off_words;
-  uint32_t nsym[kContexts];
-  uint32_t fidx[kContexts];
+  const uint16_t *freq;   // frequency section
+  const uint32_t *toff;   // tile offsets: first word of each tile, then the word count
+  const uint8_t *words;   // word section
+  const float *scales;    // row scales
+  uint32_t waves, n_units, n_tiles, words_off;  // units: groups of 64 / states consecutive tiles, one per wave
+  uint32_t ctx_freq[kContexts];  // context c: index of its first frequency | symbol count << 16
   uint32_t nzbase[kContexts];
   int32_t smin[kContexts];
   void *out;
   uint64_t cols;                  // columns of the output (padded layouts only)
   uint32_t rows, vpr;             // rows; vectors per row
   uint32_t row_magic, row_shift;  // vec / vpr = umulhi(vec, row_magic) >> row_shift  (vpr > 1)
-  uint32_t n_vec, n_tiles, n_units, waves;  // units: groups of 64 / states consecutive tiles, one per wave
-  uint32_t rec_off, mark_off, words_off;  // LDS byte offsets
+  uint32_t n_vec;
+  uint32_t rec_off, mark_off, desc_off;  // LDS byte offsets
   uint32_t wg_q, wg_rem;  // multi-tile kernel: workgroup b decodes wg_q units, one more if b < wg_rem
   uint32_t wbuf;          // multi-tile kernel: bytes of each wave's word buffer
 };
+static_assert(offsetof(Args, ctx_freq) + sizeof(uint32_t) * kContexts <= 80, "early fields in the first 80 bytes");
 
 typedef __attribute__((address_space(1))) void *gptr_t;
 typedef __attribute__((address_space(3))) void *lptr_t;
@@ -378,7 +382,7 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t dst, uint32_t
 
 // the row scale of vector vec (the last row's for vectors past the end)
 __device__ __forceinline__ float row_scale(const Args &A, uint32_t vec) {
-  const float *scales = reinterpret_cast<const float *>(A.blob + A.off_scales);
+  const float *scales = A.scales;
   const uint32_t last = A.rows - 1u, one = A.vpr == 1u ? 0xffffffffu : 0u;
   const uint32_t r = ((__umulhi(vec, A.row_magic) >> A.row_shift) & ~one) | (vec & one);
   return scales[r < last ? r : last];
@@ -413,19 +417,26 @@ __device__ __forceinline__ void group_scales(const Args &A, const UnitLane &u, u
   for (uint32_t s = 0; s < 8; ++s) gs[s] = row_scale(A, u.tile * kTv + (8u * g + s) * NS + u.q);
 }
 
-// Decodes a wave's unit.  wt, we: LDS byte addresses of the first word of
-// the lane's tile and of its end; gs: the row scales of the lane's first 8
-// vectors.  The lane reads its start state (length nibble, bit offset by a
-// prefix sum over its tile's states, three 16-bit reads) and its first word
-// (pair counts' prefix sum; odd states start at their region's end and read
-// backwards), then decodes V vectors in groups of 8, each group's row scales
-// loaded during the group before.  PARTIAL: some lane's tile holds fewer
-// vectors than a full one (the stream's last unit).
-template <int OUT, bool WIDE, bool PADDED, bool PARTIAL, bool BOP3, int NS, int V>
-__device__ __forceinline__ void decode_unit(const Args &A, const UnitLane &u, uint32_t wt, uint32_t we,
-                                            const float (&gs0)[8], uint32_t lane) {
-  static_assert((NS == 64 && (V == 8 || V == 16)) || (NS == 16 && (V == 32 || V == 64)), "tile geometry");
-  constexpr uint32_t kNs = (uint32_t)NS, kTv = (uint32_t)(NS * V), kGroups = (uint32_t)V / 8u;
+// wave priority (s_setprio): the SIMD's arbiter issues from higher-priority
+// waves first
+template <uint32_t P>
+__device__ __forceinline__ void set_priority() {
+  __builtin_amdgcn_s_setprio((int16_t)P);
+}
+
+// A lane's start: its state (as X = 8x) and its word pointer, with the first
+// word read.  wt, we: LDS byte addresses of the first word of the lane's
+// tile and of its end.  The lane reads its start state (length nibble, bit
+// offset by a prefix sum over its tile's states, three 16-bit reads) and its
+// first word (pair counts' prefix sum; odd states start at their region's
+// end and read backwards).  Reads the tile's words only, not the tables.
+struct Start {
+  uint32_t X;
+  Lane L;
+};
+template <int NS>
+__device__ __forceinline__ Start parse_start(const UnitLane &u, uint32_t wt, uint32_t we, uint32_t lane) {
+  constexpr uint32_t kNs = (uint32_t)NS;
   const uint32_t q = u.q;
   // ---- start state: W - 1 bits after the bits of the states before it
   const uint32_t nb = ((lds_u8(wt + kNs / 2u + (q >> 1)) >> ((q & 1u) << 2)) & 15u) + 11u;
@@ -442,13 +453,27 @@ __device__ __forceinline__ void decode_unit(const Args &A, const UnitLane &u, ui
   const uint32_t region = wt + kNs + (((btotal + 15u) >> 4) << 1);
   uint32_t p = (q & 1u) ? region + 2u * pincl - 2u : region + 2u * (pincl - pc);
   p = p < wt ? wt : (p > we ? we : p);  // a corrupt tile's pointers stay inside it
-  Lane L;
-  L.dp = (q & 1u) ? 0xfffffffeu : 2u;
-  L.p = p;
-  L.r = lds_u16(p);
-  const uint32_t X = x << 3;
-  table_read<0u>(X & 0x1ff8u, L.d0, L.d1);  // context F
-  L.q = X >> 13;
+  Start S;
+  S.L.dp = (q & 1u) ? 0xfffffffeu : 2u;
+  S.L.p = p;
+  S.L.r = lds_u16(p);
+  S.X = x << 3;
+  return S;
+}
+
+// Decodes a wave's unit from its lanes' starts: V vectors per lane in groups
+// of 8, each group's row scales loaded during the group before (gs0: the
+// first group's).  PARTIAL: some lane's tile holds fewer vectors than a full
+// one (the stream's last unit).
+template <int OUT, bool WIDE, bool PADDED, bool PARTIAL, bool BOP3, int NS, int V>
+__device__ __forceinline__ void decode_unit(const Args &A, const UnitLane &u, const Start &S0, const float (&gs0)[8],
+                                            uint32_t lane) {
+  static_assert((NS == 64 && (V == 8 || V == 16)) || (NS == 16 && (V == 32 || V == 64)), "tile geometry");
+  constexpr uint32_t kNs = (uint32_t)NS, kTv = (uint32_t)(NS * V), kGroups = (uint32_t)V / 8u;
+  const uint32_t q = u.q;
+  Lane L = S0.L;
+  table_read<0u>(S0.X & 0x1ff8u, L.d0, L.d1);  // context F
+  L.q = S0.X >> 13;
   constexpr uint32_t kC = kCtxBytes, kE = 3u * kCtxBytes;  // LDS bases of C_0 and E_{0,0}
   constexpr uint32_t kBitB = WIDE ? 16u : 24u;  // where bit 0 of v sits in d0
   constexpr uint32_t kVecBytes = (OUT == EP_FP8_E4M3FN || OUT == EP_INT8) ? 8u : 16u;
@@ -497,70 +522,104 @@ __device__ __forceinline__ void decode_unit(const Args &A, const UnitLane &u, ui
   }
 }
 
-// The table build: waves 0..k-1 take contexts wave, wave + k, ...: prefix
-// sums of the frequencies, the used symbols' records, a bitmap of the slots
-// where a symbol starts, then the context's 16 table rows of 64 slots.  fpre
-// holds the first 256 frequencies of context `wave`, loaded early.
+// The table build, per context: prefix sums of the frequencies (DPP scan),
+// the used symbols' records, a bitmap of the slots where a symbol starts,
+// then the context's 16 table rows of 64 slots, where a slot's record is the
+// number of starts up to it (v_mbcnt over the row's bitmap).
+//
+// context_rows: everything up to the rows.  Returns, in lane t < 16, row
+// t's row descriptor: its start bits shifted down by one (lo, hi) and the
+// record index before it.  fpre holds the first 256 frequency slots of
+// context `wave` (loaded early; slots past its symbols are masked here).
+struct RowDesc {
+  uint32_t lo, hi, base;
+};
+__device__ __forceinline__ RowDesc context_rows(const Args &A, uint8_t *lds, uint32_t c, uint32_t wave, uint32_t lane,
+                                               const uint32_t (&fpre)[4], bool wide) {
+  const uint16_t *freq = A.freq;
+  uint2 *rec = reinterpret_cast<uint2 *>(lds + A.rec_off);          // (d0, cum term) per used symbol
+  uint32_t *mark = reinterpret_cast<uint32_t *>(lds + A.mark_off);  // [ctx][32] start bits
+  const uint32_t cf = pick(A.ctx_freq, c), n = cf >> 16, fidx = cf & 0xffffu, nzbase = pick(A.nzbase, c);
+  const int32_t smin = pick(A.smin, c);
+  if (lane < kMarkWords) mark[c * kMarkWords + lane] = 0u;
+  uint32_t carry = 0, nzb = nzbase;
+  // symbols base .. base + 63, lane's frequency f (0 past the context's end)
+  auto chunk = [&](uint32_t base, uint32_t f) {
+    const uint32_t s = base + lane;
+    const uint32_t incl = wave_inclusive_sum(f);
+    const uint32_t cum = carry + incl - f;
+    const bool used = f != 0;
+    const uint64_t m = __ballot(used);
+    const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nzb));
+    if (used && cum < kProbTotal) {
+      const int32_t v = symbol_value(c, smin + (int32_t)s);
+      rec[r] = make_uint2((f << 3) | (wide ? ((uint32_t)v & 0xffffu) << 16 : ((uint32_t)v & 0xffu) << 24), cum << 3);
+      atomicOr(&mark[c * kMarkWords + (cum >> 5)], 1u << (cum & 31u));
+    }
+    carry += __builtin_amdgcn_readlane(incl, 63);
+    nzb += (uint32_t)__popcll(m);
+  };
+  // The first 256 symbols of the wave's own context come from fpre, with
+  // the loop unrolled so that each use waits for its own load only.
+  if (c == wave) {
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i)
+      if (64u * i < n) chunk(64u * i, 64u * i + lane < n ? fpre[i] : 0u);
+  }
+  for (uint32_t base = c == wave ? 256u : 0u; base < n; base += 64) {
+    const uint32_t s = base + lane;
+    chunk(base, s < n ? freq[fidx + s] : 0u);
+  }
+  RowDesc d{0u, 0u, 0u};
+  uint32_t lo = 0, hi = 0;
+  if (lane < kRows) {
+    lo = mark[c * kMarkWords + 2 * lane];
+    hi = mark[c * kMarkWords + 2 * lane + 1];
+  }
+  const uint32_t cnt = (uint32_t)(__popc(lo) + __popc(hi));
+  const uint32_t first = nzbase + row16_inclusive_sum(cnt) - cnt;
+  d.lo = __builtin_amdgcn_alignbit(hi, lo, 1u);
+  d.hi = hi >> 1;
+  d.base = first + (lo & 1u) - 1u;
+  return d;
+}
+
+// LDS context index of context c: F, C_0, C_1, then E_{b,p} at 3 + b + 2p
+__device__ __forceinline__ uint32_t lds_context(uint32_t c) {
+  return c < 3u ? c : 3u + ((c - 3u) >> 1) + 2u * ((c - 3u) & 1u);
+}
+
+// slot record = first + (starts at or below the slot) - 1
+//             = base + popcount of (lo, hi) below the lane.
+__device__ __forceinline__ uint32_t slot_record(uint32_t lo, uint32_t hi, uint32_t base) {
+  return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, base));
+}
+
+// One wave builds whole contexts: waves 0..k-1 take contexts wave, wave + k,
+// ...  The row descriptors reach every lane through LDS: lanes 0..15 store
+// them in the wave's own 256 bytes and each row's is read back with one
+// uniform (broadcast) read, three VALU instructions per row fewer than
+// v_readlane broadcasts need.  All sixteen records are read before any
+// table write: the compiler cannot tell the record list and the table apart,
+// so interleaving would put an LDS round trip on every row.
 template <bool WIDE>
 __device__ __forceinline__ void build_tables(const Args &A, uint8_t *lds, uint32_t wave, uint32_t lane, uint32_t k,
                                              const uint32_t (&fpre)[4]) {
-  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
-  uint2 *rec = reinterpret_cast<uint2 *>(lds + A.rec_off);          // (d0, cum term) per used symbol
-  uint32_t *mark = reinterpret_cast<uint32_t *>(lds + A.mark_off);  // [ctx][32] start bits
+  typedef __attribute__((address_space(3))) u32x4 *lds_u128_ptr;
+  typedef __attribute__((address_space(3))) const u32x2 *lds_u64_cptr;
   uint32_t *tab = reinterpret_cast<uint32_t *>(lds);
+  const uint32_t dsc = A.desc_off + 256u * wave;  // this wave's row descriptors
   for (uint32_t c = wave; c < (uint32_t)kContexts; c += k) {
-    const uint32_t n = pick(A.nsym, c), fidx = pick(A.fidx, c), nzbase = pick(A.nzbase, c);
-    const int32_t smin = pick(A.smin, c);
-    if (n == 0u) continue;  // context without symbols: its table is never read
-    const uint32_t lc = c < 3u ? c : 3u + ((c - 3u) >> 1) + 2u * ((c - 3u) & 1u);  // LDS context of E_{b,p}
-    if (lane < kMarkWords) mark[c * kMarkWords + lane] = 0u;
-    uint32_t carry = 0, nzb = nzbase;
-    for (uint32_t base = 0, it = 0; base < n; base += 64, ++it) {
-      const uint32_t s = base + lane;
-      uint32_t f;
-      if (c == wave && it < 4) f = it == 0 ? fpre[0] : it == 1 ? fpre[1] : it == 2 ? fpre[2] : fpre[3];
-      else f = s < n ? freq[fidx + s] : 0u;
-      const uint32_t incl = wave_inclusive_sum(f);
-      const uint32_t cum = carry + incl - f;
-      const bool used = f != 0;
-      const uint64_t m = __ballot(used);
-      const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nzb));
-      if (used && cum < kProbTotal) {
-        const int32_t v = symbol_value(c, smin + (int32_t)s);
-        rec[r] = make_uint2((f << 3) | (WIDE ? ((uint32_t)v & 0xffffu) << 16 : ((uint32_t)v & 0xffu) << 24),
-                            cum << 3);
-        atomicOr(&mark[c * kMarkWords + (cum >> 5)], 1u << (cum & 31u));
-      }
-      carry += __builtin_amdgcn_readlane(incl, 63);
-      nzb += (uint32_t)__popcll(m);
-    }
-    // row t (lane t < 16): its start bits shifted down by one and the record
-    // index before it
-    uint32_t rlo = 0, rhi = 0, rbase = 0;
-    {
-      uint32_t lo = 0, hi = 0;
-      if (lane < kRows) {
-        lo = mark[c * kMarkWords + 2 * lane];
-        hi = mark[c * kMarkWords + 2 * lane + 1];
-      }
-      const uint32_t cnt = (uint32_t)(__popc(lo) + __popc(hi));
-      const uint32_t first = nzbase + row16_inclusive_sum(cnt) - cnt;
-      rlo = __builtin_amdgcn_alignbit(hi, lo, 1u);
-      rhi = hi >> 1;
-      rbase = first + (lo & 1u) - 1u;
-    }
-    // slot record = first + (starts at or below the slot) - 1
-    //             = first + bit0 - 1 + popcount of (bits >> 1) below the lane.
-    // The row values reach every lane through readlane (no LDS traffic), and
-    // all sixteen records are read before any table write: the compiler cannot
-    // tell the record list and the table apart, so interleaving would put an
-    // LDS round trip on every row.
-    uint2 rc[kRows];
+    if ((pick(A.ctx_freq, c) >> 16) == 0u) continue;  // context without symbols: its table is never read
+    const RowDesc d = context_rows(A, lds, c, wave, lane, fpre, WIDE);
+    const uint32_t lc = lds_context(c);
+    // (lo, hi, LDS address of the record before the row)
+    if (lane < kRows) *(lds_u128_ptr)(uintptr_t)(dsc + 16u * lane) = u32x4{d.lo, d.hi, A.rec_off + 8u * d.base, 0u};
+    u32x2 rc[kRows];
 #pragma unroll
     for (uint32_t row = 0; row < kRows; ++row) {
-      const uint32_t mlo = __builtin_amdgcn_readlane(rlo, row), mhi = __builtin_amdgcn_readlane(rhi, row);
-      const uint32_t b = __builtin_amdgcn_readlane(rbase, row);
-      rc[row] = rec[__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, b))];
+      const u32x4 r = *(lds_u128_ptr)(uintptr_t)(dsc + 16u * row);
+      rc[row] = *(lds_u64_cptr)(uintptr_t)(r.z + 8u * slot_record(r.x, r.y, 0u));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -586,22 +645,23 @@ struct UnitIn {
   uint32_t wt, we;  // LDS byte addresses of the lane's tile's first word and of its end
 };
 
-// Copies the words [w_lo, w_hi) of the stream into LDS at buf: 16-byte
-// pieces from the 16-byte boundary at or below w_lo, 1 KB per instruction;
-// lanes past the end of the last, partial kilobyte re-read its last piece.
-// Returns that 16-byte aligned start (a byte offset in the stream).  Blocks
-// k0, k0 + dk, ... are this wave's share.
-__device__ __forceinline__ uint64_t copy_words(const Args &A, uint8_t *lds, uint32_t w_lo, uint32_t w_hi,
-                                               uint32_t buf, uint32_t lane, uint32_t k0, uint32_t dk) {
-  const uint64_t gbyte0 = (A.off_words + 2ull * w_lo) & ~15ull;
-  const uint32_t nchunks = (uint32_t)((((A.off_words + 2ull * w_hi + 15ull) & ~15ull) - gbyte0) >> 4);
-  const gbyte_t src = (gbyte_t)(A.blob + gbyte0);
-  for (uint32_t i = k0; 64u * i < nchunks; i += dk) {
+// The 16-byte pieces of the word section that hold words [w_lo, w_hi):
+// pieces c0 .. c1 - 1.
+__device__ __forceinline__ uint32_t first_piece(uint32_t w_lo) { return w_lo >> 3; }
+__device__ __forceinline__ uint32_t end_piece(uint32_t w_hi) { return (w_hi + 7u) >> 3; }
+
+// Copies pieces [c0, c1) of the word section into LDS at buf, 1 KB per
+// instruction; lanes past the end of the last, partial kilobyte re-read its
+// last piece.  Blocks k0, k0 + dk, ... are this wave's share.
+__device__ __forceinline__ void copy_pieces(const Args &A, uint8_t *lds, uint32_t c0, uint32_t c1, uint32_t buf,
+                                            uint32_t lane, uint32_t k0, uint32_t dk) {
+  const uint32_t n = c1 - c0;
+  const gbyte_t src = (gbyte_t)(A.words + 16ull * c0);
+  for (uint32_t i = k0; 64u * i < n; i += dk) {
     const uint32_t ch = 64u * i + lane;
-    __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (ch < nchunks ? ch : nchunks - 1u)),
-                                     (lptr_t)(lds + buf + 1024u * i), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gptr_t)(src + 16u * (ch < n ? ch : n - 1u)), (lptr_t)(lds + buf + 1024u * i),
+                                     16, 0, 0);
   }
-  return gbyte0;
 }
 
 // Issues a unit's loads: its lanes' tile offsets and row scales (vector
@@ -613,13 +673,13 @@ __device__ __forceinline__ UnitIn issue_unit(const Args &A, uint8_t *lds, uint32
   UnitIn T;
   T.u = unit_lane<NS, V>(A, unit, lane);
   group_scales<NS, V>(A, T.u, 0u, T.gs);
-  const uint32_t *toffv = reinterpret_cast<const uint32_t *>(A.blob + A.off_tile_offsets);
-  const uint32_t tb = toffv[T.u.tile], te = toffv[T.u.tile + 1u];
+  const uint32_t tb = A.toff[T.u.tile], te = A.toff[T.u.tile + 1u];
   typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
-  const cptr_u32 toff = (cptr_u32)(A.blob + A.off_tile_offsets);
+  const cptr_u32 toff = (cptr_u32)A.toff;
   const uint32_t t0 = unit * (64u / NS), t1 = min(t0 + 64u / NS, A.n_tiles);
-  const uint64_t gbyte0 = copy_words(A, lds, toff[t0], toff[t1], buf, lane, 0u, 1u);
-  T.wt = buf + (uint32_t)(A.off_words + 2ull * tb - gbyte0);
+  const uint32_t c0 = first_piece(toff[t0]);
+  copy_pieces(A, lds, c0, end_piece(toff[t1]), buf, lane, 0u, 1u);
+  T.wt = buf + 2u * tb - 16u * c0;
   T.we = T.wt + 2u * (te - tb);
   return T;
 }
@@ -628,28 +688,30 @@ __device__ __forceinline__ UnitIn issue_unit(const Args &A, uint8_t *lds, uint32
 // completed, none after it has started
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// the first 256 frequencies of this wave's first context, which need
-// nothing but the kernel arguments
+// the first 256 frequency slots of this wave's first context, which need
+// nothing but the kernel arguments; slots past the context's symbols hold
+// its first frequency and are masked where they are used
 __device__ __forceinline__ void first_frequencies(const Args &A, uint32_t wave, uint32_t lane, uint32_t (&fpre)[4]) {
-  const uint16_t *freq = reinterpret_cast<const uint16_t *>(A.blob + A.off_freq);
-  const uint32_t c0 = wave < (uint32_t)kContexts ? wave : 0u;
-  const uint32_t n0 = pick(A.nsym, c0), f0 = pick(A.fidx, c0);
+  // one scalar load of the argument word (a select over the seven would
+  // cost fourteen scalar instructions, and the workgroup's waves share one
+  // scalar unit)
+  const uint32_t cf = A.ctx_freq[__builtin_amdgcn_readfirstlane(wave < (uint32_t)kContexts ? wave : 0u)];
+  const uint32_t n0 = cf >> 16, f0 = cf & 0xffffu;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t s = 64u * i + lane;
-    const uint32_t v = freq[f0 + (s < n0 ? s : 0u)];
-    fpre[i] = s < n0 ? v : 0u;
+    fpre[i] = A.freq[f0 + (s < n0 ? s : 0u)];
   }
 }
 
 template <int OUT, bool WIDE, bool PADDED, bool BOP3, int NS, int V>
-__device__ __forceinline__ void decode_unit_any(const Args &A, const UnitLane &u, uint32_t wt, uint32_t we,
-                                                const float (&gs)[8], uint32_t lane) {
+__device__ __forceinline__ void decode_unit_any(const Args &A, const UnitLane &u, const Start &S, const float (&gs)[8],
+                                                uint32_t lane) {
   constexpr uint32_t kTv = (uint32_t)(NS * V);
   if (__ballot(u.n != kTv) == 0)
-    decode_unit<OUT, WIDE, PADDED, false, BOP3, NS, V>(A, u, wt, we, gs, lane);
+    decode_unit<OUT, WIDE, PADDED, false, BOP3, NS, V>(A, u, S, gs, lane);
   else
-    decode_unit<OUT, WIDE, PADDED, true, BOP3, NS, V>(A, u, wt, we, gs, lane);
+    decode_unit<OUT, WIDE, PADDED, true, BOP3, NS, V>(A, u, S, gs, lane);
 }
 
 // Streams with more units than one round of workgroups covers: one
@@ -686,7 +748,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_waves_kernel(Args A) {
 
   while (unit < end) {
     __builtin_amdgcn_s_waitcnt(0);  // the unit's offsets, scales and words have landed
-    decode_unit_any<OUT, WIDE, PADDED, kNarrowOut, NS, V>(A, T.u, T.wt, T.we, T.gs, lane);
+    decode_unit_any<OUT, WIDE, PADDED, kNarrowOut, NS, V>(A, T.u, parse_start<NS>(T.u, T.wt, T.we, lane), T.gs, lane);
     unit += k;
     if (unit < end) {
       __builtin_amdgcn_s_waitcnt(0);  // every read of the finished unit's words is done before they are overwritten
@@ -695,71 +757,85 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_waves_kernel(Args A) {
   }
 }
 
+// Kernel arguments of the single-round kernel: the common ones and the first
+// word of each workgroup's range of tile words (entry `grid`: the end of the
+// last range).  Scalar loads from the arguments cost one short round trip at
+// the start of a wave; loading these words from the tile offsets would put a
+// memory round trip in front of the word copy.
+constexpr uint32_t kMaxRoundWgs = 256;
+struct RoundArgs {
+  Args a;
+  uint32_t wg_word[kMaxRoundWgs + 1];
+};
+
 // Streams that one round of workgroups covers: workgroups of up to 16 waves,
-// one unit each.
+// one unit each.  Waves 0..6 build one context's table each (at raised
+// priority: until the tables exist nothing else can decode); the others copy
+// the workgroup's words into LDS with global_load_lds, 1 KB per instruction,
+// each taking every (waves - 7)th kilobyte.  Every wave then decodes its
+// unit.  The two kinds of wave run separate code up to the barrier: after a
+// copy into LDS the compiler waits for every load before the next LDS
+// access, which a table builder must not do.
 template <int OUT, bool WIDE, bool PADDED, int NS, int V>
-__global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(Args A) {
+__global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(RoundArgs R) {
   extern __shared__ __align__(16) uint8_t lds[];
+  const Args &A = R.a;
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t nwaves = A.waves;
-  constexpr uint32_t kTpw = 64u / NS;
-
-  // ---- 1. global loads, all unconditional so that each wait is exact ----
+  // the arguments the first loads need, read in one round of scalar loads
+  asm volatile("" ::"s"(A.freq), "s"(A.words), "s"(A.waves), "s"(A.n_units), "s"(A.n_tiles),
+               "s"(R.wg_word[blockIdx.x]), "s"(R.wg_word[blockIdx.x + 1u]));
+  const uint32_t builders = nwaves < (uint32_t)kContexts + 1u ? nwaves : (uint32_t)kContexts;
   const uint32_t unit = blockIdx.x * nwaves + wave;
   const bool has_unit = unit < A.n_units;
-  const UnitLane u = unit_lane<NS, V>(A, has_unit ? unit : A.n_units - 1u, lane);
-  // The workgroup's tiles are consecutive, so their words are one range of
-  // the stream.  Every lane loads its tile's first and end word and the
-  // range's first word; copying waves also its end.  These are vector loads:
-  // scalar loads would share their counter with the table build's LDS
-  // accesses, whose waits would then wait for them too.
-  const uint32_t *toff = reinterpret_cast<const uint32_t *>(A.blob + A.off_tile_offsets);
-  const uint32_t g0 = blockIdx.x * nwaves * kTpw;
-  const uint32_t gend = min(g0 + nwaves * kTpw, A.n_tiles);
-  const uint32_t tb = toff[u.tile], te = toff[u.tile + 1u];
-  const uint32_t w_lo = toff[g0];
-  uint32_t fpre[4];
-  first_frequencies(A, wave, lane, fpre);
+  // the workgroup's words: pieces c0 .. c1 - 1 of the word section
+  const uint32_t c0 = first_piece(R.wg_word[blockIdx.x]), c1 = end_piece(R.wg_word[blockIdx.x + 1u]);
+  UnitLane u;
+  uint32_t tb, te;
   float gs[8];
-  group_scales<NS, V>(A, u, 0u, gs);
-  __builtin_amdgcn_sched_barrier(0);  // the loads above go out before anything waits
-  // ---- 2. the tables (waves 0..6) and the word copy (the others) ----------
-  const uint32_t builders = nwaves < (uint32_t)kContexts + 1u ? nwaves : (uint32_t)kContexts;
-  if (wave < builders) build_tables<WIDE>(A, lds, wave, lane, builders, fpre);
-  // With eight or more waves the waves past the builders copy the
-  // workgroup's words into LDS with global_load_lds (1 KB per instruction),
-  // each taking every (waves - 7)th kilobyte; with fewer the last wave copies
-  // them after its table.  Where the copying branch rejoins, the compiler
-  // waits for every load, so a builder that copied before its table would
-  // wait for its states and scales first.
-  if (wave >= builders || (builders == nwaves && wave == nwaves - 1u)) {
-    const uint32_t w_hi = toff[gend];
-    const uint32_t k0 = wave >= builders ? wave - builders : 0u, dk = wave >= builders ? nwaves - builders : 1u;
-    (void)copy_words(A, lds, __builtin_amdgcn_readfirstlane(w_lo), __builtin_amdgcn_readfirstlane(w_hi),
-                     A.words_off, lane, k0, dk);
+  if (wave < builders) {
+    set_priority<2>();
+    uint32_t fpre[4];
+    first_frequencies(A, wave, lane, fpre);
+    __builtin_amdgcn_sched_barrier(0);
+    u = unit_lane<NS, V>(A, has_unit ? unit : A.n_units - 1u, lane);
+    tb = A.toff[opaque(u.tile)];  // vector loads: a scalar load's only wait, lgkmcnt(0), would also wait for LDS work
+    te = A.toff[opaque(u.tile + 1u)];
+    group_scales<NS, V>(A, u, 0u, gs);
+    __builtin_amdgcn_sched_barrier(0);
+    build_tables<WIDE>(A, lds, wave, lane, builders, fpre);
+    set_priority<0>();
+    if (builders == nwaves && wave == nwaves - 1u)  // fewer than eight waves: the last builder copies
+      copy_pieces(A, lds, c0, c1, A.words_off, lane, 0u, 1u);
+  } else {
+    copy_pieces(A, lds, c0, c1, A.words_off, lane, wave - builders, nwaves - builders);
+    __builtin_amdgcn_sched_barrier(0);
+    u = unit_lane<NS, V>(A, has_unit ? unit : A.n_units - 1u, lane);
+    tb = A.toff[opaque(u.tile)];
+    te = A.toff[opaque(u.tile + 1u)];
+    group_scales<NS, V>(A, u, 0u, gs);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
   __syncthreads();
 
-  // ---- 3. decode ---------------------------------------------------------
   if (!has_unit) return;
-  const uint64_t gbyte0 = (A.off_words + 2ull * w_lo) & ~15ull;  // 16-byte aligned start of the range
-  const uint32_t wt = A.words_off + (uint32_t)(A.off_words + 2ull * tb - gbyte0);  // LDS address of the tile's first word
-  const uint32_t we = wt + 2u * (te - tb);
-  decode_unit_any<OUT, WIDE, PADDED, true, NS, V>(A, u, wt, we, gs, lane);
+  const uint32_t wt = A.words_off + 2u * tb - 16u * c0;  // LDS address of the tile's first word
+  decode_unit_any<OUT, WIDE, PADDED, true, NS, V>(A, u, parse_start<NS>(u, wt, wt + 2u * (te - tb), lane), gs, lane);
 }
 
-typedef void (*KernelFn)(Args);
+typedef const void *KernelFn;  // a kernel's address: decode_waves_kernel takes Args, decode_kernel RoundArgs
 
 template <int OUT, bool WIDE, bool PADDED>
 KernelFn pick4(bool multi, int ns, int tv) {
   if (ns == kStatesLow) {
-    if (tv == kTileVecsSmall) return multi ? decode_waves_kernel<OUT, WIDE, PADDED, 16, 32> : decode_kernel<OUT, WIDE, PADDED, 16, 32>;
-    return multi ? decode_waves_kernel<OUT, WIDE, PADDED, 16, 64> : decode_kernel<OUT, WIDE, PADDED, 16, 64>;
+    if (tv == kTileVecsSmall)
+      return multi ? (KernelFn)decode_waves_kernel<OUT, WIDE, PADDED, 16, 32> : (KernelFn)decode_kernel<OUT, WIDE, PADDED, 16, 32>;
+    return multi ? (KernelFn)decode_waves_kernel<OUT, WIDE, PADDED, 16, 64> : (KernelFn)decode_kernel<OUT, WIDE, PADDED, 16, 64>;
   }
-  if (tv == kTileVecsSmall) return multi ? decode_waves_kernel<OUT, WIDE, PADDED, 64, 8> : decode_kernel<OUT, WIDE, PADDED, 64, 8>;
-  return multi ? decode_waves_kernel<OUT, WIDE, PADDED, 64, 16> : decode_kernel<OUT, WIDE, PADDED, 64, 16>;
+  if (tv == kTileVecsSmall)
+    return multi ? (KernelFn)decode_waves_kernel<OUT, WIDE, PADDED, 64, 8> : (KernelFn)decode_kernel<OUT, WIDE, PADDED, 64, 8>;
+  return multi ? (KernelFn)decode_waves_kernel<OUT, WIDE, PADDED, 64, 16> : (KernelFn)decode_kernel<OUT, WIDE, PADDED, 64, 16>;
 }
 
 template <int OUT>
@@ -841,8 +917,13 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   uint32_t nz_total = 0;
   for (int c = 0; c < kContexts; ++c) {
     A.smin[c] = s.smin[c];
-    A.nsym[c] = s.nsym[c];
-    A.fidx[c] = (uint32_t)s.freq_index[c];
+    // symbol counts and frequency indexes share a word per context: 16 bits
+    // each, far above what the 12-bit value field allows an encoder
+    if (s.nsym[c] > (uint32_t)(kValueMax - kValueMin + 1) || s.freq_index[c] + s.nsym[c] > 0xffffu) {
+      set_error("frequency table larger than the decoder's 16-bit indexes");
+      return EP_ERR_FORMAT;
+    }
+    A.ctx_freq[c] = (uint32_t)s.freq_index[c] | (uint32_t)s.nsym[c] << 16;
     A.nzbase[c] = nz_total;
     uint32_t sum = 0;
     for (uint32_t i = 0; i < s.nsym[c]; ++i) {
@@ -862,10 +943,10 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
       return EP_ERR_FORMAT;
     }
   }
-  // LDS layout: tables | records | bitmap | words | pad.  A wave decodes a
-  // unit of 64 / states consecutive tiles; the words of a workgroup's
-  // consecutive units are one range, copied in whole kilobytes from a 16-byte
-  // boundary.
+  // LDS layout: tables | records | bitmap | row descriptors | words | pad.
+  // A wave decodes a unit of 64 / states consecutive tiles; the words of a
+  // workgroup's consecutive units are one range, copied in whole kilobytes
+  // from a 16-byte boundary.
   const int64_t tpw = 64 / s.states;
   const int64_t units = (s.tiles + tpw - 1) / tpw;
   uint32_t off = kTableBytes;
@@ -873,6 +954,8 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   off += 8 * nz_total;
   A.mark_off = off;
   off = (uint32_t)align16(off + 4 * kContexts * kMarkWords);
+  A.desc_off = off;  // 256 bytes of row descriptors per table-building wave
+  off += 256 * kContexts;
   A.words_off = off;
   // bytes the copy of tiles [t0, t1) takes
   auto copy_bytes = [&](int64_t t0, int64_t t1) {
@@ -904,7 +987,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   uint32_t grid = (uint32_t)((units + waves - 1) / waves);
   // More workgroups than compute units: the multi-tile kernel instead, with
   // one workgroup per CU that builds the tables once.
-  const bool multi = (int64_t)grid > num_cus();
+  const bool multi = (int64_t)grid > std::min<int64_t>(num_cus(), kMaxRoundWgs);
   if (multi) {
     // One workgroup per CU, each with a run of consecutive units (counts that
     // differ by at most one); its k waves take the run's units in turn.  k is
@@ -926,12 +1009,12 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     A.wbuf = (uint32_t)wbuf;
     lds_bytes = A.words_off + waves * (uint32_t)wbuf + kLdsPad;
   }
-  A.blob = reinterpret_cast<const uint8_t *>(dev_blob);
+  const uint8_t *db = reinterpret_cast<const uint8_t *>(dev_blob);
+  A.freq = reinterpret_cast<const uint16_t *>(db + s.off_freq);
+  A.toff = reinterpret_cast<const uint32_t *>(db + s.off_tile_offsets);
+  A.words = db + s.off_words;
+  A.scales = reinterpret_cast<const float *>(db + s.off_scales);
   A.out = dev_out;
-  A.off_freq = s.off_freq;
-  A.off_scales = s.off_scales;
-  A.off_tile_offsets = s.off_tile_offsets;
-  A.off_words = s.off_words;
   A.cols = (uint64_t)s.cols;
   A.rows = (uint32_t)s.rows;
   A.vpr = (uint32_t)(s.cols8 / 8);
@@ -948,7 +1031,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     bool done = false;
     for (KernelFn k : configured) done |= k == fn;
     if (!done) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+      if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kLdsLimit) != hipSuccess) {
         set_error("hipFuncSetAttribute failed");
         return EP_ERR_DEVICE;
@@ -957,8 +1040,18 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
     }
   }
   A.waves = waves;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(64 * waves), lds_bytes, stream, A);
-  hipError_t err = hipGetLastError();
+  RoundArgs R;
+  void *args[1];
+  if (multi) {
+    args[0] = &A;
+  } else {
+    R.a = A;
+    for (uint32_t b = 0; b <= grid; ++b)
+      R.wg_word[b] = first_word(std::min<int64_t>((int64_t)b * waves * tpw, s.tiles));
+    args[0] = &R;
+  }
+  hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(64 * waves), args, lds_bytes, stream);
+  if (err == hipSuccess) err = hipGetLastError();
   if (err != hipSuccess) {
     set_error(std::string("kernel launch failed: ") + hipGetErrorString(err));
     return EP_ERR_DEVICE;
