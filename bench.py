@@ -20,6 +20,8 @@ Timing:
     launches in all, divided by the launch count.  One replay of a few
     launches would also time the gap before the graph's first kernel, which
     rocprof's per-kernel durations do not contain;
+  * fill_us: torch's fill kernel writing the same outputs in the same
+    rotation, timed the same way -- the cost of the output bytes alone;
   * cpu_baseline: the CPU oracle's decoder on the same stream, tiles split
     over the host cores the process may use, at most the 16 a GPU's share of
     the host holds (and on one thread, as cpu_baseline_1thread).
@@ -251,7 +253,31 @@ def main() -> int:
         torch.cuda.synchronize()
         warm_ms = w0.elapsed_time(w1) / args.steps
 
+    # context only: torch's fill kernel writing the same output copies in the
+    # same rotation, timed like kernel_us -- what the output bytes alone cost
+    # to write on this machine, the floor under a decode that must write them
+    fill_ms = None
+    if not args.eager_only:
+        gf = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gf, stream=stream):
+            for i in range(args.steps):
+                outs[i % copies].fill_(1)
+        with torch.cuda.stream(stream):
+            gf.replay()
+        reps = max(1, math.ceil(args.roofline_launches / args.steps))
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            f0.record(stream)
+            for _ in range(reps):
+                gf.replay()
+            f1.record(stream)
+        torch.cuda.synchronize()
+        fill_ms = f0.elapsed_time(f1) / (reps * args.steps)
+
     # the last decode of each copy must equal a fresh eager decode
+    with torch.cuda.stream(stream):
+        for i in range(min(copies, args.steps)):
+            step(i)
     ref = ep.decompress(packs[0], stream=stream)
     stream.synchronize()
     for o in outs[: min(copies, args.steps)]:
@@ -294,6 +320,8 @@ def main() -> int:
         "kernel_us_timed_region": round(region_kernel_ms * 1e3, 3),
         "kernel_us_eager_events": round(eager_ms * 1e3, 3),
         "kernel_us_warm": round(warm_ms * 1e3, 3) if warm_ms is not None else None,
+        "fill_us": round(fill_ms * 1e3, 3) if fill_ms is not None else None,
+        "fill_gbps": round(out_bytes / (fill_ms * 1e-3) / 1e9, 1) if fill_ms is not None else None,
         "clock_settle_s": round(settle_s, 3),
         "hbm_gbps_per_step": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "rel_l2": round(rel_l2, 5),

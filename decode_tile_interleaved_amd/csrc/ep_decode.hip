@@ -802,12 +802,16 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(RoundArgs R) {
     u = unit_lane<NS, V>(A, has_unit ? unit : A.n_units - 1u, lane);
     tb = A.toff[opaque(u.tile)];  // vector loads: a scalar load's only wait, lgkmcnt(0), would also wait for LDS work
     te = A.toff[opaque(u.tile + 1u)];
-    group_scales<NS, V>(A, u, 0u, gs);
     __builtin_amdgcn_sched_barrier(0);
     build_tables<WIDE>(A, lds, wave, lane, builders, fpre);
     set_priority<0>();
-    if (builders == nwaves && wave == nwaves - 1u)  // fewer than eight waves: the last builder copies
+    if (builders == nwaves && wave == nwaves - 1u) {  // fewer than eight waves: the last builder copies
       copy_pieces(A, lds, c0, c1, A.words_off, lane, 0u, 1u);
+      __builtin_amdgcn_s_waitcnt(0);  // the copy has landed in LDS
+    }
+    // first needed at the first store, a vector's decode after the barrier,
+    // so the barrier does not wait for them
+    group_scales<NS, V>(A, u, 0u, gs);
   } else {
     copy_pieces(A, lds, c0, c1, A.words_off, lane, wave - builders, nwaves - builders);
     __builtin_amdgcn_sched_barrier(0);
@@ -815,9 +819,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(RoundArgs R) {
     tb = A.toff[opaque(u.tile)];
     te = A.toff[opaque(u.tile + 1u)];
     group_scales<NS, V>(A, u, 0u, gs);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed in LDS
-  __syncthreads();
+  lds_barrier();  // tables built, words copied
 
   if (!has_unit) return;
   const uint32_t wt = A.words_off + 2u * tb - 16u * c0;  // LDS address of the tile's first word
