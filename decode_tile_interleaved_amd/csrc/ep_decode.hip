@@ -71,6 +71,7 @@
 // comes from the entry.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -380,13 +381,15 @@ __device__ __forceinline__ void emit_vector(const Args &A, gbyte_t dst, uint32_t
   }
 }
 
-// the row scale of vector vec (the last row's for vectors past the end)
-__device__ __forceinline__ float row_scale(const Args &A, uint32_t vec) {
-  const float *scales = A.scales;
+// the row of vector vec (the last row for vectors past the end)
+__device__ __forceinline__ uint32_t row_of(const Args &A, uint32_t vec) {
   const uint32_t last = A.rows - 1u, one = A.vpr == 1u ? 0xffffffffu : 0u;
   const uint32_t r = ((__umulhi(vec, A.row_magic) >> A.row_shift) & ~one) | (vec & one);
-  return scales[r < last ? r : last];
+  return r < last ? r : last;
 }
+
+// the row scale of vector vec (the last row's for vectors past the end)
+__device__ __forceinline__ float row_scale(const Args &A, uint32_t vec) { return A.scales[row_of(A, vec)]; }
 
 // The lanes of a wave's unit: unit u holds tiles u * 64/NS .. (64/NS tiles of
 // NS states; lanes 16r.. hold tile r's states when NS = 16).
@@ -394,6 +397,8 @@ struct UnitLane {
   uint32_t tile;  // the lane's tile (the stream's last for a tile past its end)
   uint32_t q;     // the lane's state in its tile
   uint32_t n;     // vectors in the lane's tile (0 past the stream's end)
+  uint32_t row;   // the row of the tile's first vector
+  bool one_row;   // wave-uniform: every lane's tile lies in one row of the matrix
 };
 
 template <int NS, int V>
@@ -405,14 +410,24 @@ __device__ __forceinline__ UnitLane unit_lane(const Args &A, uint32_t unit, uint
   const bool have = t < A.n_tiles;
   u.tile = have ? t : A.n_tiles - 1u;
   u.n = have ? min(kTv, A.n_vec - t * kTv) : 0u;
+  u.row = row_of(A, u.tile * kTv);
+  const bool split = u.n > 1u && row_of(A, u.tile * kTv + u.n - 1u) != u.row;
+  u.one_row = __ballot(split) == 0;
   return u;
 }
 
 // the row scales of lane's vectors 8g .. 8g + 7 (lanes past the end read the
-// last row; their values are unused)
+// last row; their values are unused).  Tiles inside one row (every tile when
+// the rows hold whole tiles) take one scale for all.
 template <int NS, int V>
 __device__ __forceinline__ void group_scales(const Args &A, const UnitLane &u, uint32_t g, float (&gs)[8]) {
   constexpr uint32_t kTv = (uint32_t)(NS * V);
+  if (u.one_row) {
+    const float v = A.scales[u.row];
+#pragma unroll
+    for (uint32_t s = 0; s < 8; ++s) gs[s] = v;
+    return;
+  }
 #pragma unroll
   for (uint32_t s = 0; s < 8; ++s) gs[s] = row_scale(A, u.tile * kTv + (8u * g + s) * NS + u.q);
 }
@@ -484,7 +499,7 @@ __device__ __forceinline__ void decode_unit(const Args &A, const UnitLane &u, co
 #pragma unroll 1
   for (uint32_t grp = 0; grp < kGroups; ++grp) {
     float gn[8];
-    if (grp + 1u < kGroups) group_scales<NS, V>(A, u, grp + 1u, gn);
+    if (grp + 1u < kGroups && !u.one_row) group_scales<NS, V>(A, u, grp + 1u, gn);  // one row: gs holds its scale
 #pragma unroll
     for (uint32_t s8 = 0; s8 < 8; ++s8) {
       const uint32_t s = grp * 8u + s8;  // step
@@ -515,7 +530,7 @@ __device__ __forceinline__ void decode_unit(const Args &A, const UnitLane &u, co
         emit_vector<OUT, WIDE, PADDED>(A, dst, tile * kTv + i, e, gs[s8]);
       }
     }
-    if (grp + 1u < kGroups) {
+    if (grp + 1u < kGroups && !u.one_row) {
 #pragma unroll
       for (int s = 0; s < 8; ++s) gs[s] = gn[s];
     }
@@ -664,6 +679,41 @@ __device__ __forceinline__ void copy_pieces(const Args &A, uint8_t *lds, uint32_
   }
 }
 
+// The same copy through registers, for waves that also build tables (after
+// a copy straight into LDS the compiler makes every later LDS access of the
+// wave wait for it).  stage_pieces loads the wave's first kStage blocks
+// (blocks k0, k0 + dk, ...; every lane loads, lanes past the end re-reading
+// the last piece, so that no load sits behind a branch and each wait counts
+// exactly); store_pieces writes them and copies any further blocks.
+constexpr uint32_t kStage = 4;
+__device__ __forceinline__ void stage_pieces(const Args &A, uint32_t c0, uint32_t c1, uint32_t lane, uint32_t k0,
+                                             uint32_t dk, u32x4 (&cp)[kStage]) {
+  const uint32_t n = c1 - c0;
+  const gbyte_t src = (gbyte_t)(A.words + 16ull * c0);
+#pragma unroll
+  for (uint32_t i = 0; i < kStage; ++i) {
+    const uint32_t ch = 64u * (k0 + i * dk) + lane;
+    cp[i] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)(src + 16ull * (ch < n ? ch : n - 1u)));
+  }
+}
+__device__ __forceinline__ void store_pieces(const Args &A, uint32_t c0, uint32_t c1, uint32_t buf, uint32_t lane,
+                                             uint32_t k0, uint32_t dk, const u32x4 (&cp)[kStage]) {
+  typedef __attribute__((address_space(3))) u32x4 *lds_u128_ptr;
+  const uint32_t n = c1 - c0;
+#pragma unroll
+  for (uint32_t i = 0; i < kStage; ++i) {
+    const uint32_t ch = 64u * (k0 + i * dk) + lane;
+    if (ch < n) *(lds_u128_ptr)(uintptr_t)(buf + 16u * ch) = cp[i];
+  }
+  const gbyte_t src = (gbyte_t)(A.words + 16ull * c0);
+  for (uint32_t b = k0 + kStage * dk; 64u * b < n; b += dk) {
+    const uint32_t ch = 64u * b + lane;
+    if (ch < n)
+      *(lds_u128_ptr)(uintptr_t)(buf + 16u * ch) =
+          __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)(src + 16ull * ch));
+  }
+}
+
 // Issues a unit's loads: its lanes' tile offsets and row scales (vector
 // loads), the unit's word range (scalar loads), and the copy of its words
 // into LDS at buf.  Only the copy's addresses wait, for the word range.
@@ -772,7 +822,8 @@ struct RoundArgs {
 // one unit each.  Waves 0..6 build one context's table each (at raised
 // priority: until the tables exist nothing else can decode); the others copy
 // the workgroup's words into LDS with global_load_lds, 1 KB per instruction,
-// each taking every (waves - 7)th kilobyte.  Every wave then decodes its
+// each taking every (waves - 7)th kilobyte.  With fewer than eight waves
+// every wave builds, and each also copies its share through registers.  Every wave then decodes its
 // unit.  The two kinds of wave run separate code up to the barrier: after a
 // copy into LDS the compiler waits for every load before the next LDS
 // access, which a table builder must not do.
@@ -798,6 +849,11 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(RoundArgs R) {
     set_priority<2>();
     uint32_t fpre[4];
     first_frequencies(A, wave, lane, fpre);
+    // fewer than eight waves, all building tables: each also copies every
+    // (waves)th block of the words, through registers
+    const bool copies = builders == nwaves;
+    u32x4 cp[kStage];
+    if (copies) stage_pieces(A, c0, c1, lane, wave, nwaves, cp);
     __builtin_amdgcn_sched_barrier(0);
     u = unit_lane<NS, V>(A, has_unit ? unit : A.n_units - 1u, lane);
     tb = A.toff[opaque(u.tile)];  // vector loads: a scalar load's only wait, lgkmcnt(0), would also wait for LDS work
@@ -805,10 +861,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(RoundArgs R) {
     __builtin_amdgcn_sched_barrier(0);
     build_tables<WIDE>(A, lds, wave, lane, builders, fpre);
     set_priority<0>();
-    if (builders == nwaves && wave == nwaves - 1u) {  // fewer than eight waves: the last builder copies
-      copy_pieces(A, lds, c0, c1, A.words_off, lane, 0u, 1u);
-      __builtin_amdgcn_s_waitcnt(0);  // the copy has landed in LDS
-    }
+    if (copies) store_pieces(A, c0, c1, A.words_off, lane, wave, nwaves, cp);
     // first needed at the first store, a vector's decode after the barrier,
     // so the barrier does not wait for them
     group_scales<NS, V>(A, u, 0u, gs);
@@ -974,9 +1027,14 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
       span = std::max<uint64_t>(span, copy_bytes(u0 * tpw, std::min<int64_t>((u0 + k) * tpw, s.tiles)));
     return span;
   };
+  // Waves per workgroup: as many as the LDS allows, up to 16 (four per
+  // SIMD), but no more than spreads the units over every CU: a stream of few
+  // units (low rates: few states, long chains) decodes faster with one wave
+  // per SIMD on every CU than with four per SIMD on a quarter of them.
   uint32_t waves = 0;
   uint64_t span = 0;
-  for (int64_t k = std::min<int64_t>(kMaxWaves, units); k >= 1; --k) {
+  const int64_t per_cu = (units + num_cus() - 1) / num_cus();
+  for (int64_t k = std::min<int64_t>({(int64_t)kMaxWaves, units, std::max<int64_t>(per_cu, 4)}); k >= 1; --k) {
     span = span_for(k);
     if (off + span + kLdsPad <= kLdsLimit) {
       waves = (uint32_t)k;
