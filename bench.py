@@ -293,6 +293,32 @@ def main() -> int:
         wd = w.double().to(dev)
         rel_l2_weights = ((ref.double() * scale.double().to(dev) - wd).norm() / wd.norm()).item()
 
+    # context only: host time per enqueued decode (Python call included),
+    # ep_decompress (checks the stream and sizes the launch on every call)
+    # against a decode plan made once
+    def host_us(call, n=200):
+        stream.synchronize()
+        t = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for i in range(n):
+                call(i)
+        dt = time.perf_counter() - t
+        stream.synchronize()
+        return dt * 1e6 / n
+
+    plans = [ep.plan(pk) for pk in packs]
+    host_decompress_us = host_us(step)
+    host_plan_us = host_us(lambda i: plans[i % copies].decompress(out=outs[i % copies], stream=stream))
+    with torch.cuda.stream(stream):
+        for i in range(min(copies, args.steps)):
+            plans[i % copies].decompress(out=outs[i % copies], stream=stream)
+    ref_plan = plans[0].decompress(stream=stream)
+    stream.synchronize()
+
+    vw = torch.int16 if ref.element_size() == 2 else torch.int8
+    for o in outs[: min(copies, args.steps)] + [ref_plan]:
+        assert torch.equal(o.view(vw), ref.view(vw))
+
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     info = ep.blob_info(p.blob)
     traffic = measured_traffic(args.workload)
@@ -327,6 +353,8 @@ def main() -> int:
         "rel_l2": round(rel_l2, 5),
         "rel_l2_vs_weights": round(rel_l2_weights, 5) if rel_l2_weights is not None else None,
         "encode_s": round(encode_s, 3),
+        "host_us_per_call": {"ep_decompress": round(host_decompress_us, 2),
+                             "ep_plan_decompress": round(host_plan_us, 2)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"], line["cpu_baseline_1thread"] = cpu_baseline(p.blob, numel)

@@ -75,6 +75,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -992,13 +993,25 @@ void row_divider(uint32_t d, uint32_t &m, uint32_t &shift) {
   shift = s - 1;
 }
 
+// Everything a decode launch needs that depends on the stream alone: the
+// kernel, its geometry and its arguments (all but the output pointer).
+struct Plan {
+  bool raw = false;        // raw container: a device-to-device copy of the payload
+  size_t raw_bytes = 0;
+  const void *dev_blob = nullptr;
+  KernelFn fn = nullptr;
+  uint32_t grid = 0, block = 0, lds_bytes = 0;
+  bool multi = false;      // multi-tile kernel: its argument is R.a alone
+  RoundArgs R{};
+};
+
 // host-side checks and launch geometry; returns 0 or an ep_status
-int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *dev_out, int out, hipStream_t stream) {
-  if (!dev_blob || !dev_out) {
+int prepare(const uint8_t *hb, const StreamView &s, const void *dev_blob, int out, Plan &P) {
+  if (!dev_blob) {
     set_error("null device pointer");
     return EP_ERR_ARG;
   }
-  if (((uintptr_t)dev_blob & 15) || ((uintptr_t)dev_out & 15)) {
+  if ((uintptr_t)dev_blob & 15) {
     set_error("device buffers must be 16-byte aligned");
     return EP_ERR_ARG;
   }
@@ -1125,7 +1138,7 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   A.toff = reinterpret_cast<const uint32_t *>(db + s.off_tile_offsets);
   A.words = db + s.off_words;
   A.scales = reinterpret_cast<const float *>(db + s.off_scales);
-  A.out = dev_out;
+  A.out = nullptr;
   A.cols = (uint64_t)s.cols;
   A.rows = (uint32_t)s.rows;
   A.vpr = (uint32_t)(s.cols8 / 8);
@@ -1135,34 +1148,78 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   A.n_units = (uint32_t)units;
   const bool padded = out != kOutSym && (s.cols % 8) != 0;
   const bool prio = multi && A.wg_rem == 0 && A.wg_q % waves == 0;
-  KernelFn fn = pick_kernel(out, wide, padded, multi, prio, s.states, s.tile_vecs);
+  A.waves = waves;
+  P.raw = false;
+  P.dev_blob = dev_blob;
+  P.fn = pick_kernel(out, wide, padded, multi, prio, s.states, s.tile_vecs);
+  P.grid = grid;
+  P.block = 64 * waves;
+  P.lds_bytes = lds_bytes;
+  P.multi = multi;
+  P.R.a = A;
+  if (!multi)
+    for (uint32_t b = 0; b <= grid; ++b)
+      P.R.wg_word[b] = first_word(std::min<int64_t>((int64_t)b * waves * tpw, s.tiles));
+  return EP_OK;
+}
+
+// the plan of a raw container: its payload is copied as it is
+int prepare_raw(const StreamView &s, const void *dev_blob, Plan &P) {
+  if (!dev_blob) {
+    set_error("null device pointer");
+    return EP_ERR_ARG;
+  }
+  P.raw = true;
+  P.dev_blob = dev_blob;
+  P.raw_bytes = (size_t)s.rows * (size_t)s.cols * elem_bytes(s.dtype);
+  return EP_OK;
+}
+
+// enqueues a planned decode into dev_out on stream
+int enqueue(const Plan &P, void *dev_out, hipStream_t stream) {
+  if (!dev_out) {
+    set_error("null device pointer");
+    return EP_ERR_ARG;
+  }
+  if (P.raw) {
+    if (hipMemcpyAsync(dev_out, reinterpret_cast<const uint8_t *>(P.dev_blob) + kHeaderBytes, P.raw_bytes,
+                       hipMemcpyDeviceToDevice, stream) != hipSuccess) {
+      set_error("hipMemcpyAsync failed");
+      return EP_ERR_DEVICE;
+    }
+    return EP_OK;
+  }
+  if ((uintptr_t)dev_out & 15) {
+    set_error("device buffers must be 16-byte aligned");
+    return EP_ERR_ARG;
+  }
   static std::mutex mu;
   static std::vector<KernelFn> configured;
   {
     std::lock_guard<std::mutex> lk(mu);
     bool done = false;
-    for (KernelFn k : configured) done |= k == fn;
+    for (KernelFn k : configured) done |= k == P.fn;
     if (!done) {
-      if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)kLdsLimit) != hipSuccess) {
+      if (hipFuncSetAttribute(P.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit) != hipSuccess) {
         set_error("hipFuncSetAttribute failed");
         return EP_ERR_DEVICE;
       }
-      configured.push_back(fn);
+      configured.push_back(P.fn);
     }
   }
-  A.waves = waves;
-  RoundArgs R;
   void *args[1];
-  if (multi) {
+  RoundArgs R;
+  Args A;
+  if (P.multi) {
+    A = P.R.a;
+    A.out = dev_out;
     args[0] = &A;
   } else {
-    R.a = A;
-    for (uint32_t b = 0; b <= grid; ++b)
-      R.wg_word[b] = first_word(std::min<int64_t>((int64_t)b * waves * tpw, s.tiles));
+    R = P.R;
+    R.a.out = dev_out;
     args[0] = &R;
   }
-  hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(64 * waves), args, lds_bytes, stream);
+  hipError_t err = hipLaunchKernel(P.fn, dim3(P.grid), dim3(P.block), args, P.lds_bytes, stream);
   if (err == hipSuccess) err = hipGetLastError();
   if (err != hipSuccess) {
     set_error(std::string("kernel launch failed: ") + hipGetErrorString(err));
@@ -1171,55 +1228,88 @@ int launch(const uint8_t *hb, const StreamView &s, const void *dev_blob, void *d
   return EP_OK;
 }
 
+// parses a stream and plans its decode into out (an output kind)
+int plan_stream(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, int out_dtype, bool symbols,
+                Plan &P) {
+  StreamView s;
+  std::string e = parse_stream(host_blob, nbytes, s);
+  if (!e.empty()) {
+    set_error(e);
+    return EP_ERR_FORMAT;
+  }
+  if (symbols) {
+    if (s.method != kLattice) {
+      set_error("raw streams hold no lattice symbols");
+      return EP_ERR_ARG;
+    }
+    return prepare(host_blob, s, dev_blob, kOutSym, P);
+  }
+  if (out_dtype != -1 && out_dtype != s.dtype) {
+    set_error("out_dtype must be -1 or the container dtype");
+    return EP_ERR_ARG;
+  }
+  if (s.method == kRaw) return prepare_raw(s, dev_blob, P);
+  return prepare(host_blob, s, dev_blob, s.dtype, P);
+}
+
 }  // namespace
 }  // namespace ep
+
+// a decode plan handed to callers
+struct ep_plan {
+  ep::Plan p;
+};
 
 extern "C" {
 
 int ep_decompress(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, void *dev_out, int out_dtype,
                   void *hip_stream) {
   ep::set_error("");
-  ep::StreamView s;
-  std::string e = ep::parse_stream(host_blob, nbytes, s);
-  if (!e.empty()) {
-    ep::set_error(e);
-    return EP_ERR_FORMAT;
-  }
-  if (out_dtype != -1 && out_dtype != s.dtype) {
-    ep::set_error("out_dtype must be -1 or the container dtype");
-    return EP_ERR_ARG;
-  }
-  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-  if (s.method == ep::kRaw) {
-    if (!dev_blob || !dev_out) {
-      ep::set_error("null device pointer");
-      return EP_ERR_ARG;
-    }
-    const size_t payload = (size_t)s.rows * (size_t)s.cols * ep::elem_bytes(s.dtype);
-    if (hipMemcpyAsync(dev_out, reinterpret_cast<const uint8_t *>(dev_blob) + ep::kHeaderBytes, payload,
-                       hipMemcpyDeviceToDevice, stream) != hipSuccess) {
-      ep::set_error("hipMemcpyAsync failed");
-      return EP_ERR_DEVICE;
-    }
-    return EP_OK;
-  }
-  return ep::launch(host_blob, s, dev_blob, dev_out, s.dtype, stream);
+  ep::Plan P;
+  const int rc = ep::plan_stream(host_blob, nbytes, dev_blob, out_dtype, false, P);
+  if (rc != EP_OK) return rc;
+  return ep::enqueue(P, dev_out, reinterpret_cast<hipStream_t>(hip_stream));
 }
 
 int ep_decode_symbols(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, int16_t *dev_sym,
                       void *hip_stream) {
   ep::set_error("");
-  ep::StreamView s;
-  std::string e = ep::parse_stream(host_blob, nbytes, s);
-  if (!e.empty()) {
-    ep::set_error(e);
-    return EP_ERR_FORMAT;
-  }
-  if (s.method != ep::kLattice) {
-    ep::set_error("raw streams hold no lattice symbols");
+  ep::Plan P;
+  const int rc = ep::plan_stream(host_blob, nbytes, dev_blob, -1, true, P);
+  if (rc != EP_OK) return rc;
+  return ep::enqueue(P, dev_sym, reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+int ep_plan_create(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, int out_dtype, ep_plan **plan_out) {
+  ep::set_error("");
+  if (!plan_out) {
+    ep::set_error("null plan_out");
     return EP_ERR_ARG;
   }
-  return ep::launch(host_blob, s, dev_blob, dev_sym, ep::kOutSym, reinterpret_cast<hipStream_t>(hip_stream));
+  *plan_out = nullptr;
+  ep_plan *h = new (std::nothrow) ep_plan;
+  if (!h) {
+    ep::set_error("out of host memory");
+    return EP_ERR_NOMEM;
+  }
+  const int rc = ep::plan_stream(host_blob, nbytes, dev_blob, out_dtype, false, h->p);
+  if (rc != EP_OK) {
+    delete h;
+    return rc;
+  }
+  *plan_out = h;
+  return EP_OK;
 }
+
+int ep_plan_decompress(const ep_plan *plan, void *dev_out, void *hip_stream) {
+  ep::set_error("");
+  if (!plan) {
+    ep::set_error("null plan");
+    return EP_ERR_ARG;
+  }
+  return ep::enqueue(plan->p, dev_out, reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+void ep_plan_free(ep_plan *plan) { delete plan; }
 
 }  // extern "C"

@@ -29,7 +29,7 @@ _CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
 
 EXPORTS = ["ep_compress", "ep_compress_ex", "ep_compress_device", "ep_compress_device_noalloc", "ep_free",
            "ep_decompress", "ep_decode_symbols", "ep_actual_bpp", "ep_storage_nbytes", "ep_blob_info", "ep_last_error",
-           "ep_last_encode_count"]
+           "ep_last_encode_count", "ep_plan_create", "ep_plan_decompress", "ep_plan_free"]
 
 
 class EPError(RuntimeError):
@@ -90,6 +90,11 @@ def lib() -> ctypes.CDLL:
         L.ep_blob_info.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(_Info)]
         L.ep_last_error.argtypes = []
         L.ep_last_error.restype = ctypes.c_char_p
+        L.ep_plan_create.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                     ctypes.POINTER(ctypes.c_void_p)]
+        L.ep_plan_decompress.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.ep_plan_free.argtypes = [ctypes.c_void_p]
+        L.ep_plan_free.restype = None
         L.ep_last_encode_count.argtypes = []
         L.ep_last_encode_count.restype = ctypes.c_int64
         _lib = L
@@ -230,6 +235,40 @@ def decompress(p: Packed, out: torch.Tensor | None = None, stream=None) -> torch
                              ctypes.c_void_p(out.data_ptr()), -1, ctypes.c_void_p(_stream_handle(stream)))
     _check(rc, "ep_decompress")
     return out
+
+
+class DecodePlan:
+    """ep_plan_create / ep_plan_decompress: a Packed stream's decode with its
+    host-side checks and launch geometry computed once.  Holds a reference to
+    the stream's device copy, which must not be modified while the plan lives."""
+
+    def __init__(self, p: Packed):
+        if p.dev is None:
+            raise EPError(ERR_ARG, "plan", "stream is not on a device; call Packed.to('cuda') first")
+        self.shape, self.dtype, self._dev = p.shape, p.dtype, p.dev
+        h = ctypes.c_void_p()
+        _check(lib().ep_plan_create(_host_ptr(p.blob), p.blob.size, ctypes.c_void_p(p.dev.data_ptr()), -1,
+                                    ctypes.byref(h)), "ep_plan_create")
+        self._h = h
+        self._free = weakref.finalize(self, lib().ep_plan_free, h)
+
+    def decompress(self, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        rows, cols = self.shape
+        if out is None:
+            out = torch.empty(rows, cols, dtype=self.dtype, device=self._dev.device)
+        if out.dtype != self.dtype or tuple(out.shape) != (rows, cols) or not out.is_contiguous():
+            raise EPError(ERR_ARG, "plan.decompress", "out must be a contiguous tensor of the stored shape and dtype")
+        _check(lib().ep_plan_decompress(self._h, ctypes.c_void_p(out.data_ptr()),
+                                        ctypes.c_void_p(_stream_handle(stream))), "ep_plan_decompress")
+        return out
+
+    def close(self) -> None:
+        self._free()
+
+
+def plan(p: Packed) -> DecodePlan:
+    """A decode plan for p (see DecodePlan)."""
+    return DecodePlan(p)
 
 
 def decode_symbols(p: Packed, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

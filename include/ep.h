@@ -175,6 +175,38 @@ int ep_decompress(const uint8_t *host_blob, size_t nbytes, const void *dev_blob,
 int ep_decode_symbols(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, int16_t *dev_sym,
                       void *hip_stream);
 
+/*
+ * Decode plans: ep_decompress with its host work done once per stream.  A
+ * layer that keeps its weights compressed decodes them again on every forward
+ * call (API reference, "CompressedLinear": reconstructed weights are used in
+ * each forward call).  ep_decompress re-reads the stream's header, tables and
+ * every tile offset on each call to check them and to size its launch; a plan
+ * does that once, and each later decode only fills in the output pointer and
+ * enqueues the kernel.
+ *
+ * ep_plan_create -- checks the stream exactly as ep_decompress does and
+ *   records the kernel, its launch geometry and its arguments.
+ *   host_blob, nbytes, dev_blob, out_dtype : as for ep_decompress; the host
+ *                       stream is not read after the call returns.
+ *   plan_out          : receives the plan (NULL on error).
+ *   Returns EP_OK, or the error ep_decompress would return for the same
+ *   stream (EP_ERR_FORMAT, EP_ERR_ARG), or EP_ERR_NOMEM.  Launches and
+ *   allocates nothing on the device; the geometry is sized for the compute
+ *   units of the device current at the call.
+ * ep_plan_decompress -- enqueues the planned decode into dev_out (rows*cols
+ *   container elements, row-major, 16-byte aligned device memory) on
+ *   hip_stream (NULL = default stream).  dev_blob must still hold the same
+ *   bytes and live on the stream's device.  Never allocates and never
+ *   synchronizes; a plan may be used from several threads at once.
+ *   EP_ERR_ARG for a NULL plan or bad dev_out, EP_ERR_DEVICE if the launch fails.
+ * ep_plan_free -- releases a plan; NULL is a no-op.  The caller owns the plan
+ *   and frees it once no call is using it.
+ */
+typedef struct ep_plan ep_plan;
+int ep_plan_create(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, int out_dtype, ep_plan **plan_out);
+int ep_plan_decompress(const ep_plan *plan, void *dev_out, void *hip_stream);
+void ep_plan_free(ep_plan *plan);
+
 /* actual_bpp = 8 * storage_nbytes() / (rows*cols), header included
  * (API reference, "CompressedTensor").  NaN for an invalid stream. */
 double ep_actual_bpp(const uint8_t *blob, size_t nbytes);

@@ -318,3 +318,49 @@ def test_sample_options_match_oracle():
         p = ep.compress(x, 3.0, sample_vecs=sv, seed=seed)
         blob, rc, _ = oracle.compress(x, 3.0, sample_vecs=sv, seed=seed)
         assert np.array_equal(p.blob, blob), (sv, seed)
+
+
+def test_plan_arguments_and_errors():
+    """ep_plan_create checks the stream as ep_decompress does and needs no GPU
+    (it only records the launch); ep_plan_decompress rejects a NULL plan or
+    output before any device call.  The device address below is never
+    dereferenced on the host."""
+    import ctypes
+    L = ep.lib()
+    x, target = W.make("gauss256_bf16_3.5")
+    p = ep.compress(x, target)
+    h, n = p.blob.ctypes.data, p.blob.size
+    fake_dev = ctypes.c_void_p(1 << 20)
+    plan = ctypes.c_void_p()
+    assert L.ep_plan_create(h, n, fake_dev, -1, ctypes.byref(plan)) == ep.OK and plan.value
+    assert L.ep_plan_decompress(plan, None, None) == ep.ERR_ARG
+    assert "null device pointer" in ep.last_error()
+    L.ep_plan_free(plan)
+    L.ep_plan_free(None)
+    assert L.ep_plan_decompress(None, fake_dev, None) == ep.ERR_ARG
+    assert L.ep_plan_create(h, n, fake_dev, -1, None) == ep.ERR_ARG
+    plan = ctypes.c_void_p(123)
+    assert L.ep_plan_create(h, n, None, -1, ctypes.byref(plan)) == ep.ERR_ARG and not plan.value
+    assert L.ep_plan_create(h, n, ctypes.c_void_p((1 << 20) + 2), -1, ctypes.byref(plan)) == ep.ERR_ARG
+    assert L.ep_plan_create(h, n, fake_dev, ep.FP16, ctypes.byref(plan)) == ep.ERR_ARG
+    bad = p.blob.copy()
+    bad[0] ^= 1
+    assert L.ep_plan_create(bad.ctypes.data, n, fake_dev, -1, ctypes.byref(plan)) == ep.ERR_FORMAT
+    # tile offsets out of order: the header parses, the plan's scan rejects it
+    info = ep.blob_info(p.blob)
+    assert info["n_tiles"] >= 2
+    bad = p.blob.copy()
+    toff = int(bad[88:96].view(np.uint64)[0])
+    offs = bad[toff:toff + 4 * (info["n_tiles"] + 1)].view(np.uint32)
+    offs[1] = offs[2] + 1
+    ep.blob_info(bad)
+    assert L.ep_plan_create(bad.ctypes.data, n, fake_dev, -1, ctypes.byref(plan)) == ep.ERR_FORMAT
+    assert "tile offsets" in ep.last_error()
+    # raw containers plan a copy
+    t = torch.zeros(4, 4096, dtype=torch.bfloat16)
+    t[:, 0] = 1.0
+    t[:, 1:] = 1e-3
+    r = ep.compress(t, 10.0)
+    assert r.status == ep.WARN_RAW
+    assert L.ep_plan_create(r.blob.ctypes.data, r.blob.size, fake_dev, -1, ctypes.byref(plan)) == ep.OK
+    L.ep_plan_free(plan)

@@ -76,7 +76,9 @@ DIT = ["dit_0_0", "dit_0_4", "dit_0_5"]
 # 8-bit code containers with padded columns (per-element stores), narrow and
 # wide tables, in one round of workgroups and in the multi-tile kernel
 CODES = ["codes_37_1030_int8_3.0", "codes_37_1030_fp8_3.0", "codes_300_1030_int8_7.0", "codes_2100_8190_int8_3.0",
-         "codes_2100_8190_fp8_7.0"]
+         "codes_2100_8190_fp8_7.0",
+         # unpadded FP8 reconstructions beyond 448 in one round of workgroups
+         "codes_300_1024_fp8_2.0"]
 
 
 @pytest.mark.parametrize("name", WORKLOADS + RAGGED + DIT + CODES)
@@ -165,6 +167,59 @@ def test_device_argument_errors():
                            ctypes.c_void_p(out.data_ptr()), -1, None)
     assert rc == ep.ERR_FORMAT
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["gauss256_bf16_3.5", "absmax8192_int8_3.0", "rowscale4096_bf16_0.2",
+                                  "ragged_64_1032_fp16_1.0", "codes_2100_8190_fp8_7.0"])
+def test_plan_decode_equals_decompress(name):
+    """ep_plan_decompress (geometry and arguments computed once) writes what
+    ep_decompress writes, which equals the oracle's reconstruction: one
+    round of workgroups and the multi-tile kernel, a 16-state stream, padded
+    FP16 columns and 8-bit codes; three calls into different outputs, then
+    five replays of a captured plan decode with eager work between them."""
+    x, blob, _, codes = oracle_case(name)
+    p = gpu_packed(blob)
+    pl = ep.plan(p)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ref = ep.decompress(p, stream=s)
+        outs = [pl.decompress(stream=s) for _ in range(3)]
+    s.synchronize()
+    view = torch.int16 if ref.element_size() == 2 else torch.int8
+    got = ref.cpu().view(view).numpy()
+    if x.dtype in (torch.bfloat16, torch.float16):
+        assert ulp_diff(got.view(np.uint16), codes.view(np.uint16), x.dtype) <= 1
+    else:
+        assert np.array_equal(got.view(np.uint8), codes.view(np.uint8))
+    for o in outs:
+        assert torch.equal(o.view(view), ref.view(view))
+    out = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pl.decompress(out=out, stream=s)
+    for _ in range(5):
+        out.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        s.synchronize()
+        assert torch.equal(out.view(view), ref.view(view))
+        with torch.cuda.stream(s):
+            pl.decompress(stream=s)
+        s.synchronize()
+    pl.close()
+
+
+def test_plan_of_raw_stream():
+    """A raw container's plan copies the payload."""
+    t = torch.zeros(4, 4096, dtype=torch.bfloat16)
+    t[:, 0] = 1.0
+    t[:, 1:] = 1e-3
+    p = ep.compress(t, 10.0).to("cuda")
+    assert p.status == ep.WARN_RAW
+    out = ep.plan(p).decompress()
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), t.view(torch.int16))
 
 
 def test_decode_replays_from_a_graph():
