@@ -59,6 +59,7 @@ PROB_BITS = 10
 N_STATES = 64
 TILE_VECS = 1024
 STATE_L = 1 << 11
+LAYOUT_ROWS, LAYOUT_BLOCKS = 0, 1
 
 
 def build(force: bool = False) -> str:
@@ -86,11 +87,11 @@ def lib():
         L.or_e8_nearest.argtypes = [f64p, i32p]
         L.or_compress.argtypes = [f64p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
                                   ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64,
-                                  ctypes.c_int, ctypes.c_int, P(u8p), P(ctypes.c_size_t), f64p]
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, P(u8p), P(ctypes.c_size_t), f64p]
         L.or_last_encode_count.argtypes = []
         L.or_last_encode_count.restype = ctypes.c_long
         L.or_estimate_bpp.argtypes = [f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int,
-                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int]
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int, ctypes.c_int]
         L.or_estimate_bpp.restype = ctypes.c_double
         L.or_free.argtypes = [ctypes.c_void_p]
         L.or_quantize_matrix.argtypes = [f64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int, f32p,
@@ -152,11 +153,13 @@ def e8_nearest(u) -> np.ndarray:
 
 
 def compress(t, target_bpp: float, fixed_a: float = 0.0, n_states: int = 0, prob_bits: int = PROB_BITS,
-             exact_select: bool = False, tile_vecs: int = 0, sample_vecs: int = 0, seed: int = 0):
+             exact_select: bool = False, tile_vecs: int = 0, sample_vecs: int = 0, seed: int = 0,
+             layout: int = 0):
     """Returns (blob bytes as np.uint8, status, chosen lattice scale a).
     n_states / tile_vecs = 0 pick the tile geometry as the product does (see
     or_compress); sample_vecs = 0 samples 65536 vectors; seed is the sample's
-    phase."""
+    phase; layout LAYOUT_ROWS (row-major tiles) or LAYOUT_BLOCKS (64 x 64
+    weight blocks, BF16 only)."""
     dt, x, raw = _as_container(t)
     if x.ndim != 2:
         raise OracleError(ERR_SHAPE, "compress")
@@ -166,7 +169,7 @@ def compress(t, target_bpp: float, fixed_a: float = 0.0, n_states: int = 0, prob
     a = ctypes.c_double(0.0)
     rc = lib().or_compress(_ptr(x, ctypes.c_double), raw.ctypes.data_as(ctypes.c_void_p), R, C, dt,
                            float(target_bpp), float(fixed_a), n_states, tile_vecs, sample_vecs, seed, prob_bits,
-                           int(exact_select), ctypes.byref(out), ctypes.byref(nb), ctypes.byref(a))
+                           int(exact_select), int(layout), ctypes.byref(out), ctypes.byref(nb), ctypes.byref(a))
     if rc < 0:
         raise OracleError(rc, "compress")
     blob = np.ctypeslib.as_array(out, shape=(nb.value,)).copy()
@@ -183,7 +186,7 @@ def compress_status(x: np.ndarray, dtype: int, target_bpp: float) -> int:
     a = ctypes.c_double(0.0)
     raw = np.zeros(max(1, x.size * 2), np.uint8)
     rc = lib().or_compress(_ptr(x, ctypes.c_double), raw.ctypes.data_as(ctypes.c_void_p), R, C, dtype,
-                           float(target_bpp), 0.0, 0, 0, 0, 0, PROB_BITS, 0, ctypes.byref(out), ctypes.byref(nb),
+                           float(target_bpp), 0.0, 0, 0, 0, 0, PROB_BITS, 0, 0, ctypes.byref(out), ctypes.byref(nb),
                            ctypes.byref(a))
     if rc >= 0:
         lib().or_free(out)
@@ -196,11 +199,11 @@ def last_encode_count() -> int:
 
 
 def estimate_bpp(t, a: float, n_states: int = N_STATES, prob_bits: int = PROB_BITS, tile_vecs: int = TILE_VECS,
-                 sample_vecs: int = 0, seed: int = 0) -> float:
+                 sample_vecs: int = 0, seed: int = 0, layout: int = 0) -> float:
     _, x, _ = _as_container(t)
     R, C = x.shape
     return lib().or_estimate_bpp(_ptr(x, ctypes.c_double), R, C, float(a), n_states, tile_vecs, sample_vecs, seed,
-                                 prob_bits)
+                                 prob_bits, layout)
 
 
 def quantize_matrix(t, a: float, prob_bits: int = PROB_BITS):
@@ -219,12 +222,12 @@ def quantize_matrix(t, a: float, prob_bits: int = PROB_BITS):
 
 def info(blob: np.ndarray) -> dict:
     blob = np.ascontiguousarray(blob, dtype=np.uint8)
-    out = np.zeros(9, np.int64)
+    out = np.zeros(10, np.int64)
     a = ctypes.c_double(0.0)
     rc = lib().or_blob_info(_ptr(blob, ctypes.c_uint8), blob.size, _ptr(out, ctypes.c_int64), ctypes.byref(a))
     if rc:
         raise OracleError(rc, "blob_info")
-    keys = ["rows", "cols", "method", "dtype", "n_states", "n_tiles", "prob_bits", "n_words", "tile_vecs"]
+    keys = ["rows", "cols", "method", "dtype", "n_states", "n_tiles", "prob_bits", "n_words", "tile_vecs", "layout"]
     d = dict(zip(keys, (int(v) for v in out)))
     d["a"] = a.value
     return d

@@ -336,9 +336,32 @@ typedef struct {
   int64_t S;           /* rANS states per tile (16 or 64) */
   int64_t T;           /* tiles */
   int prob_bits;
+  int layout;          /* OR_LAYOUT_ROWS or OR_LAYOUT_BLOCKS */
+  int64_t KB;          /* blocks layout: blocks per block row (ceil(vpr / 8)) */
 } or_geom;
 
-static void geom_init(or_geom *g, int64_t R, int64_t C, int64_t S, int64_t tile_vecs, int prob_bits) {
+/*
+ * Tile layouts.  The pages ask for independently decodable tiles and leave
+ * their shape open.
+ *   OR_LAYOUT_ROWS:   tile t holds vectors t*tile_vecs .. in row-major vector
+ *                     order (the last tile may be partial).
+ *   OR_LAYOUT_BLOCKS: the weight block of rows 64*nb .. 64*nb + 63 and vector
+ *                     columns 8*kb .. 8*kb + 7 (64 columns) is tile
+ *                     t = nb*KB + kb; its local vector i sits at row
+ *                     64*nb + i/8, vector column 8*kb + i%8, and is absent
+ *                     (coded by nobody) where that lies outside the matrix.
+ *                     A matrix product reads W one such block at a time, so a
+ *                     GPU can decode each block straight into the operand of a
+ *                     matrix multiply (API reference, "CompressedLinear":
+ *                     reconstructed weights feed every forward call).  512
+ *                     vectors and 64 states per tile.
+ */
+#define OR_LAYOUT_ROWS 0
+#define OR_LAYOUT_BLOCKS 1
+#define OR_BLOCK_ROWS 64
+#define OR_BLOCK_VECS 8
+
+static void geom_init(or_geom *g, int64_t R, int64_t C, int64_t S, int64_t tile_vecs, int prob_bits, int layout) {
   g->R = R;
   g->C = C;
   g->Cp = (C + 7) / 8 * 8;
@@ -346,8 +369,26 @@ static void geom_init(or_geom *g, int64_t R, int64_t C, int64_t S, int64_t tile_
   g->n_vec = R * g->vpr;
   g->tile_vecs = tile_vecs;
   g->S = S;
-  g->T = (g->n_vec + g->tile_vecs - 1) / g->tile_vecs;
   g->prob_bits = prob_bits;
+  g->layout = layout;
+  g->KB = (g->vpr + OR_BLOCK_VECS - 1) / OR_BLOCK_VECS;
+  if (layout == OR_LAYOUT_BLOCKS)
+    g->T = (R + OR_BLOCK_ROWS - 1) / OR_BLOCK_ROWS * g->KB;
+  else
+    g->T = (g->n_vec + g->tile_vecs - 1) / g->tile_vecs;
+}
+
+/* the global vector index (row * vpr + vector column) of local vector i of
+ * tile t, or -1 where the tile has no such vector */
+static int64_t tile_vector(const or_geom *g, int64_t t, int64_t i) {
+  if (g->layout == OR_LAYOUT_BLOCKS) {
+    int64_t r = (t / g->KB) * OR_BLOCK_ROWS + i / OR_BLOCK_VECS;
+    int64_t k = (t % g->KB) * OR_BLOCK_VECS + i % OR_BLOCK_VECS;
+    if (r >= g->R || k >= g->vpr) return -1;
+    return r * g->vpr + k;
+  }
+  int64_t vid = t * g->tile_vecs + i;
+  return vid < g->n_vec ? vid : -1;
 }
 
 /* bytes of everything except the word section, with section padding */
@@ -444,9 +485,6 @@ static void bits_put(or_bitbuf *bb, uint32_t value, int nbits) {
 /* v: the matrix's lattice coordinates; appends the tile's words to out.
  * Returns OR_WARN_RAW if a pair's word count does not fit its byte. */
 static int encode_tile(const or_geom *g, const or_tables *t, const int32_t *v, int64_t tile, or_words *out) {
-  int64_t first = tile * g->tile_vecs;
-  int64_t n = g->n_vec - first;
-  if (n > g->tile_vecs) n = g->tile_vecs;
   int64_t steps = g->tile_vecs / g->S;
   uint32_t M = 1u << g->prob_bits;
   int S = (int)g->S;
@@ -463,9 +501,8 @@ static int encode_tile(const or_geom *g, const or_tables *t, const int32_t *v, i
   for (int64_t s = steps - 1; s >= 0; s--)
     for (int j = 7; j >= 0; j--)
       for (int q = S - 1; q >= 0; q--) {
-        int64_t i = s * S + q;
-        if (i >= n) continue;
-        int64_t vid = first + i;
+        int64_t vid = tile_vector(g, tile, s * S + q);
+        if (vid < 0) continue;
         int64_t r = vid / g->vpr, k = vid % g->vpr;
         int ctx[8];
         int32_t sym[8];
@@ -569,6 +606,7 @@ static int write_lattice_blob(const or_geom *g, int dtype, double a, double targ
   put_u64(b + 96, o_w);
   put_u64(b + 104, ws->n);
   put_u64(b + 112, total);
+  b[120] = (uint8_t)g->layout;
   uint8_t *p = b + o_tab;
   for (int c = 0; c < OR_NCTX; c++) {
     put_u16(p + 4 * c, (uint32_t)(uint16_t)(int16_t)t->smin[c]);
@@ -843,7 +881,9 @@ static int check_input(const double *x, int64_t R, int64_t C, int dtype, double 
  *   sample_vecs      : 0 (65536) or the rate estimate's sample size;
  *   seed             : the sample's phase (vectors past each stride point);
  *   exact_select != 0: select with a full encode per probe instead of the
- *                      sampled estimate (slow; pins the estimate).
+ *                      sampled estimate (slow; pins the estimate);
+ *   layout           : OR_LAYOUT_ROWS or OR_LAYOUT_BLOCKS (64 x 64 weight
+ *                      blocks; BF16, C % 8 == 0, 64 states, 512 vectors).
  * With the state count chosen, tiles have 64 states, or 16 when a
  * target-selected stream's target is less than 4x the least a 64-state stream
  * costs (64 states would spend over a quarter of the bits on their overhead).  With the tile size chosen, 64-state tiles hold 512 vectors in
@@ -854,10 +894,20 @@ static int check_input(const double *x, int64_t R, int64_t C, int dtype, double 
  */
 int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, int dtype, double target,
                 double fixed_a, int n_states, int64_t tile_vecs, int64_t sample_vecs, uint64_t seed, int prob_bits,
-                int exact_select, uint8_t **blob, size_t *nbytes, double *a_out) {
+                int exact_select, int layout, uint8_t **blob, size_t *nbytes, double *a_out) {
   or_encodes = 0;
   int rc = check_input(x, R, C, dtype, target);
   if (rc) return rc;
+  if (layout != OR_LAYOUT_ROWS && layout != OR_LAYOUT_BLOCKS) return OR_ERR_ARG;
+  if (layout == OR_LAYOUT_BLOCKS) {
+    /* the blocks layout feeds a BF16 matrix multiply: BF16 containers, whole
+     * vectors per row, 64 states and 512 vectors per tile */
+    if (dtype != OR_BF16 || (n_states != 0 && n_states != 64) || (tile_vecs != 0 && tile_vecs != 512))
+      return OR_ERR_ARG;
+    if (C % 8 != 0) return OR_ERR_SHAPE;
+    n_states = 64;
+    tile_vecs = 512;
+  }
   if ((n_states != 0 && n_states != 16 && n_states != 64) ||
       (tile_vecs != 0 && tile_vecs != 512 && tile_vecs != 1024) || sample_vecs < 0 || prob_bits < 8 ||
       prob_bits > 11 || !blob || !nbytes)
@@ -867,18 +917,18 @@ int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, in
   or_geom g;
   if (n_states == 0) {
     int64_t tv = tile_vecs ? tile_vecs : (R * ((C + 7) / 8) < OR_SMALL_MATRIX_VECS ? 512 : 1024);
-    geom_init(&g, R, C, OR_STATES_DEFAULT, tv, prob_bits);
+    geom_init(&g, R, C, OR_STATES_DEFAULT, tv, prob_bits, layout);
     n_states = (chosen && target < 4.0 * floor_bpp(&g)) ? OR_STATES_LOW : OR_STATES_DEFAULT;
   }
   if (tile_vecs == 0) {
     if (n_states == OR_STATES_DEFAULT) {
       tile_vecs = R * ((C + 7) / 8) < OR_SMALL_MATRIX_VECS ? 512 : 1024;
     } else {
-      geom_init(&g, R, C, n_states, 512, prob_bits);
+      geom_init(&g, R, C, n_states, 512, prob_bits, layout);
       tile_vecs = (chosen && target < 1.1 * floor_bpp(&g)) ? 1024 : 512;
     }
   }
-  geom_init(&g, R, C, n_states, tile_vecs, prob_bits);
+  geom_init(&g, R, C, n_states, tile_vecs, prob_bits, layout);
   or_sample sp = {sample_vecs ? sample_vecs : OR_SAMPLE_VECS, seed};
   double a = fixed_a;
   double *rms = NULL;
@@ -946,9 +996,9 @@ int or_compress(const double *x, const void *src_bytes, int64_t R, int64_t C, in
 long or_last_encode_count(void) { return or_encodes; }
 
 double or_estimate_bpp(const double *x, int64_t R, int64_t C, double a, int n_states, int64_t tile_vecs,
-                       int64_t sample_vecs, uint64_t seed, int prob_bits) {
+                       int64_t sample_vecs, uint64_t seed, int prob_bits, int layout) {
   or_geom g;
-  geom_init(&g, R, C, n_states, tile_vecs, prob_bits);
+  geom_init(&g, R, C, n_states, tile_vecs, prob_bits, layout);
   or_sample sp = {sample_vecs ? sample_vecs : OR_SAMPLE_VECS, seed};
   double *rms = (double *)malloc(sizeof(double) * (size_t)R);
   if (!rms) return NAN;
@@ -966,7 +1016,7 @@ int or_quantize_matrix(const double *x, int64_t R, int64_t C, double a, int prob
                        int32_t *v_out) {
   if (!x || R <= 0 || C <= 0 || !g_out || !v_out) return OR_ERR_ARG;
   or_geom g;
-  geom_init(&g, R, C, 64, 1024, prob_bits);
+  geom_init(&g, R, C, 64, 1024, prob_bits, OR_LAYOUT_ROWS);
   for (int64_t r = 0; r < R; r++) g_out[r] = stored_scale(row_rms(x + r * C, C), a);
   for (int64_t r = 0; r < R; r++)
     for (int64_t k = 0; k < g.vpr; k++) quantize_vector(x + r * C, C, k, g_out[r], v_out + r * g.Cp + 8 * k);
@@ -1003,7 +1053,7 @@ static int parse_header(const uint8_t *b, size_t nb, or_header *h) {
   if (h->total != nb) return OR_ERR_FORMAT;
   h->target = get_f64(b + 56);
   if (h->method == 1) {
-    geom_init(&h->g, (int64_t)R, (int64_t)C, 64, 1024, 10);
+    geom_init(&h->g, (int64_t)R, (int64_t)C, 64, 1024, 10, OR_LAYOUT_ROWS);
     h->o_w = get_u64(b + 96);
     if (h->o_w != OR_HDR || !span_ok(OR_HDR, R * C * (uint64_t)esize_of(h->dtype), nb)) return OR_ERR_FORMAT;
     return OR_OK;
@@ -1013,7 +1063,10 @@ static int parse_header(const uint8_t *b, size_t nb, or_header *h) {
   int64_t S = get_u32(b + 16), TV = get_u32(b + 12);
   if ((S != 16 && S != 64) || (TV != 512 && TV != 1024)) return OR_ERR_FORMAT;
   if (R * ((C + 7) / 8) >= ((uint64_t)1 << 31)) return OR_ERR_FORMAT;
-  geom_init(&h->g, (int64_t)R, (int64_t)C, S, TV, pb);
+  int layout = b[120];
+  if (layout > OR_LAYOUT_BLOCKS) return OR_ERR_FORMAT;
+  if (layout == OR_LAYOUT_BLOCKS && (S != 64 || TV != 512 || C % 8 != 0 || h->dtype != OR_BF16)) return OR_ERR_FORMAT;
+  geom_init(&h->g, (int64_t)R, (int64_t)C, S, TV, pb, layout);
   if ((int64_t)get_u64(b + 40) != h->g.Cp || (int64_t)get_u32(b + 20) != h->g.T) return OR_ERR_FORMAT;
   h->a = get_f64(b + 48);
   h->o_tab = get_u64(b + 64);
@@ -1065,9 +1118,6 @@ static int decode_lattice_tiles(const uint8_t *b, const or_header *h, int32_t *v
   int32_t vb[OR_STATES_DEFAULT], zp[OR_STATES_DEFAULT];           /* coset bit, running z sum */
   const uint8_t *words = b + h->o_w;
   for (int64_t tile = t0; tile < t1; tile++) {
-    int64_t first = tile * g->tile_vecs;
-    int64_t n = g->n_vec - first;
-    if (n > g->tile_vecs) n = g->tile_vecs;
     int64_t wp = get_u32(b + h->o_to + 4 * tile);
     int64_t wend = get_u32(b + h->o_to + 4 * (tile + 1));
     int64_t hw = S / 2; /* words of pair counts and length codes */
@@ -1096,8 +1146,8 @@ static int decode_lattice_tiles(const uint8_t *b, const or_header *h, int32_t *v
     for (int64_t s = 0; s < steps; s++)
       for (int j = 0; j < 8; j++) {
         for (int q = 0; q < S; q++) {
-          int64_t i = s * S + q;
-          if (i >= n) continue;
+          int64_t vid = tile_vector(g, tile, s * S + q);
+          if (vid < 0) continue;
           int ctx;
           if (j == 0) ctx = 0;
           else if (j < 7) ctx = 1 + vb[q];
@@ -1114,7 +1164,6 @@ static int decode_lattice_tiles(const uint8_t *b, const or_header *h, int32_t *v
             x[q] = (x[q] << 16) | get_u16(words + 2 * at);
           }
           int32_t sym = t.smin[ctx] + si;
-          int64_t vid = first + i;
           int32_t *vv = v + (vid / g->vpr) * g->Cp + 8 * (vid % g->vpr);
           if (j == 0) {
             vv[0] = sym;
@@ -1284,12 +1333,15 @@ int or_decompress_tiles(const uint8_t *b, size_t nb, int64_t t0, int64_t t1, int
   if (!out || !v_work || h.method != 0 || t0 < 0 || t1 > h.g.T || t0 > t1) return OR_ERR_ARG;
   rc = decode_lattice_tiles(b, &h, v_work, t0, t1);
   if (rc) return rc;
-  int64_t vend = t1 * h.g.tile_vecs < h.g.n_vec ? t1 * h.g.tile_vecs : h.g.n_vec;
-  for (int64_t vid = t0 * h.g.tile_vecs; vid < vend; vid++) {
-    int64_t r = vid / h.g.vpr, c0 = 8 * (vid % h.g.vpr);
-    float g = get_f32(b + h.o_sc + 4 * r);
-    for (int64_t c = c0; c < c0 + 8 && c < h.g.C; c++) store_value(out, h.dtype, r * h.g.C + c, v_work[r * h.g.Cp + c], g);
-  }
+  for (int64_t t = t0; t < t1; t++)
+    for (int64_t i = 0; i < h.g.tile_vecs; i++) {
+      int64_t vid = tile_vector(&h.g, t, i);
+      if (vid < 0) continue;
+      int64_t r = vid / h.g.vpr, c0 = 8 * (vid % h.g.vpr);
+      float g = get_f32(b + h.o_sc + 4 * r);
+      for (int64_t c = c0; c < c0 + 8 && c < h.g.C; c++)
+        store_value(out, h.dtype, r * h.g.C + c, v_work[r * h.g.Cp + c], g);
+    }
   return OR_OK;
 }
 
@@ -1302,7 +1354,7 @@ int or_reconstruct(const int32_t *v, const float *g, int64_t R, int64_t C, int d
   return OR_OK;
 }
 
-/* header fields for tests: rows, cols, method, dtype, S, T, prob_bits, n_words, tile_vecs, a */
+/* header fields for tests: rows, cols, method, dtype, S, T, prob_bits, n_words, tile_vecs, layout, a */
 int or_blob_info(const uint8_t *b, size_t nb, int64_t *i64_out, double *a_out) {
   or_header h;
   int rc = parse_header(b, nb, &h);
@@ -1316,6 +1368,7 @@ int or_blob_info(const uint8_t *b, size_t nb, int64_t *i64_out, double *a_out) {
   i64_out[6] = h.g.prob_bits;
   i64_out[7] = (int64_t)h.n_words;
   i64_out[8] = h.g.tile_vecs;
+  i64_out[9] = h.g.layout;
   *a_out = h.a;
   return OR_OK;
 }
