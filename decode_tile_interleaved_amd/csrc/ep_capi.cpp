@@ -30,6 +30,7 @@ int read_options(const struct ep_options *opt, ep::EncodeOptions &eo, int &threa
   eo.tile_vecs = opt->tile_vecs;
   eo.sample_vecs = opt->sample_vecs;
   eo.seed = opt->seed;
+  eo.layout = opt->layout;
   threads = opt->n_threads;
   if (!(eo.fixed_a >= 0.0) || std::isinf(eo.fixed_a)) {
     ep::set_error("fixed_scale must be finite and >= 0");
@@ -38,6 +39,10 @@ int read_options(const struct ep_options *opt, ep::EncodeOptions &eo, int &threa
   if ((eo.n_states != 0 && eo.n_states != 16 && eo.n_states != 64) ||
       (eo.tile_vecs != 0 && eo.tile_vecs != 512 && eo.tile_vecs != 1024) || eo.sample_vecs < 0) {
     ep::set_error("n_states must be 0, 16 or 64, tile_vecs 0, 512 or 1024, sample_vecs >= 0");
+    return EP_ERR_ARG;
+  }
+  if (eo.layout != EP_LAYOUT_ROWS && eo.layout != EP_LAYOUT_BLOCKS) {
+    ep::set_error("layout must be EP_LAYOUT_ROWS or EP_LAYOUT_BLOCKS");
     return EP_ERR_ARG;
   }
   return 0;
@@ -158,6 +163,7 @@ int ep_blob_info(const uint8_t *blob, size_t nbytes, struct ep_info *info) {
   info->n_words = (int64_t)s.n_words;
   info->scale_a = s.scale_a;
   info->target_bpp = s.target;
+  info->layout = s.layout;
   return EP_OK;
 }
 

@@ -924,6 +924,252 @@ __global__ void __launch_bounds__(64 * kMaxWaves) decode_kernel(RoundArgs R) {
   decode_unit_any<OUT, WIDE, PADDED, true, NS, V>(A, u, parse_start<NS>(u, wt, wt + 2u * (te - tb), lane), gs, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Streams in the blocks layout: each tile is a 64 x 64 block of W (rows
+// 64 nb .., columns 64 kb ..; local vector i at block row i / 8, vector
+// column i % 8), so lane q decodes, at step s, the vector of block row
+// 8 s + q / 8 and vector column q % 8.  A vector of 8 consecutive weights of
+// one row is exactly what one lane supplies to a BF16 matrix-core multiply
+// as its B operand (8 consecutive k of one column n of B = W^T), so the
+// decoded block goes to LDS as it is and feeds the MFMA.
+//
+// Fused linear Y = X W^T (X: M x K BF16, W: N x K in the stream, Y: M x N).
+// A workgroup of 8 waves owns the output block of kLinRows * RB rows of X
+// (RB row-blocks of 16 per wave) and one block row of W (64 output columns):
+//   1. waves 0..6 build the tables (one context each);
+//   2. per chunk of up to 8 consecutive tiles of the block row (512 columns
+//      of K): all waves copy the chunk's words into LDS; wave j decodes tile
+//      j of the chunk, multiplies by the row scales, rounds to BF16 and
+//      writes the block into LDS slot j (64 rows of 144 bytes: 128 of data
+//      and 16 of pad, so the 16 rows one B read touches fall in distinct
+//      banks); then every wave multiplies its rows of X by the chunk's
+//      blocks with v_mfma_f32_16x16x32_bf16, A fragments loaded straight
+//      from global memory (16 bytes of one row of X per lane);
+//   3. the FP32 accumulators go to Y (FP32 or BF16, rounded to nearest even).
+// The same kernel decodes blocks-layout streams for ep_decompress (BF16
+// weights) and ep_decode_symbols (int16 coordinates), one chunk per
+// workgroup, writing each vector to global memory instead of LDS.
+constexpr int kLinWaves = 8;
+constexpr uint32_t kSlotRowBytes = 144;
+constexpr uint32_t kSlotBytes = 64 * kSlotRowBytes;
+constexpr uint32_t kLinMaxChunk = 8;
+enum LinMode : int { kLinGemm = 0, kLinWeights = 1, kLinSymbols = 2 };
+
+struct LinArgs {
+  Args a;                  // tables, scales, tile offsets, words; a.out: weights or symbols (modes 1, 2)
+  const uint16_t *x;       // X, M x K BF16 row-major (GEMM)
+  void *y;                 // Y, M x N (GEMM)
+  uint32_t m, n, k;        // M; N = rows of W; K = columns of W
+  uint32_t kb_n, nb_n;     // blocks per block row (ceil(K / 64)); block rows (ceil(N / 64))
+  uint32_t chunks;         // chunks per block row: ceil(kb_n / chunk)
+  uint32_t chunk;          // tiles per chunk (at most 8, as the LDS allows)
+  uint32_t mb_n;           // GEMM: workgroups along M
+  uint32_t slots_off;      // LDS byte offset of the block slots
+  uint32_t y_f32;          // GEMM: Y is FP32 (1) or BF16 (0)
+  uint32_t grid;           // workgroups
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 *lds_u128_wptr;
+typedef __attribute__((address_space(3))) const u32x4 *lds_u128_rptr;
+
+// Workgroup b runs on XCD b % 8 (round-robin dispatch).  The logical index
+// gives each XCD a contiguous run, so that the workgroups sharing one XCD's
+// L2 share their rows of X (consecutive logical indices differ in the block
+// row of W only).
+__device__ __forceinline__ uint32_t xcd_logical(uint32_t b, uint32_t grid) {
+  const uint32_t q = grid / 8u, r = grid % 8u, x = b % 8u, j = b / 8u;
+  return x < r ? x * (q + 1u) + j : r * (q + 1u) + (x - r) * q + j;
+}
+
+// Decodes one block tile whose words are at LDS [wt, we): 8 steps, each
+// giving the lane's vector of block row 8 s + lane / 8 to sink(s, act, e).
+// present: bit s set where that vector exists (absent vectors come last in
+// a lane's sequence: rows past the matrix, or a vector column past it).
+template <bool WIDE, class Sink>
+__device__ __forceinline__ void decode_block(uint32_t wt, uint32_t we, uint32_t lane, uint32_t present, Sink &&sink) {
+  UnitLane u{};
+  u.q = lane;
+  const Start S0 = parse_start<64>(u, wt, we, lane);
+  Lane L = S0.L;
+  table_read<0u>(S0.X & 0x1ff8u, L.d0, L.d1);  // context F
+  L.q = S0.X >> 13;
+  constexpr uint32_t kC = kCtxBytes, kE = 3u * kCtxBytes;
+  constexpr uint32_t kBitB = WIDE ? 16u : 24u;
+#pragma unroll
+  for (uint32_t s = 0; s < 8; ++s) {
+    const bool act = (present >> s) & 1u;
+    uint32_t e[8];
+    const uint32_t cb = __builtin_amdgcn_ubfe(L.d0, kBitB, 1u) << 13;
+    e[0] = rans_step<WIDE, kC, true>(L, cb, act);
+#pragma unroll
+    for (int j = 1; j < 6; ++j) e[j] = rans_step<WIDE, kC, true>(L, cb, act);
+    uint32_t acc = __builtin_amdgcn_bitop3_b32(e[0], e[1], e[2], 0x96);
+    acc = __builtin_amdgcn_bitop3_b32(acc, e[3], e[4], 0x96);
+    acc = __builtin_amdgcn_bitop3_b32(acc, e[5], L.d0, 0x96);
+    const uint32_t eb = __builtin_amdgcn_ubfe(acc, kBitB, 2u) << 13;
+    e[6] = rans_step<WIDE, kE, true>(L, eb, act);
+    e[7] = rans_step<WIDE, 0u, true>(L, 0u, act);
+    sink(s, act, e);
+  }
+}
+
+// the 8 weights of a decoded vector as BF16, 16 bytes (zeros if absent)
+template <bool WIDE>
+__device__ __forceinline__ u32x4 block_weights(const uint32_t (&e)[8], float g, bool act) {
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = entry_weight<WIDE>(e[j], g);
+  u32x4 pk = {pack2<EP_BF16>(y[0], y[1]), pack2<EP_BF16>(y[2], y[3]), pack2<EP_BF16>(y[4], y[5]),
+              pack2<EP_BF16>(y[6], y[7])};
+  if (!act) pk = u32x4{0u, 0u, 0u, 0u};
+  return pk;
+}
+
+// RB: 16-row blocks of X per wave (GEMM)
+template <int MODE, bool WIDE, int RB>
+__global__ void __launch_bounds__(64 * kLinWaves) linear_kernel(LinArgs P) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const Args &A = P.a;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t L = xcd_logical(blockIdx.x, P.grid);
+  uint32_t nb, mb, c_begin, c_end;
+  if constexpr (MODE == kLinGemm) {
+    mb = L / P.nb_n;
+    nb = L - mb * P.nb_n;
+    c_begin = 0u;
+    c_end = P.chunks;
+  } else {
+    nb = L / P.chunks;
+    mb = 0u;
+    c_begin = L - nb * P.chunks;
+    c_end = c_begin + 1u;
+  }
+  // the tables (waves 0..6, one context each)
+  if (wave < (uint32_t)kContexts) {
+    uint32_t fpre[4];
+    first_frequencies(A, wave, lane, fpre);
+    build_tables<WIDE>(A, lds, wave, lane, (uint32_t)kContexts, fpre);
+  }
+  // the lane's block rows 8 s + lane / 8 and their scales (the last row's
+  // past the matrix; those vectors are absent)
+  const uint32_t r0 = 64u * nb + (lane >> 3), vcol = lane & 7u;
+  float gs[8];
+#pragma unroll
+  for (uint32_t s = 0; s < 8; ++s) gs[s] = A.scales[min(r0 + 8u * s, A.rows - 1u)];
+  uint32_t present_rows = 0;
+#pragma unroll
+  for (uint32_t s = 0; s < 8; ++s) present_rows |= (r0 + 8u * s < A.rows ? 1u : 0u) << s;
+
+  constexpr int kCb = 4;  // 16-column blocks of the 64 output columns
+  f32x4 acc[RB][kCb];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < kCb; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t m0 = (mb * (uint32_t)kLinWaves + wave) * 16u * (uint32_t)RB;  // the wave's first row of X
+
+  typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
+  const cptr_u32 toff = (cptr_u32)A.toff;
+  for (uint32_t c = c_begin; c < c_end; ++c) {
+    const uint32_t kb0 = c * P.chunk, nt = min(P.chunk, P.kb_n - kb0);
+    const uint32_t t0 = nb * P.kb_n + kb0;
+    const uint32_t p0 = first_piece(toff[t0]), p1 = end_piece(toff[t0 + nt]);
+    lds_barrier();  // tables built; the slots and words of the last chunk are no longer read
+    copy_pieces(A, lds, p0, p1, A.words_off, lane, wave, (uint32_t)kLinWaves);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();  // the chunk's words are in LDS
+    if (wave < nt) {
+      const uint32_t t = t0 + wave;
+      const uint32_t tb = toff[t], te = toff[t + 1u];
+      const uint32_t wt = A.words_off + 2u * tb - 16u * p0;
+      const uint32_t kv = 8u * (kb0 + wave) + vcol;  // the lane's vector column in W
+      const uint32_t present = kv < A.vpr ? present_rows : 0u;
+      if constexpr (MODE == kLinGemm) {
+        const uint32_t slot = P.slots_off + wave * kSlotBytes + (lane >> 3) * kSlotRowBytes + 16u * vcol;
+        decode_block<WIDE>(wt, wt + 2u * (te - tb), lane, present, [&](uint32_t s, bool act, const uint32_t(&e)[8]) {
+          *(lds_u128_wptr)(uintptr_t)(slot + 8u * s * kSlotRowBytes) = block_weights<WIDE>(e, gs[s], act);
+        });
+      } else if constexpr (MODE == kLinWeights) {
+        decode_block<WIDE>(wt, wt + 2u * (te - tb), lane, present, [&](uint32_t s, bool act, const uint32_t(&e)[8]) {
+          if (act) {
+            const uint64_t at = (uint64_t)(r0 + 8u * s) * A.cols + 8ull * kv;
+            __builtin_nontemporal_store(block_weights<WIDE>(e, gs[s], true),
+                                        (__attribute__((address_space(1))) u32x4 *)((uint16_t *)A.out + at));
+          }
+        });
+      } else {
+        decode_block<WIDE>(wt, wt + 2u * (te - tb), lane, present, [&](uint32_t s, bool act, const uint32_t(&e)[8]) {
+          if (act) {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              w[k] = ((uint32_t)entry_value<WIDE>(e[2 * k]) & 0xffffu) | ((uint32_t)entry_value<WIDE>(e[2 * k + 1]) << 16);
+            const uint64_t at = (uint64_t)(r0 + 8u * s) * (8ull * A.vpr) + 8ull * kv;
+            __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
+                                        (__attribute__((address_space(1))) u32x4 *)((int16_t *)A.out + at));
+          }
+        });
+      }
+    }
+    if constexpr (MODE == kLinGemm) {
+      lds_barrier();  // the chunk's blocks are in their slots
+      // lane's fragments: A row m0 + 16 i + lane % 16, k 8 (lane / 16) ..;
+      // B column (W row) 16 j + lane % 16 of the block, same k
+      const uint32_t lr = lane & 15u, lk = lane >> 4;
+      for (uint32_t sl = 0; sl < nt; ++sl) {
+#pragma unroll
+        for (uint32_t kh = 0; kh < 2u; ++kh) {
+          const uint32_t kg = 64u * (kb0 + sl) + 32u * kh + 8u * lk;  // global k of the lane's 8 values
+          u32x4 a[RB];
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const uint32_t row = m0 + 16u * (uint32_t)i + lr;
+            const bool ok = row < P.m && kg < P.k;
+            const uint64_t at = ok ? (uint64_t)row * P.k + kg : 0ull;
+            a[i] = *(const __attribute__((address_space(1))) u32x4 *)(P.x + at);
+            if (!ok) a[i] = u32x4{0u, 0u, 0u, 0u};
+          }
+          u32x4 b[kCb];
+#pragma unroll
+          for (int j = 0; j < kCb; ++j)
+            b[j] = *(lds_u128_rptr)(uintptr_t)(P.slots_off + sl * kSlotBytes + (16u * (uint32_t)j + lr) * kSlotRowBytes +
+                                               16u * (4u * kh + lk));
+#pragma unroll
+          for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < kCb; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                                  __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if constexpr (MODE == kLinGemm) {
+    // lane holds D[4 (lane / 16) + r][lane % 16] of each 16 x 16 block
+    const uint32_t lr = lane & 15u, lk = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < kCb; ++j) {
+      const uint32_t col = 64u * nb + 16u * (uint32_t)j + lr;
+      if (col >= P.n) continue;
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (uint32_t r = 0; r < 4u; ++r) {
+          const uint32_t row = m0 + 16u * (uint32_t)i + 4u * lk + r;
+          if (row >= P.m) continue;
+          const uint64_t at = (uint64_t)row * P.n + col;
+          if (P.y_f32)
+            reinterpret_cast<float *>(P.y)[at] = acc[i][j][r];
+          else
+            reinterpret_cast<uint16_t *>(P.y)[at] = (uint16_t)(pack2<EP_BF16>(acc[i][j][r], 0.0f) & 0xffffu);
+        }
+    }
+  }
+}
+
 typedef const void *KernelFn;  // a kernel's address: decode_waves_kernel takes Args, decode_kernel RoundArgs
 
 template <int OUT, bool WIDE, bool PADDED, int NS, int V>
@@ -1003,20 +1249,13 @@ struct Plan {
   uint32_t grid = 0, block = 0, lds_bytes = 0;
   bool multi = false;      // multi-tile kernel: its argument is R.a alone
   RoundArgs R{};
+  bool blocks = false;     // blocks layout: linear_kernel in a weights or symbols mode, argument L
+  LinArgs L{};
 };
 
-// host-side checks and launch geometry; returns 0 or an ep_status
-int prepare(const uint8_t *hb, const StreamView &s, const void *dev_blob, int out, Plan &P) {
-  if (!dev_blob) {
-    set_error("null device pointer");
-    return EP_ERR_ARG;
-  }
-  if ((uintptr_t)dev_blob & 15) {
-    set_error("device buffers must be 16-byte aligned");
-    return EP_ERR_ARG;
-  }
-  // tile offsets: monotone, inside the word section, room for the pair counts
-  // and length codes
+// Tile offsets: monotone, inside the word section, room for the pair counts
+// and length codes.  Returns 0 or EP_ERR_FORMAT.
+int check_tile_offsets(const uint8_t *hb, const StreamView &s) {
   const uint8_t *toff = hb + s.off_tile_offsets;
   auto first_word = [&](int64_t t) { return rd<uint32_t>(toff + 4 * t); };
   for (int64_t t = 0; t < s.tiles; ++t) {
@@ -1030,10 +1269,15 @@ int prepare(const uint8_t *hb, const StreamView &s, const void *dev_blob, int ou
     set_error("corrupt tile offsets");
     return EP_ERR_FORMAT;
   }
-  // tables: frequencies sum to 2^10, used values inside the entry field
-  Args A{};
-  bool wide = false;
-  uint32_t nz_total = 0;
+  return EP_OK;
+}
+
+// Tables: frequencies sum to 2^10, used values inside the entry field; fills
+// the table fields of A.  wide: some used value lies outside [-128, 127].
+// Returns 0 or EP_ERR_FORMAT.
+int check_tables(const uint8_t *hb, const StreamView &s, Args &A, bool &wide, uint32_t &nz_total) {
+  wide = false;
+  nz_total = 0;
   for (int c = 0; c < kContexts; ++c) {
     A.smin[c] = s.smin[c];
     // symbol counts and frequency indexes share a word per context: 16 bits
@@ -1062,6 +1306,26 @@ int prepare(const uint8_t *hb, const StreamView &s, const void *dev_blob, int ou
       return EP_ERR_FORMAT;
     }
   }
+  return EP_OK;
+}
+
+// host-side checks and launch geometry; returns 0 or an ep_status
+int prepare(const uint8_t *hb, const StreamView &s, const void *dev_blob, int out, Plan &P) {
+  if (!dev_blob) {
+    set_error("null device pointer");
+    return EP_ERR_ARG;
+  }
+  if ((uintptr_t)dev_blob & 15) {
+    set_error("device buffers must be 16-byte aligned");
+    return EP_ERR_ARG;
+  }
+  if (const int rc = check_tile_offsets(hb, s); rc != EP_OK) return rc;
+  const uint8_t *toff = hb + s.off_tile_offsets;
+  auto first_word = [&](int64_t t) { return rd<uint32_t>(toff + 4 * t); };
+  Args A{};
+  bool wide = false;
+  uint32_t nz_total = 0;
+  if (const int rc = check_tables(hb, s, A, wide, nz_total); rc != EP_OK) return rc;
   // LDS layout: tables | records | bitmap | row descriptors | words | pad.
   // A wave decodes a unit of 64 / states consecutive tiles; the words of a
   // workgroup's consecutive units are one range, copied in whole kilobytes
@@ -1175,6 +1439,136 @@ int prepare_raw(const StreamView &s, const void *dev_blob, Plan &P) {
   return EP_OK;
 }
 
+template <int MODE, bool WIDE>
+KernelFn pick_linear_rb(int rb) {
+  if (rb == 1) return (KernelFn)linear_kernel<MODE, WIDE, 1>;
+  if (rb == 2) return (KernelFn)linear_kernel<MODE, WIDE, 2>;
+  return (KernelFn)linear_kernel<MODE, WIDE, 4>;
+}
+KernelFn pick_linear(int mode, bool wide, int rb) {
+  if (mode == kLinGemm) return wide ? pick_linear_rb<kLinGemm, true>(rb) : pick_linear_rb<kLinGemm, false>(rb);
+  if (mode == kLinWeights)
+    return wide ? (KernelFn)linear_kernel<kLinWeights, true, 1> : (KernelFn)linear_kernel<kLinWeights, false, 1>;
+  return wide ? (KernelFn)linear_kernel<kLinSymbols, true, 1> : (KernelFn)linear_kernel<kLinSymbols, false, 1>;
+}
+
+// Plans linear_kernel on a blocks-layout stream: the tables and tile offsets
+// checked, the LDS layout (tables | table-build scratch, later the chunk's
+// words | pad | block slots), the chunk size (up to 8 tiles, as many as the
+// LDS holds for the stream's largest chunk) and the grid.  GEMM: one
+// workgroup per (row block of X, block row of W), every chunk; weights and
+// symbols: one workgroup per chunk.  rb: 16-row blocks of X per wave.
+int prepare_linear(const uint8_t *hb, const StreamView &s, const void *dev_blob, int mode, int64_t m, int rb,
+                   LinArgs &L, KernelFn &fn, uint32_t &grid, uint32_t &lds_bytes) {
+  if (!dev_blob) {
+    set_error("null device pointer");
+    return EP_ERR_ARG;
+  }
+  if ((uintptr_t)dev_blob & 15) {
+    set_error("device buffers must be 16-byte aligned");
+    return EP_ERR_ARG;
+  }
+  if (const int rc = check_tile_offsets(hb, s); rc != EP_OK) return rc;
+  Args A{};
+  bool wide = false;
+  uint32_t nz_total = 0;
+  if (const int rc = check_tables(hb, s, A, wide, nz_total); rc != EP_OK) return rc;
+  const uint8_t *toff = hb + s.off_tile_offsets;
+  auto first_word = [&](int64_t t) { return rd<uint32_t>(toff + 4 * t); };
+  uint32_t off = kTableBytes;
+  A.rec_off = off;
+  off += 8 * nz_total;
+  A.mark_off = off;
+  off = (uint32_t)align16(off + 4 * kContexts * kMarkWords);
+  A.desc_off = off;
+  off += 256 * kContexts;
+  const uint32_t build_end = off;
+  A.words_off = kTableBytes;  // the build's scratch is dead once the first chunk is copied
+  const int64_t vpr = s.cols8 / 8, kb_n = (vpr + kBlockVecs - 1) / kBlockVecs, nb_n = (s.rows + kBlockRows - 1) / kBlockRows;
+  auto copy_bytes = [&](int64_t t0, int64_t t1) {
+    const uint64_t a0 = (s.off_words + 2ull * first_word(t0)) & ~15ull;
+    const uint64_t a1 = (s.off_words + 2ull * first_word(t1) + 15ull) & ~15ull;
+    return (a1 - a0 + 1023ull) & ~1023ull;
+  };
+  uint32_t chunk = 0;
+  uint64_t wbuf = 0, need = 0, slots_off = 0;
+  for (int64_t ch = kLinMaxChunk; ch >= 1; --ch) {
+    wbuf = 0;
+    for (int64_t nb = 0; nb < nb_n; ++nb)
+      for (int64_t k0 = 0; k0 < kb_n; k0 += ch)
+        wbuf = std::max<uint64_t>(wbuf, copy_bytes(nb * kb_n + k0, nb * kb_n + std::min<int64_t>(k0 + ch, kb_n)));
+    slots_off = align16(A.words_off + wbuf + kLdsPad);
+    need = std::max<uint64_t>(build_end, mode == kLinGemm ? slots_off + (uint64_t)ch * kSlotBytes : slots_off);
+    if (need <= kLdsLimit) {
+      chunk = (uint32_t)ch;
+      break;
+    }
+  }
+  if (!chunk) {
+    set_error("tile too large for the fused decoder's LDS budget");
+    return EP_ERR_FORMAT;
+  }
+  const uint8_t *db = reinterpret_cast<const uint8_t *>(dev_blob);
+  A.freq = reinterpret_cast<const uint16_t *>(db + s.off_freq);
+  A.toff = reinterpret_cast<const uint32_t *>(db + s.off_tile_offsets);
+  A.words = db + s.off_words;
+  A.scales = reinterpret_cast<const float *>(db + s.off_scales);
+  A.cols = (uint64_t)s.cols;
+  A.rows = (uint32_t)s.rows;
+  A.vpr = (uint32_t)vpr;
+  A.n_tiles = (uint32_t)s.tiles;
+  A.waves = kLinWaves;
+  L = LinArgs{};
+  L.a = A;
+  L.n = (uint32_t)s.rows;
+  L.k = (uint32_t)s.cols;
+  L.kb_n = (uint32_t)kb_n;
+  L.nb_n = (uint32_t)nb_n;
+  L.chunk = chunk;
+  L.chunks = (uint32_t)((kb_n + chunk - 1) / chunk);
+  L.slots_off = (uint32_t)slots_off;
+  const uint64_t rows_per_wg = (uint64_t)kLinWaves * 16u * (uint64_t)rb;
+  L.m = (uint32_t)m;
+  L.mb_n = mode == kLinGemm ? (uint32_t)(((uint64_t)m + rows_per_wg - 1) / rows_per_wg) : 1u;
+  const uint64_t g = mode == kLinGemm ? (uint64_t)L.mb_n * (uint64_t)nb_n : (uint64_t)nb_n * L.chunks;
+  if (g == 0 || g > 0x7fffffffull) {
+    set_error("grid too large");
+    return EP_ERR_SHAPE;
+  }
+  L.grid = (uint32_t)g;
+  grid = L.grid;
+  lds_bytes = (uint32_t)need;
+  fn = pick_linear(mode, wide, rb);
+  return EP_OK;
+}
+
+// launches a planned linear_kernel
+int launch_linear(KernelFn fn, const LinArgs &L, uint32_t grid, uint32_t lds_bytes, hipStream_t stream) {
+  static std::mutex mu;
+  static std::vector<KernelFn> configured;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    bool done = false;
+    for (KernelFn k : configured) done |= k == fn;
+    if (!done) {
+      if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit) != hipSuccess) {
+        set_error("hipFuncSetAttribute failed");
+        return EP_ERR_DEVICE;
+      }
+      configured.push_back(fn);
+    }
+  }
+  LinArgs a = L;
+  void *args[1] = {&a};
+  hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(64 * kLinWaves), args, lds_bytes, stream);
+  if (err == hipSuccess) err = hipGetLastError();
+  if (err != hipSuccess) {
+    set_error(std::string("kernel launch failed: ") + hipGetErrorString(err));
+    return EP_ERR_DEVICE;
+  }
+  return EP_OK;
+}
+
 // enqueues a planned decode into dev_out on stream
 int enqueue(const Plan &P, void *dev_out, hipStream_t stream) {
   if (!dev_out) {
@@ -1192,6 +1586,11 @@ int enqueue(const Plan &P, void *dev_out, hipStream_t stream) {
   if ((uintptr_t)dev_out & 15) {
     set_error("device buffers must be 16-byte aligned");
     return EP_ERR_ARG;
+  }
+  if (P.blocks) {
+    LinArgs L = P.L;
+    L.a.out = dev_out;
+    return launch_linear(P.fn, L, P.grid, P.lds_bytes, stream);
   }
   static std::mutex mu;
   static std::vector<KernelFn> configured;
@@ -1242,6 +1641,10 @@ int plan_stream(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, i
       set_error("raw streams hold no lattice symbols");
       return EP_ERR_ARG;
     }
+    if (s.layout == kLayoutBlocks) {
+      P.blocks = true;
+      return prepare_linear(host_blob, s, dev_blob, kLinSymbols, 0, 1, P.L, P.fn, P.grid, P.lds_bytes);
+    }
     return prepare(host_blob, s, dev_blob, kOutSym, P);
   }
   if (out_dtype != -1 && out_dtype != s.dtype) {
@@ -1249,6 +1652,10 @@ int plan_stream(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, i
     return EP_ERR_ARG;
   }
   if (s.method == kRaw) return prepare_raw(s, dev_blob, P);
+  if (s.layout == kLayoutBlocks) {
+    P.blocks = true;
+    return prepare_linear(host_blob, s, dev_blob, kLinWeights, 0, 1, P.L, P.fn, P.grid, P.lds_bytes);
+  }
   return prepare(host_blob, s, dev_blob, s.dtype, P);
 }
 
@@ -1311,5 +1718,47 @@ int ep_plan_decompress(const ep_plan *plan, void *dev_out, void *hip_stream) {
 }
 
 void ep_plan_free(ep_plan *plan) { delete plan; }
+
+int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, const void *dev_x, int64_t m,
+              void *dev_y, int y_dtype, void *hip_stream) {
+  ep::set_error("");
+  ep::StreamView s;
+  std::string e = ep::parse_stream(host_blob, nbytes, s);
+  if (!e.empty()) {
+    ep::set_error(e);
+    return EP_ERR_FORMAT;
+  }
+  if (s.method != ep::kLattice || s.layout != ep::kLayoutBlocks) {
+    ep::set_error("ep_linear takes lattice streams in the blocks layout (EP_LAYOUT_BLOCKS)");
+    return EP_ERR_ARG;
+  }
+  if (y_dtype != EP_BF16 && y_dtype != EP_F32) {
+    ep::set_error("y_dtype must be EP_BF16 or EP_F32");
+    return EP_ERR_ARG;
+  }
+  if (m < 0 || m >= (int64_t(1) << 31) || (uint64_t)m * (uint64_t)s.rows >= (uint64_t(1) << 62)) {
+    ep::set_error("m must lie in [0, 2^31)");
+    return EP_ERR_SHAPE;
+  }
+  if (m == 0) return EP_OK;
+  if (!dev_x || !dev_y) {
+    ep::set_error("null device pointer");
+    return EP_ERR_ARG;
+  }
+  if (((uintptr_t)dev_x & 15) || ((uintptr_t)dev_y & 3)) {
+    ep::set_error("dev_x must be 16-byte aligned, dev_y 4-byte aligned");
+    return EP_ERR_ARG;
+  }
+  const int rb = m > 512 ? 4 : (m > 128 ? 2 : 1);
+  ep::LinArgs L;
+  ep::KernelFn fn = nullptr;
+  uint32_t grid = 0, lds = 0;
+  const int rc = ep::prepare_linear(host_blob, s, dev_blob, ep::kLinGemm, m, rb, L, fn, grid, lds);
+  if (rc != EP_OK) return rc;
+  L.x = reinterpret_cast<const uint16_t *>(dev_x);
+  L.y = dev_y;
+  L.y_f32 = y_dtype == EP_F32 ? 1u : 0u;
+  return ep::launch_linear(fn, L, grid, lds, reinterpret_cast<hipStream_t>(hip_stream));
+}
 
 }  // extern "C"

@@ -308,7 +308,7 @@ class HostBackend final : public EncodeBackend {
         return EP_ERR_ARG;
       }
     }
-    const int64_t tiles = (S_.n_vec + tile_vecs_ - 1) / tile_vecs_;
+    const int64_t tiles = tile_count(layout_, S_.R, S_.vpr, tile_vecs_);
     tiles_.assign((size_t)tiles, TileOut{});
     parallel_for(tiles, std::max(1, threads_), [&](int64_t b, int64_t e) {
       for (int64_t t = b; t < e; ++t) encode_tile(tb, t, tiles_[(size_t)t]);
@@ -387,12 +387,13 @@ class HostBackend final : public EncodeBackend {
   // tile as the stream stores it (pair counts, length codes, start bits,
   // pair regions)
   void encode_tile(const Tables &tb, int64_t tile, TileOut &out) const {
-    const int64_t first = tile * tile_vecs_;
-    const int n = (int)std::min<int64_t>(tile_vecs_, S_.n_vec - first);
-    // (frequency, cumulative) of every coordinate, vector-major
-    std::vector<uint32_t> fc((size_t)n * 8 * 2);
+    // (frequency, cumulative) of every coordinate, vector-major; absent
+    // vectors (past the matrix) are marked by frequency 0
+    const int n = tile_vecs_;
+    std::vector<uint32_t> fc((size_t)n * 8 * 2, 0u);
     for (int i = 0; i < n; ++i) {
-      int64_t vid = first + i;
+      const int64_t vid = tile_vector(layout_, S_.R, S_.vpr, tile_vecs_, tile, i);
+      if (vid < 0) continue;
       const int32_t *v = &V_[(size_t)((vid / S_.vpr) * S_.C8 + 8 * (vid % S_.vpr))];
       Coded cd = model(v);
       for (int j = 0; j < 8; ++j) {
@@ -413,8 +414,8 @@ class HostBackend final : public EncodeBackend {
       for (int j = 7; j >= 0; --j)
         for (int q = S - 1; q >= 0; --q) {
           int i = s * S + q;
-          if (i >= n) continue;
           uint32_t f = fc[(size_t)(i * 8 + j) * 2], c = fc[(size_t)(i * 8 + j) * 2 + 1];
+          if (f == 0) continue;  // no vector here
           uint32_t st = x[q];
           if ((uint64_t)st >= ((uint64_t)f << (kStateTop - kProbBits))) {
             emitted.push_back((uint16_t)st);
@@ -609,6 +610,7 @@ int encode_at(const Problem &P, double a, double target, Blob &blob, std::string
   wr<uint64_t>(b + hdr::off_words, o_w);
   wr<uint64_t>(b + hdr::n_words, n_words);
   wr<uint64_t>(b + hdr::total, total);
+  b[hdr::layout] = (uint8_t)S.layout;
   uint8_t *p = b + o_tab + 4 * kContexts;
   for (int c = 0; c < kContexts; ++c) {
     wr<int16_t>(b + o_tab + 4 * c, tb.smin[c]);
@@ -687,26 +689,43 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, co
   g_encodes = 0;
   if ((opt.n_states != 0 && opt.n_states != kStatesLow && opt.n_states != kStatesPerTile) ||
       (opt.tile_vecs != 0 && opt.tile_vecs != kTileVecsSmall && opt.tile_vecs != kTileVecsLarge) ||
-      opt.sample_vecs < 0 || !(opt.fixed_a >= 0.0) || std::isinf(opt.fixed_a)) {
+      opt.sample_vecs < 0 || !(opt.fixed_a >= 0.0) || std::isinf(opt.fixed_a) ||
+      (opt.layout != kLayoutRows && opt.layout != kLayoutBlocks)) {
     err = "invalid ep_options";
     return EP_ERR_ARG;
   }
-  Problem P{shape, &be, {}, opt.sample_vecs ? opt.sample_vecs : kSampleVecs, opt.seed};
+  EncodeOptions o = opt;
+  if (o.layout == kLayoutBlocks) {
+    // the blocks layout feeds the fused linear's BF16 matrix multiply
+    if (shape.dtype != EP_BF16 || (o.n_states != 0 && o.n_states != kStatesPerTile) ||
+        (o.tile_vecs != 0 && o.tile_vecs != kTileVecsSmall)) {
+      err = "the blocks layout takes BF16 matrices with 64-state, 512-vector tiles";
+      return EP_ERR_ARG;
+    }
+    if (shape.C % 8 != 0) {
+      err = "the blocks layout needs cols % 8 == 0";
+      return EP_ERR_SHAPE;
+    }
+    o.n_states = kStatesPerTile;
+    o.tile_vecs = kTileVecsSmall;
+  }
+  Problem P{shape, &be, {}, o.sample_vecs ? o.sample_vecs : kSampleVecs, o.seed};
   EncodeShape &S = P.S;
-  const bool chosen = !(opt.fixed_a > 0.0);
+  S.layout = o.layout;
+  const bool chosen = !(o.fixed_a > 0.0);
   // Tile geometry.  64 states per tile, or 16 when a target-selected
   // stream's target is less than 4x the least a 64-state stream costs (64
   // would spend over a quarter of the bits on their overhead).  64-state
   // tiles hold 512 vectors in matrices of fewer than 2^22 vectors (twice the
   // states decoding in parallel), else 1024; 16-state tiles hold 512, or
   // 1024 when the target lies below 1.1x the least 512 allow.
-  const int tv64 = opt.tile_vecs ? opt.tile_vecs : (S.n_vec < kSmallMatrixVecs ? kTileVecsSmall : kTileVecsLarge);
-  int states = opt.n_states;
+  const int tv64 = o.tile_vecs ? o.tile_vecs : (S.n_vec < kSmallMatrixVecs ? kTileVecsSmall : kTileVecsLarge);
+  int states = o.n_states;
   if (!states) {
     S.set_tiles(kStatesPerTile, tv64);
     states = (chosen && target < 4.0 * floor_bpp(S)) ? kStatesLow : kStatesPerTile;
   }
-  int tile_vecs = opt.tile_vecs;
+  int tile_vecs = o.tile_vecs;
   if (!tile_vecs) {
     if (states == kStatesPerTile) {
       tile_vecs = tv64;
@@ -716,7 +735,7 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, co
     }
   }
   S.set_tiles(states, tile_vecs);
-  be.set_geometry(states, tile_vecs);
+  be.set_geometry(states, tile_vecs, S.layout);
   // finiteness and row RMS (sequential sum per row)
   if (const int rc = be.row_rms(P.rms, err); rc != 0) return rc;
   const bool eight_bit = elem_bytes(S.dtype) == 1;
@@ -724,7 +743,7 @@ int compress_with(EncodeBackend &be, const EncodeShape &shape, double target, co
     err = "target_bpp outside the supported range for this container";
     return EP_ERR_TARGET;
   }
-  double a = opt.fixed_a;
+  double a = o.fixed_a;
   if (chosen) {
     const double fl = floor_bpp(S);
     if (target < 1.02 * fl) {

@@ -73,11 +73,14 @@ struct EncodeShape {
   int64_t R = 0, C = 0, C8 = 0, vpr = 0, n_vec = 0, tiles = 0;
   int states = kStatesPerTile;      // rANS states per tile: kStatesPerTile or kStatesLow
   int tile_vecs = kTileVecsSmall;   // E8 vectors per tile: kTileVecsSmall or kTileVecsLarge
+  int layout = kLayoutRows;         // kLayoutRows or kLayoutBlocks
   void set_tiles(int s, int tv) {
     states = s;
     tile_vecs = tv;
-    tiles = (n_vec + tv - 1) / tv;
+    tiles = tile_count(layout, R, vpr, tv);
   }
+  // global vector index of local vector i of tile t, or -1 if absent
+  int64_t vector_of(int64_t t, int64_t i) const { return tile_vector(layout, R, vpr, tile_vecs, t, i); }
 };
 
 // The caller's choices (ep_options); zero fields are chosen by the encoder.
@@ -87,6 +90,7 @@ struct EncodeOptions {
   int tile_vecs = 0;         // 0, kTileVecsSmall or kTileVecsLarge
   int64_t sample_vecs = 0;   // 0: kSampleVecs
   uint64_t seed = 0;         // phase of the rate estimate's stride sample
+  int layout = 0;            // kLayoutRows or kLayoutBlocks
 };
 
 // Normalized frequencies of each context over its symbol range
@@ -125,9 +129,10 @@ class EncodeBackend {
  public:
   virtual ~EncodeBackend() = default;
   // the tile geometry encode_tiles uses (states per tile, vectors per tile)
-  void set_geometry(int states, int tile_vecs) {
+  void set_geometry(int states, int tile_vecs, int layout) {
     states_ = states;
     tile_vecs_ = tile_vecs;
+    layout_ = layout;
   }
   // RMS of every row (f64 sum of squares in column order).  Returns 0,
   // EP_ERR_NONFINITE if the input holds NaN or Inf, or another negative
@@ -153,6 +158,7 @@ class EncodeBackend {
  protected:
   int states_ = kStatesPerTile;
   int tile_vecs_ = kTileVecsSmall;
+  int layout_ = kLayoutRows;
 };
 
 // The encoder on a backend: row normalization, rate selection from sampled

@@ -673,6 +673,10 @@ int compress_device(const void *dev_src, int dtype, int64_t rows, int64_t cols, 
     err = "null input";
     return EP_ERR_ARG;
   }
+  if (opt.layout != kLayoutRows) {  // its tile passes walk row-major tiles only
+    err = "the GPU encoder writes row-major tiles; the blocks layout is encoded on the host";
+    return EP_ERR_ARG;
+  }
   GpuBackend be(dev_src, S, reinterpret_cast<hipStream_t>(stream));
   return compress_with(be, S, target, opt, blob, err);
 }
@@ -684,6 +688,10 @@ int compress_device_noalloc(const void *dev_src, int dtype, int64_t rows, int64_
   if (!make_shape(dtype, rows, cols, S, status, err)) return status;
   if (!dev_src) {
     err = "null input";
+    return EP_ERR_ARG;
+  }
+  if (opt.layout != kLayoutRows) {  // its tile passes walk row-major tiles only
+    err = "the GPU encoder writes row-major tiles; the blocks layout is encoded on the host";
     return EP_ERR_ARG;
   }
   if (S.R * S.C8 > kNoAllocMaxElements) {

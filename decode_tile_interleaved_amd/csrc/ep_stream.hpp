@@ -5,7 +5,7 @@
 //                    prob_bits, context count, tile_vecs, states per tile,
 //                    tiles, rows, cols, padded cols, lattice scale a, target
 //                    bpp, section offsets (the states-section field is 0),
-//                    word count, total bytes
+//                    word count, total bytes, tile layout (byte 120)
 //   tables           7 x {int16 smin, uint16 nsym} then every context's
 //                    uint16 frequencies back to back
 //   scales           float32 g_r per row
@@ -58,6 +58,38 @@ constexpr int kValueMin = -2048, kValueMax = 2047;  // lattice coordinates the s
 
 enum Method : uint8_t { kLattice = 0, kRaw = 1 };
 
+// Tile layouts (header byte 120).  The pages ask for independently decodable
+// tiles and leave their shape open.
+//   kLayoutRows:   tile t holds vectors t * tile_vecs ... in row-major vector
+//                  order; the last tile may be partial.
+//   kLayoutBlocks: tile t = nb * KB + kb (KB = ceil(vpr / 8)) is the weight
+//                  block of rows 64 nb .. 64 nb + 63 and vector columns
+//                  8 kb .. 8 kb + 7; its local vector i lies at row
+//                  64 nb + i / 8, vector column 8 kb + i % 8 and is absent
+//                  where that falls outside the matrix.  A matrix product
+//                  reads W one block at a time, so the fused linear decodes
+//                  each block straight into a matrix-core operand (API
+//                  reference, "CompressedLinear": reconstructed weights feed
+//                  every forward call).  BF16 containers, cols % 8 == 0, 64
+//                  states and 512 vectors per tile.
+enum Layout : uint8_t { kLayoutRows = 0, kLayoutBlocks = 1 };
+constexpr int kBlockRows = 64, kBlockVecs = 8;
+
+inline int64_t tile_count(int layout, int64_t rows, int64_t vpr, int64_t tile_vecs) {
+  if (layout == kLayoutBlocks) return (rows + kBlockRows - 1) / kBlockRows * ((vpr + kBlockVecs - 1) / kBlockVecs);
+  return (rows * vpr + tile_vecs - 1) / tile_vecs;
+}
+
+inline int64_t tile_vector(int layout, int64_t rows, int64_t vpr, int64_t tile_vecs, int64_t t, int64_t i) {
+  if (layout == kLayoutBlocks) {
+    const int64_t kb_n = (vpr + kBlockVecs - 1) / kBlockVecs;
+    const int64_t r = (t / kb_n) * kBlockRows + i / kBlockVecs, k = (t % kb_n) * kBlockVecs + i % kBlockVecs;
+    return (r < rows && k < vpr) ? r * vpr + k : -1;
+  }
+  const int64_t v = t * tile_vecs + i;
+  return v < rows * vpr ? v : -1;
+}
+
 inline size_t elem_bytes(int dtype) { return dtype <= 1 ? 2 : 1; }
 inline uint64_t align16(uint64_t n) { return (n + 15) & ~uint64_t(15); }
 
@@ -66,7 +98,7 @@ namespace hdr {
 constexpr size_t magic = 0, version = 4, header_bytes = 6, method = 8, dtype = 9, prob_bits = 10, contexts = 11,
                  tile_vecs = 12, states = 16, tiles = 20, rows = 24, cols = 32, cols8 = 40, scale_a = 48,
                  target = 56, off_tables = 64, off_scales = 72, off_states = 80, off_tile_offsets = 88,
-                 off_words = 96, n_words = 104, total = 112;
+                 off_words = 96, n_words = 104, total = 112, layout = 120;
 }
 
 template <class T>
@@ -81,7 +113,7 @@ inline void wr(uint8_t *p, T v) {
 }
 
 struct StreamView {
-  int method = 0, dtype = 0, prob_bits = 0, states = 0, tile_vecs = 0;
+  int method = 0, dtype = 0, prob_bits = 0, states = 0, tile_vecs = 0, layout = 0;
   int64_t rows = 0, cols = 0, cols8 = 0, tiles = 0, n_vec = 0;
   double scale_a = 0, target = 0;
   uint64_t off_tables = 0, off_scales = 0, off_tile_offsets = 0, off_words = 0;
@@ -134,8 +166,13 @@ inline std::string parse_stream(const uint8_t *b, size_t n, StreamView &s) {
   if (s.cols8 != (s.cols + 7) / 8 * 8) return "bad padded column count";
   s.n_vec = s.rows * (s.cols8 / 8);
   if (s.n_vec >= (int64_t(1) << 31)) return "stream too large";
+  s.layout = b[hdr::layout];
+  if (s.layout > kLayoutBlocks) return "unknown tile layout";
+  if (s.layout == kLayoutBlocks &&
+      (s.states != kStatesPerTile || s.tile_vecs != kTileVecsSmall || s.cols % 8 != 0 || s.dtype != 0))
+    return "blocks layout needs 64-state 512-vector tiles of a BF16 matrix with cols % 8 == 0";
   s.tiles = rd<uint32_t>(b + hdr::tiles);
-  if (s.tiles != (s.n_vec + s.tile_vecs - 1) / s.tile_vecs) return "bad tile count";
+  if (s.tiles != tile_count(s.layout, s.rows, s.cols8 / 8, s.tile_vecs)) return "bad tile count";
   s.scale_a = rd<double>(b + hdr::scale_a);
   s.off_tables = rd<uint64_t>(b + hdr::off_tables);
   s.off_scales = rd<uint64_t>(b + hdr::off_scales);

@@ -20,7 +20,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libep.so")
 
-BF16, FP16, FP8_E4M3FN, INT8 = 0, 1, 2, 3
+BF16, FP16, FP8_E4M3FN, INT8, F32 = 0, 1, 2, 3, 4
+LAYOUT_ROWS, LAYOUT_BLOCKS = 0, 1
 OK, WARN_RAW = 0, 1
 ERR_ARG, ERR_SHAPE, ERR_NONFINITE, ERR_TARGET, ERR_FORMAT, ERR_DEVICE, ERR_NOMEM = -1, -2, -3, -4, -5, -6, -7
 
@@ -29,7 +30,7 @@ _CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
 
 EXPORTS = ["ep_compress", "ep_compress_ex", "ep_compress_device", "ep_compress_device_noalloc", "ep_free",
            "ep_decompress", "ep_decode_symbols", "ep_actual_bpp", "ep_storage_nbytes", "ep_blob_info", "ep_last_error",
-           "ep_last_encode_count", "ep_plan_create", "ep_plan_decompress", "ep_plan_free"]
+           "ep_last_encode_count", "ep_plan_create", "ep_plan_decompress", "ep_plan_free", "ep_linear"]
 
 
 class EPError(RuntimeError):
@@ -41,19 +42,19 @@ class EPError(RuntimeError):
 class _Options(ctypes.Structure):
     _fields_ = [("fixed_scale", ctypes.c_double), ("n_threads", ctypes.c_int), ("n_states", ctypes.c_int),
                 ("tile_vecs", ctypes.c_int), ("sample_vecs", ctypes.c_int), ("seed", ctypes.c_uint64),
-                ("reserved", ctypes.c_int * 4)]
+                ("layout", ctypes.c_int), ("reserved", ctypes.c_int * 3)]
 
 
 class _Info(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("dtype", ctypes.c_int), ("method", ctypes.c_int),
                 ("n_states", ctypes.c_int), ("tile_vecs", ctypes.c_int), ("prob_bits", ctypes.c_int),
                 ("n_tiles", ctypes.c_int64), ("n_words", ctypes.c_int64), ("scale_a", ctypes.c_double),
-                ("target_bpp", ctypes.c_double)]
+                ("target_bpp", ctypes.c_double), ("layout", ctypes.c_int)]
 
 
-def _options(fixed_scale=0.0, n_threads=0, n_states=0, tile_vecs=0, sample_vecs=0, seed=0) -> _Options:
+def _options(fixed_scale=0.0, n_threads=0, n_states=0, tile_vecs=0, sample_vecs=0, seed=0, layout=0) -> _Options:
     return _Options(float(fixed_scale), int(n_threads), int(n_states), int(tile_vecs), int(sample_vecs), int(seed),
-                    (ctypes.c_int * 4)())
+                    int(layout), (ctypes.c_int * 3)())
 
 
 _lib = None
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.ep_plan_decompress.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.ep_plan_free.argtypes = [ctypes.c_void_p]
         L.ep_plan_free.restype = None
+        L.ep_linear.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         L.ep_last_encode_count.argtypes = []
         L.ep_last_encode_count.restype = ctypes.c_int64
         _lib = L
@@ -150,7 +153,7 @@ def _host_ptr(a: np.ndarray) -> int:
 
 
 def compress(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, n_threads: int = 0, n_states: int = 0,
-             tile_vecs: int = 0, sample_vecs: int = 0, seed: int = 0) -> Packed:
+             tile_vecs: int = 0, sample_vecs: int = 0, seed: int = 0, layout: int = LAYOUT_ROWS) -> Packed:
     """ep_compress_ex on a 2-D CPU tensor (BF16, FP16, FP8-E4M3FN or INT8);
     the keyword arguments are the ep_options fields."""
     if t.dtype not in _DTYPE_CODE:
@@ -158,7 +161,7 @@ def compress(t: torch.Tensor, target_bpp: float, fixed_scale: float = 0.0, n_thr
     if t.dim() != 2:
         raise EPError(ERR_SHAPE, "compress", "input must be 2-D")
     t = t.detach().to("cpu").contiguous()
-    opt = _options(fixed_scale, n_threads, n_states, tile_vecs, sample_vecs, seed)
+    opt = _options(fixed_scale, n_threads, n_states, tile_vecs, sample_vecs, seed, layout)
     out = ctypes.POINTER(ctypes.c_uint8)()
     nb = ctypes.c_size_t(0)
     src = t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16)
@@ -290,3 +293,28 @@ def from_blob(blob: np.ndarray) -> Packed:
     d = blob_info(blob)
     return Packed(blob=np.ascontiguousarray(blob, dtype=np.uint8), status=OK if d["method"] == 0 else WARN_RAW,
                   shape=(d["rows"], d["cols"]), dtype=_CODE_DTYPE[d["dtype"]])
+
+
+def linear(p: Packed, x: torch.Tensor, out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+           stream=None) -> torch.Tensor:
+    """ep_linear: Y = X W^T with W decoded inside the product (p: a BF16
+    stream in the blocks layout, on the device; x: BF16, m x cols of W, on
+    the same device).  Y is m x rows of W, BF16 or FP32."""
+    if p.dev is None:
+        raise EPError(ERR_ARG, "linear", "stream is not on a device; call Packed.to('cuda') first")
+    rows, cols = p.shape
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != cols or not x.is_contiguous():
+        raise EPError(ERR_ARG, "linear", "x must be a contiguous BF16 m x cols tensor")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise EPError(ERR_ARG, "linear", "out_dtype must be bfloat16 or float32")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty(m, rows, dtype=out_dtype, device=p.dev.device)
+    if out.dtype != out_dtype or tuple(out.shape) != (m, rows) or not out.is_contiguous():
+        raise EPError(ERR_ARG, "linear", "out must be a contiguous m x rows tensor of out_dtype")
+    rc = lib().ep_linear(_host_ptr(p.blob), p.blob.size, ctypes.c_void_p(p.dev.data_ptr()),
+                         ctypes.c_void_p(x.data_ptr() if m else 0), m,
+                         ctypes.c_void_p(out.data_ptr() if m else 0),
+                         F32 if out_dtype == torch.float32 else BF16, ctypes.c_void_p(_stream_handle(stream)))
+    _check(rc, "ep_linear")
+    return out

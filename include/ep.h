@@ -28,7 +28,7 @@ extern "C" {
 
 /* Container dtypes (EntroPack README "Multiple dtypes"; the abstract lists
  * BF16, FP16, FP8 and INT8 weight containers).  FP8 is OCP E4M3FN. */
-enum ep_dtype { EP_BF16 = 0, EP_FP16 = 1, EP_FP8_E4M3FN = 2, EP_INT8 = 3 };
+enum ep_dtype { EP_BF16 = 0, EP_FP16 = 1, EP_FP8_E4M3FN = 2, EP_INT8 = 3, EP_F32 = 4 /* ep_linear output only */ };
 
 /* Status codes.  0 is success; a positive value is a warning with a valid
  * result; a negative value is an error and leaves outputs untouched.  The API
@@ -64,8 +64,27 @@ struct ep_options {
   int sample_vecs;     /* vectors in the rate estimate's stride sample; 0 = 65536 */
   uint64_t seed;       /* phase of that sample: vector floor(k n / S) + seed mod
                           floor(n / S) for sample point k */
-  int reserved[4];     /* must be zero */
+  int layout;          /* tile layout: EP_LAYOUT_ROWS (0) or EP_LAYOUT_BLOCKS */
+  int reserved[3];     /* must be zero */
 };
+
+/* Tile layouts.  The abstract asks for independently decodable tiles and
+ * leaves their shape open.
+ *   EP_LAYOUT_ROWS:   tiles of 512 or 1024 E8 vectors in row-major vector
+ *                     order (the default; what ep_decompress is fastest on).
+ *   EP_LAYOUT_BLOCKS: each tile is the 64 x 64 weight block of rows
+ *                     64 nb .. 64 nb + 63 and columns 64 kb .. 64 kb + 63
+ *                     (tile nb * ceil(cols / 64) + kb; its vector i sits at
+ *                     block row i / 8, block vector column i % 8; vectors
+ *                     outside the matrix are absent), 64 states, 512 vectors.
+ *                     This is the layout ep_linear decodes straight into a
+ *                     matrix-core operand (API reference, "CompressedLinear":
+ *                     reconstructed weights feed every forward call).  BF16
+ *                     containers with cols % 8 == 0 only (EP_ERR_ARG /
+ *                     EP_ERR_SHAPE otherwise); host encoder only
+ *                     (ep_compress_device gives EP_ERR_ARG).  ep_decompress
+ *                     and ep_decode_symbols read both layouts. */
+enum ep_layout { EP_LAYOUT_ROWS = 0, EP_LAYOUT_BLOCKS = 1 };
 
 /*
  * ep_compress -- lossy lattice-rANS compression of a rows x cols row-major
@@ -227,8 +246,38 @@ struct ep_info {
   int64_t n_words;   /* 16-bit words in the entropy-coded section */
   double scale_a;    /* lattice resolution (row-normalized units) */
   double target_bpp; /* the target the stream was built for */
+  int layout;        /* EP_LAYOUT_ROWS or EP_LAYOUT_BLOCKS */
 };
 int ep_blob_info(const uint8_t *blob, size_t nbytes, struct ep_info *info);
+
+/*
+ * ep_linear -- the fused CompressedLinear product Y = X W^T with W decoded
+ * on the fly (API reference, "CompressedLinear": the layer keeps its weight
+ * compressed and uses the reconstructed weight in every forward call; the
+ * abstract: fused symbol decoding and numerical reconstruction suit
+ * Transformer prefill).  Each 64 x 64 block of W is decoded, scaled and
+ * rounded to BF16 (the values ep_decompress returns) into LDS and multiplied
+ * there by the BF16 matrix cores (v_mfma_f32_16x16x32_bf16), FP32
+ * accumulation; W never reaches global memory.
+ *   host_blob, nbytes : the stream (host copy), a lattice stream in the
+ *                       blocks layout (ep_options.layout = EP_LAYOUT_BLOCKS):
+ *                       W is rows x cols BF16, N = rows, K = cols.
+ *   dev_blob   : the same bytes in device memory, 16-byte aligned.
+ *   dev_x      : X, m x K BF16, row-major, device memory, 16-byte aligned.
+ *   m          : rows of X (tokens); 0 does nothing.
+ *   dev_y      : Y, m x N row-major, device memory, 4-byte aligned; dtype
+ *                y_dtype: EP_F32, or EP_BF16 (FP32 sums rounded to nearest
+ *                even).  Caller-owned; fully overwritten.
+ *   hip_stream : hipStream_t the kernel is enqueued on (NULL = default).
+ * Allocates nothing, does not synchronize.  The sum over K runs in a fixed
+ * order (64-column blocks ascending, 32 columns per matrix-core step), so
+ * results are deterministic.  Returns EP_OK; EP_ERR_ARG for a raw or
+ * row-major stream, a bad y_dtype, a null or misaligned pointer;
+ * EP_ERR_SHAPE for m outside [0, 2^31); EP_ERR_FORMAT for a corrupt stream;
+ * EP_ERR_DEVICE if the launch fails.
+ */
+int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, const void *dev_x, int64_t m,
+              void *dev_y, int y_dtype, void *hip_stream);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char *ep_last_error(void);

@@ -364,3 +364,60 @@ def test_plan_arguments_and_errors():
     assert r.status == ep.WARN_RAW
     assert L.ep_plan_create(r.blob.ctypes.data, r.blob.size, fake_dev, -1, ctypes.byref(plan)) == ep.OK
     L.ep_plan_free(plan)
+
+
+@pytest.mark.parametrize("rows,cols,target", [(200, 136, 4.0), (64, 64, 4.0), (130, 3840, 3.0), (257, 72, 5.0),
+                                              (1000, 1024, 2.75)])
+def test_blocks_stream_identical_to_oracle(rows, cols, target):
+    """The host encoder writes the oracle's blocks-layout stream byte for byte."""
+    x = W.rowscale_gaussian(rows, cols, seed=rows * 5 + cols)
+    p = ep.compress(x, target, layout=ep.LAYOUT_BLOCKS)
+    blob, rc, _ = oracle.compress(x, target, layout=oracle.LAYOUT_BLOCKS)
+    assert rc == p.status == ep.OK
+    assert np.array_equal(p.blob, blob)
+    assert p.info()["layout"] == ep.LAYOUT_BLOCKS and ep.last_encode_count() == 1
+
+
+def test_blocks_layout_rules_and_linear_argument_errors():
+    """The blocks layout's argument rules match the oracle's; the GPU encoder
+    refuses it; ep_linear checks its arguments on the host before any device
+    work, so these run without a GPU (the device addresses are never
+    dereferenced on the host)."""
+    import ctypes
+    L = ep.lib()
+    x = W.gaussian(64, 64, 0.02, seed=1)
+    for t, kw, code in ((x.to(torch.float16), {}, ep.ERR_ARG), (W.gaussian(64, 60, 0.02, seed=1), {}, ep.ERR_SHAPE),
+                        (x, {"n_states": 16}, ep.ERR_ARG), (x, {"tile_vecs": 1024}, ep.ERR_ARG)):
+        with pytest.raises(ep.EPError) as e:
+            ep.compress(t, 4.0, layout=ep.LAYOUT_BLOCKS, **kw)
+        assert e.value.code == code
+    with pytest.raises(ep.EPError) as e:
+        ep.compress(x, 4.0, layout=2)
+    assert e.value.code == ep.ERR_ARG
+    out = ctypes.POINTER(ctypes.c_uint8)()
+    nb = ctypes.c_size_t(0)
+    opt = ep._options(layout=ep.LAYOUT_BLOCKS)
+    assert L.ep_compress_device(ctypes.c_void_p(0x1000), ep.BF16, 64, 512, 4.0, ctypes.byref(opt), None,
+                                ctypes.byref(out), ctypes.byref(nb)) == ep.ERR_ARG
+    assert "blocks layout" in ep.last_error()
+    pb = ep.compress(W.gaussian(200, 136, 0.02, seed=2), 4.0, layout=ep.LAYOUT_BLOCKS)
+    pr = ep.compress(W.gaussian(200, 136, 0.02, seed=2), 4.0)
+    dev, xd, yd = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 28)
+
+    def lin(p, x_, m, y_, ydt, dev_=dev):
+        return L.ep_linear(p.blob.ctypes.data, p.blob.size, dev_, x_, m, y_, ydt, None)
+    assert lin(pr, xd, 4, yd, ep.BF16) == ep.ERR_ARG and "blocks layout" in ep.last_error()
+    assert lin(pb, xd, 4, yd, ep.FP16) == ep.ERR_ARG
+    assert lin(pb, xd, -1, yd, ep.F32) == ep.ERR_SHAPE
+    assert lin(pb, xd, 1 << 31, yd, ep.F32) == ep.ERR_SHAPE
+    assert lin(pb, None, 0, None, ep.F32) == ep.OK
+    assert lin(pb, None, 4, yd, ep.F32) == ep.ERR_ARG
+    assert lin(pb, ctypes.c_void_p((1 << 24) + 8), 4, yd, ep.F32) == ep.ERR_ARG
+    assert lin(pb, xd, 4, yd, ep.F32, dev_=None) == ep.ERR_ARG
+    bad = pb.blob.copy()
+    bad[0] ^= 1
+    assert L.ep_linear(bad.ctypes.data, bad.size, dev, xd, 4, yd, ep.F32, None) == ep.ERR_FORMAT
+    # a decode plan of a blocks stream records its launch without a GPU
+    plan = ctypes.c_void_p()
+    assert L.ep_plan_create(pb.blob.ctypes.data, pb.blob.size, dev, -1, ctypes.byref(plan)) == ep.OK
+    L.ep_plan_free(plan)
