@@ -967,6 +967,8 @@ struct LinArgs {
   uint32_t slots_off;      // LDS byte offset of the block slots
   uint32_t y_f32;          // GEMM: Y is FP32 (1) or BF16 (0)
   uint32_t grid;           // workgroups
+  uint32_t split, cps;     // GEMM: workgroups per output block along K; chunks each
+  float *part;             // split > 1: FP32 partial sums, split x M x N
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -987,7 +989,10 @@ __device__ __forceinline__ uint32_t xcd_logical(uint32_t b, uint32_t grid) {
 // giving the lane's vector of block row 8 s + lane / 8 to sink(s, act, e).
 // present: bit s set where that vector exists (absent vectors come last in
 // a lane's sequence: rows past the matrix, or a vector column past it).
-template <bool WIDE, class Sink>
+// FULL: every vector of the tile exists (present is all ones), so that the
+// refill test is the state comparison alone, with no per-lane mask in the
+// serial chain.
+template <bool WIDE, bool FULL, class Sink>
 __device__ __forceinline__ void decode_block(uint32_t wt, uint32_t we, uint32_t lane, uint32_t present, Sink &&sink) {
   UnitLane u{};
   u.q = lane;
@@ -999,7 +1004,7 @@ __device__ __forceinline__ void decode_block(uint32_t wt, uint32_t we, uint32_t 
   constexpr uint32_t kBitB = WIDE ? 16u : 24u;
 #pragma unroll
   for (uint32_t s = 0; s < 8; ++s) {
-    const bool act = (present >> s) & 1u;
+    const bool act = FULL ? true : ((present >> s) & 1u) != 0u;
     uint32_t e[8];
     const uint32_t cb = __builtin_amdgcn_ubfe(L.d0, kBitB, 1u) << 13;
     e[0] = rans_step<WIDE, kC, true>(L, cb, act);
@@ -1027,6 +1032,25 @@ __device__ __forceinline__ u32x4 block_weights(const uint32_t (&e)[8], float g, 
   return pk;
 }
 
+// The lane's A fragments of one block slot: rows row0 + 16 i + lane % 16 of
+// X, 8 values at k = kbase + 32 h + 8 (lane / 16), h = 0, 1 (zeros past M or
+// K; K is a multiple of 8, so a fragment is all in or all out).
+template <int RB>
+__device__ __forceinline__ void load_x(const LinArgs &P, uint32_t row0, uint32_t kbase, uint32_t lane,
+                                       u32x4 (&a)[RB][2]) {
+  const uint32_t lr = lane & 15u, lk = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t row = row0 + 16u * (uint32_t)i + lr, kg = kbase + 32u * (uint32_t)h + 8u * lk;
+      const bool ok = row < P.m && kg < P.k;
+      const uint64_t at = ok ? (uint64_t)row * P.k + kg : 0ull;
+      const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)(P.x + at);
+      a[i][h] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
 // RB: 16-row blocks of X per wave (GEMM)
 template <int MODE, bool WIDE, int RB>
 __global__ void __launch_bounds__(64 * kLinWaves) linear_kernel(LinArgs P) {
@@ -1035,23 +1059,33 @@ __global__ void __launch_bounds__(64 * kLinWaves) linear_kernel(LinArgs P) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t L = xcd_logical(blockIdx.x, P.grid);
-  uint32_t nb, mb, c_begin, c_end;
+  uint32_t nb, mb, c_begin, c_end, sp = 0u;
   if constexpr (MODE == kLinGemm) {
-    mb = L / P.nb_n;
-    nb = L - mb * P.nb_n;
-    c_begin = 0u;
-    c_end = P.chunks;
+    // consecutive logical indices: the splits of one output block, then the
+    // block rows of W, then the row blocks of X
+    const uint32_t blk = L / P.split;
+    sp = L - blk * P.split;
+    mb = blk / P.nb_n;
+    nb = blk - mb * P.nb_n;
+    c_begin = sp * P.cps;
+    c_end = min(c_begin + P.cps, P.chunks);
   } else {
     nb = L / P.chunks;
     mb = 0u;
     c_begin = L - nb * P.chunks;
     c_end = c_begin + 1u;
   }
-  // the tables (waves 0..6, one context each)
+  typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
+  const cptr_u32 toff = (cptr_u32)A.toff;
+  // the tables (waves 0..6, one context each); meanwhile the last wave copies
+  // the first chunk's words into LDS
   if (wave < (uint32_t)kContexts) {
     uint32_t fpre[4];
     first_frequencies(A, wave, lane, fpre);
     build_tables<WIDE>(A, lds, wave, lane, (uint32_t)kContexts, fpre);
+  } else if (wave == (uint32_t)kLinWaves - 1u) {
+    const uint32_t kb0 = c_begin * P.chunk, t0 = nb * P.kb_n + kb0, nt = min(P.chunk, P.kb_n - kb0);
+    copy_pieces(A, lds, first_piece(toff[t0]), end_piece(toff[t0 + nt]), A.words_off, lane, 0u, 1u);
   }
   // the lane's block rows 8 s + lane / 8 and their scales (the last row's
   // past the matrix; those vectors are absent)
@@ -1071,29 +1105,47 @@ __global__ void __launch_bounds__(64 * kLinWaves) linear_kernel(LinArgs P) {
     for (int j = 0; j < kCb; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint32_t m0 = (mb * (uint32_t)kLinWaves + wave) * 16u * (uint32_t)RB;  // the wave's first row of X
 
-  typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
-  const cptr_u32 toff = (cptr_u32)A.toff;
   for (uint32_t c = c_begin; c < c_end; ++c) {
     const uint32_t kb0 = c * P.chunk, nt = min(P.chunk, P.kb_n - kb0);
     const uint32_t t0 = nb * P.kb_n + kb0;
-    const uint32_t p0 = first_piece(toff[t0]), p1 = end_piece(toff[t0 + nt]);
-    lds_barrier();  // tables built; the slots and words of the last chunk are no longer read
-    copy_pieces(A, lds, p0, p1, A.words_off, lane, wave, (uint32_t)kLinWaves);
+    const uint32_t p0 = first_piece(toff[t0]);
+    // the chunk's words were copied during the table build (first chunk) or
+    // during the last chunk's products; this barrier also ends every read of
+    // the last chunk's slots
     __builtin_amdgcn_s_waitcnt(0);
-    lds_barrier();  // the chunk's words are in LDS
+    lds_barrier();
+    // GEMM: the A fragments of the chunk's first kRing - 1 slots load during
+    // its decode; each later slot's load leaves kRing - 1 slots ahead of its
+    // use.  With few rows per wave a slot's products are too short to cover
+    // a load, so the whole chunk's fragments load during the decode.
+    constexpr uint32_t kRing = RB == 1 ? kLinMaxChunk + 1u : (RB == 2 ? 4u : 3u);
+    u32x4 xa[kRing][RB][2];
+    if constexpr (MODE == kLinGemm) {
+#pragma unroll
+      for (uint32_t i = 0; i + 1u < kRing; ++i)
+        if (i < nt && m0 < P.m) load_x<RB>(P, m0, 64u * (kb0 + i), lane, xa[i]);
+    }
     if (wave < nt) {
       const uint32_t t = t0 + wave;
       const uint32_t tb = toff[t], te = toff[t + 1u];
       const uint32_t wt = A.words_off + 2u * tb - 16u * p0;
       const uint32_t kv = 8u * (kb0 + wave) + vcol;  // the lane's vector column in W
       const uint32_t present = kv < A.vpr ? present_rows : 0u;
+      const bool full = __ballot(present != 0xffu) == 0;
+      // one decode of the tile through sink, in its whole-block or edge form
+      auto decode = [&](auto &&sink) {
+        if (full)
+          decode_block<WIDE, true>(wt, wt + 2u * (te - tb), lane, present, sink);
+        else
+          decode_block<WIDE, false>(wt, wt + 2u * (te - tb), lane, present, sink);
+      };
       if constexpr (MODE == kLinGemm) {
         const uint32_t slot = P.slots_off + wave * kSlotBytes + (lane >> 3) * kSlotRowBytes + 16u * vcol;
-        decode_block<WIDE>(wt, wt + 2u * (te - tb), lane, present, [&](uint32_t s, bool act, const uint32_t(&e)[8]) {
+        decode([&](uint32_t s, bool act, const uint32_t(&e)[8]) {
           *(lds_u128_wptr)(uintptr_t)(slot + 8u * s * kSlotRowBytes) = block_weights<WIDE>(e, gs[s], act);
         });
       } else if constexpr (MODE == kLinWeights) {
-        decode_block<WIDE>(wt, wt + 2u * (te - tb), lane, present, [&](uint32_t s, bool act, const uint32_t(&e)[8]) {
+        decode([&](uint32_t s, bool act, const uint32_t(&e)[8]) {
           if (act) {
             const uint64_t at = (uint64_t)(r0 + 8u * s) * A.cols + 8ull * kv;
             __builtin_nontemporal_store(block_weights<WIDE>(e, gs[s], true),
@@ -1101,7 +1153,7 @@ __global__ void __launch_bounds__(64 * kLinWaves) linear_kernel(LinArgs P) {
           }
         });
       } else {
-        decode_block<WIDE>(wt, wt + 2u * (te - tb), lane, present, [&](uint32_t s, bool act, const uint32_t(&e)[8]) {
+        decode([&](uint32_t s, bool act, const uint32_t(&e)[8]) {
           if (act) {
             uint32_t w[4];
 #pragma unroll
@@ -1114,41 +1166,73 @@ __global__ void __launch_bounds__(64 * kLinWaves) linear_kernel(LinArgs P) {
         });
       }
     }
-    if constexpr (MODE == kLinGemm) {
-      lds_barrier();  // the chunk's blocks are in their slots
+    if constexpr (MODE != kLinGemm) {
+      if (c + 1u < c_end) {
+        lds_barrier();  // every wave is done with the chunk's words
+        const uint32_t kb1 = kb0 + P.chunk, t1 = nb * P.kb_n + kb1, n1 = min(P.chunk, P.kb_n - kb1);
+        copy_pieces(A, lds, first_piece(toff[t1]), end_piece(toff[t1 + n1]), A.words_off, lane, wave,
+                    (uint32_t)kLinWaves);
+      }
+    } else {
+      lds_barrier();  // the chunk's blocks are in their slots; its words are no longer read
+      // the next chunk's words load into registers during this chunk's
+      // products (a copy straight into LDS would make the products' LDS reads
+      // wait for it) and go to LDS after them
+      const bool more = c + 1u < c_end;
+      uint32_t q0 = 0, q1 = 0;
+      u32x4 cp[kStage];
+      if (more) {
+        const uint32_t kb1 = kb0 + P.chunk, t1 = nb * P.kb_n + kb1, n1 = min(P.chunk, P.kb_n - kb1);
+        q0 = first_piece(toff[t1]);
+        q1 = end_piece(toff[t1 + n1]);
+        stage_pieces(A, q0, q1, lane, wave, (uint32_t)kLinWaves, cp);
+      }
       // lane's fragments: A row m0 + 16 i + lane % 16, k 8 (lane / 16) ..;
       // B column (W row) 16 j + lane % 16 of the block, same k
       const uint32_t lr = lane & 15u, lk = lane >> 4;
-      for (uint32_t sl = 0; sl < nt; ++sl) {
+      const bool rows = m0 < P.m;  // wave-uniform: waves whose rows all lie past M skip the products
+      // B fragments of slot sl, both halves of its 64 columns of K; with few
+      // rows per wave (registers to spare) the next slot's are read before
+      // this slot's products, so that no product waits for an LDS read
+      constexpr bool kAheadB = RB <= 2;
+      auto read_b = [&](uint32_t sl, u32x4 (&b)[2][kCb]) {
 #pragma unroll
-        for (uint32_t kh = 0; kh < 2u; ++kh) {
-          const uint32_t kg = 64u * (kb0 + sl) + 32u * kh + 8u * lk;  // global k of the lane's 8 values
-          u32x4 a[RB];
-#pragma unroll
-          for (int i = 0; i < RB; ++i) {
-            const uint32_t row = m0 + 16u * (uint32_t)i + lr;
-            const bool ok = row < P.m && kg < P.k;
-            const uint64_t at = ok ? (uint64_t)row * P.k + kg : 0ull;
-            a[i] = *(const __attribute__((address_space(1))) u32x4 *)(P.x + at);
-            if (!ok) a[i] = u32x4{0u, 0u, 0u, 0u};
-          }
-          u32x4 b[kCb];
+        for (uint32_t kh = 0; kh < 2u; ++kh)
 #pragma unroll
           for (int j = 0; j < kCb; ++j)
-            b[j] = *(lds_u128_rptr)(uintptr_t)(P.slots_off + sl * kSlotBytes + (16u * (uint32_t)j + lr) * kSlotRowBytes +
-                                               16u * (4u * kh + lk));
+            b[kh][j] = *(lds_u128_rptr)(uintptr_t)(P.slots_off + sl * kSlotBytes +
+                                                   (16u * (uint32_t)j + lr) * kSlotRowBytes + 16u * (4u * kh + lk));
+      };
+      u32x4 bq[2][2][kCb];
+      if (kAheadB && rows) read_b(0u, bq[0]);
 #pragma unroll
-          for (int i = 0; i < RB; ++i)
+      for (uint32_t sl = 0; sl < kLinMaxChunk; ++sl) {
+        if (rows && sl < nt) {
+          if (sl + kRing - 1u < nt)
+            load_x<RB>(P, m0, 64u * (kb0 + sl + kRing - 1u), lane, xa[(sl + kRing - 1u) % kRing]);
+          if constexpr (kAheadB) {
+            if (sl + 1u < nt) read_b(sl + 1u, bq[(sl + 1u) & 1u]);
+          } else {
+            read_b(sl, bq[sl & 1u]);
+          }
+          const u32x4(&b)[2][kCb] = bq[sl & 1u];
 #pragma unroll
-            for (int j = 0; j < kCb; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
-                                                                  __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+          for (uint32_t kh = 0; kh < 2u; ++kh)
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+              for (int j = 0; j < kCb; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[sl % kRing][i][kh]),
+                                                                    __builtin_bit_cast(bf16x8, b[kh][j]), acc[i][j], 0,
+                                                                    0, 0);
         }
       }
+      if (more) store_pieces(A, q0, q1, A.words_off, lane, wave, (uint32_t)kLinWaves, cp);
     }
   }
   if constexpr (MODE == kLinGemm) {
     // lane holds D[4 (lane / 16) + r][lane % 16] of each 16 x 16 block
+    // (split: this workgroup's share of the sum over K, to its partial slab)
     const uint32_t lr = lane & 15u, lk = lane >> 4;
 #pragma unroll
     for (int j = 0; j < kCb; ++j) {
@@ -1161,13 +1245,29 @@ __global__ void __launch_bounds__(64 * kLinWaves) linear_kernel(LinArgs P) {
           const uint32_t row = m0 + 16u * (uint32_t)i + 4u * lk + r;
           if (row >= P.m) continue;
           const uint64_t at = (uint64_t)row * P.n + col;
-          if (P.y_f32)
+          if (P.split > 1u)
+            P.part[(uint64_t)sp * P.m * P.n + at] = acc[i][j][r];
+          else if (P.y_f32)
             reinterpret_cast<float *>(P.y)[at] = acc[i][j][r];
           else
             reinterpret_cast<uint16_t *>(P.y)[at] = (uint16_t)(pack2<EP_BF16>(acc[i][j][r], 0.0f) & 0xffffu);
         }
     }
   }
+}
+
+// Y = the sum of the split partial slabs, in slab order (so the result does
+// not depend on which workgroup finished first), as FP32 or BF16.
+__global__ void __launch_bounds__(256) linear_reduce_kernel(const float *part, uint32_t split, uint64_t mn, void *y,
+                                                            uint32_t y_f32) {
+  const uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  if (i >= mn) return;
+  float s = part[i];
+  for (uint32_t k = 1; k < split; ++k) s += part[(uint64_t)k * mn + i];
+  if (y_f32)
+    reinterpret_cast<float *>(y)[i] = s;
+  else
+    reinterpret_cast<uint16_t *>(y)[i] = (uint16_t)(pack2<EP_BF16>(s, 0.0f) & 0xffffu);
 }
 
 typedef const void *KernelFn;  // a kernel's address: decode_waves_kernel takes Args, decode_kernel RoundArgs
@@ -1483,7 +1583,7 @@ int prepare_linear(const uint8_t *hb, const StreamView &s, const void *dev_blob,
   A.desc_off = off;
   off += 256 * kContexts;
   const uint32_t build_end = off;
-  A.words_off = kTableBytes;  // the build's scratch is dead once the first chunk is copied
+  A.words_off = (uint32_t)align16(build_end);  // the first chunk's words arrive during the build
   const int64_t vpr = s.cols8 / 8, kb_n = (vpr + kBlockVecs - 1) / kBlockVecs, nb_n = (s.rows + kBlockRows - 1) / kBlockRows;
   auto copy_bytes = [&](int64_t t0, int64_t t1) {
     const uint64_t a0 = (s.off_words + 2ull * first_word(t0)) & ~15ull;
@@ -1498,7 +1598,7 @@ int prepare_linear(const uint8_t *hb, const StreamView &s, const void *dev_blob,
       for (int64_t k0 = 0; k0 < kb_n; k0 += ch)
         wbuf = std::max<uint64_t>(wbuf, copy_bytes(nb * kb_n + k0, nb * kb_n + std::min<int64_t>(k0 + ch, kb_n)));
     slots_off = align16(A.words_off + wbuf + kLdsPad);
-    need = std::max<uint64_t>(build_end, mode == kLinGemm ? slots_off + (uint64_t)ch * kSlotBytes : slots_off);
+    need = mode == kLinGemm ? slots_off + (uint64_t)ch * kSlotBytes : slots_off;
     if (need <= kLdsLimit) {
       chunk = (uint32_t)ch;
       break;
@@ -1530,7 +1630,18 @@ int prepare_linear(const uint8_t *hb, const StreamView &s, const void *dev_blob,
   const uint64_t rows_per_wg = (uint64_t)kLinWaves * 16u * (uint64_t)rb;
   L.m = (uint32_t)m;
   L.mb_n = mode == kLinGemm ? (uint32_t)(((uint64_t)m + rows_per_wg - 1) / rows_per_wg) : 1u;
-  const uint64_t g = mode == kLinGemm ? (uint64_t)L.mb_n * (uint64_t)nb_n : (uint64_t)nb_n * L.chunks;
+  // GEMM with fewer output blocks than compute units: split the sum over K
+  // across workgroups (partial slabs summed by linear_reduce_kernel) so that
+  // every CU decodes
+  L.split = 1;
+  L.cps = L.chunks;
+  if (mode == kLinGemm) {
+    const uint64_t base = (uint64_t)L.mb_n * (uint64_t)nb_n;
+    uint64_t sp = std::max<uint64_t>(1, std::min<uint64_t>(L.chunks, ((uint64_t)num_cus() + base / 2) / base));
+    L.cps = (uint32_t)((L.chunks + sp - 1) / sp);
+    L.split = (L.chunks + L.cps - 1) / L.cps;
+  }
+  const uint64_t g = mode == kLinGemm ? (uint64_t)L.mb_n * (uint64_t)nb_n * L.split : (uint64_t)nb_n * L.chunks;
   if (g == 0 || g > 0x7fffffffull) {
     set_error("grid too large");
     return EP_ERR_SHAPE;
@@ -1562,6 +1673,16 @@ int launch_linear(KernelFn fn, const LinArgs &L, uint32_t grid, uint32_t lds_byt
   void *args[1] = {&a};
   hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(64 * kLinWaves), args, lds_bytes, stream);
   if (err == hipSuccess) err = hipGetLastError();
+  if (err == hipSuccess && L.split > 1u) {
+    const uint64_t mn = (uint64_t)L.m * L.n;
+    const float *part = L.part;
+    uint32_t split = L.split, y_f32 = L.y_f32;
+    void *y = L.y;
+    void *rargs[5] = {&part, &split, (void *)&mn, &y, &y_f32};
+    err = hipLaunchKernel((const void *)linear_reduce_kernel, dim3((uint32_t)((mn + 255) / 256)), dim3(256), rargs, 0,
+                          stream);
+    if (err == hipSuccess) err = hipGetLastError();
+  }
   if (err != hipSuccess) {
     set_error(std::string("kernel launch failed: ") + hipGetErrorString(err));
     return EP_ERR_DEVICE;
@@ -1719,9 +1840,9 @@ int ep_plan_decompress(const ep_plan *plan, void *dev_out, void *hip_stream) {
 
 void ep_plan_free(ep_plan *plan) { delete plan; }
 
-int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, const void *dev_x, int64_t m,
-              void *dev_y, int y_dtype, void *hip_stream) {
-  ep::set_error("");
+// the fused linear's plan for m > 0 rows of X: 0 or an ep_status
+static int linear_plan(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, int64_t m, ep::LinArgs &L,
+                       ep::KernelFn &fn, uint32_t &grid, uint32_t &lds) {
   ep::StreamView s;
   std::string e = ep::parse_stream(host_blob, nbytes, s);
   if (!e.empty()) {
@@ -1732,29 +1853,59 @@ int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, con
     ep::set_error("ep_linear takes lattice streams in the blocks layout (EP_LAYOUT_BLOCKS)");
     return EP_ERR_ARG;
   }
-  if (y_dtype != EP_BF16 && y_dtype != EP_F32) {
-    ep::set_error("y_dtype must be EP_BF16 or EP_F32");
-    return EP_ERR_ARG;
-  }
   if (m < 0 || m >= (int64_t(1) << 31) || (uint64_t)m * (uint64_t)s.rows >= (uint64_t(1) << 62)) {
     ep::set_error("m must lie in [0, 2^31)");
     return EP_ERR_SHAPE;
   }
   if (m == 0) return EP_OK;
-  if (!dev_x || !dev_y) {
-    ep::set_error("null device pointer");
-    return EP_ERR_ARG;
-  }
-  if (((uintptr_t)dev_x & 15) || ((uintptr_t)dev_y & 3)) {
-    ep::set_error("dev_x must be 16-byte aligned, dev_y 4-byte aligned");
-    return EP_ERR_ARG;
-  }
-  const int rb = m > 512 ? 4 : (m > 128 ? 2 : 1);
+  // 16-row blocks per wave: few rows give one, so that waves past M skip
+  // the products (each product wave reads the chunk's every block from LDS)
+  const int rb = m > 512 ? 4 : (m > 64 ? 2 : 1);
+  return ep::prepare_linear(host_blob, s, dev_blob, ep::kLinGemm, m, rb, L, fn, grid, lds);
+}
+
+int64_t ep_linear_workspace_bytes(const uint8_t *host_blob, size_t nbytes, int64_t m) {
+  ep::set_error("");
   ep::LinArgs L;
   ep::KernelFn fn = nullptr;
   uint32_t grid = 0, lds = 0;
-  const int rc = ep::prepare_linear(host_blob, s, dev_blob, ep::kLinGemm, m, rb, L, fn, grid, lds);
+  // a stand-in device address: the plan only records it
+  const int rc = linear_plan(host_blob, nbytes, reinterpret_cast<const void *>(uintptr_t(256)), m, L, fn, grid, lds);
   if (rc != EP_OK) return rc;
+  return (m > 0 && L.split > 1u) ? (int64_t)L.split * m * (int64_t)L.n * 4 : 0;
+}
+
+int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, const void *dev_x, int64_t m,
+              void *dev_y, int y_dtype, void *dev_workspace, size_t workspace_bytes, void *hip_stream) {
+  ep::set_error("");
+  if (y_dtype != EP_BF16 && y_dtype != EP_F32) {
+    ep::set_error("y_dtype must be EP_BF16 or EP_F32");
+    return EP_ERR_ARG;
+  }
+  if (m > 0 && (!dev_x || !dev_y)) {
+    ep::set_error("null device pointer");
+    return EP_ERR_ARG;
+  }
+  if (((uintptr_t)dev_x & 15) || ((uintptr_t)dev_y & 3) || ((uintptr_t)dev_workspace & 15)) {
+    ep::set_error("dev_x and dev_workspace must be 16-byte aligned, dev_y 4-byte aligned");
+    return EP_ERR_ARG;
+  }
+  ep::LinArgs L;
+  ep::KernelFn fn = nullptr;
+  uint32_t grid = 0, lds = 0;
+  const int rc = linear_plan(host_blob, nbytes, dev_blob, m, L, fn, grid, lds);
+  if (rc != EP_OK || m == 0) return rc;
+  if (L.split > 1u) {
+    const uint64_t need = (uint64_t)L.split * (uint64_t)m * L.n * 4u;
+    if (!dev_workspace || workspace_bytes < need) {
+      // no room for the partial sums: one workgroup per output block instead
+      L.split = 1;
+      L.cps = L.chunks;
+      grid = L.grid = L.mb_n * L.nb_n;
+    } else {
+      L.part = reinterpret_cast<float *>(dev_workspace);
+    }
+  }
   L.x = reinterpret_cast<const uint16_t *>(dev_x);
   L.y = dev_y;
   L.y_f32 = y_dtype == EP_F32 ? 1u : 0u;

@@ -30,7 +30,8 @@ _CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
 
 EXPORTS = ["ep_compress", "ep_compress_ex", "ep_compress_device", "ep_compress_device_noalloc", "ep_free",
            "ep_decompress", "ep_decode_symbols", "ep_actual_bpp", "ep_storage_nbytes", "ep_blob_info", "ep_last_error",
-           "ep_last_encode_count", "ep_plan_create", "ep_plan_decompress", "ep_plan_free", "ep_linear"]
+           "ep_last_encode_count", "ep_plan_create", "ep_plan_decompress", "ep_plan_free", "ep_linear",
+           "ep_linear_workspace_bytes"]
 
 
 class EPError(RuntimeError):
@@ -97,7 +98,9 @@ def lib() -> ctypes.CDLL:
         L.ep_plan_free.argtypes = [ctypes.c_void_p]
         L.ep_plan_free.restype = None
         L.ep_linear.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+                                ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.ep_linear_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64]
+        L.ep_linear_workspace_bytes.restype = ctypes.c_int64
         L.ep_last_encode_count.argtypes = []
         L.ep_last_encode_count.restype = ctypes.c_int64
         _lib = L
@@ -295,11 +298,18 @@ def from_blob(blob: np.ndarray) -> Packed:
                   shape=(d["rows"], d["cols"]), dtype=_CODE_DTYPE[d["dtype"]])
 
 
+def linear_workspace_bytes(p: Packed, m: int) -> int:
+    """ep_linear_workspace_bytes: device scratch ep_linear uses for m rows."""
+    return _check(lib().ep_linear_workspace_bytes(_host_ptr(p.blob), p.blob.size, m), "ep_linear_workspace_bytes")
+
+
 def linear(p: Packed, x: torch.Tensor, out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
-           stream=None) -> torch.Tensor:
+           stream=None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """ep_linear: Y = X W^T with W decoded inside the product (p: a BF16
     stream in the blocks layout, on the device; x: BF16, m x cols of W, on
-    the same device).  Y is m x rows of W, BF16 or FP32."""
+    the same device).  Y is m x rows of W, BF16 or FP32.  workspace: a
+    device tensor of at least linear_workspace_bytes(p, m) bytes (allocated
+    here when None and needed; pass an empty tensor to forbid the split)."""
     if p.dev is None:
         raise EPError(ERR_ARG, "linear", "stream is not on a device; call Packed.to('cuda') first")
     rows, cols = p.shape
@@ -312,9 +322,15 @@ def linear(p: Packed, x: torch.Tensor, out: torch.Tensor | None = None, out_dtyp
         out = torch.empty(m, rows, dtype=out_dtype, device=p.dev.device)
     if out.dtype != out_dtype or tuple(out.shape) != (m, rows) or not out.is_contiguous():
         raise EPError(ERR_ARG, "linear", "out must be a contiguous m x rows tensor of out_dtype")
+    if workspace is None:
+        need = linear_workspace_bytes(p, m)
+        workspace = torch.empty(need, dtype=torch.uint8, device=p.dev.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     rc = lib().ep_linear(_host_ptr(p.blob), p.blob.size, ctypes.c_void_p(p.dev.data_ptr()),
                          ctypes.c_void_p(x.data_ptr() if m else 0), m,
                          ctypes.c_void_p(out.data_ptr() if m else 0),
-                         F32 if out_dtype == torch.float32 else BF16, ctypes.c_void_p(_stream_handle(stream)))
+                         F32 if out_dtype == torch.float32 else BF16,
+                         ctypes.c_void_p(workspace.data_ptr() if ws_bytes else 0), ws_bytes,
+                         ctypes.c_void_p(_stream_handle(stream)))
     _check(rc, "ep_linear")
     return out

@@ -10,17 +10,19 @@ calls hipBLASLt):
 * decode + GEMM: each weight decoded from its stream into one scratch buffer
   right before its GEMM;
 * decode ahead: the same on two streams with two scratch buffers: weight j+1
-  is decoded on a second stream while the GEMM of weight j runs.
+  is decoded on a second stream while the GEMM of weight j runs;
+* fused: ep_linear on streams in the blocks layout (64 x 64 weight blocks),
+  each block decoded into LDS and multiplied there by the BF16 matrix cores;
+  no decoded weight reaches global memory.
 
 Shapes: four 3840 x 3840 projections, 10240 x 3840 (up) and 3840 x 10240
 (down), as (out, in); X is 4096 x 3840 (4096 x 10240 for the down
 projection).  Weights N(0, 0.02^2), seeds 5000 + j; activations N(0, 1), seed
 4999; weights compressed at 4.0 bits per parameter by the library's encoder.
 
-    python -m decode_tile_interleaved_amd.linear_bench [--steps K] [--blocks B]
+    python -m decode_tile_interleaved_amd.linear_bench [--steps K] [--blocks B] [--tokens M]
 
-Prints one JSON line.  The decode of a block's weights is what a fused
-decode-into-MFMA kernel would hide; this script is the unfused baseline.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--blocks", type=int, default=4,
                     help="distinct blocks, replayed in turn, so that weights and streams come from HBM")
+    ap.add_argument("--tokens", type=int, default=4096, help="rows of X (prefill tokens)")
     args = ap.parse_args()
 
     import torch
@@ -53,8 +56,9 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     target = 4.0
-    x_in = W.dit_activation(3840).to(dev)
-    x_down = W.dit_activation(10240).to(dev)
+    M = args.tokens
+    x_in = W.dit_activation(3840)[:M].contiguous().to(dev)
+    x_down = W.dit_activation(10240)[:M].contiguous().to(dev)
     blocks = []
     enc_s = 0.0
     for b in range(args.blocks):
@@ -64,11 +68,12 @@ def main() -> int:
             t0 = time.perf_counter()
             p = ep.compress(w, target)
             enc_s += time.perf_counter() - t0
-            mats.append((w.to(dev), p.to(dev)))
+            pb = ep.compress(w, target, layout=ep.LAYOUT_BLOCKS)
+            mats.append((w.to(dev), p.to(dev), pb.to(dev)))
         blocks.append(mats)
     scratch = torch.empty(max(r * c for r, c in W.DIT_SHAPES), dtype=torch.bfloat16, device=dev)
     scratch2 = [torch.empty(max(r * c for r, c in W.DIT_SHAPES), dtype=torch.bfloat16, device=dev) for _ in range(2)]
-    outs = [torch.empty(4096, r, dtype=torch.bfloat16, device=dev) for r, _ in W.DIT_SHAPES]
+    outs = [torch.empty(M, r, dtype=torch.bfloat16, device=dev) for r, _ in W.DIT_SHAPES]
     stream = torch.cuda.Stream()
     side = torch.cuda.Stream()
 
@@ -76,11 +81,15 @@ def main() -> int:
         return x_down if W.DIT_SHAPES[j][1] == 10240 else x_in
 
     def gemm_block(b):
-        for j, (w, _) in enumerate(blocks[b]):
+        for j, (w, _, _) in enumerate(blocks[b]):
             torch.mm(x_for(j), w.t(), out=outs[j])
 
+    def fused_block(b):
+        for j, (_, _, pb) in enumerate(blocks[b]):
+            ep.linear(pb, x_for(j), out=outs[j], stream=stream)
+
     def decode_gemm_block(b):
-        for j, (_, p) in enumerate(blocks[b]):
+        for j, (_, p, _) in enumerate(blocks[b]):
             r, c = W.DIT_SHAPES[j]
             w = scratch[: r * c].view(r, c)
             ep.decompress(p, out=w, stream=stream)
@@ -89,7 +98,7 @@ def main() -> int:
     def decode_ahead_run(b):
         mats = blocks[b]
         gemm_done = []
-        for j, (_, p) in enumerate(mats):
+        for j, (_, p, _) in enumerate(mats):
             r, c = W.DIT_SHAPES[j]
             w = scratch2[j % 2][: r * c].view(r, c)
             with torch.cuda.stream(side):
@@ -111,20 +120,16 @@ def main() -> int:
         stream.wait_stream(side)
 
     def decode_block(b):
-        for j, (_, p) in enumerate(blocks[b]):
+        for j, (_, p, _) in enumerate(blocks[b]):
             r, c = W.DIT_SHAPES[j]
             ep.decompress(p, out=scratch[: r * c].view(r, c), stream=stream)
 
     # the decoded weights equal the resident ones (rANS is lossless up to the
     # lattice; the resident copy is the decoder's own output here)
-    with torch.cuda.stream(stream):
-        for j, (w, p) in enumerate(blocks[0]):
-            blocks[0][j] = (ep.decompress(p, stream=stream), p)
-    stream.synchronize()
-    for b in range(1, args.blocks):
+    for b in range(args.blocks):
         with torch.cuda.stream(stream):
-            for j, (w, p) in enumerate(blocks[b]):
-                blocks[b][j] = (ep.decompress(p, stream=stream), p)
+            for j, (w, p, pb) in enumerate(blocks[b]):
+                blocks[b][j] = (ep.decompress(p, stream=stream), p, pb)
     stream.synchronize()
 
     def timed(fn):
@@ -160,24 +165,36 @@ def main() -> int:
     t_dec = timed(decode_block)
     t_both = timed(decode_gemm_block)
     t_ahead = timed(decode_ahead_run)
+    t_fused = timed(fused_block)
+    # the fused product against X times its own stream's decoded weights
+    # (FP32 accumulation in another order, each rounded to BF16: a few ulps)
+    with torch.cuda.stream(stream):
+        fused_block(0)
+        fused_out = [o.float() for o in outs]
+        ref_f = [torch.mm(x_for(j).float(), ep.decompress(pb, stream=stream).float().t())
+                 for j, (_, _, pb) in enumerate(blocks[0])]
+    stream.synchronize()
+    fused_rel = max(float((o - r).abs().max() / r.abs().max()) for o, r in zip(fused_out, ref_f))
     with torch.cuda.stream(stream):
         decode_ahead_run(0)
-        ref2 = [torch.mm(x_for(j), w.t()) for j, (w, _) in enumerate(blocks[0])]
+        ref2 = [torch.mm(x_for(j), w.t()) for j, (w, _, _) in enumerate(blocks[0])]
     torch.cuda.synchronize()
     same_ahead = all(torch.equal(o, r) for o, r in zip(outs, ref2))
     # the decoded-then-multiplied result equals the product with the decoded
     # weight held resident
     with torch.cuda.stream(stream):
         decode_gemm_block(0)
-        ref = [torch.mm(x_for(j), w.t()) for j, (w, _) in enumerate(blocks[0])]
+        ref = [torch.mm(x_for(j), w.t()) for j, (w, _, _) in enumerate(blocks[0])]
     stream.synchronize()
     same = all(torch.equal(o, r) for o, r in zip(outs, ref))
 
-    flops = sum(2 * 4096 * r * c for r, c in W.DIT_SHAPES)
+    flops = sum(2 * M * r * c for r, c in W.DIT_SHAPES)
     params = sum(r * c for r, c in W.DIT_SHAPES)
-    stream_bytes = sum(p.nbytes for _, p in blocks[0])
+    stream_bytes = sum(p.nbytes for _, p, _ in blocks[0])
+    blocks_bytes = sum(pb.nbytes for _, _, pb in blocks[0])
     line = {
-        "metric": "DiT block prefill (6 linears, 4096 tokens): decode + GEMM vs GEMM with resident BF16 weights",
+        "metric": f"DiT block prefill (6 linears, {M} tokens): fused decode+MFMA and decode + GEMM vs GEMM with "
+                  "resident BF16 weights",
         "unit": "ms per block",
         "gemm_only_ms": round(t_gemm, 4),
         "decode_only_ms": round(t_dec, 4),
@@ -186,6 +203,13 @@ def main() -> int:
         "decode_ahead_ms": round(t_ahead, 4),
         "decode_ahead_overhead_pct": round(100.0 * (t_ahead - t_gemm) / t_gemm, 2),
         "decode_ahead_outputs_equal": same_ahead,
+        "fused_ms": round(t_fused, 4),
+        "fused_overhead_pct": round(100.0 * (t_fused - t_gemm) / t_gemm, 2),
+        "fused_tflops": round(flops / (t_fused * 1e-3) / 1e12, 1),
+        "fused_max_rel_diff": fused_rel,
+        "blocks_stream_bytes": blocks_bytes,
+        "blocks_actual_bpp": round(8 * blocks_bytes / params, 4),
+        "tokens": M,
         "gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
         "decode_gparams_s": round(params / (t_dec * 1e-3) / 1e9, 1),
         "weights_bf16_bytes": 2 * params,

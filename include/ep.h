@@ -268,16 +268,32 @@ int ep_blob_info(const uint8_t *blob, size_t nbytes, struct ep_info *info);
  *   dev_y      : Y, m x N row-major, device memory, 4-byte aligned; dtype
  *                y_dtype: EP_F32, or EP_BF16 (FP32 sums rounded to nearest
  *                even).  Caller-owned; fully overwritten.
- *   hip_stream : hipStream_t the kernel is enqueued on (NULL = default).
+ *   dev_workspace, workspace_bytes : device scratch for partial sums, 16-byte
+ *                aligned, caller-owned, contents ignored and overwritten; at
+ *                least ep_linear_workspace_bytes(host_blob, nbytes, m) bytes
+ *                lets the call split the sum over K across workgroups when
+ *                the output has fewer 64-column blocks than the GPU has
+ *                compute units (small m), so that every CU decodes; the
+ *                partial sums are then added in a fixed order by a second
+ *                kernel.  NULL or too small: no split, one workgroup per
+ *                output block (the last bits may differ from a split call's;
+ *                both sum in FP32 in a fixed order).
+ *   hip_stream : hipStream_t the kernels are enqueued on (NULL = default).
  * Allocates nothing, does not synchronize.  The sum over K runs in a fixed
- * order (64-column blocks ascending, 32 columns per matrix-core step), so
- * results are deterministic.  Returns EP_OK; EP_ERR_ARG for a raw or
- * row-major stream, a bad y_dtype, a null or misaligned pointer;
- * EP_ERR_SHAPE for m outside [0, 2^31); EP_ERR_FORMAT for a corrupt stream;
- * EP_ERR_DEVICE if the launch fails.
+ * order for a given m and workspace (64-column blocks ascending within each
+ * split, 32 columns per matrix-core step, splits added in order), so results
+ * are deterministic.  Returns EP_OK; EP_ERR_ARG for a raw or row-major
+ * stream, a bad y_dtype, a null or misaligned pointer; EP_ERR_SHAPE for m
+ * outside [0, 2^31); EP_ERR_FORMAT for a corrupt stream; EP_ERR_DEVICE if a
+ * launch fails.  Calls that share a workspace must not overlap.
  */
 int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, const void *dev_x, int64_t m,
-              void *dev_y, int y_dtype, void *hip_stream);
+              void *dev_y, int y_dtype, void *dev_workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Workspace bytes ep_linear uses for m rows of X on this device (0: it does
+ * not split), or a negative ep_status for a stream ep_linear refuses.  Needs
+ * no GPU work; reads the device's compute-unit count. */
+int64_t ep_linear_workspace_bytes(const uint8_t *host_blob, size_t nbytes, int64_t m);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char *ep_last_error(void);

@@ -405,7 +405,7 @@ def test_blocks_layout_rules_and_linear_argument_errors():
     dev, xd, yd = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 28)
 
     def lin(p, x_, m, y_, ydt, dev_=dev):
-        return L.ep_linear(p.blob.ctypes.data, p.blob.size, dev_, x_, m, y_, ydt, None)
+        return L.ep_linear(p.blob.ctypes.data, p.blob.size, dev_, x_, m, y_, ydt, None, 0, None)
     assert lin(pr, xd, 4, yd, ep.BF16) == ep.ERR_ARG and "blocks layout" in ep.last_error()
     assert lin(pb, xd, 4, yd, ep.FP16) == ep.ERR_ARG
     assert lin(pb, xd, -1, yd, ep.F32) == ep.ERR_SHAPE
@@ -416,7 +416,13 @@ def test_blocks_layout_rules_and_linear_argument_errors():
     assert lin(pb, xd, 4, yd, ep.F32, dev_=None) == ep.ERR_ARG
     bad = pb.blob.copy()
     bad[0] ^= 1
-    assert L.ep_linear(bad.ctypes.data, bad.size, dev, xd, 4, yd, ep.F32, None) == ep.ERR_FORMAT
+    assert L.ep_linear(bad.ctypes.data, bad.size, dev, xd, 4, yd, ep.F32, None, 0, None) == ep.ERR_FORMAT
+    # workspace size: 0 rows need none; a row-major stream is refused; a
+    # small output on a big GPU splits
+    assert L.ep_linear_workspace_bytes(pb.blob.ctypes.data, pb.blob.size, 0) == 0
+    assert L.ep_linear_workspace_bytes(pr.blob.ctypes.data, pr.blob.size, 4) == ep.ERR_ARG
+    ws = L.ep_linear_workspace_bytes(pb.blob.ctypes.data, pb.blob.size, 4)
+    assert ws >= 0 and ws % (4 * 4 * 200) == 0
     # a decode plan of a blocks stream records its launch without a GPU
     plan = ctypes.c_void_p()
     assert L.ep_plan_create(pb.blob.ctypes.data, pb.blob.size, dev, -1, ctypes.byref(plan)) == ep.OK

@@ -159,3 +159,29 @@ def test_linear_dit_prefill_sampled_rows(j):
     rows = np.sort(np.random.default_rng(j).choice(4096, 96, replace=False))
     rows = np.unique(np.append(rows, 4095))
     check_linear(y, x, w64, rows_idx=rows, what=f"dit {j}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 100])
+def test_linear_split_k_matches_unsplit_bound_and_is_deterministic(m):
+    """Small m: the sum over K is split across workgroups (partials added in
+    slab order by a second kernel).  Split and unsplit results both lie
+    within the FP32 summation bound of the float64 product; repeated split
+    calls give identical bits."""
+    w = W.dit_matrix(1, 0)
+    blob, rc, _ = oracle.compress(w, 4.0, layout=oracle.LAYOUT_BLOCKS)
+    assert rc == 0
+    w64 = oracle_weights(blob)
+    x = W.gaussian(m, 3840, 1.0, seed=77 + m, dtype=torch.bfloat16)
+    p = ep.from_blob(blob).to("cuda")
+    need = ep.linear_workspace_bytes(p, m)
+    print(f"split-K m={m}: workspace {need} bytes", flush=True)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    xd = x.to("cuda")
+    y1 = ep.linear(p, xd, out_dtype=torch.float32, workspace=ws)
+    y2 = ep.linear(p, xd, out_dtype=torch.float32, workspace=ws)
+    y0 = ep.linear(p, xd, out_dtype=torch.float32, workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    check_linear(y1, x, w64, what=f"split m={m}")
+    check_linear(y0, x, w64, what=f"unsplit m={m}")
