@@ -967,8 +967,10 @@ struct LinArgs {
   uint32_t slots_off;      // LDS byte offset of the block slots
   uint32_t y_f32;          // GEMM: Y is FP32 (1) or BF16 (0)
   uint32_t grid;           // workgroups
-  uint32_t split, cps;     // GEMM: workgroups per output block along K; chunks each
+  uint32_t split, cps;     // GEMM: workgroups per output block along K; chunks (K-blocks for
+                           // linear_waves_kernel) each
   float *part;             // split > 1: FP32 partial sums, split x M x N
+  uint32_t waves_kernel;   // nonzero: the plan launches linear_waves_kernel with this many waves
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1253,6 +1255,134 @@ __global__ void __launch_bounds__(64 * kLinWaves) linear_kernel(LinArgs P) {
             reinterpret_cast<uint16_t *>(P.y)[at] = (uint16_t)(pack2<EP_BF16>(acc[i][j][r], 0.0f) & 0xffffu);
         }
     }
+  }
+}
+
+// Few rows of X (m <= 16 RB, RB <= 2): every wave works on its own.  A
+// workgroup of 16 waves owns one block row of W (64 output columns) and a
+// range of K-blocks; wave w decodes blocks w, w + 16, ... of the range, each
+// from its own copy of the block's words, with nothing shared but the
+// tables.  Every two decode steps give 16 consecutive rows of the block;
+// the wave stages them in its own 16 x 144-byte LDS area, reads them back
+// as B fragments (no other wave touches the area, and one wave's LDS
+// accesses complete in order) and multiplies them by its A fragments of X
+// right away.  After the last block the 16 waves' FP32 sums are added in a
+// fixed tree order in LDS and wave 0 writes Y or the split's partial slab.
+// Without slots shared by all waves, 16 waves fit beside the tables: the
+// decode runs at the width of the standalone decoder.
+constexpr int kLwWaves = 16;
+constexpr uint32_t kStageBytes = 16 * kSlotRowBytes;
+constexpr uint32_t kCbBytes = 4 * 1024;  // one wave's sums of a 16-row block of X: 4 x 16 x 16 FP32
+
+// NW waves per workgroup: 16 for RB <= 2, 8 for RB = 4 (two waves per SIMD
+// leave room for four row blocks' sums and fragments)
+template <bool WIDE, int RB, int NW>
+__global__ void __launch_bounds__(64 * NW) linear_waves_kernel(LinArgs P) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const Args &A = P.a;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t L = xcd_logical(blockIdx.x, P.grid);
+  const uint32_t nb = L / P.split, sp = L - nb * P.split;
+  const uint32_t kb_lo = sp * P.cps, kb_hi = min(kb_lo + P.cps, P.kb_n);
+  typedef __attribute__((address_space(4))) const uint32_t *cptr_u32;
+  const cptr_u32 toff = (cptr_u32)A.toff;
+  if (wave < (uint32_t)kContexts) {
+    uint32_t fpre[4];
+    first_frequencies(A, wave, lane, fpre);
+    build_tables<WIDE>(A, lds, wave, lane, (uint32_t)kContexts, fpre);
+  }
+  const uint32_t r0 = 64u * nb + (lane >> 3), vcol = lane & 7u, lr = lane & 15u, lk = lane >> 4;
+  float gs[8];
+#pragma unroll
+  for (uint32_t s = 0; s < 8; ++s) gs[s] = A.scales[min(r0 + 8u * s, A.rows - 1u)];
+  uint32_t present_rows = 0;
+#pragma unroll
+  for (uint32_t s = 0; s < 8; ++s) present_rows |= (r0 + 8u * s < A.rows ? 1u : 0u) << s;
+  constexpr int kCb = 4;
+  f32x4 acc[RB][kCb];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < kCb; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t buf = A.words_off + wave * A.wbuf;            // this wave's words
+  const uint32_t stg = P.slots_off + wave * kStageBytes;       // this wave's 16 staged rows
+  const uint32_t put = stg + (lane >> 3) * kSlotRowBytes + 16u * vcol;  // + 8 rows for odd steps
+  const uint32_t get = stg + lr * kSlotRowBytes + 16u * lk;             // + 64 bytes for the upper half of K
+  lds_barrier();  // tables built
+  for (uint32_t kb = kb_lo + wave; kb < kb_hi; kb += (uint32_t)NW) {
+    const uint32_t t = nb * P.kb_n + kb;
+    const uint32_t tb = toff[t], te = toff[t + 1u];
+    const uint32_t c0 = first_piece(tb);
+    copy_pieces(A, lds, c0, end_piece(te), buf, lane, 0u, 1u);
+    u32x4 xa[RB][2];
+    load_x<RB>(P, 0u, 64u * kb, lane, xa);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's words and X fragments have landed
+    const uint32_t wt = buf + 2u * tb - 16u * c0;
+    const uint32_t present = 8u * kb + vcol < A.vpr ? present_rows : 0u;
+    auto sink = [&](uint32_t s, bool act, const uint32_t(&e)[8]) {
+      *(lds_u128_wptr)(uintptr_t)(put + (s & 1u) * 8u * kSlotRowBytes) = block_weights<WIDE>(e, gs[s], act);
+      if (s & 1u) {  // block rows 16 (s / 2) .. + 15 are staged: one product per half of K
+#pragma unroll
+        for (uint32_t h = 0; h < 2u; ++h) {
+          const u32x4 b = *(lds_u128_rptr)(uintptr_t)(get + 64u * h);
+#pragma unroll
+          for (int i = 0; i < RB; ++i)
+            acc[i][s >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[i][h]),
+                                                                     __builtin_bit_cast(bf16x8, b), acc[i][s >> 1], 0,
+                                                                     0, 0);
+        }
+      }
+    };
+    if (__ballot(present != 0xffu) == 0)
+      decode_block<WIDE, true>(wt, wt + 2u * (te - tb), lane, present, sink);
+    else
+      decode_block<WIDE, false>(wt, wt + 2u * (te - tb), lane, present, sink);
+  }
+  // the waves' sums, added in a fixed tree order: at distance d, wave w with
+  // w mod 2d = d stores its sums and wave w - d adds them
+  const uint32_t red = A.words_off;  // the word buffers are no longer read after the next barrier
+#pragma unroll
+  for (uint32_t d = 1; d < (uint32_t)NW; d *= 2u) {
+    lds_barrier();
+    if (wave % (2u * d) == d) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < kCb; ++j)
+          *(__attribute__((address_space(3))) f32x4 *)(uintptr_t)(red + (wave / (2u * d)) * (uint32_t)RB * kCbBytes +
+                                                                  (uint32_t)(i * kCb + j) * 1024u + 16u * lane) =
+              acc[i][j];
+    }
+    lds_barrier();
+    if (wave % (2u * d) == 0u && wave + d < (uint32_t)NW) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < kCb; ++j)
+          acc[i][j] += *(__attribute__((address_space(3))) const f32x4 *)(uintptr_t)(
+              red + (wave / (2u * d)) * (uint32_t)RB * kCbBytes + (uint32_t)(i * kCb + j) * 1024u + 16u * lane);
+    }
+  }
+  if (wave != 0u) return;
+#pragma unroll
+  for (int j = 0; j < kCb; ++j) {
+    const uint32_t col = 64u * nb + 16u * (uint32_t)j + lr;
+    if (col >= P.n) continue;
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (uint32_t r = 0; r < 4u; ++r) {
+        const uint32_t row = 16u * (uint32_t)i + 4u * lk + r;
+        if (row >= P.m) continue;
+        const uint64_t at = (uint64_t)row * P.n + col;
+        if (P.split > 1u)
+          P.part[(uint64_t)sp * P.m * P.n + at] = acc[i][j][r];
+        else if (P.y_f32)
+          reinterpret_cast<float *>(P.y)[at] = acc[i][j][r];
+        else
+          reinterpret_cast<uint16_t *>(P.y)[at] = (uint16_t)(pack2<EP_BF16>(acc[i][j][r], 0.0f) & 0xffffu);
+      }
   }
 }
 
@@ -1650,6 +1780,37 @@ int prepare_linear(const uint8_t *hb, const StreamView &s, const void *dev_blob,
   grid = L.grid;
   lds_bytes = (uint32_t)need;
   fn = pick_linear(mode, wide, rb);
+  // Few rows (m <= 32): the wave-independent kernel, if each wave's word
+  // buffer, its staging rows and the final sums fit the LDS
+  if (mode == kLinGemm && m <= 64) {
+    uint64_t wb1 = 0;
+    for (int64_t t = 0; t < s.tiles; ++t) wb1 = std::max<uint64_t>(wb1, copy_bytes(t, t + 1));
+    const int rbw = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+    const int64_t nw = rbw == 4 ? 8 : kLwWaves;
+    const uint64_t stg = align16(A.words_off + (uint64_t)nw * wb1 + kLdsPad);
+    const uint64_t need_w = std::max<uint64_t>(stg + (uint64_t)nw * kStageBytes,
+                                               (uint64_t)A.words_off + (uint64_t)(nw / 2) * rbw * kCbBytes);
+    if (need_w <= kLdsLimit) {
+      L.a.wbuf = (uint32_t)wb1;
+      L.slots_off = (uint32_t)stg;
+      // splits of K: about one workgroup per CU, at least one block per wave
+      const uint64_t sp = std::max<int64_t>(
+          1, std::min<int64_t>(num_cus() / std::max<int64_t>(nb_n, 1), (kb_n + nw - 1) / nw));
+      L.cps = (uint32_t)((kb_n + (int64_t)sp - 1) / (int64_t)sp);
+      L.split = (uint32_t)((kb_n + L.cps - 1) / L.cps);
+      L.mb_n = 1;
+      L.grid = (uint32_t)((uint64_t)nb_n * L.split);
+      grid = L.grid;
+      lds_bytes = (uint32_t)need_w;
+      L.waves_kernel = (uint32_t)nw;
+      if (rbw == 1)
+        fn = wide ? (KernelFn)linear_waves_kernel<true, 1, kLwWaves> : (KernelFn)linear_waves_kernel<false, 1, kLwWaves>;
+      else if (rbw == 2)
+        fn = wide ? (KernelFn)linear_waves_kernel<true, 2, kLwWaves> : (KernelFn)linear_waves_kernel<false, 2, kLwWaves>;
+      else
+        fn = wide ? (KernelFn)linear_waves_kernel<true, 4, 8> : (KernelFn)linear_waves_kernel<false, 4, 8>;
+    }
+  }
   return EP_OK;
 }
 
@@ -1671,7 +1832,9 @@ int launch_linear(KernelFn fn, const LinArgs &L, uint32_t grid, uint32_t lds_byt
   }
   LinArgs a = L;
   void *args[1] = {&a};
-  hipError_t err = hipLaunchKernel(fn, dim3(grid), dim3(64 * kLinWaves), args, lds_bytes, stream);
+  hipError_t err =
+      hipLaunchKernel(fn, dim3(grid), dim3(64 * (L.waves_kernel ? L.waves_kernel : (uint32_t)kLinWaves)), args,
+                      lds_bytes, stream);
   if (err == hipSuccess) err = hipGetLastError();
   if (err == hipSuccess && L.split > 1u) {
     const uint64_t mn = (uint64_t)L.m * L.n;
@@ -1900,7 +2063,7 @@ int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, con
     if (!dev_workspace || workspace_bytes < need) {
       // no room for the partial sums: one workgroup per output block instead
       L.split = 1;
-      L.cps = L.chunks;
+      L.cps = L.waves_kernel ? L.kb_n : L.chunks;
       grid = L.grid = L.mb_n * L.nb_n;
     } else {
       L.part = reinterpret_cast<float *>(dev_workspace);

@@ -98,6 +98,11 @@ def test_blocks_decode_matches_oracle(rows, cols, target):
     (300, 257, 72, 5.0),       # one row past a block; K one vector past a block
     (1000, 384, 640, 4.0),     # several chunks of K, m over 512
     (520, 64, 4104, 2.75),     # K: eight full chunks and one vector
+    (32, 257, 520, 3.0),       # few rows (wave-independent kernel), ragged N and K
+    (17, 64, 4104, 2.75),      # few rows, several blocks per wave, one vector past a block
+    (16, 1000, 1032, 4.0),     # few rows, many block rows
+    (64, 200, 2056, 3.0),      # up to 64 rows: four row blocks per wave
+    (45, 130, 136, 4.0),       # ragged rows inside the last row block
 ])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_linear_matches_fp64_product(m, rows, cols, target, out_dtype):
