@@ -2038,6 +2038,49 @@ int64_t ep_linear_workspace_bytes(const uint8_t *host_blob, size_t nbytes, int64
   return (m > 0 && L.split > 1u) ? (int64_t)L.split * m * (int64_t)L.n * 4 : 0;
 }
 
+// a planned fused linear
+struct ep_linear_plan {
+  ep::LinArgs L{};
+  ep::KernelFn fn = nullptr;
+  uint32_t grid = 0, lds = 0;
+  int64_t m = 0;
+};
+
+// enqueues a planned fused linear (m > 0) on X, Y and the workspace
+static int linear_run(const ep_linear_plan &P, const void *dev_x, void *dev_y, int y_dtype, void *dev_workspace,
+                      size_t workspace_bytes, void *hip_stream) {
+  if (y_dtype != EP_BF16 && y_dtype != EP_F32) {
+    ep::set_error("y_dtype must be EP_BF16 or EP_F32");
+    return EP_ERR_ARG;
+  }
+  if (P.m == 0) return EP_OK;
+  if (!dev_x || !dev_y) {
+    ep::set_error("null device pointer");
+    return EP_ERR_ARG;
+  }
+  if (((uintptr_t)dev_x & 15) || ((uintptr_t)dev_y & 3) || ((uintptr_t)dev_workspace & 15)) {
+    ep::set_error("dev_x and dev_workspace must be 16-byte aligned, dev_y 4-byte aligned");
+    return EP_ERR_ARG;
+  }
+  ep::LinArgs L = P.L;
+  uint32_t grid = P.grid;
+  if (L.split > 1u) {
+    const uint64_t need = (uint64_t)L.split * (uint64_t)P.m * L.n * 4u;
+    if (!dev_workspace || workspace_bytes < need) {
+      // no room for the partial sums: one workgroup per output block instead
+      L.split = 1;
+      L.cps = L.waves_kernel ? L.kb_n : L.chunks;
+      grid = L.grid = L.mb_n * L.nb_n;
+    } else {
+      L.part = reinterpret_cast<float *>(dev_workspace);
+    }
+  }
+  L.x = reinterpret_cast<const uint16_t *>(dev_x);
+  L.y = dev_y;
+  L.y_f32 = y_dtype == EP_F32 ? 1u : 0u;
+  return ep::launch_linear(P.fn, L, grid, P.lds, reinterpret_cast<hipStream_t>(hip_stream));
+}
+
 int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, const void *dev_x, int64_t m,
               void *dev_y, int y_dtype, void *dev_workspace, size_t workspace_bytes, void *hip_stream) {
   ep::set_error("");
@@ -2053,26 +2096,55 @@ int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, con
     ep::set_error("dev_x and dev_workspace must be 16-byte aligned, dev_y 4-byte aligned");
     return EP_ERR_ARG;
   }
-  ep::LinArgs L;
-  ep::KernelFn fn = nullptr;
-  uint32_t grid = 0, lds = 0;
-  const int rc = linear_plan(host_blob, nbytes, dev_blob, m, L, fn, grid, lds);
+  ep_linear_plan P;
+  P.m = m;
+  const int rc = linear_plan(host_blob, nbytes, dev_blob, m, P.L, P.fn, P.grid, P.lds);
   if (rc != EP_OK || m == 0) return rc;
-  if (L.split > 1u) {
-    const uint64_t need = (uint64_t)L.split * (uint64_t)m * L.n * 4u;
-    if (!dev_workspace || workspace_bytes < need) {
-      // no room for the partial sums: one workgroup per output block instead
-      L.split = 1;
-      L.cps = L.waves_kernel ? L.kb_n : L.chunks;
-      grid = L.grid = L.mb_n * L.nb_n;
-    } else {
-      L.part = reinterpret_cast<float *>(dev_workspace);
-    }
-  }
-  L.x = reinterpret_cast<const uint16_t *>(dev_x);
-  L.y = dev_y;
-  L.y_f32 = y_dtype == EP_F32 ? 1u : 0u;
-  return ep::launch_linear(fn, L, grid, lds, reinterpret_cast<hipStream_t>(hip_stream));
+  return linear_run(P, dev_x, dev_y, y_dtype, dev_workspace, workspace_bytes, hip_stream);
 }
+
+int ep_linear_plan_create(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, int64_t m,
+                          ep_linear_plan **plan_out) {
+  ep::set_error("");
+  if (!plan_out) {
+    ep::set_error("null plan_out");
+    return EP_ERR_ARG;
+  }
+  *plan_out = nullptr;
+  ep_linear_plan *h = new (std::nothrow) ep_linear_plan;
+  if (!h) {
+    ep::set_error("out of host memory");
+    return EP_ERR_NOMEM;
+  }
+  h->m = m;
+  const int rc = linear_plan(host_blob, nbytes, dev_blob, m, h->L, h->fn, h->grid, h->lds);
+  if (rc != EP_OK) {
+    delete h;
+    return rc;
+  }
+  *plan_out = h;
+  return EP_OK;
+}
+
+int64_t ep_linear_plan_workspace_bytes(const ep_linear_plan *plan) {
+  ep::set_error("");
+  if (!plan) {
+    ep::set_error("null plan");
+    return EP_ERR_ARG;
+  }
+  return (plan->m > 0 && plan->L.split > 1u) ? (int64_t)plan->L.split * plan->m * (int64_t)plan->L.n * 4 : 0;
+}
+
+int ep_linear_plan_run(const ep_linear_plan *plan, const void *dev_x, void *dev_y, int y_dtype, void *dev_workspace,
+                       size_t workspace_bytes, void *hip_stream) {
+  ep::set_error("");
+  if (!plan) {
+    ep::set_error("null plan");
+    return EP_ERR_ARG;
+  }
+  return linear_run(*plan, dev_x, dev_y, y_dtype, dev_workspace, workspace_bytes, hip_stream);
+}
+
+void ep_linear_plan_free(ep_linear_plan *plan) { delete plan; }
 
 }  // extern "C"

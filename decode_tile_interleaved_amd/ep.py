@@ -31,7 +31,8 @@ _CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
 EXPORTS = ["ep_compress", "ep_compress_ex", "ep_compress_device", "ep_compress_device_noalloc", "ep_free",
            "ep_decompress", "ep_decode_symbols", "ep_actual_bpp", "ep_storage_nbytes", "ep_blob_info", "ep_last_error",
            "ep_last_encode_count", "ep_plan_create", "ep_plan_decompress", "ep_plan_free", "ep_linear",
-           "ep_linear_workspace_bytes"]
+           "ep_linear_workspace_bytes", "ep_linear_plan_create", "ep_linear_plan_workspace_bytes", "ep_linear_plan_run",
+           "ep_linear_plan_free"]
 
 
 class EPError(RuntimeError):
@@ -101,6 +102,14 @@ def lib() -> ctypes.CDLL:
                                 ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.ep_linear_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64]
         L.ep_linear_workspace_bytes.restype = ctypes.c_int64
+        L.ep_linear_plan_create.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.POINTER(ctypes.c_void_p)]
+        L.ep_linear_plan_workspace_bytes.argtypes = [ctypes.c_void_p]
+        L.ep_linear_plan_workspace_bytes.restype = ctypes.c_int64
+        L.ep_linear_plan_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.ep_linear_plan_free.argtypes = [ctypes.c_void_p]
+        L.ep_linear_plan_free.restype = None
         L.ep_last_encode_count.argtypes = []
         L.ep_last_encode_count.restype = ctypes.c_int64
         _lib = L
@@ -334,3 +343,41 @@ def linear(p: Packed, x: torch.Tensor, out: torch.Tensor | None = None, out_dtyp
                          ctypes.c_void_p(_stream_handle(stream)))
     _check(rc, "ep_linear")
     return out
+
+
+class LinearPlan:
+    """ep_linear_plan_*: ep_linear on one stream and row count with its host
+    work done once.  Holds a reference to the stream's device copy, which
+    must not be modified while the plan lives, and its own workspace."""
+
+    def __init__(self, p: Packed, m: int):
+        if p.dev is None:
+            raise EPError(ERR_ARG, "linear plan", "stream is not on a device; call Packed.to('cuda') first")
+        self.shape, self.m, self._dev = p.shape, int(m), p.dev
+        h = ctypes.c_void_p()
+        _check(lib().ep_linear_plan_create(_host_ptr(p.blob), p.blob.size, ctypes.c_void_p(p.dev.data_ptr()), self.m,
+                                           ctypes.byref(h)), "ep_linear_plan_create")
+        self._h = h
+        self._free = weakref.finalize(self, lib().ep_linear_plan_free, h)
+        need = _check(lib().ep_linear_plan_workspace_bytes(h), "ep_linear_plan_workspace_bytes")
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=p.dev.device)
+
+    def run(self, x: torch.Tensor, out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+            stream=None) -> torch.Tensor:
+        rows, cols = self.shape
+        if x.dtype != torch.bfloat16 or tuple(x.shape) != (self.m, cols) or not x.is_contiguous():
+            raise EPError(ERR_ARG, "linear plan", "x must be a contiguous BF16 m x cols tensor")
+        if out is None:
+            out = torch.empty(self.m, rows, dtype=out_dtype, device=self._dev.device)
+        if out.dtype != out_dtype or tuple(out.shape) != (self.m, rows) or not out.is_contiguous():
+            raise EPError(ERR_ARG, "linear plan", "out must be a contiguous m x rows tensor of out_dtype")
+        ws = self.workspace
+        _check(lib().ep_linear_plan_run(self._h, ctypes.c_void_p(x.data_ptr() if self.m else 0),
+                                        ctypes.c_void_p(out.data_ptr() if self.m else 0),
+                                        F32 if out_dtype == torch.float32 else BF16,
+                                        ctypes.c_void_p(ws.data_ptr() if ws.numel() else 0), ws.numel(),
+                                        ctypes.c_void_p(_stream_handle(stream))), "ep_linear_plan_run")
+        return out
+
+    def close(self) -> None:
+        self._free()

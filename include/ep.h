@@ -295,6 +295,33 @@ int ep_linear(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, con
  * no GPU work; reads the device's compute-unit count. */
 int64_t ep_linear_workspace_bytes(const uint8_t *host_blob, size_t nbytes, int64_t m);
 
+/*
+ * Linear plans: ep_linear with its host work done once per stream and row
+ * count (the stream's header, tables and every tile offset checked, the
+ * kernel, chunk size, split and grid chosen), for a layer that runs its
+ * compressed weight on every forward call (API reference, "CompressedLinear").
+ * ep_linear_plan_create -- as ep_linear's checks for the stream, dev_blob and
+ *   m (its errors: EP_ERR_FORMAT, EP_ERR_ARG, EP_ERR_SHAPE; EP_ERR_NOMEM);
+ *   plan_out receives the plan (NULL on error).  Launches and allocates
+ *   nothing on the device; sized for the compute units of the current
+ *   device.  The host stream is not read after the call returns.
+ * ep_linear_plan_workspace_bytes -- ep_linear_workspace_bytes for the plan's
+ *   stream and m (EP_ERR_ARG for a NULL plan).
+ * ep_linear_plan_run -- ep_linear on the planned stream with m rows of X:
+ *   dev_x, dev_y, y_dtype, dev_workspace, workspace_bytes and hip_stream as
+ *   for ep_linear; dev_blob must still hold the same bytes.  Never allocates
+ *   and never synchronizes; a plan may be used from several threads at once
+ *   (with separate workspaces).  Results equal ep_linear's bit for bit.
+ * ep_linear_plan_free -- releases a plan; NULL is a no-op.
+ */
+typedef struct ep_linear_plan ep_linear_plan;
+int ep_linear_plan_create(const uint8_t *host_blob, size_t nbytes, const void *dev_blob, int64_t m,
+                          ep_linear_plan **plan_out);
+int64_t ep_linear_plan_workspace_bytes(const ep_linear_plan *plan);
+int ep_linear_plan_run(const ep_linear_plan *plan, const void *dev_x, void *dev_y, int y_dtype, void *dev_workspace,
+                       size_t workspace_bytes, void *hip_stream);
+void ep_linear_plan_free(ep_linear_plan *plan);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char *ep_last_error(void);
 

@@ -427,3 +427,34 @@ def test_blocks_layout_rules_and_linear_argument_errors():
     plan = ctypes.c_void_p()
     assert L.ep_plan_create(pb.blob.ctypes.data, pb.blob.size, dev, -1, ctypes.byref(plan)) == ep.OK
     L.ep_plan_free(plan)
+
+
+def test_linear_plan_arguments_and_errors():
+    """ep_linear_plan_create checks the stream as ep_linear does and needs no
+    GPU (it only records the launch); ep_linear_plan_run rejects a NULL plan
+    or bad pointers before any device call.  The device addresses are never
+    dereferenced on the host."""
+    import ctypes
+    L = ep.lib()
+    pb = ep.compress(W.gaussian(200, 136, 0.02, seed=2), 4.0, layout=ep.LAYOUT_BLOCKS)
+    pr = ep.compress(W.gaussian(200, 136, 0.02, seed=2), 4.0)
+    dev = ctypes.c_void_p(1 << 20)
+    plan = ctypes.c_void_p()
+    for m in (0, 4, 300):
+        assert L.ep_linear_plan_create(pb.blob.ctypes.data, pb.blob.size, dev, m, ctypes.byref(plan)) == ep.OK
+        assert L.ep_linear_plan_workspace_bytes(plan) == L.ep_linear_workspace_bytes(pb.blob.ctypes.data,
+                                                                                      pb.blob.size, m)
+        if m:
+            assert L.ep_linear_plan_run(plan, None, ctypes.c_void_p(1 << 24), ep.F32, None, 0, None) == ep.ERR_ARG
+            assert L.ep_linear_plan_run(plan, ctypes.c_void_p(1 << 24), ctypes.c_void_p(1 << 26), 7, None, 0,
+                                        None) == ep.ERR_ARG
+        L.ep_linear_plan_free(plan)
+    L.ep_linear_plan_free(None)
+    assert L.ep_linear_plan_run(None, dev, dev, ep.F32, None, 0, None) == ep.ERR_ARG
+    assert L.ep_linear_plan_workspace_bytes(None) == ep.ERR_ARG
+    assert L.ep_linear_plan_create(pb.blob.ctypes.data, pb.blob.size, dev, 4, None) == ep.ERR_ARG
+    plan = ctypes.c_void_p(123)
+    assert L.ep_linear_plan_create(pr.blob.ctypes.data, pr.blob.size, dev, 4, ctypes.byref(plan)) == ep.ERR_ARG
+    assert not plan.value
+    assert L.ep_linear_plan_create(pb.blob.ctypes.data, pb.blob.size, dev, -3, ctypes.byref(plan)) == ep.ERR_SHAPE
+    assert L.ep_linear_plan_create(pb.blob.ctypes.data, pb.blob.size, None, 4, ctypes.byref(plan)) == ep.ERR_ARG

@@ -190,3 +190,37 @@ def test_linear_split_k_matches_unsplit_bound_and_is_deterministic(m):
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
     check_linear(y1, x, w64, what=f"split m={m}")
     check_linear(y0, x, w64, what=f"unsplit m={m}")
+
+
+@pytest.mark.parametrize("m", [1, 32, 300])
+def test_linear_plan_matches_call_and_replays_in_a_graph(m):
+    """A linear plan gives ep_linear's bits; captured in a HIP graph it
+    replays exactly, with eager work on the same stream between replays."""
+    w = W.gaussian(384, 1032, 0.02, seed=m + 3, dtype=torch.bfloat16)
+    blob, rc, _ = oracle.compress(w, 4.0, layout=oracle.LAYOUT_BLOCKS)
+    assert rc == 0
+    print(f"linear plan m={m}", flush=True)
+    p = ep.from_blob(blob).to("cuda")
+    x = W.gaussian(m, 1032, 1.0, seed=m, dtype=torch.bfloat16).cuda()
+    plan = ep.LinearPlan(p, m)
+    ws = torch.empty(ep.linear_workspace_bytes(p, m), dtype=torch.uint8, device="cuda")
+    ref = ep.linear(p, x, out_dtype=torch.float32, workspace=ws)
+    got = plan.run(x, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    s = torch.cuda.Stream()
+    y = torch.empty(m, 384, dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        plan.run(x, out=y, out_dtype=torch.float32, stream=s)  # eager pass on the capture stream
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        plan.run(x, out=y, out_dtype=torch.float32, stream=s)
+    for i in range(3):
+        with torch.cuda.stream(s):
+            y.fill_(float("nan"))
+            junk = torch.randn(257, 259, device="cuda") @ torch.randn(259, 263, device="cuda")
+            g.replay()
+        s.synchronize()
+        assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), f"replay {i}"
+        del junk
