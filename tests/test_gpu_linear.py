@@ -224,3 +224,38 @@ def test_linear_plan_matches_call_and_replays_in_a_graph(m):
         s.synchronize()
         assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), f"replay {i}"
         del junk
+
+
+@pytest.mark.parametrize("m", [0, 16, 300])
+def test_corrupt_words_blocks_stream_within_bounds(m):
+    """A blocks-layout stream whose whole word section is random bytes (pair
+    counts, length codes and start bits included): the host checks the
+    header, tables and tile offsets but not the words.  Decode and the fused
+    linear (the wave-independent kernel at 16 rows, the chunk kernel at 300)
+    still complete: each lane's word pointer starts clamped into its tile and
+    moves at most one word per symbol (64 per lane), inside the LDS slack
+    after the word buffers or the words and tables before them; table
+    addresses are masked into the tables.  Coordinates stay in the value
+    range, the products are finite, and a clean call right after is exact."""
+    w = W.gaussian(200, 1032, 0.02, seed=8300, dtype=torch.bfloat16)
+    blob, rc, _ = oracle.compress(w, 4.0, layout=oracle.LAYOUT_BLOCKS)
+    assert rc == 0
+    n_words = ep.blob_info(blob)["n_words"]
+    o_w = blob.size - (2 * n_words + 15) // 16 * 16  # the word section ends the stream
+    bad = blob.copy()
+    bad[o_w:o_w + 2 * n_words] = np.random.default_rng(8301 + m).integers(0, 256, 2 * n_words, dtype=np.uint8)
+    print(f"corrupt blocks stream, m={m}", flush=True)
+    pb = ep.from_blob(bad).to("cuda")
+    v = ep.decode_symbols(pb)
+    yw = ep.decompress(pb)
+    x = W.gaussian(max(m, 1), 1032, 1.0, seed=m, dtype=torch.bfloat16).cuda()
+    yl = ep.linear(pb, x, out_dtype=torch.float32) if m else None
+    torch.cuda.synchronize()
+    assert int(v.abs().max()) <= 2047
+    assert bool(torch.isfinite(yw.float()).all())
+    if m:
+        assert bool(torch.isfinite(yl).all())
+    p = ep.from_blob(blob).to("cuda")
+    y2 = ep.decompress(p)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().view(torch.int16).numpy(), oracle.decompress_raw(blob).view(np.int16))
